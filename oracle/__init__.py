@@ -1,0 +1,25 @@
+"""CPU oracle for paged varlen attention and the paged KV store.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or execute anything in this
+package.  The product path (``attention_kv_store_amd``) never does, and it shares
+no code, constants or helpers with this package.
+
+Every function here is a plain numpy float64 transcription of what the pages
+define, with no tiling, fusion or reordering beyond that definition:
+
+* ``attention_oracle`` -- softmax(scale * Q K^T + mask) V with the full score rows
+  materialised, as in the naive schedule of Transformer 추론 커널 (3/10), §10
+  (equation for O), gathered through the block table of §14.
+* ``kv_store_oracle`` -- the scatter of new K/V rows into their slots
+  (Transformer 추론 커널 (3/10), §2 "RoPE + KV cache store" step; slot = block *
+  page_size + offset per 장부가 커널 인자로 바뀌는 지점과 CUDA graph, page-table part).
+* ``lse_merge`` -- the stable merge of partial results over disjoint key sets
+  (Transformer 추론 커널 (3/10), §12 equations for m_new / l_new, and §16).
+
+Pins (tests/test_oracle_pins.py) tie every function to something other than
+itself: closed forms, invariants, a multi-precision brute force and CPU torch
+SDPA.  The readings taken where the pages are silent are listed in the design doc.
+"""
+from .attention import attention_oracle, gather_sequence, lse_merge, BLOCK_SIZE  # noqa: F401
+from .store import kv_store_oracle  # noqa: F401
