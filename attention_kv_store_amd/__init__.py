@@ -1,0 +1,120 @@
+"""MI355X (gfx950) paged varlen attention and KV store.
+
+Python names mirror the C ABI (include/kvstore.h):
+
+* ``kv_store_paged(k_new, v_new, slot_mapping, k_cache, v_cache)``
+* ``attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
+  scale, causal, out=None, lse=None, ...)``
+
+They take torch tensors on the current HIP device (torch supplies memory and
+the stream) and enqueue the library's kernels on torch's current stream.  The
+binding marshals arguments only; every step runs in the HIP kernels, and a
+missing library is an error, never a fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from . import _lib
+from ._lib import KVS_BF16, KVS_F32, KVS_I32, KvsError, KvsHints, describe, last_dispatch  # noqa: F401
+
+__all__ = ["kv_store_paged", "attn_varlen_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    m = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16, torch.int32: KVS_I32}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _desc(t):
+    if t is None:
+        return None
+    return describe(t.data_ptr(), _dtype_code(t), list(t.shape), list(t.stride()))
+
+
+def _ref(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+def _stream(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def kv_store_paged(k_new, v_new, slot_mapping, k_cache, v_cache) -> None:
+    """Write row t of k_new/v_new [T, Hkv, D] into slot slot_mapping[t] of the
+    [NB, 16, Hkv, D] pools (negative slots are skipped), in place."""
+    lib = _lib.load()
+    d = [_desc(x) for x in (k_new, v_new, slot_mapping, k_cache, v_cache)]
+    _lib.check(lib.kv_store_paged(*[_ref(x) for x in d], _stream(k_cache)))
+
+
+def _hints(max_seqlen_q=0, max_seqlen_k=0, num_splits=0):
+    h = KvsHints()
+    h.max_seqlen_q = int(max_seqlen_q or 0)
+    h.max_seqlen_k = int(max_seqlen_k or 0)
+    h.num_splits = int(num_splits or 0)
+    return h
+
+
+def workspace_size(q, k_cache, block_table, *, max_seqlen_q=0, max_seqlen_k=0, num_splits=0) -> int:
+    lib = _lib.load()
+    h = _hints(max_seqlen_q, max_seqlen_k, num_splits)
+    n = lib.attn_varlen_paged_workspace_size(_ref(_desc(q)), _ref(_desc(k_cache)), _ref(_desc(block_table)),
+                                             ctypes.byref(h))
+    if n == ctypes.c_size_t(-1).value:
+        raise KvsError(_lib.KVS_ERR_INVALID, lib.kvs_last_error().decode())
+    return int(n)
+
+
+def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale: float,
+                      causal: bool = True, out=None, lse=None, *, return_lse: bool = True,
+                      max_seqlen_q: int = 0, max_seqlen_k: int = 0, num_splits: int = 0,
+                      workspace=None):
+    """Exact paged varlen attention.  Returns ``(out, lse)`` (lse is None when
+    ``return_lse`` is False and no ``lse`` tensor was given).
+
+    Uses the allocation-free ``attn_varlen_paged_ex`` entry point with a
+    torch-allocated workspace (or the one passed in)."""
+    import torch
+
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    h = _hints(max_seqlen_q, max_seqlen_k, num_splits)
+    dq, dk, dt_ = _desc(q), _desc(k_cache), _desc(block_table)
+    need = lib.attn_varlen_paged_workspace_size(_ref(dq), _ref(dk), _ref(dt_), ctypes.byref(h))
+    if need == ctypes.c_size_t(-1).value:
+        raise KvsError(_lib.KVS_ERR_INVALID, lib.kvs_last_error().decode())
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    d = [dq, dk, _desc(v_cache), dt_, _desc(cu_seqlens_q), _desc(seqlens_k)]
+    st = lib.attn_varlen_paged_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)),
+                                  _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
+                                  _stream(q))
+    _lib.check(st)
+    return out, lse
+
+
+def attn_varlen_paged_plain(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale: float,
+                            causal: bool, out, lse=None) -> None:
+    """The plain ``attn_varlen_paged`` entry point (library-owned scratch)."""
+    lib = _lib.load()
+    d = [_desc(x) for x in (q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k)]
+    st = lib.attn_varlen_paged(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)),
+                               _ref(_desc(out)), _ref(_desc(lse)), _stream(q))
+    _lib.check(st)
+
+
+def release_workspace() -> None:
+    _lib.check(_lib.load().kvs_release_workspace())

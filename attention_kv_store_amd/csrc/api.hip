@@ -1,0 +1,357 @@
+// extern "C" entry points of libkvstore.so: host-side validation, dispatch
+// planning and launches.  Validation touches no device memory and makes no HIP
+// call, so every error path can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/kvstore.h"
+#include "kvs_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local std::string g_dispatch;
+
+kvs_status fail(kvs_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+void set_dispatch(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_dispatch = buf;
+}
+
+const char* dtname(int dt) {
+  switch (dt) {
+    case KVS_F32: return "f32";
+    case KVS_BF16: return "bf16";
+    case KVS_I32: return "i32";
+    default: return "?";
+  }
+}
+
+int esize(int dt) { return dt == KVS_BF16 ? 2 : 4; }
+
+// Checks a descriptor: present, dtype in `allowed` (bitmask of 1 << dtype),
+// rank, dense row-major strides, alignment.  Returns KVS_OK or sets g_err.
+kvs_status check_tensor(const kvs_tensor* t, const char* name, unsigned allowed, int ndim,
+                        bool allow_empty = false) {
+  if (!t) return fail(KVS_ERR_INVALID, "%s: descriptor is NULL", name);
+  if (t->dtype < 0 || t->dtype > 2 || !(allowed & (1u << t->dtype)))
+    return fail(KVS_ERR_INVALID, "%s: dtype %s not allowed here", name, dtname(t->dtype));
+  if (t->ndim != ndim) return fail(KVS_ERR_INVALID, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  int64_t numel = 1;
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0) return fail(KVS_ERR_INVALID, "%s: negative extent in dim %d", name, i);
+    numel *= t->shape[i];
+  }
+  int64_t expect = 1;
+  for (int i = ndim - 1; i >= 0; --i) {
+    if (t->shape[i] > 1 && t->stride[i] != expect)
+      return fail(KVS_ERR_INVALID, "%s: not dense row-major (dim %d stride %lld, expected %lld)", name, i,
+                  (long long)t->stride[i], (long long)expect);
+    expect *= t->shape[i];
+  }
+  if (numel == 0) {
+    if (!allow_empty) return fail(KVS_ERR_INVALID, "%s: empty tensor", name);
+    return KVS_OK;
+  }
+  if (!t->data) return fail(KVS_ERR_INVALID, "%s: data pointer is NULL", name);
+  const uintptr_t align = t->dtype == KVS_I32 ? 4 : 16;
+  if (reinterpret_cast<uintptr_t>(t->data) % align)
+    return fail(KVS_ERR_INVALID, "%s: data pointer not %zu-byte aligned", name, (size_t)align);
+  return KVS_OK;
+}
+
+#define KVS_TRY(expr)                    \
+  do {                                   \
+    kvs_status _st = (expr);             \
+    if (_st != KVS_OK) return _st;       \
+  } while (0)
+
+constexpr unsigned kFloatTypes = (1u << KVS_F32) | (1u << KVS_BF16);
+constexpr unsigned kIntTypes = (1u << KVS_I32);
+
+// ---- attention plan --------------------------------------------------------
+struct Plan {
+  kvs::AttnParams p{};
+  kvs::DType dt;
+  int D = 0;
+  bool decode = false;
+  size_t ws_bytes = 0;   // scratch needed (decode with >1 split)
+  size_t ws_lse_off = 0; // byte offset of part_lse inside the scratch
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Validates shapes (not device values) and fills the plan.  `v_cache`,
+// `cu`, `lk`, `out`, `lse` may be NULL when only sizing the workspace.
+kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                     const kvs_tensor* table, const kvs_tensor* cu, const kvs_tensor* lk, float scale,
+                     int causal, const kvs_tensor* out, const kvs_tensor* lse, const kvs_hints* hints,
+                     bool sizing_only, Plan* plan) {
+  KVS_TRY(check_tensor(q, "q", kFloatTypes, 3));
+  KVS_TRY(check_tensor(k_cache, "k_cache", kFloatTypes, 4));
+  KVS_TRY(check_tensor(table, "block_table", kIntTypes, 2));
+  const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  const int64_t NB = k_cache->shape[0], page = k_cache->shape[1], Hkv = k_cache->shape[2];
+  const int64_t B = table->shape[0], MB = table->shape[1];
+  if (k_cache->dtype != q->dtype) return fail(KVS_ERR_INVALID, "k_cache dtype %s != q dtype %s", dtname(k_cache->dtype), dtname(q->dtype));
+  if (k_cache->shape[3] != D) return fail(KVS_ERR_INVALID, "k_cache head dim %lld != q head dim %lld", (long long)k_cache->shape[3], (long long)D);
+  if (page != 16) return fail(KVS_ERR_UNSUPPORTED, "page size %lld not supported (only 16)", (long long)page);
+  if (D != 64 && D != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)D);
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv) return fail(KVS_ERR_INVALID, "Hq (%lld) must be a positive multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (B < 1) return fail(KVS_ERR_INVALID, "batch must hold at least one sequence");
+  if (T < B) return fail(KVS_ERR_INVALID, "total query rows T=%lld < batch B=%lld (every sequence needs >= 1 row)", (long long)T, (long long)B);
+  if (MB < 1) return fail(KVS_ERR_INVALID, "block_table needs at least one column");
+  if (T > INT32_MAX / 2 || Hq > 4096 || NB * 16 > INT32_MAX || B * MB > INT32_MAX)
+    return fail(KVS_ERR_UNSUPPORTED, "sizes beyond the 32-bit index ranges the kernels use");
+  if (!sizing_only) {
+    KVS_TRY(check_tensor(v_cache, "v_cache", kFloatTypes, 4));
+    for (int i = 0; i < 4; ++i)
+      if (v_cache->shape[i] != k_cache->shape[i]) return fail(KVS_ERR_INVALID, "v_cache shape != k_cache shape");
+    if (v_cache->dtype != q->dtype) return fail(KVS_ERR_INVALID, "v_cache dtype != q dtype");
+    KVS_TRY(check_tensor(cu, "cu_seqlens_q", kIntTypes, 1));
+    KVS_TRY(check_tensor(lk, "seqlens_k", kIntTypes, 1));
+    if (cu->shape[0] != B + 1) return fail(KVS_ERR_INVALID, "cu_seqlens_q has %lld entries, expected B+1=%lld", (long long)cu->shape[0], (long long)(B + 1));
+    if (lk->shape[0] != B) return fail(KVS_ERR_INVALID, "seqlens_k has %lld entries, expected B=%lld", (long long)lk->shape[0], (long long)B);
+    KVS_TRY(check_tensor(out, "out", kFloatTypes, 3));
+    if (out->dtype != q->dtype) return fail(KVS_ERR_INVALID, "out dtype != q dtype");
+    for (int i = 0; i < 3; ++i)
+      if (out->shape[i] != q->shape[i]) return fail(KVS_ERR_INVALID, "out shape != q shape");
+    if (lse) {
+      KVS_TRY(check_tensor(lse, "lse", 1u << KVS_F32, 2));
+      if (lse->shape[0] != T || lse->shape[1] != Hq) return fail(KVS_ERR_INVALID, "lse must be [T, Hq]");
+    }
+    if (!std::isfinite(scale)) return fail(KVS_ERR_INVALID, "scale must be finite");
+  }
+
+  kvs::AttnParams& p = plan->p;
+  p = kvs::AttnParams{};
+  p.q = q->data;
+  p.k = k_cache->data;
+  p.v = v_cache ? v_cache->data : nullptr;
+  p.table = static_cast<const int32_t*>(table->data);
+  p.cu_q = cu ? static_cast<const int32_t*>(cu->data) : nullptr;
+  p.lens_k = lk ? static_cast<const int32_t*>(lk->data) : nullptr;
+  p.out = out ? out->data : nullptr;
+  p.lse = lse ? static_cast<float*>(lse->data) : nullptr;
+  p.B = (int32_t)B;
+  p.T = (int32_t)T;
+  p.Hq = (int32_t)Hq;
+  p.Hkv = (int32_t)Hkv;
+  p.MB = (int32_t)MB;
+  p.G = (int32_t)(Hq / Hkv);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.causal = causal ? 1 : 0;
+  plan->dt = q->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32;
+  plan->D = (int)D;
+  plan->decode = (T == B);
+  plan->ws_bytes = 0;
+
+  if (!plan->decode) {
+    p.HW = p.G % 4 == 0 ? 4 : (p.G % 2 == 0 ? 2 : 1);
+    p.TPW = 4 / p.HW;
+    p.NHG = p.Hq / p.HW;
+    const int64_t TW = 32 * p.TPW;
+    const int64_t NV = T / TW + B;
+    if (NV * p.NHG > (int64_t)UINT32_MAX) return fail(KVS_ERR_UNSUPPORTED, "prefill grid too large");
+    p.NV = (int32_t)NV;
+    return KVS_OK;
+  }
+
+  // decode: split plan from shapes and hints only
+  if (p.G > 16) return fail(KVS_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", p.G);
+  if (B > 65535 || Hkv > 65535) return fail(KVS_ERR_UNSUPPORTED, "decode grid limits: B and Hkv must be <= 65535");
+  int64_t maxk = 16 * MB;
+  if (hints && hints->max_seqlen_k > 0) maxk = std::min<int64_t>(maxk, hints->max_seqlen_k);
+  int64_t chunk;
+  if (hints && hints->num_splits > 0) {
+    chunk = (maxk + hints->num_splits - 1) / hints->num_splits;
+  } else {
+    // aim for ~4096 waves over the whole batch (16 per CU on 256 CUs), but
+    // never below 256 keys per chunk, where the merge starts to cost more
+    // than the extra parallelism buys
+    const int64_t units = 4096;
+    chunk = (maxk * B * Hkv + units - 1) / units;
+    if (chunk < 256) chunk = 256;
+  }
+  chunk = align_up((size_t)std::max<int64_t>(chunk, 1), 64);
+  const int64_t splits = (maxk + chunk - 1) / chunk;
+  if (splits > 65535) return fail(KVS_ERR_UNSUPPORTED, "too many decode splits");
+  p.chunk = (int32_t)chunk;
+  p.max_splits = (int32_t)splits;
+  if (splits > 1) {
+    const size_t o_bytes = (size_t)splits * T * Hq * D * sizeof(float);
+    plan->ws_lse_off = align_up(o_bytes, 256);
+    plan->ws_bytes = plan->ws_lse_off + align_up((size_t)splits * T * Hq * sizeof(float), 256);
+  }
+  return KVS_OK;
+}
+
+// ---- grow-only scratch for the plain call (one buffer per device) ----------
+std::mutex g_ws_mu;
+std::vector<std::pair<void*, size_t>> g_ws;
+
+kvs_status get_plain_workspace(size_t need, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if ((size_t)dev >= g_ws.size()) g_ws.resize(dev + 1, {nullptr, 0});
+  auto& slot = g_ws[dev];
+  if (slot.second < need) {
+    if (slot.first) {
+      // the old buffer may still be read by queued kernels
+      if (hipDeviceSynchronize() != hipSuccess) return fail(KVS_ERR_HIP, "hipDeviceSynchronize failed");
+      (void)hipFree(slot.first);
+      slot = {nullptr, 0};
+    }
+    void* ptr = nullptr;
+    const hipError_t e = hipMalloc(&ptr, need);
+    if (e != hipSuccess) return fail(KVS_ERR_HIP, "hipMalloc(%zu) for decode scratch: %s", need, hipGetErrorString(e));
+    slot = {ptr, need};
+  }
+  *out = slot.first;
+  return KVS_OK;
+}
+
+kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
+  kvs::AttnParams& p = plan.p;
+  if (plan.decode) {
+    if (plan.ws_bytes) {
+      if (!ws || ws_bytes < plan.ws_bytes)
+        return fail(KVS_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
+      if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(KVS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+      p.part_o = static_cast<float*>(ws);
+      p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.ws_lse_off);
+    }
+    const hipError_t e = kvs::launch_decode(p, plan.dt, plan.D, stream);
+    if (e != hipSuccess) return fail(KVS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    set_dispatch("decode_split_%s_d%d grid=(%d,%d,%d) chunk=%d splits=%d merge=%d", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
+                 plan.D, p.max_splits, p.Hkv, p.B, p.chunk, p.max_splits, p.max_splits > 1 ? 1 : 0);
+    return KVS_OK;
+  }
+  const hipError_t e = kvs::launch_prefill(p, plan.dt, plan.D, stream);
+  if (e != hipSuccess) return fail(KVS_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  set_dispatch("prefill_%s_d%d grid=%u (NV=%d x NHG=%d) heads/wg=%d tokens/wg=%d", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
+               plan.D, (unsigned)(p.NV * p.NHG), p.NV, p.NHG, p.HW, 32 * p.TPW);
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
+                          kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_stream_t stream) {
+  g_err.clear();
+  KVS_TRY(check_tensor(k_cache, "k_cache", kFloatTypes, 4));
+  KVS_TRY(check_tensor(v_cache, "v_cache", kFloatTypes, 4));
+  KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3, true));
+  KVS_TRY(check_tensor(v_new, "v_new", kFloatTypes, 3, true));
+  KVS_TRY(check_tensor(slot_mapping, "slot_mapping", kIntTypes, 1, true));
+  const int64_t Tn = k_new->shape[0];
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i]) return fail(KVS_ERR_INVALID, "v_cache shape != k_cache shape");
+  for (int i = 0; i < 3; ++i)
+    if (v_new->shape[i] != k_new->shape[i]) return fail(KVS_ERR_INVALID, "v_new shape != k_new shape");
+  if (k_cache->dtype != v_cache->dtype || k_new->dtype != k_cache->dtype || v_new->dtype != k_cache->dtype)
+    return fail(KVS_ERR_INVALID, "k_new, v_new, k_cache and v_cache must share one dtype");
+  if (k_cache->shape[1] != 16) return fail(KVS_ERR_UNSUPPORTED, "page size %lld not supported (only 16)", (long long)k_cache->shape[1]);
+  if (k_new->shape[1] != k_cache->shape[2] || k_new->shape[2] != k_cache->shape[3])
+    return fail(KVS_ERR_INVALID, "k_new [T, Hkv, D] does not match the pool's [.., .., Hkv, D]");
+  if (slot_mapping->shape[0] != Tn) return fail(KVS_ERR_INVALID, "slot_mapping has %lld entries for %lld rows", (long long)slot_mapping->shape[0], (long long)Tn);
+  const int64_t row_bytes = k_new->shape[1] * k_new->shape[2] * esize(k_new->dtype);
+  if (row_bytes % 16) return fail(KVS_ERR_UNSUPPORTED, "token row of %lld bytes is not a multiple of 16", (long long)row_bytes);
+  if (Tn == 0) {
+    set_dispatch("kv_store_paged: empty (nothing enqueued)");
+    return KVS_OK;
+  }
+  kvs::StoreParams p{};
+  p.k_new = k_new->data;
+  p.v_new = v_new->data;
+  p.slots = static_cast<const int32_t*>(slot_mapping->data);
+  p.k_cache = k_cache->data;
+  p.v_cache = v_cache->data;
+  p.t_new = Tn;
+  p.row_chunks = row_bytes / 16;
+  p.num_slots = k_cache->shape[0] * 16;
+  const hipError_t e = kvs::launch_store(p, k_new->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32,
+                                         reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVS_ERR_HIP, "kv_store_paged launch failed: %s", hipGetErrorString(e));
+  set_dispatch("kv_store_paged rows=%lld row_bytes=%lld", (long long)Tn, (long long)row_bytes);
+  return KVS_OK;
+}
+
+kvs_status attn_varlen_paged(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                             const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
+                             const kvs_tensor* seqlens_k, float scale, int causal, kvs_tensor* out,
+                             kvs_tensor* lse, kvs_stream_t stream) {
+  g_err.clear();
+  Plan plan;
+  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, nullptr,
+                    false, &plan));
+  void* ws = nullptr;
+  if (plan.ws_bytes) KVS_TRY(get_plain_workspace(plan.ws_bytes, &ws));
+  return run_plan(plan, ws, plan.ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k_cache,
+                                        const kvs_tensor* block_table, const kvs_hints* hints) {
+  g_err.clear();
+  Plan plan;
+  if (make_plan(q, k_cache, nullptr, block_table, nullptr, nullptr, 1.0f, 1, nullptr, nullptr, hints, true,
+                &plan) != KVS_OK)
+    return (size_t)-1;
+  return plan.ws_bytes;
+}
+
+kvs_status attn_varlen_paged_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
+                                const kvs_tensor* seqlens_k, float scale, int causal, kvs_tensor* out,
+                                kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
+    return fail(KVS_ERR_INVALID, "hints must be non-negative");
+  Plan plan;
+  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, hints,
+                    false, &plan));
+  return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+const char* kvs_last_error(void) { return g_err.c_str(); }
+
+const char* kvs_last_dispatch(void) { return g_dispatch.c_str(); }
+
+kvs_status kvs_release_workspace(void) {
+  g_err.clear();
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if ((size_t)dev < g_ws.size() && g_ws[dev].first) {
+    if (hipDeviceSynchronize() != hipSuccess) return fail(KVS_ERR_HIP, "hipDeviceSynchronize failed");
+    (void)hipFree(g_ws[dev].first);
+    g_ws[dev] = {nullptr, 0};
+  }
+  return KVS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA
+// wrappers, cross-lane reductions and bf16 packing.  CDNA4 only: wave64,
+// 160 KB LDS per CU, bf16 MFMA with fp32 accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvs {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;               // tokens per KV block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite stand-in for -inf in masked scores: exp2 of it minus any finite
+// running max is exactly 0, and it never produces inf - inf.
+constexpr float kMaskedScore = -3.0e38f;
+
+// ---- bf16 <-> fp32 -------------------------------------------------------
+// bf16 is the top half of an fp32 word, so widening is a shift / mask.
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two fp32 values to bf16 (nearest even) and pack them, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---- MFMA wrappers (operand layouts are documented where they are used) ----
+__device__ __forceinline__ f32x16 mfma32x32x16_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x16_bf16(const u32x2& a, const u32x2& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                    __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x2_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x4_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---- cross-lane ------------------------------------------------------------
+// Combine a value with the one in lane (lane ^ 32).  ds_bpermute through the
+// LDS crossbar; one instruction per call.
+__device__ __forceinline__ float max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
+// Value of lane (lane ^ 16) via the LDS crossbar swizzle (no LDS storage used).
+__device__ __forceinline__ float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+// ---- memory --------------------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Map a linear workgroup id so that each of the 8 XCDs (which receive
+// workgroups round-robin) walks one contiguous range of the logical order;
+// consecutive logical tiles then share an XCD and its L2.  A bijection on
+// [0, n) for any n.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t id, uint32_t n) {
+  const uint32_t xcd = id & 7u, idx = id >> 3;
+  const uint32_t per = n >> 3, rem = n & 7u;
+  return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+}  // namespace kvs

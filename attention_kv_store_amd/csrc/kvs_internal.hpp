@@ -1,0 +1,52 @@
+// Host/device shared parameter blocks and launcher declarations (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvs {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+struct StoreParams {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slots;
+  void* k_cache;
+  void* v_cache;
+  int64_t t_new;       // rows to store
+  int64_t row_chunks;  // 16-byte chunks per token row (Hkv * D * esize / 16)
+  int64_t num_slots;   // 16 * NB (only used by debug checks)
+};
+
+struct AttnParams {
+  const void* q;          // [T, Hq, D]
+  const void* k;          // [NB, 16, Hkv, D]
+  const void* v;
+  const int32_t* table;   // [B, MB]
+  const int32_t* cu_q;    // [B + 1]
+  const int32_t* lens_k;  // [B]
+  void* out;              // [T, Hq, D]
+  float* lse;             // [T, Hq] or null
+  int32_t B, T, Hq, Hkv, MB;
+  int32_t G;              // Hq / Hkv
+  float scale_log2;       // scale * log2(e): scores are kept in base-2 units
+  int32_t causal;
+  // prefill work map
+  int32_t HW;             // query heads per workgroup (divides G)
+  int32_t TPW;            // 32-token blocks per workgroup (HW * TPW == 4 waves)
+  int32_t NHG;            // head groups = Hq / HW
+  int32_t NV;             // virtual tiles per head group = T / (32 * TPW) + B
+  // decode split plan
+  int32_t chunk;          // keys per split (multiple of 64)
+  int32_t max_splits;     // splits per sequence the grid covers
+  float* part_o;          // [max_splits, T, Hq, D] fp32 partial outputs (normalised)
+  float* part_lse;        // [max_splits, T, Hq]   fp32 partial lse (base 2)
+};
+
+hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);
+hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s);
+hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s);
+
+}  // namespace kvs

@@ -1,0 +1,371 @@
+// Prefill / extend attention over the paged KV cache (many query rows per
+// sequence).  gfx950: MFMA for both contractions, K/V tiles staged in LDS.
+//
+// What is computed is the scaled dot-product attention of Transformer 추론 커널
+// (3/10), §10, in the tiled online-softmax order of §11-§12: per query tile the
+// output accumulator, running max and running sum stay on chip while K/V tiles
+// stream through; the score matrix never reaches HBM and the result is exact
+// (up to rounding).  Keys come through the block table (§14); the query heads
+// that share one KV head are served by the same workgroup so each K/V tile is
+// loaded once for the whole group (§15).
+//
+// Layout of the work (one workgroup = 4 waves):
+//  * A wave owns 32 query rows of ONE query head: rows = tokens
+//    [wt0, wt0 + 32) of one sequence.  The 4 waves are HW heads x TPW token
+//    blocks of the same KV head (HW * TPW = 4; HW divides the group size).
+//  * Scores are formed transposed, S^T = K . Q^T, with the 32x32 MFMA.  In the
+//    accumulator layout every lane then holds ONE query row (lane % 32) and 16
+//    of the 32 keys of a block, so row max / row sum are in-lane plus a single
+//    exchange with lane ^ 32, and the probabilities P are already laid out as
+//    the B operand of O^T = V^T . P^T -- no shuffle between the two MFMAs.
+//  * bf16: V is written to LDS transposed (d-major) so the A operand of the PV
+//    MFMA (8 keys of one d per lane) is two 8-byte LDS reads.  fp32: the 32x32x2
+//    MFMA takes one element per lane, so V stays row-major.
+//  * K/V tiles are double-buffered in LDS; the next tile's global loads are
+//    issued before the current tile's math, the block-table entries two tiles
+//    ahead.  Rows past the last key a workgroup needs are zero-filled, never
+//    loaded, so tail rows and table entries past a sequence's last block are
+//    never touched.
+//  * Causal (bottom-right, with cached prefix c = Lk - Lq): tiles wholly above
+//    a wave's rows are skipped; only tiles crossing the diagonal are masked.
+#include <type_traits>
+
+#include "kvs_device.hpp"
+#include "kvs_internal.hpp"
+
+namespace kvs {
+
+template <int D, bool BF16>
+struct PCfg {
+  static constexpr int BN = BF16 ? 64 : 32;   // keys per tile
+  static constexpr int ESZ = BF16 ? 2 : 4;    // element bytes
+  static constexpr int KROW = D * ESZ + 16;   // padded K row in LDS (bytes)
+  // bf16: one V^T row holds one d for the BN keys; fp32: one V row per key
+  static constexpr int VROW = BF16 ? (BN * 2 + 8) : (D * 4 + 16);
+  static constexpr int KTILE = BN * KROW;
+  static constexpr int VTILE = BF16 ? D * VROW : BN * VROW;
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int NPG = BN / 16;          // pages per tile
+  static constexpr int CPR = D * ESZ / 16;     // 16-byte chunks per token row
+  static constexpr int KCH = BN * CPR;         // K chunks per tile
+  static constexpr int KIT = (KCH + 255) / 256;
+  // bf16 V items: 4 keys x 8 d (four 16-byte chunks); fp32 V: plain chunks
+  static constexpr int VITEMS = BF16 ? (BN / 4) * (D / 8) : KCH;
+  static constexpr int VIT = (VITEMS + 255) / 256;
+  static constexpr int VREGS = BF16 ? VIT * 4 : VIT;
+  static constexpr int NDB = D / 32;           // 32-wide d blocks of the output
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
+  using C = PCfg<D, BF16>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+
+  // ---- workgroup -> (sequence, token tile, head group) -------------------
+  const int TW = 32 * p.TPW;
+  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+  const int hgrp = (int)(L / (uint32_t)p.NV);
+  // reversed so the last (heaviest, under a causal mask) tiles start first
+  const int vt = p.NV - 1 - (int)(L - (uint32_t)hgrp * (uint32_t)p.NV);
+  int lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu_q[mid] / TW + mid <= vt) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int q0 = p.cu_q[b];
+  const int Lq = p.cu_q[b + 1] - q0;
+  const int tile = vt - (q0 / TW + b);
+  if (tile >= (Lq + TW - 1) / TW) return;  // surplus virtual tile (whole workgroup)
+  const int Lk = p.lens_k[b];
+  const int cached = Lk - Lq;
+  const int tok0 = tile * TW;
+  const int tlast = min(tok0 + TW, Lq) - 1;
+  const int nkeys = p.causal ? min(Lk, cached + tlast + 1) : Lk;
+  const int ntiles = (nkeys + C::BN - 1) / C::BN;
+  const int npages = (nkeys + 15) >> 4;
+
+  const int hw = wave % p.HW, tb = wave / p.HW;
+  const int h = hgrp * p.HW + hw;
+  const int g = h / p.G;
+  const int wt0 = tok0 + tb * 32;
+  const bool wave_live = wt0 < Lq;
+  const int qrow = wt0 + n;                 // this lane's query row in the sequence
+  const int qpos = cached + qrow;           // its position among the keys
+
+  const int32_t* trow = p.table + (int64_t)b * p.MB;
+  const int64_t kv_tok_stride = (int64_t)p.Hkv * D;   // elements between token rows
+
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  const E* kbase = static_cast<const E*>(p.k) + (int64_t)g * D;
+  const E* vbase = static_cast<const E*>(p.v) + (int64_t)g * D;
+
+  // ---- Q fragment (B operand of S^T = K . Q^T), loaded once -------------
+  // bf16 32x32x16: lane holds Q[row n][ks*16 + hh*8 .. +8] for k-step ks.
+  // fp32 32x32x2: lane holds Q[row n][hh*D/2 + ks] for k-step ks.
+  constexpr int QF = BF16 ? D / 16 : D / 2;
+  typename std::conditional<BF16, u32x4, float>::type qf[QF];
+  {
+    const bool ok = wave_live && qrow < Lq;
+    const E* qp = static_cast<const E*>(p.q) + ((int64_t)(q0 + (ok ? qrow : 0)) * p.Hq + h) * D;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int ks = 0; ks < QF; ++ks) qf[ks] = ok ? ld16(qp + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int c4 = 0; c4 < QF / 4; ++c4) {
+        const u32x4 w = ok ? ld16(qp + hh * (D / 2) + c4 * 4) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(w[e]);
+      }
+    }
+  }
+
+  // ---- staging helpers ----------------------------------------------------
+  int pg_cur[C::NPG], pg_nxt[C::NPG];
+  auto load_pages = [&](int t, int* pg) {
+#pragma unroll
+    for (int i = 0; i < C::NPG; ++i) {
+      const int page = t * C::NPG + i;
+      pg[i] = page < npages ? trow[page] : 0;
+    }
+  };
+  u32x4 kreg[C::KIT];
+  u32x4 vreg[C::VREGS];
+  auto row_ptr = [&](const E* base, int kv0, int j, const int* pg) -> const E* {
+    const int pos = kv0 + j;
+    return base + ((int64_t)pg[j >> 4] * kPage + (pos & 15)) * kv_tok_stride;
+  };
+  auto issue_loads = [&](int t, const int* pg) {
+    const int kv0 = t * C::BN;
+#pragma unroll
+    for (int it = 0; it < C::KIT; ++it) {
+      const int c = it * 256 + tid;
+      const int j = c / C::CPR, ch = c % C::CPR;
+      const bool ok = c < C::KCH && kv0 + j < nkeys;
+      kreg[it] = ok ? ld16(row_ptr(kbase, kv0, j, pg) + ch * (16 / C::ESZ)) : u32x4{0, 0, 0, 0};
+    }
+    if constexpr (BF16) {
+#pragma unroll
+      for (int iv = 0; iv < C::VIT; ++iv) {
+        const int it = iv * 256 + tid;
+        const int kq = it % (C::BN / 4), dch = it / (C::BN / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = kq * 4 + r;
+          const bool ok = it < C::VITEMS && kv0 + j < nkeys;
+          vreg[iv * 4 + r] = ok ? ld16(row_ptr(vbase, kv0, j, pg) + dch * 8) : u32x4{0, 0, 0, 0};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < C::VIT; ++it) {
+        const int c = it * 256 + tid;
+        const int j = c / C::CPR, ch = c % C::CPR;
+        const bool ok = c < C::KCH && kv0 + j < nkeys;
+        vreg[it] = ok ? ld16(row_ptr(vbase, kv0, j, pg) + ch * 4) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto write_stage = [&](int buf) {
+    char* Ks = smem + buf * C::STAGE;
+    char* Vs = Ks + C::KTILE;
+#pragma unroll
+    for (int it = 0; it < C::KIT; ++it) {
+      const int c = it * 256 + tid;
+      if (c < C::KCH) st16(Ks + (c / C::CPR) * C::KROW + (c % C::CPR) * 16, kreg[it]);
+    }
+    if constexpr (BF16) {
+      // transpose 4 keys x 8 d into 8 rows (one per d) of 4 keys
+#pragma unroll
+      for (int iv = 0; iv < C::VIT; ++iv) {
+        const int it = iv * 256 + tid;
+        if (it >= C::VITEMS) continue;
+        const int kq = it % (C::BN / 4), dch = it / (C::BN / 4);
+        const u32x4* w = vreg + iv * 4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t lo01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u);
+          const uint32_t lo23 = __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u);
+          const uint32_t hi01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u);
+          char* r0 = Vs + (dch * 8 + 2 * m) * C::VROW + kq * 8;
+          *reinterpret_cast<u32x2*>(r0) = u32x2{lo01, lo23};
+          *reinterpret_cast<u32x2*>(r0 + C::VROW) = u32x2{hi01, hi23};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < C::VIT; ++it) {
+        const int c = it * 256 + tid;
+        if (c < C::KCH) st16(Vs + (c / C::CPR) * C::VROW + (c % C::CPR) * 16, vreg[it]);
+      }
+    }
+  };
+
+  // ---- online-softmax state -------------------------------------------
+  float m_run = kMaskedScore;   // running max, base-2 units, same in both lane halves
+  float l_run = 0.f;            // this lane's share of the running sum
+  f32x16 o[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
+
+  // ---- prologue -----------------------------------------------------------
+  load_pages(0, pg_cur);
+  if (ntiles > 1) load_pages(1, pg_nxt);
+  issue_loads(0, pg_cur);
+  write_stage(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kv0 = t * C::BN;
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) {
+      issue_loads(t + 1, pg_nxt);
+#pragma unroll
+      for (int i = 0; i < C::NPG; ++i) pg_cur[i] = pg_nxt[i];
+      if (t + 2 < ntiles) load_pages(t + 2, pg_nxt);
+    }
+
+    const bool skip = !wave_live || (p.causal && kv0 > cached + wt0 + 31);
+    if (!skip) {
+      const bool need_mask = p.causal ? (kv0 + C::BN - 1 > cached + wt0) : (kv0 + C::BN > Lk);
+      const char* Ks = smem + (t & 1) * C::STAGE;
+      const char* Vs = Ks + C::KTILE;
+      constexpr int NKB = C::BN / 32;
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+        const char* krow = Ks + (kb * 32 + n) * C::KROW;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int ks = 0; ks < D / 16; ++ks)
+            s[kb] = mfma32x32x16_bf16(*reinterpret_cast<const u32x4*>(krow + ks * 32 + hh * 16), qf[ks], s[kb]);
+        } else {
+#pragma unroll
+          for (int c4 = 0; c4 < D / 8; ++c4) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(krow + (hh * (D / 2) + c4 * 4) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[kb] = mfma32x32x2_f32(a4[e], qf[c4 * 4 + e], s[kb]);
+          }
+        }
+      }
+      // scale into base-2 units, mask, tile max
+      float mt = kMaskedScore;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[kb][r] * p.scale_log2;
+          if (need_mask) {
+            const int key = kv0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+            const bool vis = p.causal ? (key <= qpos) : (key < Lk);
+            x = vis ? x : kMaskedScore;
+          }
+          s[kb][r] = x;
+          mt = fmaxf(mt, x);
+        }
+      }
+      mt = max_xor32(mt);
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
+          s[kb][r] = e;
+          lsum += e;
+        }
+      }
+      l_run = l_run * alpha + lsum;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+
+      // O^T += V^T . P^T
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        if constexpr (BF16) {
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const u32x4 pb = {pack_bf16x2(s[kb][8 * pp + 0], s[kb][8 * pp + 1]),
+                              pack_bf16x2(s[kb][8 * pp + 2], s[kb][8 * pp + 3]),
+                              pack_bf16x2(s[kb][8 * pp + 4], s[kb][8 * pp + 5]),
+                              pack_bf16x2(s[kb][8 * pp + 6], s[kb][8 * pp + 7])};
+            const int key0 = kb * 32 + 16 * pp + 4 * hh;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+              const char* vr = Vs + (db * 32 + n) * C::VROW + key0 * 2;
+              const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr);
+              const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + 16);
+              o[db] = mfma32x32x16_bf16(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pb, o[db]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+            const float* vr = reinterpret_cast<const float*>(Vs + key * C::VROW);
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) o[db] = mfma32x32x2_f32(vr[db * 32 + n], s[kb][r], o[db]);
+          }
+        }
+      }
+    }
+
+    if (has_next) write_stage((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l, lse = (m + log2 l) ln 2 ---------------------------
+  if (!wave_live || qrow >= Lq) return;
+  const float l_tot = sum_xor32(l_run);
+  const float inv = 1.0f / l_tot;
+  const int64_t orow = ((int64_t)(q0 + qrow) * p.Hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = db * 32 + g4 * 8 + hh * 4;
+      const float a0 = o[db][g4 * 4 + 0] * inv, a1 = o[db][g4 * 4 + 1] * inv;
+      const float a2 = o[db][g4 * 4 + 2] * inv, a3 = o[db][g4 * 4 + 3] * inv;
+      if constexpr (BF16) {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + orow + d) =
+            u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow + d) = f32x4{a0, a1, a2, a3};
+      }
+    }
+  }
+  if (p.lse && hh == 0) p.lse[(int64_t)(q0 + qrow) * p.Hq + h] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+}
+
+template <int D, bool BF16>
+static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
+  using C = PCfg<D, BF16>;
+  const unsigned grid = (unsigned)p.NV * (unsigned)p.NHG;
+  const size_t lds = 2 * C::STAGE;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((prefill_kernel<D, BF16>), dim3(grid), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s) {
+  if (dt == DType::BF16) return D == 64 ? launch_prefill_t<64, true>(p, s) : launch_prefill_t<128, true>(p, s);
+  return D == 64 ? launch_prefill_t<64, false>(p, s) : launch_prefill_t<128, false>(p, s);
+}
+
+}  // namespace kvs

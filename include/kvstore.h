@@ -1,0 +1,186 @@
+/*
+ * kvstore.h -- C ABI of the MI355X (gfx950) paged varlen attention library.
+ *
+ * Two operations, both from the step list of one decoder layer in
+ * "Transformer 추론 커널: GEMM·Attention·FlashAttention·Fusion (3/10)", §2:
+ * the KV-cache store that precedes attention, and attention of the new query
+ * rows against the paged K/V.  Everything else is plumbing for those two.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors travel as borrowed descriptors (kvs_tensor): a data pointer plus
+ *    dtype, rank, shape and strides in ELEMENTS.  The library never copies,
+ *    frees or retains them.  Every tensor must be dense row-major
+ *    (stride[ndim-1] == 1, stride[i] == stride[i+1] * shape[i+1]) and its data
+ *    pointer 16-byte aligned.
+ *  - Every data pointer is a DEVICE pointer on the current HIP device, owned by
+ *    the caller, except where a comment says "host".
+ *  - Calls are asynchronous on `stream`: they validate on the host, enqueue
+ *    kernels, and return.  No call synchronises the device or reads device
+ *    memory from the host.
+ *  - The paged pool (k_cache, v_cache) is [num_blocks, 16, Hkv, D]: token row
+ *    `r` of physical block `p` holds the K (or V) vectors of all Hkv heads.  A
+ *    slot number names one token row: slot = p * 16 + r.  Page size 16 follows
+ *    "tiny-vLLM: CUDA로 직접 쓴 LLM 추론 엔진 읽기", entry 6; page = slot // 16 and
+ *    row = slot % 16 follow the token-granular table of "장부가 커널 인자로 바뀌는
+ *    지점과 CUDA graph", section "장부에서 텐서로".
+ *  - Errors: a non-zero kvs_status means nothing was enqueued (except
+ *    KVS_ERR_HIP, where a launch was attempted).  kvs_last_error() returns the
+ *    calling thread's message for its last non-OK status.
+ *  - Values that live on the device (lengths, table entries, slots) cannot be
+ *    checked without a synchronisation; the preconditions stated below for them
+ *    are the caller's responsibility, and violating them is undefined behaviour
+ *    (out-of-range table entries or slots are out-of-bounds device accesses).
+ */
+#ifndef KVSTORE_H
+#define KVSTORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* kvs_stream_t; /* a hipStream_t; NULL = the null stream */
+
+typedef enum {
+  KVS_OK = 0,
+  KVS_ERR_INVALID = 1,      /* bad argument: null pointer, shape/dtype/stride mismatch   */
+  KVS_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head dim, page size, group) */
+  KVS_ERR_WORKSPACE = 3,    /* caller workspace too small                                */
+  KVS_ERR_HIP = 4           /* a HIP runtime call or launch failed                       */
+} kvs_status;
+
+typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_I32 = 2 } kvs_dtype;
+
+typedef struct {
+  void* data;          /* device pointer (16-byte aligned)                 */
+  int32_t dtype;       /* kvs_dtype                                        */
+  int32_t ndim;        /* 1..4                                             */
+  int64_t shape[4];
+  int64_t stride[4];   /* in elements; must describe a dense row-major view */
+} kvs_tensor;
+
+/*
+ * kv_store_paged -- write new K/V token rows into their slots.
+ *
+ * Defined by the store step that comes right before attention ("Transformer 추론
+ * 커널 (3/10)", §2) and by the decode path appending the new token's K/V to the
+ * paged cache ("tiny-vLLM ...", entry 5).
+ *
+ *   k_new, v_new   [T_new, Hkv, D], dtype f32 or bf16 (same as the caches)
+ *   slot_mapping   i32 [T_new]; row t goes to slot slot_mapping[t];
+ *                  a negative slot skips the row (a padding row owns no slot)
+ *   k_cache,v_cache [NB, 16, Hkv, D], written in place
+ *
+ * Preconditions on device values: every non-negative slot < 16 * NB, and no two
+ * rows name the same slot (duplicates leave either row's data, unspecified).
+ * The copy is bit-exact.  T_new == 0 is a valid no-op.
+ */
+kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new,
+                          const kvs_tensor* slot_mapping,
+                          kvs_tensor* k_cache, kvs_tensor* v_cache,
+                          kvs_stream_t stream);
+
+/*
+ * attn_varlen_paged -- exact softmax attention of packed varlen query rows over
+ * a paged K/V cache.
+ *
+ * Computes, for every sequence b, new row i and query head h,
+ *     out[t, h, :] = sum_j softmax_j(scale * q[t, h, :] . K_b[j, g, :]) V_b[j, g, :]
+ *     lse[t, h]    = ln sum_j exp(scale * q[t, h, :] . K_b[j, g, :])
+ * over the visible keys j, where t = cu_seqlens_q[b] + i, g = h / (Hq / Hkv)
+ * (several query heads share one KV head: "Transformer 추론 커널 (3/10)", §15),
+ * and K_b[j] is row j % 16 of physical block block_table[b, j / 16] (§14).
+ * The formula is the scaled dot-product attention of §10; it is computed as a
+ * tiled pass with online softmax (§11, §12), which reaches the same exact result
+ * without materialising the score matrix.
+ *
+ * Visible keys: with Lq_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] new rows and
+ * Lk_b = seqlens_k[b] keys in total, the cached prefix is c_b = Lk_b - Lq_b and
+ * row i sits at position c_b + i.  If `causal` and Lq_b > 1, row i sees keys
+ * 0 .. c_b + i; otherwise it sees all Lk_b keys.  (Query length = extend length,
+ * key length = the whole length so far, as in "장부가 커널 인자로 바뀌는 지점과 CUDA
+ * graph", section "장부에서 텐서로".)
+ *
+ *   q            [T, Hq, D]  f32 or bf16, T = total new rows
+ *   k_cache/v_cache [NB, 16, Hkv, D], same dtype as q
+ *   block_table  i32 [B, MB]; only entries 0 .. ceil(Lk_b/16)-1 of row b are read
+ *   cu_seqlens_q i32 [B+1]
+ *   seqlens_k    i32 [B]
+ *   scale        multiplies q.k before the mask and softmax (1/sqrt(D) usually)
+ *   out          [T, Hq, D]  same dtype as q (rounded to nearest even for bf16)
+ *   lse          f32 [T, Hq], or NULL to skip it
+ *
+ * Supported: D in {64, 128}; page size 16; Hq % Hkv == 0; for the decode path
+ * Hq / Hkv <= 16.  Anything else returns KVS_ERR_UNSUPPORTED -- there is no
+ * slower fallback path.
+ * Preconditions on device values: cu_seqlens_q[0] == 0, cu_seqlens_q[B] == T,
+ * 1 <= Lq_b <= Lk_b <= 16 * MB, and every table entry that is read lies in
+ * [0, NB).  Tail rows of a sequence's last block and entries past its last block
+ * are never used (their contents do not matter).
+ * Dispatch uses shapes only: T == B (one new row per sequence) takes the decode
+ * path (split-KV pass + merge pass); otherwise the prefill/extend path.  The
+ * decode path needs scratch memory: this call keeps one grow-only device buffer
+ * per device for it (allocated on first need; kvs_release_workspace frees it).
+ * Use attn_varlen_paged_ex to supply the scratch yourself.
+ */
+kvs_status attn_varlen_paged(const kvs_tensor* q,
+                             const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                             const kvs_tensor* block_table,
+                             const kvs_tensor* cu_seqlens_q,
+                             const kvs_tensor* seqlens_k,
+                             float scale, int causal,
+                             kvs_tensor* out, kvs_tensor* lse,
+                             kvs_stream_t stream);
+
+/* Optional host-side hints for attn_varlen_paged_ex; 0 means "unknown / choose". */
+typedef struct {
+  int32_t max_seqlen_q;  /* upper bound on Lq_b (host value), 0 = unknown            */
+  int32_t max_seqlen_k;  /* upper bound on Lk_b (host value), 0 = use 16 * MB         */
+  int32_t num_splits;    /* decode: force the number of key chunks per sequence (>=1) */
+} kvs_hints;
+
+/* Bytes of device scratch attn_varlen_paged_ex needs for these shapes and hints
+ * (0 when the chosen path needs none).  Returns (size_t)-1 on invalid shapes. */
+size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k_cache,
+                                        const kvs_tensor* block_table,
+                                        const kvs_hints* hints);
+
+/*
+ * attn_varlen_paged_ex -- attn_varlen_paged with caller-owned scratch and hints.
+ * Same computation and argument meaning.  `workspace` is a device buffer of at
+ * least attn_varlen_paged_workspace_size(q, k_cache, block_table, hints) bytes
+ * (may be NULL when that size is 0); its contents on entry do not matter, and
+ * two calls that overlap in time must not share it.  Allocates nothing.
+ * `hints` may be NULL.
+ */
+kvs_status attn_varlen_paged_ex(const kvs_tensor* q,
+                                const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                const kvs_tensor* block_table,
+                                const kvs_tensor* cu_seqlens_q,
+                                const kvs_tensor* seqlens_k,
+                                float scale, int causal,
+                                kvs_tensor* out, kvs_tensor* lse,
+                                const kvs_hints* hints,
+                                void* workspace, size_t workspace_bytes,
+                                kvs_stream_t stream);
+
+/* Text of the calling thread's last non-OK status ("" if none).  The pointer is
+ * valid until that thread's next library call. */
+const char* kvs_last_error(void);
+
+/* Text naming the kernel variant, grid and split plan of the calling thread's
+ * last successful enqueue (so a caller can log which path ran). */
+const char* kvs_last_dispatch(void);
+
+/* Frees the grow-only scratch buffer that attn_varlen_paged keeps on the current
+ * device.  Synchronises the device first (the buffer may be in use). */
+kvs_status kvs_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSTORE_H */

@@ -13,8 +13,9 @@ def oracle_pool(batch: PagedBatch, dtype=np.float64):
     shape = batch.pool_shape()
     kc = np.full(shape, np.nan, dtype=dtype)
     vc = np.full(shape, np.nan, dtype=dtype)
-    return kv_store_oracle(batch.k_tokens.astype(dtype), batch.v_tokens.astype(dtype),
-                           batch.slots, kc, vc)
+    rows = batch.store_rows()
+    return kv_store_oracle(batch.k_tokens[rows].astype(dtype), batch.v_tokens[rows].astype(dtype),
+                           batch.slots[rows], kc, vc)
 
 
 def oracle_attention(batch: PagedBatch, rows=None, pool=None, causal=None):

@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad descriptors before any HIP call (so nothing
+is enqueued).  Data pointers here are fake and are never dereferenced."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_kv_store_amd import _lib as L
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvstore.h")
+FAKE = 0x10000  # 16-byte aligned, never touched
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def T(shape, dtype=L.KVS_BF16, data=FAKE, strides=None):
+    return L.describe(data, dtype, shape, strides)
+
+
+def ref(t):
+    return ctypes.byref(t) if t is not None else None
+
+
+def test_header_symbols_exported(lib):
+    decl = re.findall(r"^\s*(?:kvs_status|size_t|const char\*)\s+(\w+)\s*\(", open(HDR).read(), re.M)
+    assert set(decl) == set(L.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def _attn_args(T_=8, Hq=4, Hkv=2, D=64, NB=8, B=2, MB=2, dtype=L.KVS_BF16):
+    return dict(q=T([T_, Hq, D], dtype), k=T([NB, 16, Hkv, D], dtype), v=T([NB, 16, Hkv, D], dtype),
+                table=T([B, MB], L.KVS_I32), cu=T([B + 1], L.KVS_I32), lk=T([B], L.KVS_I32),
+                out=T([T_, Hq, D], dtype), lse=T([T_, Hq], L.KVS_F32))
+
+
+def _call_ex(lib, a, hints=None, ws=None, ws_bytes=0, scale=0.125):
+    return lib.attn_varlen_paged_ex(ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["table"]), ref(a["cu"]),
+                                    ref(a["lk"]), ctypes.c_float(scale), 1, ref(a["out"]), ref(a.get("lse")),
+                                    ctypes.byref(hints) if hints else None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("mutate,expect,msg", [
+    (lambda a: a.update(q=T([8, 4, 96]), k=T([8, 16, 2, 96]), v=T([8, 16, 2, 96]), out=T([8, 4, 96])),
+     L.KVS_ERR_UNSUPPORTED, "head dim"),
+    (lambda a: a.update(q=T([8, 4, 128])), L.KVS_ERR_INVALID, "head dim 64 != q head dim 128"),
+    (lambda a: a.update(k=T([8, 32, 2, 64]), v=T([8, 32, 2, 64])), L.KVS_ERR_UNSUPPORTED, "page size"),
+    (lambda a: a.update(k=T([8, 16, 3, 64]), v=T([8, 16, 3, 64])), L.KVS_ERR_INVALID, "multiple of Hkv"),
+    (lambda a: a.update(q=T([8, 4, 64], L.KVS_F32)), L.KVS_ERR_INVALID, "dtype"),
+    (lambda a: a.update(out=T([8, 4, 64], L.KVS_F32)), L.KVS_ERR_INVALID, "out dtype"),
+    (lambda a: a.update(out=T([8, 3, 64])), L.KVS_ERR_INVALID, "out shape"),
+    (lambda a: a.update(lse=T([8, 4], L.KVS_BF16)), L.KVS_ERR_INVALID, "lse"),
+    (lambda a: a.update(lse=T([8, 5], L.KVS_F32)), L.KVS_ERR_INVALID, "lse"),
+    (lambda a: a.update(cu=T([2], L.KVS_I32)), L.KVS_ERR_INVALID, "cu_seqlens_q"),
+    (lambda a: a.update(lk=T([3], L.KVS_I32)), L.KVS_ERR_INVALID, "seqlens_k"),
+    (lambda a: a.update(table=T([2, 2], L.KVS_F32)), L.KVS_ERR_INVALID, "block_table"),
+    (lambda a: a.update(q=T([1, 4, 64])), L.KVS_ERR_INVALID, "T=1 < batch"),
+    (lambda a: a.update(q=T([8, 4, 64], data=FAKE + 8)), L.KVS_ERR_INVALID, "aligned"),
+    (lambda a: a.update(q=T([8, 4, 64], data=0)), L.KVS_ERR_INVALID, "NULL"),
+    (lambda a: a.update(q=T([8, 4, 64], strides=[512, 1, 4])), L.KVS_ERR_INVALID, "row-major"),
+    (lambda a: a.update(v=T([9, 16, 2, 64])), L.KVS_ERR_INVALID, "v_cache shape"),
+    (lambda a: a.update(v=None), L.KVS_ERR_INVALID, "v_cache"),
+])
+def test_attention_validation(lib, mutate, expect, msg):
+    a = _attn_args()
+    mutate(a)
+    st = _call_ex(lib, a)
+    assert st == expect
+    assert msg in lib.kvs_last_error().decode()
+
+
+def test_nonfinite_scale_rejected(lib):
+    a = _attn_args()
+    assert _call_ex(lib, a, scale=float("nan")) == L.KVS_ERR_INVALID
+
+
+def test_decode_group_limit(lib):
+    a = _attn_args(T_=2, Hq=34, Hkv=2, B=2)
+    a["out"] = T([2, 34, 64])
+    a["lse"] = None
+    assert _call_ex(lib, a) == L.KVS_ERR_UNSUPPORTED
+    assert "16 query heads" in lib.kvs_last_error().decode()
+
+
+def test_workspace_sizing_and_check(lib):
+    # decode shapes (T == B) with a long table need split scratch
+    a = _attn_args(T_=4, Hq=8, Hkv=2, B=4, MB=128)
+    a["out"] = T([4, 8, 64])
+    a["lse"] = T([4, 8], L.KVS_F32)
+    h = L.KvsHints()
+    h.num_splits = 4
+    need = lib.attn_varlen_paged_workspace_size(ref(a["q"]), ref(a["k"]), ref(a["table"]), ctypes.byref(h))
+    # 4 splits x 4 rows x 8 heads x (64 + 1) floats, each part 256-byte aligned
+    assert need == 4 * 4 * 8 * 64 * 4 + 512
+    st = _call_ex(lib, a, hints=h, ws=FAKE, ws_bytes=need - 1)
+    assert st == L.KVS_ERR_WORKSPACE
+    h.num_splits = 1
+    assert lib.attn_varlen_paged_workspace_size(ref(a["q"]), ref(a["k"]), ref(a["table"]), ctypes.byref(h)) == 0
+    # prefill shapes need none
+    p = _attn_args(T_=40, B=2)
+    assert lib.attn_varlen_paged_workspace_size(ref(p["q"]), ref(p["k"]), ref(p["table"]), None) == 0
+    # invalid shapes report (size_t)-1
+    bad = T([4, 8, 96])
+    assert lib.attn_varlen_paged_workspace_size(ref(bad), ref(a["k"]), ref(a["table"]), None) == ctypes.c_size_t(-1).value
+
+
+def test_negative_hints_rejected(lib):
+    a = _attn_args()
+    h = L.KvsHints()
+    h.num_splits = -1
+    assert _call_ex(lib, a, hints=h) == L.KVS_ERR_INVALID
+
+
+@pytest.mark.parametrize("mutate,expect,msg", [
+    (lambda a: a.update(kn=T([4, 2, 32]), vn=T([4, 2, 32])), L.KVS_ERR_INVALID, "does not match"),
+    (lambda a: a.update(kn=T([4, 2, 32])), L.KVS_ERR_INVALID, "v_new shape"),
+    (lambda a: a.update(kn=T([4, 2, 64], L.KVS_F32), vn=T([4, 2, 64], L.KVS_F32)), L.KVS_ERR_INVALID, "one dtype"),
+    (lambda a: a.update(slots=T([5], L.KVS_I32)), L.KVS_ERR_INVALID, "slot_mapping"),
+    (lambda a: a.update(slots=T([4], L.KVS_F32)), L.KVS_ERR_INVALID, "slot_mapping"),
+    (lambda a: a.update(kc=T([8, 8, 2, 64]), vc=T([8, 8, 2, 64])), L.KVS_ERR_UNSUPPORTED, "page size"),
+    (lambda a: a.update(vc=T([7, 16, 2, 64])), L.KVS_ERR_INVALID, "v_cache shape"),
+    (lambda a: a.update(kc=None), L.KVS_ERR_INVALID, "NULL"),
+])
+def test_store_validation(lib, mutate, expect, msg):
+    a = dict(kn=T([4, 2, 64]), vn=T([4, 2, 64]), slots=T([4], L.KVS_I32), kc=T([8, 16, 2, 64]), vc=T([8, 16, 2, 64]))
+    mutate(a)
+    st = lib.kv_store_paged(ref(a["kn"]), ref(a["vn"]), ref(a["slots"]), ref(a["kc"]), ref(a["vc"]), None)
+    assert st == expect
+    assert msg in lib.kvs_last_error().decode()
+
+
+def test_store_empty_is_noop(lib):
+    st = lib.kv_store_paged(ref(T([0, 2, 64], data=0)), ref(T([0, 2, 64], data=0)), ref(T([0], L.KVS_I32, data=0)),
+                            ref(T([8, 16, 2, 64])), ref(T([8, 16, 2, 64])), None)
+    assert st == L.KVS_OK
+    assert "empty" in lib.kvs_last_dispatch().decode()
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+
+    mod = importlib.import_module("attention_kv_store_amd._lib")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(ImportError):
+            mod.load(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved

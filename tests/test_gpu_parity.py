@@ -1,0 +1,261 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Tolerances (max-abs, on both out and lse): 1e-5 for fp32 inputs, 2e-2 for
+bf16 inputs (fp32 accumulation inside the kernels).  The store, the one-hot
+probes and the indexing are bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_kv_store_amd._lib as L
+    L.load()
+
+
+def _mk(seed, q_lens, k_lens, **kw):
+    from workloads import make_batch
+    return make_batch(seed, q_lens, k_lens, **kw)
+
+
+def _check(batch, out, lse, rows=None, tol=None):
+    from tests.gpu_side import to_f64
+    from tests.oracle_side import oracle_attention
+
+    ro, rl = oracle_attention(batch, rows=rows)
+    go, gl = to_f64(out), to_f64(lse)
+    if rows is not None:
+        ro, rl, go, gl = ro[rows], rl[rows], go[rows], gl[rows]
+    tol = TOL[batch.dtype] if tol is None else tol
+    assert np.isfinite(go).all() and np.isfinite(gl).all(), "NaN/Inf in GPU output"
+    eo = np.max(np.abs(go - ro))
+    el = np.max(np.abs(gl - rl))
+    print(f"[{batch.name or 'case'}] max|dout|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= tol, f"out max-abs {eo} > {tol}"
+    assert el <= tol, f"lse max-abs {el} > {tol}"
+
+
+def _run(batch, **kw):
+    from tests.gpu_side import run_attention, to_device
+    db = to_device(batch)
+    return run_attention(db, **kw)
+
+
+# ------------------------------------------------------------------ store --
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_store_bitwise(dtype):
+    from tests.gpu_side import to_device
+    from tests.oracle_side import oracle_pool
+    b = _mk(201, [17, 9, 40], [33, 9, 80], Hq=8, Hkv=2, D=64, dtype=dtype, extra_blocks=5)
+    db = to_device(b)
+    kc, vc = oracle_pool(b, dtype=np.float32)
+    bits = np.uint32 if dtype == "fp32" else np.uint16
+    for dev, ref in ((db.k_cache, kc), (db.v_cache, vc)):
+        got = dev.cpu()
+        if dtype == "bf16":
+            got_bits = got.view(torch.int16).numpy().view(np.uint16)
+            ref_bits = (ref.view(np.uint32) >> 16).astype(np.uint16)
+        else:
+            got_bits = got.numpy().view(np.uint32)
+            ref_bits = ref.view(np.uint32)
+        # NaN poison has one bit pattern on each side; compare owned rows bitwise
+        owned = ~np.isnan(ref)
+        assert np.array_equal(got_bits[owned], ref_bits[owned])
+        assert np.isnan(got.float().numpy()[~owned]).all()
+
+
+def test_store_negative_slots_skip():
+    import attention_kv_store_amd as kvs
+    kc = torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kn = torch.randn(5, 2, 64, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(5, 2, 64, device="cuda").to(torch.bfloat16)
+    slots = torch.tensor([3, -1, 63, -5, 17], dtype=torch.int32, device="cuda")
+    kvs.kv_store_paged(kn, vn, slots, kc, vc)
+    torch.cuda.synchronize()
+    flat_k = kc.view(-1, 2, 64)
+    for t, s in enumerate([3, -1, 63, -5, 17]):
+        if s >= 0:
+            assert torch.equal(flat_k[s], kn[t])
+    touched = {3, 63, 17}
+    for s in range(64):
+        if s not in touched:
+            assert flat_k[s].abs().sum().item() == 0
+
+
+# ------------------------------------------------------------- tiny fp32 ---
+def test_tiny_varlen_fp32():
+    from workloads import tiny_varlen_fp32
+    b = tiny_varlen_fp32()
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
+# --------------------------------------------------------- edge matrix ----
+EDGE_LENS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("heads", [(4, 2), (8, 2), (4, 4), (12, 4), (6, 2)])
+def test_prefill_edge_lengths(dtype, D, heads):
+    Hq, Hkv = heads
+    lens = [l for l in EDGE_LENS if l > 1]
+    b = _mk(300 + D + Hq, lens, lens, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, causal=True, name=f"edge-{dtype}-{D}-{Hq}/{Hkv}")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_extend_with_cached_prefix(dtype, causal):
+    q = [1, 5, 16, 17, 40, 64, 3, 130]
+    c = [0, 11, 16, 15, 100, 3, 200, 60]
+    b = _mk(411, q, [a + x for a, x in zip(q, c)], Hq=8, Hkv=2, D=128, dtype=dtype, causal=causal,
+            name=f"extend-{dtype}-{causal}")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_batch_of_one_and_long_table(dtype):
+    b = _mk(421, [200], [333], Hq=4, Hkv=1, D=64, dtype=dtype, causal=True, extra_table_cols=7, name="b1")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
+def test_shared_prefix_blocks():
+    """Several table rows name the same physical blocks (a shared prefix)."""
+    b = _mk(431, [20, 7, 33], [84, 71, 97], Hq=8, Hkv=2, D=128, dtype="bf16", causal=True,
+            shared_prefix_blocks=3, name="shared-prefix")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
+# --------------------------------------------------------------- decode ---
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("splits", [0, 1, 2, 7, 64])
+def test_decode_forced_splits(dtype, D, splits):
+    k = [1, 15, 16, 17, 64, 65, 300, 1000, 2048, 129]
+    b = _mk(500 + D + splits, [1] * len(k), k, Hq=8, Hkv=2, D=D, dtype=dtype, causal=True,
+            name=f"decode-{dtype}-{D}-s{splits}")
+    out, lse = _run(b, num_splits=splits)
+    _check(b, out, lse)
+
+
+@pytest.mark.parametrize("heads", [(32, 8), (4, 4), (16, 1), (6, 3)])
+def test_decode_group_sizes(heads):
+    Hq, Hkv = heads
+    k = [5, 77, 160, 1024, 513]
+    b = _mk(551 + Hq, [1] * len(k), k, Hq=Hq, Hkv=Hkv, D=64, dtype="bf16", causal=True, name=f"decode-G{Hq}/{Hkv}")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
+def test_decode_plain_entry_point():
+    """The plain call (library-owned scratch) gives the same bits as _ex."""
+    import attention_kv_store_amd as kvs
+    from tests.gpu_side import to_device
+    k = [100, 900, 2000, 33]
+    b = _mk(561, [1] * 4, k, Hq=8, Hkv=2, D=64, dtype="bf16", causal=True)
+    db = to_device(b)
+    out1, lse1 = kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q,
+                                       db.seqlens_k, db.scale, True)
+    out2 = torch.empty_like(out1)
+    lse2 = torch.empty_like(lse1)
+    kvs.attn_varlen_paged_plain(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q,
+                                db.seqlens_k, db.scale, True, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    kvs.release_workspace()
+
+
+# ------------------------------------------------------ one-hot probes ----
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("first", [False, True])
+@pytest.mark.parametrize("decode", [False, True])
+def test_one_hot_probes_bitwise(dtype, first, decode):
+    """Scores scale*alpha*t with a huge slope make P exactly one-hot, so every
+    output row must equal one V row bit for bit: the last visible key (causal
+    boundary, cached prefix, block table, GQA map) or key 0 (alpha < 0)."""
+    from tests.gpu_side import to_device, run_attention
+    if decode:
+        q_lens, k_lens = [1] * 5, [1, 17, 300, 64, 1999]
+    else:
+        q_lens, k_lens = [17, 1, 40, 9, 70], [17, 20, 40, 100, 333]
+    D = 128 if dtype == "bf16" else 64
+    b = _mk(600 + decode * 2 + first, q_lens, k_lens, Hq=8, Hkv=2, D=D, dtype=dtype, causal=True)
+    for s in range(b.B):
+        k0, k1 = int(b.cu_seqlens_k[s]), int(b.cu_seqlens_k[s + 1])
+        t = np.arange(k1 - k0, dtype=np.float32)
+        b.k_tokens[k0:k1] = 0.0
+        b.k_tokens[k0:k1, :, 0] = (t // 256)[:, None]
+        b.k_tokens[k0:k1, :, 1] = (t % 256)[:, None]
+    alpha = -2048.0 if first else 2048.0
+    b.q[:] = 0.0
+    b.q[:, :, 0] = 256 * alpha
+    b.q[:, :, 1] = alpha
+    db = to_device(b)
+    out, _ = run_attention(db)
+    got = out.cpu()
+    G = b.Hq // b.Hkv
+    vt = torch.from_numpy(b.v_tokens).to(got.dtype)
+    for s in range(b.B):
+        lq, lk = int(b.q_lens[s]), int(b.k_lens[s])
+        c = lk - lq
+        for i in range(lq):
+            j = 0 if first else ((c + i) if lq > 1 else lk - 1)
+            r = int(b.cu_seqlens_q[s]) + i
+            for h in range(b.Hq):
+                assert torch.equal(got[r, h], vt[int(b.cu_seqlens_k[s]) + j, h // G]), (s, i, h)
+
+
+# --------------------------------------------------- poison invariance ---
+def test_poison_never_reaches_output():
+    """Unowned blocks, tail rows and unused table entries hold NaN (the table
+    entries point at a NaN block); the output has no NaN and matches the oracle."""
+    b = _mk(701, [17, 9, 1, 33], [30, 9, 47, 33], Hq=8, Hkv=2, D=64, dtype="bf16", causal=True,
+            extra_table_cols=4, name="poison")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
+# ------------------------------------------------------ named workloads --
+def _sample_rows(batch, per_seq=4, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for s in range(batch.B):
+        r0, r1 = int(batch.cu_seqlens_q[s]), int(batch.cu_seqlens_q[s + 1])
+        rows += [r0, r1 - 1]
+        if r1 - r0 > 2:
+            rows += list(rng.integers(r0, r1, size=min(per_seq, r1 - r0 - 2)))
+    return sorted(set(int(r) for r in rows))
+
+
+@pytest.mark.parametrize("name", ["paged_decode_bf16", "causal_prefill_bf16", "extend_prefill_bf16"])
+def test_named_workload_sampled(name):
+    from workloads import NAMED
+    b = NAMED[name]()
+    out, lse = _run(b)
+    rows = None if name == "paged_decode_bf16" else _sample_rows(b)
+    _check(b, out, lse, rows=rows)
+
+
+def test_long_prefill_sampled():
+    from workloads import long_prefill_bf16
+    b = long_prefill_bf16()
+    out, lse = _run(b)
+    rows = [0, 1, 15, 16, 17, 1000, 4095, 4096, 16383, 20000, 32766, 32767]
+    _check(b, out, lse, rows=rows)

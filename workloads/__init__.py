@@ -92,6 +92,12 @@ class PagedBatch:
             idx.append(np.arange(s, e - int(self.q_lens[b])))
         return np.concatenate(idx) if idx else np.zeros(0, np.int64)
 
+    def store_rows(self) -> np.ndarray:
+        """Indices into k_tokens/slots that write each slot exactly once (rows of
+        a shared prefix appear in several sequences but own one slot)."""
+        _, first = np.unique(self.slots, return_index=True)
+        return np.sort(first)
+
     def pool_shape(self):
         return (self.num_blocks, BLOCK_SIZE, self.Hkv, self.D)
 
