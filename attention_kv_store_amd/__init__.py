@@ -81,7 +81,8 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
     ``return_lse`` is False and no ``lse`` tensor was given).
 
     Uses the allocation-free ``attn_varlen_paged_ex`` entry point with a
-    torch-allocated workspace (or the one passed in)."""
+    torch-allocated workspace, or the one passed in, which must have been
+    zero-filled before its first use (see ``workspace_size``)."""
     import torch
 
     lib = _lib.load()
@@ -95,7 +96,9 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
     if need == ctypes.c_size_t(-1).value:
         raise KvsError(_lib.KVS_ERR_INVALID, lib.kvs_last_error().decode())
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+        # zero-filled once: the decode counters in it must start at zero (and
+        # every call leaves them at zero, so a caller may keep and reuse it)
+        workspace = torch.zeros(int(need), dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
     ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
     d = [dq, dk, _desc(v_cache), dt_, _desc(cu_seqlens_q), _desc(seqlens_k)]

@@ -97,6 +97,7 @@ struct Plan {
   bool decode = false;
   size_t ws_bytes = 0;   // scratch needed (decode with >1 split)
   size_t ws_lse_off = 0; // byte offset of part_lse inside the scratch
+  size_t ws_cnt_off = 0; // byte offset of the per-sequence counters
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -177,31 +178,27 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     return KVS_OK;
   }
 
-  // decode: split plan from shapes and hints only
+  // decode: work plan from shapes and hints only
   if (p.G > 16) return fail(KVS_ERR_UNSUPPORTED, "decode supports at most 16 query heads per KV head (got %d)", p.G);
-  if (B > 65535 || Hkv > 65535) return fail(KVS_ERR_UNSUPPORTED, "decode grid limits: B and Hkv must be <= 65535");
-  int64_t maxk = 16 * MB;
-  if (hints && hints->max_seqlen_k > 0) maxk = std::min<int64_t>(maxk, hints->max_seqlen_k);
-  int64_t chunk;
-  if (hints && hints->num_splits > 0) {
-    chunk = (maxk + hints->num_splits - 1) / hints->num_splits;
-  } else {
-    // aim for ~4096 waves over the whole batch (16 per CU on 256 CUs), but
-    // never below 256 keys per chunk, where the merge starts to cost more
-    // than the extra parallelism buys
-    const int64_t units = 4096;
-    chunk = (maxk * B * Hkv + units - 1) / units;
-    if (chunk < 256) chunk = 256;
-  }
-  chunk = align_up((size_t)std::max<int64_t>(chunk, 1), 64);
-  const int64_t splits = (maxk + chunk - 1) / chunk;
-  if (splits > 65535) return fail(KVS_ERR_UNSUPPORTED, "too many decode splits");
-  p.chunk = (int32_t)chunk;
-  p.max_splits = (int32_t)splits;
-  if (splits > 1) {
-    const size_t o_bytes = (size_t)splits * T * Hq * D * sizeof(float);
-    plan->ws_lse_off = align_up(o_bytes, 256);
-    plan->ws_bytes = plan->ws_lse_off + align_up((size_t)splits * T * Hq * sizeof(float), 256);
+  if (B > 8192) return fail(KVS_ERR_UNSUPPORTED, "decode supports at most 8192 sequences per call (got %lld)", (long long)B);
+  int hpw = 1;
+  for (int c = 8; c >= 1; --c)
+    if (Hkv % c == 0) { hpw = c; break; }
+  if (Hkv / hpw > 65535) return fail(KVS_ERR_UNSUPPORTED, "too many KV heads for the decode grid");
+  // one resident round: 8 waves per CU on 256 CUs, one wave per KV head
+  int64_t nwg = std::max<int64_t>(1, 2048 / Hkv);
+  if (hints && hints->num_splits > 0) nwg = hints->num_splits;
+  // a workgroup's range holds at most 2048 blocks (its table entries sit in
+  // LDS); B * MB bounds the batch's blocks from above
+  nwg = std::max<int64_t>(nwg, (B * MB + 2047) / 2048);
+  if (nwg > (1 << 20)) return fail(KVS_ERR_UNSUPPORTED, "num_splits too large");
+  p.hpw = hpw;
+  p.nwg = (int32_t)nwg;
+  if (nwg > 1) {
+    const size_t slots = (size_t)nwg + B;
+    plan->ws_lse_off = align_up(slots * Hq * D * sizeof(float), 256);
+    plan->ws_cnt_off = plan->ws_lse_off + align_up(slots * Hq * sizeof(float), 256);
+    plan->ws_bytes = plan->ws_cnt_off + align_up((size_t)B * Hkv * sizeof(int32_t), 256);
   }
   return KVS_OK;
 }
@@ -224,8 +221,14 @@ kvs_status get_plain_workspace(size_t need, void** out) {
       slot = {nullptr, 0};
     }
     void* ptr = nullptr;
-    const hipError_t e = hipMalloc(&ptr, need);
+    hipError_t e = hipMalloc(&ptr, need);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "hipMalloc(%zu) for decode scratch: %s", need, hipGetErrorString(e));
+    // the decode counters in the scratch must start at zero; kernels leave them zero
+    e = hipMemset(ptr, 0, need);
+    if (e != hipSuccess) {
+      (void)hipFree(ptr);
+      return fail(KVS_ERR_HIP, "hipMemset of decode scratch: %s", hipGetErrorString(e));
+    }
     slot = {ptr, need};
   }
   *out = slot.first;
@@ -241,11 +244,12 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
       if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(KVS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
       p.part_o = static_cast<float*>(ws);
       p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.ws_lse_off);
+      p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.ws_cnt_off);
     }
     const hipError_t e = kvs::launch_decode(p, plan.dt, plan.D, stream);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-    set_dispatch("decode_split_%s_d%d grid=(%d,%d,%d) chunk=%d splits=%d merge=%d", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
-                 plan.D, p.max_splits, p.Hkv, p.B, p.chunk, p.max_splits, p.max_splits > 1 ? 1 : 0);
+    set_dispatch("decode_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
+                 plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg);
     return KVS_OK;
   }
   const hipError_t e = kvs::launch_prefill(p, plan.dt, plan.D, stream);

@@ -1,29 +1,46 @@
 // Decode attention (one query row per sequence) over the paged KV cache.
 //
 // Decode scans a long paged K/V context per sequence with few query rows, so it
-// is bound by HBM bandwidth and needs its own work split (Transformer 추론 커널
-// (3/10), §13).  Long or uneven contexts are cut into key chunks whose partial
+// is bound by HBM bandwidth and needs its own load balancing (Transformer 추론
+// 커널 (3/10), §13).  Long or uneven contexts are cut into pieces whose partial
 // results (m_i, l_i, O_i) are merged afterwards in a numerically stable way
-// (same page, §16), using the running-statistics update of §12.
+// (same page, §16), with the running-statistics update of §12.
 //
-// Pass 1 (decode_split_kernel): one wave per (sequence, KV head, key chunk).
+// Work split.  The key blocks of the whole batch, laid end to end in sequence
+// order (sequence b owns ceil(Lk_b / 16) of them), are cut into `nwg` equal
+// contiguous ranges, one per workgroup, so every workgroup streams the same
+// number of bytes whatever the length mix, and the grid is sized to be
+// resident in one round (8 waves per CU on 256 CUs).  A range covers the tail
+// of one sequence, whole sequences, and the head of another.  A workgroup walks
+// its range as one continuous stream of steps (up to NBS blocks, never crossing
+// a sequence): the next step -- including the next sequence's query row -- is
+// always being loaded while the current one is computed, so sequence switches
+// cost no pipeline drain.  A sequence wholly inside the range is finished in
+// place.  A sequence cut by a range boundary leaves a normalised partial
+// (O_i / l_i, lse_i) per piece; after its stream, each wave adds its pieces'
+// block counts to per-(sequence, KV head) counters, and the wave that completes
+// a sequence merges its pieces in one round of loads:
+//   lse = M + log2 sum 2^(lse_i - M),  out = sum 2^(lse_i - lse) O_i,
+// then resets the counter, so no second launch is needed.  Partials and counts
+// travel through agent-scope atomics only (never agent-scope fences, which on
+// this chip write back and invalidate a whole XCD's L2).
+//
+// Inside a workgroup, wave w handles KV head hg * hpw + w; the waves run
+// independently (each has a private LDS slab).  Per wave:
 //  * The G query heads that share the KV head ride in the 16 columns of the
 //    MFMA (G <= 16; unused columns are zero), so each K/V byte is read once
 //    for the whole group (§15).
 //  * S^T = K . Q^T with the 16x16x32 bf16 MFMA: the A operand (16 keys x 32 d)
-//    is exactly one 16-byte global load per lane from the paged pool, so K
-//    goes HBM -> registers with no LDS hop.
+//    is one 16-byte global load per lane from the pool -- K goes straight from
+//    HBM into registers.
 //  * The accumulator layout of S^T (lane: one query column, 4 keys) is the B
 //    operand layout of the 16x16x16 MFMA, so P feeds O^T = V^T . P^T directly.
-//    V is transposed through a small per-wave LDS slab (d-major rows of 16
-//    keys, padded to 40 bytes so the 8-byte reads are bank-conflict free).
-//  * The next step's K/V loads are issued before the current step's math
-//    (two register buffers), and block-table entries are scalar loads.
-//  * Writes the normalised partial O_i and its base-2 lse_i, or the final
-//    out/lse directly when the sequence has a single chunk.
-// Pass 2 (decode_merge_kernel): per (row, head, d): lse = M + log2 sum
-//  exp2(lse_i - M), out = sum exp2(lse_i - lse) O_i.  Chunks past a sequence's
-//  end are never written or read.
+//    V is transposed through the wave's LDS slab (d-major rows of 16 keys,
+//    padded to 40 bytes so the 8-byte reads are bank-conflict free).
+//  * All loads of a step are unconditional and masked at the point of use, so
+//    the compiler can count outstanding loads exactly and a prefetch is never
+//    waited on early.  Addresses past a sequence's end stay readable: tail
+//    rows lie in an owned block, and blocks past a step's end read block 0.
 #include <type_traits>
 
 #include "kvs_device.hpp"
@@ -33,224 +50,245 @@ namespace kvs {
 
 template <int D>
 struct DCfg {
-  static constexpr int NBS = D == 64 ? 4 : 2;     // 16-key blocks per step
-  static constexpr int KEYS = NBS * 16;           // keys per step
+  static constexpr int NBS = D == 64 ? 4 : 1;     // 16-key blocks per step (K+V per wave: 16 KB at D 64, 8 KB at D 128)
   static constexpr int KI = D / 32;               // 16x16x32 k-steps over d
   static constexpr int NDB = D / 16;              // 16-wide d blocks of the output
   static constexpr int VROW = 40;                 // bytes per V^T row (16 keys + pad)
   static constexpr int VBLK = D * VROW;           // V^T bytes per 16-key block
-  static constexpr int VITEMS = 8 * (D / 8);      // (key pair, 8-d chunk) items per block
-  static constexpr int VIL = VITEMS / 64;         // items per lane per block
+  static constexpr int SLAB = NBS * VBLK;         // V^T bytes per wave
+  static constexpr int VIL = D / 64;              // (key pair, 8-d chunk) items per lane per block
+  static constexpr int DPL = D / 64;              // d values per lane in the merge
+};
+
+constexpr int kDecodeMaxB = 8192;   // sequences whose block prefix fits in LDS
+constexpr int kTblWin = 2048;       // most blocks in one workgroup's range (its table entries sit in LDS)
+constexpr int kMergeChunk = 16;     // pieces merged per round of loads
+// s_waitcnt immediate with vmcnt = 0 and the other counters left alone (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Start of range w on the flattened block axis: floor(w * total / nwg).
+__device__ __forceinline__ int64_t range_start64(int64_t w, int total, int nwg) { return (w * total) / nwg; }
+
+__device__ __forceinline__ float atomic_ld(const float* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_st(float* a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One step of a workgroup's stream: up to NBS blocks of one sequence.
+struct Step {
+  int b;      // sequence (-1: no step; its loads are harmless dummies)
+  int t;      // the sequence's query row
+  int Lk;     // its key count
+  int lblk;   // first block of the step, counted within the sequence
+  int nblk;   // blocks in the step
+  int gblk;   // first block of the step on the flattened axis
+  int first;  // first step of this sequence's piece
+  int last;   // last step of the piece
 };
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(64) void decode_split_kernel(AttnParams p) {
+struct DecodeWave {
   using C = DCfg<D>;
-  const int lane = threadIdx.x;
-  const int col = lane & 15, grp = lane >> 4;
-  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int Lk = p.lens_k[b];
-  // clamped so a max_seqlen_k hint below a real length stays in bounds
-  const int nsplit = min((Lk + p.chunk - 1) / p.chunk, p.max_splits);
-  if (sp >= nsplit) return;
-  const int kbeg = sp * p.chunk;
-  const int kend = min(Lk, kbeg + p.chunk);
-  const int nsteps = (kend - kbeg + C::KEYS - 1) / C::KEYS;
-  const int t = p.cu_q[b];
-  const bool head_ok = col < p.G;
-  const int h = g * p.G + (head_ok ? col : 0);
-  const int32_t* trow = p.table + (int64_t)b * p.MB;
-  const int64_t tok_stride = (int64_t)p.Hkv * D;
-
   using E = typename std::conditional<BF16, uint16_t, float>::type;
-  const E* kbase = static_cast<const E*>(p.k) + (int64_t)g * D;
-  const E* vbase = static_cast<const E*>(p.v) + (int64_t)g * D;
-  const E* qp = static_cast<const E*>(p.q) + ((int64_t)t * p.Hq + h) * D;
 
-  float m_run = kMaskedScore, l_run = 0.f;
+  const AttnParams p;   // by value: a reference would pin the kernel arguments to scratch memory
+  const int lane, col, grp, g;
+  const bool head_ok;
+  const int h;
+  const int64_t tok_stride;
+  const E* kbase;
+  const E* vbase;
+  char* slab;
+
+  float m_run, l_run;
   f32x4 o[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) o[db] = f32x4{};
 
-  if constexpr (BF16) {
-    __shared__ __attribute__((aligned(16))) char vt[C::NBS * C::VBLK];
-    // B operand of S^T = K . Q^T: lane holds Q[col][i*32 + grp*8 .. +8]
-    u32x4 qf[C::KI];
-#pragma unroll
-    for (int i = 0; i < C::KI; ++i) qf[i] = head_ok ? ld16(qp + i * 32 + grp * 8) : u32x4{0, 0, 0, 0};
+  __device__ __forceinline__ DecodeWave(const AttnParams& p_, int g_, char* slab_)
+      : p(p_), lane(threadIdx.x & 63), col(lane & 15), grp(lane >> 4), g(g_), head_ok(col < p_.G),
+        h(g_ * p_.G + (col < p_.G ? col : 0)), tok_stride((int64_t)p_.Hkv * D),
+        kbase(static_cast<const E*>(p_.k) + (int64_t)g_ * D), vbase(static_cast<const E*>(p_.v) + (int64_t)g_ * D),
+        slab(slab_) {}
 
-    u32x4 kA[C::NBS][C::KI], kB[C::NBS][C::KI];
-    u32x4 vA[C::NBS][2 * C::VIL], vB[C::NBS][2 * C::VIL];
-    // K: lane reads row (lane % 16) of each block, d = i*32 + grp*8.
-    // V: lane reads the two rows of key pair kp = lane % 8 at d-chunk
-    //    lane / 8 (+ 8 per extra item).
-    auto load = [&](int step, u32x4 (&kr)[C::NBS][C::KI], u32x4 (&vr)[C::NBS][2 * C::VIL]) {
-      const int k0 = kbeg + step * C::KEYS;
+  __device__ __forceinline__ void reset() {
+    m_run = kMaskedScore;
+    l_run = 0.f;
 #pragma unroll
-      for (int j = 0; j < C::NBS; ++j) {
-        const int kb0 = k0 + 16 * j;
-        const bool blk_ok = kb0 < kend;
-        const int phys = blk_ok ? trow[kb0 >> 4] : 0;
-        const E* kblk = kbase + (int64_t)phys * kPage * tok_stride;
-        const E* vblk = vbase + (int64_t)phys * kPage * tok_stride;
-        const bool krow_ok = kb0 + col < kend;
-#pragma unroll
-        for (int i = 0; i < C::KI; ++i)
-          kr[j][i] = krow_ok ? ld16(kblk + col * tok_stride + i * 32 + grp * 8) : u32x4{0, 0, 0, 0};
-        const int kp = lane & 7;
-        const bool v0_ok = kb0 + 2 * kp < kend, v1_ok = kb0 + 2 * kp + 1 < kend;
-#pragma unroll
-        for (int it = 0; it < C::VIL; ++it) {
-          const int dch = (lane >> 3) + 8 * it;
-          vr[j][2 * it] = v0_ok ? ld16(vblk + (2 * kp) * tok_stride + dch * 8) : u32x4{0, 0, 0, 0};
-          vr[j][2 * it + 1] = v1_ok ? ld16(vblk + (2 * kp + 1) * tok_stride + dch * 8) : u32x4{0, 0, 0, 0};
-        }
-      }
-    };
-    auto compute = [&](int step, const u32x4 (&kr)[C::NBS][C::KI], const u32x4 (&vr)[C::NBS][2 * C::VIL]) {
-      const int k0 = kbeg + step * C::KEYS;
-      // V^T into LDS: word (V[2kp][d], V[2kp+1][d]) at row d, key pair kp
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < C::NBS; ++j) {
-        const int kp = lane & 7;
-#pragma unroll
-        for (int it = 0; it < C::VIL; ++it) {
-          const int dch = (lane >> 3) + 8 * it;
-          const u32x4 w0 = vr[j][2 * it], w1 = vr[j][2 * it + 1];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            char* r0 = vt + j * C::VBLK + (dch * 8 + 2 * m) * C::VROW + kp * 4;
-            *reinterpret_cast<uint32_t*>(r0) = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);
-            *reinterpret_cast<uint32_t*>(r0 + C::VROW) = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);
-          }
-        }
-      }
-      // scores
-      f32x4 s[C::NBS];
-#pragma unroll
-      for (int j = 0; j < C::NBS; ++j) {
-        s[j] = f32x4{};
-#pragma unroll
-        for (int i = 0; i < C::KI; ++i) s[j] = mfma16x16x32_bf16(kr[j][i], qf[i], s[j]);
-      }
-      float mt = kMaskedScore;
-      const bool tail = k0 + C::KEYS > kend;
-#pragma unroll
-      for (int j = 0; j < C::NBS; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = s[j][r] * p.scale_log2;
-          if (tail) x = (k0 + 16 * j + grp * 4 + r < kend) ? x : kMaskedScore;
-          s[j][r] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, xor16(mt));
-      mt = max_xor32(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < C::NBS; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[j][r] - m_new);
-          s[j][r] = e;
-          lsum += e;
-        }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
-      __syncthreads();
-      // O^T += V^T . P^T
-#pragma unroll
-      for (int j = 0; j < C::NBS; ++j) {
-        const u32x2 pb = {pack_bf16x2(s[j][0], s[j][1]), pack_bf16x2(s[j][2], s[j][3])};
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const u32x2 a = *reinterpret_cast<const u32x2*>(vt + j * C::VBLK + (db * 16 + col) * C::VROW + grp * 8);
-          o[db] = mfma16x16x16_bf16(a, pb, o[db]);
-        }
-      }
-    };
+    for (int db = 0; db < C::NDB; ++db) o[db] = f32x4{};
+  }
 
-    load(0, kA, vA);
-    for (int step = 0; step < nsteps; step += 2) {
-      if (step + 1 < nsteps) load(step + 1, kB, vB);
-      compute(step, kA, vA);
-      if (step + 1 < nsteps) {
-        if (step + 2 < nsteps) load(step + 2, kA, vA);
-        compute(step + 1, kB, vB);
-      }
-    }
-  } else {
-    // fp32: 16x16x4 MFMA, one element per lane per operand; k-slot grp of
-    // step i covers d = grp * D/4 + i.
-    constexpr int QF = D / 4;
-    float qf[QF];
+  // s[j][r] holds the score of key k0 + 16 j + 4 grp + r for query column col;
+  // on return it holds exp2(scaled score - running max).  Keys at or past
+  // kend get a masked score by select (their K may be garbage).
+  template <int NB>
+  __device__ __forceinline__ void softmax_update(f32x4 (&s)[NB], int k0, int kend) {
+    float mt = kMaskedScore;
+    const bool tail = k0 + 16 * NB > kend;
 #pragma unroll
-    for (int c4 = 0; c4 < QF / 4; ++c4) {
-      const u32x4 w = head_ok ? ld16(qp + grp * QF + c4 * 4) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(w[e]);
-    }
-    const int nblk = (kend - kbeg + 15) >> 4;
-    for (int j = 0; j < nblk; ++j) {
-      const int kb0 = kbeg + 16 * j;
-      const int phys = trow[kb0 >> 4];
-      const float* kblk = static_cast<const float*>(static_cast<const void*>(kbase)) + (int64_t)phys * kPage * tok_stride;
-      const float* vblk = static_cast<const float*>(static_cast<const void*>(vbase)) + (int64_t)phys * kPage * tok_stride;
-      f32x4 s = f32x4{};
-      const bool krow_ok = kb0 + col < kend;
-#pragma unroll
-      for (int c4 = 0; c4 < QF / 4; ++c4) {
-        const u32x4 w = krow_ok ? ld16(kblk + col * tok_stride + grp * QF + c4 * 4) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s = mfma16x16x4_f32(__uint_as_float(w[e]), qf[c4 * 4 + e], s);
-      }
-      float mt = kMaskedScore;
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = s[r] * p.scale_log2;
-        x = (kb0 + grp * 4 + r < kend) ? x : kMaskedScore;
-        s[r] = x;
+        float x = s[j][r] * p.scale_log2;
+        if (tail) x = (k0 + 16 * j + grp * 4 + r < kend) ? x : kMaskedScore;
+        s[j][r] = x;
         mt = fmaxf(mt, x);
       }
-      mt = fmaxf(mt, xor16(mt));
-      mt = max_xor32(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float lsum = 0.f;
+    mt = fmaxf(mt, xor16(mt));
+    mt = max_xor32(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
-        lsum += s[r];
+        const float e = __builtin_amdgcn_exp2f(s[j][r] - m_new);
+        s[j][r] = e;
+        lsum += e;
       }
-      l_run = l_run * alpha + lsum;
+    l_run = l_run * alpha + lsum;
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+    for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+  }
+
+  // ---- bf16 path -----------------------------------------------------------
+  struct Buf {
+    u32x4 k[C::NBS][C::KI];
+    u32x4 v[C::NBS][2 * C::VIL];
+    u32x4 q[C::KI];
+  };
+
+  // Raw, unconditional loads of one step into `bf` (phys[j] = physical block of
+  // the step's j-th block, 0 for blocks past its end).
+  __device__ __forceinline__ void load(const Step& st, const int* phys, Buf& bf) {
+    const int hq = st.b < 0 ? 0 : h;
+    const E* qp = static_cast<const E*>(p.q) + ((int64_t)(st.b < 0 ? 0 : st.t) * p.Hq + hq) * D;
+#pragma unroll
+    for (int i = 0; i < C::KI; ++i) bf.q[i] = ld16(qp + i * 32 + grp * 8);
+    const int kp = lane & 7;
+#pragma unroll
+    for (int j = 0; j < C::NBS; ++j) {
+      const E* kblk = kbase + (int64_t)phys[j] * kPage * tok_stride;
+      const E* vblk = vbase + (int64_t)phys[j] * kPage * tok_stride;
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i) bf.k[j][i] = ld16(kblk + col * tok_stride + i * 32 + grp * 8);
+#pragma unroll
+      for (int it = 0; it < C::VIL; ++it) {
+        const int dch = (lane >> 3) + 8 * it;
+        bf.v[j][2 * it] = ld16(vblk + (2 * kp) * tok_stride + dch * 8);
+        bf.v[j][2 * it + 1] = ld16(vblk + (2 * kp + 1) * tok_stride + dch * 8);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void compute(const Step& st, const Buf& bf) {
+    const int k0 = st.lblk * 16;
+    const int kend = min(st.Lk, (st.lblk + st.nblk) * 16);
+    const bool tail = k0 + 16 * C::NBS > kend;
+    const u32x4 zero = {0, 0, 0, 0};
+    // V^T into the slab: word (V[2kp][d], V[2kp+1][d]) at row d, key pair kp.
+    // The slab is private to this wave and LDS operations of one wave execute
+    // in order, so a compiler-level fence is all the ordering needed.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < C::NBS; ++j) {
+      const int kp = lane & 7;
+      const bool v0_ok = !tail || k0 + 16 * j + 2 * kp < kend;
+      const bool v1_ok = !tail || k0 + 16 * j + 2 * kp + 1 < kend;
+#pragma unroll
+      for (int it = 0; it < C::VIL; ++it) {
+        const int dch = (lane >> 3) + 8 * it;
+        const u32x4 w0 = v0_ok ? bf.v[j][2 * it] : zero;
+        const u32x4 w1 = v1_ok ? bf.v[j][2 * it + 1] : zero;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          char* r0 = slab + j * C::VBLK + (dch * 8 + 2 * m) * C::VROW + kp * 4;
+          *reinterpret_cast<uint32_t*>(r0) = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);
+          *reinterpret_cast<uint32_t*>(r0 + C::VROW) = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);
+        }
+      }
+    }
+    u32x4 q[C::KI];
+#pragma unroll
+    for (int i = 0; i < C::KI; ++i) q[i] = head_ok ? bf.q[i] : zero;
+    f32x4 s[C::NBS];
+#pragma unroll
+    for (int j = 0; j < C::NBS; ++j) {
+      s[j] = f32x4{};
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i) s[j] = mfma16x16x32_bf16(bf.k[j][i], q[i], s[j]);
+    }
+    softmax_update<C::NBS>(s, k0, kend);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < C::NBS; ++j) {
+      const u32x2 pb = {pack_bf16x2(s[j][0], s[j][1]), pack_bf16x2(s[j][2], s[j][3])};
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(slab + j * C::VBLK + (db * 16 + col) * C::VROW + grp * 8);
+        o[db] = mfma16x16x16_bf16(a, pb, o[db]);
+      }
+    }
+  }
+
+  // ---- fp32 path: 16x16x4 MFMA, one element per lane per operand ------------
+  // k-slot grp of k-step i covers d = grp * D/4 + i.  Not pipelined.
+  __device__ __forceinline__ void compute_f32(const Step& st, const int* phys) {
+    constexpr int QF = D / 4;
+    const float* qp = static_cast<const float*>(p.q) + ((int64_t)st.t * p.Hq + h) * D;
+    float qv[QF];
+#pragma unroll
+    for (int c4 = 0; c4 < QF / 4; ++c4) {
+      const u32x4 w = ld16_keep(qp + grp * QF + c4 * 4, head_ok);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[c4 * 4 + e] = __uint_as_float(w[e]);
+    }
+    const float* kb = reinterpret_cast<const float*>(kbase);
+    const float* vb = reinterpret_cast<const float*>(vbase);
+    const int kend = min(st.Lk, (st.lblk + st.nblk) * 16);
+#pragma unroll
+    for (int j = 0; j < C::NBS; ++j) {
+      if (j >= st.nblk) break;
+      const int kb0 = (st.lblk + j) * 16;
+      const float* kblk = kb + (int64_t)phys[j] * kPage * tok_stride;
+      const float* vblk = vb + (int64_t)phys[j] * kPage * tok_stride;
+      f32x4 s[1] = {f32x4{}};
+#pragma unroll
+      for (int c4 = 0; c4 < QF / 4; ++c4) {
+        const u32x4 w = ld16(kblk + col * tok_stride + grp * QF + c4 * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[0] = mfma16x16x4_f32(__uint_as_float(w[e]), qv[c4 * 4 + e], s[0]);
+      }
+      softmax_update<1>(s, kb0, kend);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = grp * 4 + r;
         const bool ok = kb0 + key < kend;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          const float v = ok ? vblk[key * tok_stride + db * 16 + col] : 0.f;
-          o[db] = mfma16x16x4_f32(v, s[r], o[db]);
+          const float v = vblk[key * tok_stride + db * 16 + col];
+          o[db] = mfma16x16x4_f32(ok ? v : 0.f, s[0][r], o[db]);
         }
       }
     }
   }
 
-  // ---- finish the chunk: combine the 4 lane groups' shares of l ----------
-  float l_tot = l_run + xor16(l_run);
-  l_tot = sum_xor32(l_tot);
-  if (!head_ok) return;
-  const float inv = 1.0f / l_tot;
-  const float lse2 = m_run + __builtin_amdgcn_logf(l_tot);
-  if (nsplit == 1) {
+  // ---- end of a piece ------------------------------------------------------
+  // Combine the 4 lane groups' shares of l; returns the base-2 lse.
+  __device__ __forceinline__ float finish(float* inv_out) {
+    float l_tot = l_run + xor16(l_run);
+    l_tot = sum_xor32(l_tot);
+    *inv_out = 1.0f / l_tot;
+    return m_run + __builtin_amdgcn_logf(l_tot);
+  }
+
+  __device__ __forceinline__ void store_final(int t) {
+    float inv;
+    const float lse2 = finish(&inv);
+    if (!head_ok) return;
     const int64_t orow = ((int64_t)t * p.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
@@ -264,55 +302,333 @@ __global__ __launch_bounds__(64) void decode_split_kernel(AttnParams p) {
       }
     }
     if (p.lse && grp == 0) p.lse[(int64_t)t * p.Hq + h] = lse2 * kLn2;
-  } else {
-    const int64_t prow = (((int64_t)sp * p.T + t) * p.Hq + h);
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const int d = db * 16 + grp * 4;
-      *reinterpret_cast<f32x4*>(p.part_o + prow * D + d) = o[db] * inv;
-    }
-    if (grp == 0) p.part_lse[prow] = lse2;
   }
-}
 
-// One thread per (row, head, d); rows whose sequence had a single chunk were
-// finished by pass 1.
+  // Partials are published with agent-scope relaxed atomic stores (written
+  // through to the device-wide coherence point); nothing waits for them here.
+  __device__ __forceinline__ void store_partial(int slot) {
+    float inv;
+    const float lse2 = finish(&inv);
+    if (!head_ok) return;
+    const int64_t prow = (int64_t)slot * p.Hq + h;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) atomic_st(p.part_o + prow * D + db * 16 + grp * 4 + r, o[db][r] * inv);
+    if (grp == 0) atomic_st(p.part_lse + prow, lse2);
+  }
+
+  // Merge the pieces of sequence b (query row t) for this wave's query heads:
+  // the pieces are the partial slots w + b of the workgroups w whose ranges
+  // meet blocks [s0, s1).  Heads go HB at a time and pieces PC at a time; in a
+  // round, lane i loads the lse of (piece i / HB, head i % HB), every lane loads
+  // its d = lane + 64 k of each (piece, head) output, and all loads are issued
+  // before any is used (one memory round trip per round).
+  __device__ __forceinline__ void merge(int t, int b, int s0, int s1, int total, int nwg) {
+    constexpr int HB = 4;
+    constexpr int PC = D == 64 ? 8 : 4;
+    const int64_t wf = (((int64_t)s0 + 1) * nwg - 1) / total;   // range holding block s0
+    const int64_t wl = ((int64_t)s1 * nwg - 1) / total;         // range holding block s1 - 1
+    for (int qh0 = 0; qh0 < p.G; qh0 += HB) {
+      float M[HB], wsum[HB], acc[HB][C::DPL];
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        M[j] = kMaskedScore;
+        wsum[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < C::DPL; ++k) acc[j][k] = 0.f;
+      }
+      for (int64_t w0 = wf; w0 <= wl; w0 += PC) {
+        // this lane's lse: piece w0 + lane / HB, head qh0 + lane % HB
+        float lsl = kMaskedScore;
+        {
+          const int64_t w = w0 + (lane % (PC * HB)) / HB;
+          const bool live = lane < PC * HB && w <= wl && range_start64(w + 1, total, nwg) > range_start64(w, total, nwg);
+          const int hh = g * p.G + min(qh0 + lane % HB, p.G - 1);
+          const float l = atomic_ld(p.part_lse + ((live ? w : wf) + b) * p.Hq + hh);
+          lsl = live ? l : kMaskedScore;
+        }
+        float ov[PC][HB][C::DPL];
+#pragma unroll
+        for (int i = 0; i < PC; ++i) {
+          const int64_t slot = min(w0 + i, wl) + b;
+#pragma unroll
+          for (int j = 0; j < HB; ++j) {
+            const int hh = g * p.G + min(qh0 + j, p.G - 1);
+#pragma unroll
+            for (int k = 0; k < C::DPL; ++k) ov[i][j][k] = atomic_ld(p.part_o + (slot * p.Hq + hh) * D + lane + 64 * k);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < HB; ++j) {
+          float ls[PC];
+#pragma unroll
+          for (int i = 0; i < PC; ++i) ls[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsl), i * HB + j));
+          float Mn = M[j];
+#pragma unroll
+          for (int i = 0; i < PC; ++i) Mn = fmaxf(Mn, ls[i]);
+          const float sc = __builtin_amdgcn_exp2f(M[j] - Mn);
+          wsum[j] *= sc;
+#pragma unroll
+          for (int k = 0; k < C::DPL; ++k) acc[j][k] *= sc;
+#pragma unroll
+          for (int i = 0; i < PC; ++i) {
+            // pieces that do not exist are selected away, never multiplied by 0
+            const bool use = ls[i] != kMaskedScore;
+            const float wt = use ? __builtin_amdgcn_exp2f(ls[i] - Mn) : 0.f;
+            wsum[j] += wt;
+#pragma unroll
+            for (int k = 0; k < C::DPL; ++k) acc[j][k] = use ? acc[j][k] + wt * ov[i][j][k] : acc[j][k];
+          }
+          M[j] = Mn;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        if (qh0 + j >= p.G) break;
+        const int hh = g * p.G + qh0 + j;
+        const float inv = 1.0f / wsum[j];
+        const int64_t orow = ((int64_t)t * p.Hq + hh) * D;
+#pragma unroll
+        for (int k = 0; k < C::DPL; ++k) {
+          if constexpr (BF16) {
+            reinterpret_cast<__bf16*>(p.out)[orow + lane + 64 * k] = (__bf16)(acc[j][k] * inv);
+          } else {
+            static_cast<float*>(p.out)[orow + lane + 64 * k] = acc[j][k] * inv;
+          }
+        }
+        if (p.lse && lane == 0) p.lse[(int64_t)t * p.Hq + hh] = (M[j] + __builtin_amdgcn_logf(wsum[j])) * kLn2;
+      }
+    }
+  }
+};
+
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void decode_merge_kernel(AttnParams p) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.T * p.Hq * D;
-  if (idx >= total) return;
-  const int d = (int)(idx % D);
-  const int64_t th = idx / D;            // t * Hq + h
-  const int t = (int)(th / p.Hq);
-  const int Lk = p.lens_k[t];            // decode: row t belongs to sequence t
-  const int nsplit = min((Lk + p.chunk - 1) / p.chunk, p.max_splits);
-  if (nsplit <= 1) return;
-  const int64_t plane = (int64_t)p.T * p.Hq;
-  float M = kMaskedScore;
-  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, p.part_lse[i * plane + th]);
-  float wsum = 0.f, acc = 0.f;
-  for (int i = 0; i < nsplit; ++i) {
-    const float w = __builtin_amdgcn_exp2f(p.part_lse[i * plane + th] - M);
-    wsum += w;
-    acc += w * p.part_o[(i * plane + th) * D + d];
+__global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
+  using C = DCfg<D>;
+  using W = DecodeWave<D, BF16>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int B = p.B;
+  int* sstart = reinterpret_cast<int*>(smem);        // [B + 1] block prefix
+  int* sflag = sstart + ((B + 1 + 3) & ~3);          // [4]    broadcast slots
+  int* tbl = sflag + 4;                              // [kTblWin] physical blocks of the range window
+  char* slabs = reinterpret_cast<char*>(tbl + kTblWin);
+  __shared__ int wtot[8];
+
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int w = blockIdx.x, hg = blockIdx.y, nwg = p.nwg;
+
+  // ---- exclusive prefix of ceil(Lk_b / 16) over the batch, in LDS ---------
+  {
+    const int per = (B + nthr - 1) / nthr;
+    const int b0 = tid * per;
+    int run = 0;
+    for (int i = 0; i < per; ++i) {
+      const int b = b0 + i;
+      if (b < B) run += (p.lens_k[b] + 15) >> 4;
+    }
+    int x = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wtot[wave] = x;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wave; ++i) base += wtot[i];
+    int acc = base + x - run;
+    for (int i = 0; i < per; ++i) {
+      const int b = b0 + i;
+      if (b < B) {
+        sstart[b] = acc;
+        acc += (p.lens_k[b] + 15) >> 4;
+      }
+    }
+    if (tid == nthr - 1) sstart[B] = acc;
+    __syncthreads();
   }
-  const float val = acc / wsum;
-  if constexpr (BF16) {
-    reinterpret_cast<__bf16*>(p.out)[th * D + d] = (__bf16)val;
-  } else {
-    static_cast<float*>(p.out)[th * D + d] = val;
+  const int total = sstart[B];
+  const int r0 = (int)(((int64_t)w * total) / nwg), r1 = (int)(((int64_t)(w + 1) * total) / nwg);
+  if (r0 >= r1) return;  // empty range (whole workgroup)
+
+  auto seq_of = [&](int gb) __attribute__((always_inline)) {  // largest b with sstart[b] <= gb
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sstart[mid] <= gb) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+
+  const int g = hg * p.hpw + wave;
+  W wv(p, g, slabs + wave * C::SLAB);
+
+  // The range's table entries, once, in LDS (the planner keeps a range within
+  // kTblWin blocks).
+  for (int i = tid; i < r1 - r0; i += nthr) {
+    const int gb = r0 + i;
+    const int b = seq_of(gb);
+    tbl[i] = p.table[(int64_t)b * p.MB + (gb - sstart[b])];
   }
-  if (p.lse && d == 0) p.lse[th] = (M + __builtin_amdgcn_logf(wsum)) * kLn2;
+  __syncthreads();
+
+  // Segments of the range, in processing order: the piece of the last sequence
+  // Z (its head, unless it starts in this range), the piece of the first
+  // sequence A (its tail), then the whole sequences in between.  The two
+  // pieces that may be split come first, so they are published -- and their
+  // sequences merged -- while other workgroups are still streaming.
+  const int A = seq_of(r0), Z = seq_of(r1 - 1);
+  const int nseg = A == Z ? 1 : 3;
+  const int seg_lo0 = A == Z ? r0 : sstart[Z], seg_hi0 = r1;
+  const int seg_lo1 = r0, seg_hi1 = A == Z ? r0 : sstart[A + 1];
+  const int seg_lo2 = seg_hi1, seg_hi2 = A == Z ? r0 : sstart[Z];
+  auto seg_lo = [&](int i) __attribute__((always_inline)) { return i == 0 ? seg_lo0 : (i == 1 ? seg_lo1 : seg_lo2); };
+  auto seg_hi = [&](int i) __attribute__((always_inline)) { return i == 0 ? seg_hi0 : (i == 1 ? seg_hi1 : seg_hi2); };
+
+  // split pieces: at most two (the pieces of Z and of A)
+  int split_b0 = -1, split_n0 = 0, split_b1 = -1, split_n1 = 0;
+
+  // step generator over segments [seg, seg_end): steps never cross a
+  // sequence or a segment
+  int seg = 0, seg_end = 0, pos = seg_lo0, sb = seq_of(seg_lo0);
+  auto gen = [&]() __attribute__((always_inline)) {
+    Step st;
+    while (seg < seg_end && pos >= seg_hi(seg)) {
+      ++seg;
+      if (seg < seg_end) {
+        pos = seg_lo(seg);
+        if (pos < seg_hi(seg)) sb = seq_of(pos);
+      }
+    }
+    if (seg >= seg_end) {
+      st.b = -1; st.t = 0; st.Lk = 0; st.lblk = 0; st.nblk = 0; st.gblk = r0; st.first = 0; st.last = 0;
+      return st;
+    }
+    while (sstart[sb + 1] <= pos) ++sb;
+    const int s0 = sstart[sb], s1 = sstart[sb + 1];
+    const int hi = seg_hi(seg);
+    const int end = min(min(pos + C::NBS, s1), hi);
+    st.b = sb;
+    st.t = p.cu_q[sb];
+    st.Lk = p.lens_k[sb];
+    st.lblk = pos - s0;
+    st.nblk = end - pos;
+    st.gblk = pos;
+    st.first = pos == max(seg_lo(seg), s0) ? 1 : 0;
+    st.last = end == min(hi, s1) ? 1 : 0;
+    pos = end;
+    return st;
+  };
+  auto phys_of = [&](const Step& st, int* ph) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < C::NBS; ++j)
+      ph[j] = __builtin_amdgcn_readfirstlane(j < st.nblk ? tbl[st.gblk - r0 + j] : 0);
+  };
+  auto finish_piece = [&](const Step& st) __attribute__((always_inline)) {
+    const int s0 = sstart[st.b], s1 = sstart[st.b + 1];
+    const int a = max(r0, s0), z = min(r1, s1);
+    if (a == s0 && z == s1) {
+      wv.store_final(st.t);
+    } else {
+      wv.store_partial(w + st.b);
+      if (split_b0 < 0) {
+        split_b0 = st.b;
+        split_n0 = z - a;
+      } else {
+        split_b1 = st.b;
+        split_n1 = z - a;
+      }
+    }
+  };
+  // Publish this wave's split pieces: count their blocks per (sequence, KV
+  // head); the wave that completes a count merges that sequence's pieces.
+  auto publish = [&]() __attribute__((always_inline)) {
+    if (split_b0 < 0) return;
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's partial stores are complete
+    auto count = [&](int b, int n) __attribute__((always_inline)) {
+      int done = 0;
+      if (lane == 0) {
+        int* cnt = p.counters + (int64_t)b * p.Hkv + g;
+        done = __hip_atomic_fetch_add(cnt, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + n;
+        if (done == sstart[b + 1] - sstart[b])
+          __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+      }
+      return __builtin_amdgcn_readfirstlane(done) == sstart[b + 1] - sstart[b];
+    };
+    const bool last0 = count(split_b0, split_n0);
+    const bool last1 = split_b1 >= 0 && count(split_b1, split_n1);
+    if (last0) wv.merge(p.cu_q[split_b0], split_b0, sstart[split_b0], sstart[split_b0 + 1], total, nwg);
+    if (last1) wv.merge(p.cu_q[split_b1], split_b1, sstart[split_b1], sstart[split_b1 + 1], total, nwg);
+  };
+
+  // Stream segments [s_begin, s_end) through the two-buffer pipeline.
+  auto stream = [&](int s_begin, int s_end) __attribute__((always_inline)) {
+    seg = s_begin;
+    seg_end = s_end;
+    pos = seg_lo(s_begin);
+    if (pos < seg_hi(s_begin)) sb = seq_of(pos);
+    if constexpr (BF16) {
+      typename W::Buf bA, bB;
+      int ph[C::NBS];
+      Step cur = gen();
+      if (cur.b < 0) return;
+      phys_of(cur, ph);
+      wv.load(cur, ph, bA);
+      Step nxt = gen();
+      for (;;) {
+        phys_of(nxt, ph);
+        wv.load(nxt, ph, bB);
+        if (cur.first) wv.reset();
+        wv.compute(cur, bA);
+        if (cur.last) finish_piece(cur);
+        cur = nxt;
+        if (cur.b < 0) break;
+        nxt = gen();
+        phys_of(nxt, ph);
+        wv.load(nxt, ph, bA);
+        if (cur.first) wv.reset();
+        wv.compute(cur, bB);
+        if (cur.last) finish_piece(cur);
+        cur = nxt;
+        if (cur.b < 0) break;
+        nxt = gen();
+      }
+    } else {
+      int ph[C::NBS];
+      for (Step cur = gen(); cur.b >= 0; cur = gen()) {
+        phys_of(cur, ph);
+        if (cur.first) wv.reset();
+        wv.compute_f32(cur, ph);
+        if (cur.last) finish_piece(cur);
+      }
+    }
+  };
+
+  // the pieces that may be split, then publish them, then the whole sequences
+  const int nsplit_seg = nseg == 1 ? 1 : 2;
+  stream(0, nsplit_seg);
+  publish();
+  if (nseg > nsplit_seg) stream(nsplit_seg, nseg);
 }
 
 template <int D, bool BF16>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((decode_split_kernel<D, BF16>), dim3(p.max_splits, p.Hkv, p.B), dim3(64), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.max_splits <= 1) return e;
-  const int64_t total = (int64_t)p.T * p.Hq * D;
-  hipLaunchKernelGGL((decode_merge_kernel<D, BF16>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+  using C = DCfg<D>;
+  const size_t lds = (size_t)(((p.B + 1 + 3) & ~3) + 4 + kTblWin) * sizeof(int) + (size_t)p.hpw * C::SLAB;
+  // dynamic LDS above the default limit must be requested; grow it as needed
+  static size_t lds_granted = 0;
+  if (lds > lds_granted) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
+      return e;
+    }
+    lds_granted = lds;
+  }
+  hipLaunchKernelGGL((decode_kernel<D, BF16>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
   return hipGetLastError();
 }
 

@@ -69,6 +69,13 @@ __device__ __forceinline__ float xor16(float x) {
 
 // ---- memory --------------------------------------------------------------
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Load unconditionally (the address must be readable either way) and keep the
+// data only where `keep` holds.  Branch-free, so the compiler can count the
+// outstanding loads exactly and a prefetch is not waited on early.
+__device__ __forceinline__ u32x4 ld16_keep(const void* p, bool keep) {
+  const u32x4 v = ld16(p);
+  return keep ? v : u32x4{0, 0, 0, 0};
+}
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Map a linear workgroup id so that each of the 8 XCDs (which receive

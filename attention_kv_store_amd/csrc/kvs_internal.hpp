@@ -38,11 +38,14 @@ struct AttnParams {
   int32_t TPW;            // 32-token blocks per workgroup (HW * TPW == 4 waves)
   int32_t NHG;            // head groups = Hq / HW
   int32_t NV;             // virtual tiles per head group = T / (32 * TPW) + B
-  // decode split plan
-  int32_t chunk;          // keys per split (multiple of 64)
-  int32_t max_splits;     // splits per sequence the grid covers
-  float* part_o;          // [max_splits, T, Hq, D] fp32 partial outputs (normalised)
-  float* part_lse;        // [max_splits, T, Hq]   fp32 partial lse (base 2)
+  // decode work plan: the batch's key blocks, flattened sequence-major, are cut
+  // into `nwg` equal contiguous ranges, one per workgroup; a workgroup holds the
+  // waves of `hpw` consecutive KV heads.
+  int32_t nwg;            // workgroups along the flattened block axis
+  int32_t hpw;            // KV heads (waves) per workgroup
+  float* part_o;          // [nwg + B, Hq, D] fp32 partial outputs (normalised)
+  float* part_lse;        // [nwg + B, Hq]    fp32 partial lse (base 2)
+  int32_t* counters;      // [B, Hkv]         finished-block counts; zero between calls
 };
 
 hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);

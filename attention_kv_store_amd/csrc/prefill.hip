@@ -62,7 +62,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // wave-uniform by construction; readfirstlane lets the compiler see it, so
+  // every per-wave decision below is a scalar branch
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
 
   // ---- workgroup -> (sequence, token tile, head group) -------------------
@@ -114,11 +116,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
     const E* qp = static_cast<const E*>(p.q) + ((int64_t)(q0 + (ok ? qrow : 0)) * p.Hq + h) * D;
     if constexpr (BF16) {
 #pragma unroll
-      for (int ks = 0; ks < QF; ++ks) qf[ks] = ok ? ld16(qp + ks * 16 + hh * 8) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < QF; ++ks) qf[ks] = ld16_keep(qp + ks * 16 + hh * 8, ok);  // row clamped to 0 if !ok
     } else {
 #pragma unroll
       for (int c4 = 0; c4 < QF / 4; ++c4) {
-        const u32x4 w = ok ? ld16(qp + hh * (D / 2) + c4 * 4) : u32x4{0, 0, 0, 0};
+        const u32x4 w = ld16_keep(qp + hh * (D / 2) + c4 * 4, ok);
 #pragma unroll
         for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(w[e]);
       }
@@ -146,8 +148,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
     for (int it = 0; it < C::KIT; ++it) {
       const int c = it * 256 + tid;
       const int j = c / C::CPR, ch = c % C::CPR;
-      const bool ok = c < C::KCH && kv0 + j < nkeys;
-      kreg[it] = ok ? ld16(row_ptr(kbase, kv0, j, pg) + ch * (16 / C::ESZ)) : u32x4{0, 0, 0, 0};
+      // raw load, masked when written to LDS (see write_stage); readable
+      // either way: a row past nkeys lies in an owned block or, past the last
+      // owned page, in block 0 (pg entries default to 0)
+      kreg[it] = ld16(row_ptr(kbase, kv0, j & (C::BN - 1), pg) + ch * (16 / C::ESZ));
     }
     if constexpr (BF16) {
 #pragma unroll
@@ -157,8 +161,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = kq * 4 + r;
-          const bool ok = it < C::VITEMS && kv0 + j < nkeys;
-          vreg[iv * 4 + r] = ok ? ld16(row_ptr(vbase, kv0, j, pg) + dch * 8) : u32x4{0, 0, 0, 0};
+          vreg[iv * 4 + r] = ld16(row_ptr(vbase, kv0, j, pg) + (dch % (D / 8)) * 8);
         }
       }
     } else {
@@ -166,18 +169,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
       for (int it = 0; it < C::VIT; ++it) {
         const int c = it * 256 + tid;
         const int j = c / C::CPR, ch = c % C::CPR;
-        const bool ok = c < C::KCH && kv0 + j < nkeys;
-        vreg[it] = ok ? ld16(row_ptr(vbase, kv0, j, pg) + ch * 4) : u32x4{0, 0, 0, 0};
+        vreg[it] = ld16(row_ptr(vbase, kv0, j & (C::BN - 1), pg) + ch * 4);
       }
     }
   };
-  auto write_stage = [&](int buf) {
+  // Writes tile t's registers to LDS buffer `buf`; rows at or past nkeys are
+  // zeroed here (only the last tile has any).
+  auto write_stage = [&](int buf, int t) {
     char* Ks = smem + buf * C::STAGE;
     char* Vs = Ks + C::KTILE;
+    const int kv0 = t * C::BN;
+    const bool tail = kv0 + C::BN > nkeys;
+    const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
     for (int it = 0; it < C::KIT; ++it) {
       const int c = it * 256 + tid;
-      if (c < C::KCH) st16(Ks + (c / C::CPR) * C::KROW + (c % C::CPR) * 16, kreg[it]);
+      const bool keep = !tail || kv0 + c / C::CPR < nkeys;
+      if (c < C::KCH) st16(Ks + (c / C::CPR) * C::KROW + (c % C::CPR) * 16, keep ? kreg[it] : zero);
     }
     if constexpr (BF16) {
       // transpose 4 keys x 8 d into 8 rows (one per d) of 4 keys
@@ -186,7 +194,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
         const int it = iv * 256 + tid;
         if (it >= C::VITEMS) continue;
         const int kq = it % (C::BN / 4), dch = it / (C::BN / 4);
-        const u32x4* w = vreg + iv * 4;
+        u32x4 w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (!tail || kv0 + kq * 4 + r < nkeys) ? vreg[iv * 4 + r] : zero;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const uint32_t lo01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u);
@@ -202,7 +212,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
 #pragma unroll
       for (int it = 0; it < C::VIT; ++it) {
         const int c = it * 256 + tid;
-        if (c < C::KCH) st16(Vs + (c / C::CPR) * C::VROW + (c % C::CPR) * 16, vreg[it]);
+        const bool keep = !tail || kv0 + c / C::CPR < nkeys;
+        if (c < C::KCH) st16(Vs + (c / C::CPR) * C::VROW + (c % C::CPR) * 16, keep ? vreg[it] : zero);
       }
     }
   };
@@ -218,7 +229,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
   load_pages(0, pg_cur);
   if (ntiles > 1) load_pages(1, pg_nxt);
   issue_loads(0, pg_cur);
-  write_stage(0);
+  write_stage(0, 0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -255,20 +266,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
           }
         }
       }
-      // scale into base-2 units, mask, tile max
+      // scale into base-2 units, mask (diagonal / tail tiles only), tile max
       float mt = kMaskedScore;
+      if (need_mask) {
+        // key offset of register r inside a 32-key block: (r/4)*8 + hh*4 + r%4
+        const int lim = (p.causal ? qpos + 1 : Lk) - kv0 - hh * 4;   // visible iff offset < lim
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * p.scale_log2;
-          if (need_mask) {
-            const int key = kv0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-            const bool vis = p.causal ? (key <= qpos) : (key < Lk);
-            x = vis ? x : kMaskedScore;
+          for (int r = 0; r < 16; ++r) {
+            const float x = ((r >> 2) * 8 + (r & 3) + kb * 32 < lim) ? s[kb][r] * p.scale_log2 : kMaskedScore;
+            s[kb][r] = x;
+            mt = fmaxf(mt, x);
           }
-          s[kb][r] = x;
-          mt = fmaxf(mt, x);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x = s[kb][r] * p.scale_log2;
+            s[kb][r] = x;
+            mt = fmaxf(mt, x);
+          }
         }
       }
       mt = max_xor32(mt);
@@ -320,7 +340,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
       }
     }
 
-    if (has_next) write_stage((t + 1) & 1);
+    if (has_next) write_stage((t + 1) & 1, t + 1);
     __syncthreads();
   }
 
@@ -354,9 +374,12 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const size_t lds = 2 * C::STAGE;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
+      return e;
+    }
     attr_set = true;
   }
   hipLaunchKernelGGL((prefill_kernel<D, BF16>), dim3(grid), dim3(256), lds, s, p);

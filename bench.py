@@ -78,7 +78,7 @@ class Workload:
         self.kvs = kvs
         db = self.reps[0][0]
         need = kvs.workspace_size(db.q, db.k_cache, db.block_table)
-        self.ws = [torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") for _ in range(replicas)]
+        self.ws = [torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") for _ in range(replicas)]
         torch.cuda.synchronize()
 
     def store(self, i):

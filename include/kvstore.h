@@ -121,10 +121,13 @@ kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new,
  * [0, NB).  Tail rows of a sequence's last block and entries past its last block
  * are never used (their contents do not matter).
  * Dispatch uses shapes only: T == B (one new row per sequence) takes the decode
- * path (split-KV pass + merge pass); otherwise the prefill/extend path.  The
- * decode path needs scratch memory: this call keeps one grow-only device buffer
- * per device for it (allocated on first need; kvs_release_workspace frees it).
- * Use attn_varlen_paged_ex to supply the scratch yourself.
+ * path; otherwise the prefill/extend path.  The decode path cuts the batch's
+ * key blocks into equal ranges (split-KV, "Transformer 추론 커널 (3/10)", §16)
+ * and needs scratch memory for the pieces of split sequences: this call keeps
+ * one grow-only, zero-initialised device buffer per device for it (allocated
+ * on first need; kvs_release_workspace frees it).  Calls on one device that
+ * overlap in time (different streams) share that buffer and must not overlap;
+ * use attn_varlen_paged_ex with separate workspaces for that.
  */
 kvs_status attn_varlen_paged(const kvs_tensor* q,
                              const kvs_tensor* k_cache, const kvs_tensor* v_cache,
@@ -137,9 +140,11 @@ kvs_status attn_varlen_paged(const kvs_tensor* q,
 
 /* Optional host-side hints for attn_varlen_paged_ex; 0 means "unknown / choose". */
 typedef struct {
-  int32_t max_seqlen_q;  /* upper bound on Lq_b (host value), 0 = unknown            */
-  int32_t max_seqlen_k;  /* upper bound on Lk_b (host value), 0 = use 16 * MB         */
-  int32_t num_splits;    /* decode: force the number of key chunks per sequence (>=1) */
+  int32_t max_seqlen_q;  /* upper bound on Lq_b (host value), 0 = unknown; unused now  */
+  int32_t max_seqlen_k;  /* upper bound on Lk_b (host value), 0 = unknown; unused now  */
+  int32_t num_splits;    /* decode: number of equal ranges the batch's key blocks are
+                            cut into (one workgroup each); 0 = automatic.  Raised
+                            if needed so a range holds at most 2048 blocks.       */
 } kvs_hints;
 
 /* Bytes of device scratch attn_varlen_paged_ex needs for these shapes and hints
@@ -151,10 +156,12 @@ size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k
 /*
  * attn_varlen_paged_ex -- attn_varlen_paged with caller-owned scratch and hints.
  * Same computation and argument meaning.  `workspace` is a device buffer of at
- * least attn_varlen_paged_workspace_size(q, k_cache, block_table, hints) bytes
- * (may be NULL when that size is 0); its contents on entry do not matter, and
- * two calls that overlap in time must not share it.  Allocates nothing.
- * `hints` may be NULL.
+ * least attn_varlen_paged_workspace_size(q, k_cache, block_table, hints) bytes,
+ * 256-byte aligned (may be NULL when that size is 0).  It must be zero-filled
+ * before its first use with this library; every call leaves it in a state
+ * valid for the next call (its counters back at zero), so zero it once and
+ * reuse it.  Two calls that overlap in time must not share it.  Allocates
+ * nothing.  `hints` may be NULL.
  */
 kvs_status attn_varlen_paged_ex(const kvs_tensor* q,
                                 const kvs_tensor* k_cache, const kvs_tensor* v_cache,

@@ -97,8 +97,9 @@ def test_workspace_sizing_and_check(lib):
     h = L.KvsHints()
     h.num_splits = 4
     need = lib.attn_varlen_paged_workspace_size(ref(a["q"]), ref(a["k"]), ref(a["table"]), ctypes.byref(h))
-    # 4 splits x 4 rows x 8 heads x (64 + 1) floats, each part 256-byte aligned
-    assert need == 4 * 4 * 8 * 64 * 4 + 512
+    # (4 ranges + 4 sequences) slots x 8 heads x 64 floats, their lse, and one
+    # counter per (sequence, KV head), each part 256-byte aligned
+    assert need == 8 * 8 * 64 * 4 + 256 + 256
     st = _call_ex(lib, a, hints=h, ws=FAKE, ws_bytes=need - 1)
     assert st == L.KVS_ERR_WORKSPACE
     h.num_splits = 1
