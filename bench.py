@@ -39,8 +39,74 @@ def log(*a):
 
 
 def _src_sha(name: str) -> str:
-    path = os.path.join(ROOT, "attention_kv_store_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel's source file together with the shared headers and the
+    planner that sets its launch shape."""
+    h = hashlib.sha256()
+    for f in (name, "kvs_device.hpp", "kvs_internal.hpp", "api.hip"):
+        h.update(open(os.path.join(ROOT, "attention_kv_store_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# kernel symbol (as rocprofv3 names it) and source file of each timed workload
+COUNTED = {
+    "paged_decode_bf16": ("kvs::decode_kernel<64, true>", "decode.hip"),
+    "causal_prefill_bf16": ("kvs::prefill_kernel<128, true>", "prefill.hip"),
+}
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> None:
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) into HBM bytes per launch.
+
+    Both counters are scaled by what they read for a plain copy of known size:
+    the kv_store_paged launch that fills a decode replica's pool copies every
+    context row (K+V of all KV heads, 2 * sum(Lk) * Hkv * D * 2 bytes read and
+    written, plus the int32 slots read)."""
+    import csv
+    from collections import defaultdict
+
+    from workloads import kv_bytes, paged_decode_bf16
+
+    def load(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                rows[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+        return rows
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    dec = paged_decode_bf16()
+    copy_bytes = kv_bytes(dec)                       # K+V rows written (and read)
+    slot_bytes = 4 * int(dec.k_lens.sum())
+    cal = [i for i, (k, v) in write.items()
+           if "kv_store_kernel" in k and abs(v * 1024 - copy_bytes) < 0.01 * copy_bytes]
+    if not cal:
+        raise SystemExit("no full-pool kv_store_paged dispatch found for calibration")
+    f_kib = sum(fetch[i][1] for i in cal) / len(cal)
+    w_kib = sum(write[i][1] for i in cal) / len(cal)
+    read_factor = (copy_bytes + slot_bytes) / (f_kib * 1024)
+    write_factor = copy_bytes / (w_kib * 1024)
+    out = {"_calibration": {
+        "copy": f"kv_store_paged of all {int(dec.k_lens.sum())} context rows of paged_decode_bf16",
+        "copy_read_bytes": copy_bytes + slot_bytes, "copy_write_bytes": copy_bytes,
+        "fetch_kib": round(f_kib, 3), "write_kib": round(w_kib, 3),
+        "read_factor": round(read_factor, 5), "write_factor": round(write_factor, 5),
+        "dispatches": len(cal), "command": command}}
+    for wl, (sym, src) in COUNTED.items():
+        fk = [v for k, v in fetch.values() if sym in k]
+        wk = [v for k, v in write.values() if sym in k]
+        if not fk or not wk:
+            continue
+        fmean, wmean = sum(fk) / len(fk), sum(wk) / len(wk)
+        out[wl] = {"kernel": sym, "kernel_src_sha": _src_sha(src), "dispatches": len(fk),
+                   "fetch_kib": round(fmean, 3), "write_kib": round(wmean, 3),
+                   "read_bytes_per_launch": round(fmean * 1024 * read_factor),
+                   "write_bytes_per_launch": round(wmean * 1024 * write_factor),
+                   "hbm_bytes_per_launch": round(fmean * 1024 * read_factor + wmean * 1024 * write_factor)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    log(json.dumps(out, indent=1))
 
 
 def _traffic(kernel_src: str, workload: str):
@@ -154,7 +220,13 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--counter-command", default="", help="command line recorded with --summarize-counters")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.counter_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the attention shards by KV head with no exchange; see the design notes).", file=sys.stderr)
@@ -201,7 +273,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_kernel + decode_merge_kernel (one attn_varlen_paged call)",
+            "kernel": COUNTED["paged_decode_bf16"][0] + " (the one launch of each attn_varlen_paged call)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -227,6 +299,7 @@ def main():
         line["prefill"] = {
             "workload": "causal_prefill_bf16",
             "metric": "attention TFLOP/s", "unit": "TFLOP/s", "bound": "mfma",
+            "kernel": COUNTED["causal_prefill_bf16"][0],
             "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "frac": round(tf / BF16_PEAK_TFLOPS, 4),
             "flops_per_launch": fl, "avg_launch_us": round(pattn * 1e3, 3),
             "ms_per_step": round(pms, 6), "steps": psteps,
