@@ -35,6 +35,9 @@
 
 namespace kvs {
 
+// Largest growth (base 2) of a row maximum absorbed without rescaling.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, bool BF16>
 struct PCfg {
   static constexpr int BN = BF16 ? 64 : 32;   // keys per tile
@@ -56,8 +59,10 @@ struct PCfg {
   static constexpr int NDB = D / 32;           // 32-wide d blocks of the output
 };
 
+// Two workgroups per CU (two waves per SIMD): one workgroup's barrier and
+// load waits overlap the other's math.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(AttnParams p) {
   using C = PCfg<D, BF16>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -109,20 +114,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
   // ---- Q fragment (B operand of S^T = K . Q^T), loaded once -------------
   // bf16 32x32x16: lane holds Q[row n][ks*16 + hh*8 .. +8] for k-step ks.
   // fp32 32x32x2: lane holds Q[row n][hh*D/2 + ks] for k-step ks.
+  // The sign of the scale is moved into Q (an exact sign flip), so the score
+  // multiplier c is >= 0 and a row maximum of raw scores is also the maximum of
+  // the scaled ones.
   constexpr int QF = BF16 ? D / 16 : D / 2;
   typename std::conditional<BF16, u32x4, float>::type qf[QF];
+  const float c = fabsf(p.scale_log2);
   {
     const bool ok = wave_live && qrow < Lq;
+    const uint32_t flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
     const E* qp = static_cast<const E*>(p.q) + ((int64_t)(q0 + (ok ? qrow : 0)) * p.Hq + h) * D;
     if constexpr (BF16) {
 #pragma unroll
-      for (int ks = 0; ks < QF; ++ks) qf[ks] = ld16_keep(qp + ks * 16 + hh * 8, ok);  // row clamped to 0 if !ok
+      for (int ks = 0; ks < QF; ++ks) {
+        const u32x4 w = ld16_keep(qp + ks * 16 + hh * 8, ok);  // row clamped to 0 if !ok
+        qf[ks] = u32x4{w[0] ^ flip, w[1] ^ flip, w[2] ^ flip, w[3] ^ flip};
+      }
     } else {
 #pragma unroll
       for (int c4 = 0; c4 < QF / 4; ++c4) {
         const u32x4 w = ld16_keep(qp + hh * (D / 2) + c4 * 4, ok);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(w[e]);
+        for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(w[e] ^ (flip << 16));
       }
     }
   }
@@ -219,7 +232,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
   };
 
   // ---- online-softmax state -------------------------------------------
-  float m_run = kMaskedScore;   // running max, base-2 units, same in both lane halves
+  // m_run is the reference maximum that P and l are taken against (base-2
+  // units, same in both lane halves).  It is only moved up when a tile's
+  // maximum exceeds it by more than kRescaleSlack: until then P <= 2^slack, and
+  // since l and O use the same reference the quotient O / l is unchanged, so
+  // most tiles skip rescaling the output accumulators.
+  float m_run = kMaskedScore;
   float l_run = 0.f;            // this lane's share of the running sum
   f32x16 o[C::NDB];
 #pragma unroll
@@ -266,7 +284,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
           }
         }
       }
-      // scale into base-2 units, mask (diagonal / tail tiles only), tile max
+      // Tile maximum.  Unmasked tiles take it over raw scores (c >= 0) and fold
+      // the scale into the exponent's fma; tiles that cross the causal
+      // diagonal or the key tail scale first and select masked keys away.
       float mt = kMaskedScore;
       if (need_mask) {
         // key offset of register r inside a 32-key block: (r/4)*8 + hh*4 + r%4
@@ -275,9 +295,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float x = ((r >> 2) * 8 + (r & 3) + kb * 32 < lim) ? s[kb][r] * p.scale_log2 : kMaskedScore;
+            const float x = ((r >> 2) * 8 + (r & 3) + kb * 32 < lim) ? s[kb][r] * c : kMaskedScore;
             s[kb][r] = x;
             mt = fmaxf(mt, x);
+          }
+        }
+        mt = max_xor32(mt);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+        }
+        mt = max_xor32(mt) * c;
+      }
+      if (__ballot(mt > m_run + kRescaleSlack)) {   // wave-uniform
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+      }
+      float lsum = 0.f;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_run);
+            s[kb][r] = e;
+            lsum += e;
           }
         }
       } else {
@@ -285,29 +333,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnParams p) {
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float x = s[kb][r] * p.scale_log2;
-            s[kb][r] = x;
-            mt = fmaxf(mt, x);
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_run));
+            s[kb][r] = e;
+            lsum += e;
           }
         }
       }
-      mt = max_xor32(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
-          s[kb][r] = e;
-          lsum += e;
-        }
-      }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+      l_run += lsum;
 
       // O^T += V^T . P^T
 #pragma unroll

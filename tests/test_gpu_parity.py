@@ -143,6 +143,29 @@ def test_shared_prefix_blocks():
     _check(b, out, lse)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("scale", [-0.11, 0.0, 0.9])
+@pytest.mark.parametrize("decode", [False, True])
+def test_scale_sign_and_size(dtype, scale, decode):
+    """Negative, zero and large score scales.  A zero scale weighs the visible
+    keys uniformly (masked keys must still get none); a large one makes row
+    maxima jump by many powers of two between key tiles."""
+    if decode:
+        k = [1, 17, 300, 1000, 64]
+        q = [1] * len(k)
+    else:
+        q = [1, 33, 70, 130, 64]
+        k = [1, 38, 110, 130, 200]
+    b = _mk(601, q, k, Hq=8, Hkv=2, D=64, dtype=dtype, causal=True, scale=scale,
+            name=f"scale{scale}-{dtype}-{'dec' if decode else 'pre'}")
+    out, lse = _run(b)
+    # The fp32 bound is set for scale 1/sqrt(D), where scaled scores are O(1);
+    # the rounding of the fp32 dot product q.k is multiplied by |scale|, so the
+    # bound grows with |scale| * sqrt(D) beyond that.
+    tol = TOL[dtype] * max(1.0, abs(scale) * 8.0) if dtype == "fp32" else None
+    _check(b, out, lse, tol=tol)
+
+
 # --------------------------------------------------------------- decode ---
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
