@@ -194,6 +194,13 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   if (nwg > (1 << 20)) return fail(KVS_ERR_UNSUPPORTED, "num_splits too large");
   p.hpw = hpw;
   p.nwg = (int32_t)nwg;
+  // dynamic LDS a decode workgroup may take (160 KiB per CU, less the kernel's static LDS)
+  constexpr size_t kLdsBudget = 160 * 1024 - 256;
+  // partial outputs are addressed with 32-bit byte offsets
+  if ((double)(nwg + B) * Hq * D * sizeof(float) >= 2147483648.0)
+    return fail(KVS_ERR_UNSUPPORTED, "decode partial buffer would exceed 2 GiB (num_splits %lld)", (long long)nwg);
+  if (kvs::decode_lds_bytes((int)B, hpw, kvs::decode_slab_bytes((int)D)) > kLdsBudget)
+    return fail(KVS_ERR_UNSUPPORTED, "decode batch too large for one workgroup's LDS (B=%lld)", (long long)B);
   if (nwg > 1) {
     const size_t slots = (size_t)nwg + B;
     plan->ws_lse_off = align_up(slots * Hq * D * sizeof(float), 256);

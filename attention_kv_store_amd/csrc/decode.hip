@@ -12,18 +12,20 @@
 // number of bytes whatever the length mix, and the grid is sized to be
 // resident in one round (8 waves per CU on 256 CUs).  A range covers the tail
 // of one sequence, whole sequences, and the head of another.  A workgroup walks
-// its range as one continuous stream of steps (up to NBS blocks, never crossing
-// a sequence): the next step -- including the next sequence's query row -- is
-// always being loaded while the current one is computed, so sequence switches
-// cost no pipeline drain.  A sequence wholly inside the range is finished in
-// place.  A sequence cut by a range boundary leaves a normalised partial
-// (O_i / l_i, lse_i) per piece; after its stream, each wave adds its pieces'
-// block counts to per-(sequence, KV head) counters, and the wave that completes
-// a sequence merges its pieces in one round of loads:
+// its range as one continuous stream of steps (never crossing a sequence): the
+// next step -- including the next sequence's query row -- is always being
+// loaded while the current one is computed, so sequence switches cost no
+// pipeline drain.  A sequence wholly inside the range is finished in place.
+// A sequence cut by a range boundary leaves a normalised partial
+// (O_i / l_i, lse_i) per piece.  The (at most two) pieces of a range are
+// streamed first; each wave then adds their block counts to per-(sequence,
+// KV head) counters, and the wave that completes a sequence merges its pieces
+// in one round of loads:
 //   lse = M + log2 sum 2^(lse_i - M),  out = sum 2^(lse_i - lse) O_i,
-// then resets the counter, so no second launch is needed.  Partials and counts
-// travel through agent-scope atomics only (never agent-scope fences, which on
-// this chip write back and invalidate a whole XCD's L2).
+// then resets the counter, so no second launch is needed; the whole sequences
+// of the range follow.  Partials and counts travel through device-scope
+// stores, loads and atomics only (never agent-scope fences, which on this chip
+// write back and invalidate a whole XCD's L2).
 //
 // Inside a workgroup, wave w handles KV head hg * hpw + w; the waves run
 // independently (each has a private LDS slab).  Per wave:
@@ -50,25 +52,46 @@ namespace kvs {
 
 template <int D>
 struct DCfg {
-  static constexpr int NBS = D == 64 ? 4 : 1;     // 16-key blocks per step (K+V per wave: 16 KB at D 64, 8 KB at D 128)
+  // 16-key blocks per step.  One block keeps the bytes in flight near the
+  // bandwidth-latency product: a deeper prefetch only lengthens the memory
+  // queues (and so the latency of every access, including the publication
+  // of partials at the end), without raising the throughput.
+  static constexpr int NBS = 1;
   static constexpr int KI = D / 32;               // 16x16x32 k-steps over d
   static constexpr int NDB = D / 16;              // 16-wide d blocks of the output
   static constexpr int VROW = 40;                 // bytes per V^T row (16 keys + pad)
   static constexpr int VBLK = D * VROW;           // V^T bytes per 16-key block
-  static constexpr int SLAB = NBS * VBLK;         // V^T bytes per wave
+  static constexpr int SLAB = NBS * VBLK;         // V^T bytes per wave (decode_slab_bytes)
   static constexpr int VIL = D / 64;              // (key pair, 8-d chunk) items per lane per block
   static constexpr int DPL = D / 64;              // d values per lane in the merge
 };
 
-constexpr int kDecodeMaxB = 8192;   // sequences whose block prefix fits in LDS
-constexpr int kTblWin = 2048;       // most blocks in one workgroup's range (its table entries sit in LDS)
-constexpr int kMergeChunk = 16;     // pieces merged per round of loads
+constexpr int kTblWin = kDecodeTblWin;  // most blocks in one workgroup's range (its table entries sit in LDS)
 // s_waitcnt immediate with vmcnt = 0 and the other counters left alone (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// floor(x / d) for x < 2^52: a 32-bit division whenever x fits in 32 bits
+// (the 64-bit division is a long instruction sequence).
+__device__ __forceinline__ int64_t udiv_small(uint64_t x, uint32_t d) {
+  if ((x >> 32) == 0) return (int64_t)((uint32_t)x / d);
+  return (int64_t)(x / d);
+}
 // Start of range w on the flattened block axis: floor(w * total / nwg).
-__device__ __forceinline__ int64_t range_start64(int64_t w, int total, int nwg) { return (w * total) / nwg; }
+__device__ __forceinline__ int64_t range_start64(int64_t w, int total, int nwg) {
+  return udiv_small((uint64_t)w * (uint32_t)total, (uint32_t)nwg);
+}
+
+// Cache-policy operand of the buffer intrinsics for device (agent) scope: the
+// access goes to the device-wide coherence point, bypassing a stale or
+// non-coherent copy in one XCD's L2.
+constexpr int kDeviceScope = 16;
+// Word 3 of a raw (untyped) buffer resource on gfx9.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
 
 __device__ __forceinline__ float atomic_ld(const float* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -135,8 +158,7 @@ struct DecodeWave {
         s[j][r] = x;
         mt = fmaxf(mt, x);
       }
-    mt = fmaxf(mt, xor16(mt));
-    mt = max_xor32(mt);
+    mt = max_xor32(max_xor16(mt));
     const float m_new = fmaxf(m_run, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -279,8 +301,7 @@ struct DecodeWave {
   // ---- end of a piece ------------------------------------------------------
   // Combine the 4 lane groups' shares of l; returns the base-2 lse.
   __device__ __forceinline__ float finish(float* inv_out) {
-    float l_tot = l_run + xor16(l_run);
-    l_tot = sum_xor32(l_tot);
+    const float l_tot = sum_xor32(sum_xor16(l_run));
     *inv_out = 1.0f / l_tot;
     return m_run + __builtin_amdgcn_logf(l_tot);
   }
@@ -304,100 +325,171 @@ struct DecodeWave {
     if (p.lse && grp == 0) p.lse[(int64_t)t * p.Hq + h] = lse2 * kLn2;
   }
 
-  // Partials are published with agent-scope relaxed atomic stores (written
-  // through to the device-wide coherence point); nothing waits for them here.
+  // Bytes of the partial-output array [nwg + B, Hq, D] (the planner keeps it
+  // below 2 GiB, so 32-bit buffer offsets reach all of it).
+  __device__ __forceinline__ uint32_t part_bytes() const {
+    return (uint32_t)(p.nwg + p.B) * (uint32_t)p.Hq * (uint32_t)(D * 4);
+  }
+
+  // Partials are published with device-scope stores (written through to the
+  // device-wide coherence point); nothing waits for them here.
   __device__ __forceinline__ void store_partial(int slot) {
     float inv;
     const float lse2 = finish(&inv);
     if (!head_ok) return;
-    const int64_t prow = (int64_t)slot * p.Hq + h;
+    const uint32_t prow = (uint32_t)slot * (uint32_t)p.Hq + (uint32_t)h;
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(p.part_o, part_bytes());
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) atomic_st(p.part_o + prow * D + db * 16 + grp * 4 + r, o[db][r] * inv);
+    for (int db = 0; db < C::NDB; ++db) {
+      const u32x4 v = {__float_as_uint(o[db][0] * inv), __float_as_uint(o[db][1] * inv),
+                       __float_as_uint(o[db][2] * inv), __float_as_uint(o[db][3] * inv)};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (prow * D + db * 16 + grp * 4) * 4, 0, kDeviceScope);
+    }
     if (grp == 0) atomic_st(p.part_lse + prow, lse2);
   }
 
-  // Merge the pieces of sequence b (query row t) for this wave's query heads:
-  // the pieces are the partial slots w + b of the workgroups w whose ranges
-  // meet blocks [s0, s1).  Heads go HB at a time and pieces PC at a time; in a
-  // round, lane i loads the lse of (piece i / HB, head i % HB), every lane loads
-  // its d = lane + 64 k of each (piece, head) output, and all loads are issued
-  // before any is used (one memory round trip per round).
-  __device__ __forceinline__ void merge(int t, int b, int s0, int s1, int total, int nwg) {
+  // Merge the pieces of up to two sequences (nm of them; query rows t[m],
+  // blocks [s0[m], s1[m]) on the flattened axis) for this wave's query heads.
+  // The pieces of sequence b are the partial slots w + b of the workgroups w
+  // whose ranges meet its blocks; the pieces of both sequences form one list
+  // of items.  Heads go HB at a time and items PC at a time.  In a round, lane
+  // i loads the lse of (item i / HB, head j = i % HB) and every lane loads its
+  // d = lane + 64 k of each (item, head) output, all before any is used (one
+  // memory round trip).  The lanes of head j then hold that head's running
+  // maximum M and weight sum W per sequence (cross-lane reductions), and each
+  // output element adds its items with independent fmas:
+  //   M' = max(M, max_i lse_i),  W' = W 2^(M - M') + sum_i 2^(lse_i - M'),
+  //   acc' = acc 2^(M - M') + sum_i 2^(lse_i - M') O_i,   out = acc / W.
+  __device__ __forceinline__ void merge(int nm, const int* t, const int* bs, const int* s0, const int* s1, int total,
+                                        int nwg) {
     constexpr int HB = 4;
-    constexpr int PC = D == 64 ? 8 : 4;
-    const int64_t wf = (((int64_t)s0 + 1) * nwg - 1) / total;   // range holding block s0
-    const int64_t wl = ((int64_t)s1 * nwg - 1) / total;         // range holding block s1 - 1
+    constexpr int PC = D == 64 ? 16 : 8;
+    int wf[2], cnt[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int mm = m < nm ? m : 0;
+      // ranges holding the first and the last block of the sequence
+      wf[m] = (int)udiv_small((uint64_t)(s0[mm] + 1) * (uint32_t)nwg - 1, (uint32_t)total);
+      const int wl = (int)udiv_small((uint64_t)s1[mm] * (uint32_t)nwg - 1, (uint32_t)total);
+      cnt[m] = m < nm ? wl - wf[m] + 1 : 0;
+    }
+    const int nitems = cnt[0] + cnt[1];
+    const bool none_empty = total >= nwg;   // then every range holds at least one block
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(p.part_o, part_bytes());
+    const int hj = lane % HB;                // the head whose running state this lane holds
     for (int qh0 = 0; qh0 < p.G; qh0 += HB) {
-      float M[HB], wsum[HB], acc[HB][C::DPL];
+      float M[2] = {kMaskedScore, kMaskedScore}, W[2] = {0.f, 0.f};
+      float acc[2][HB][C::DPL];
 #pragma unroll
-      for (int j = 0; j < HB; ++j) {
-        M[j] = kMaskedScore;
-        wsum[j] = 0.f;
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int k = 0; k < C::DPL; ++k) acc[j][k] = 0.f;
-      }
-      for (int64_t w0 = wf; w0 <= wl; w0 += PC) {
-        // this lane's lse: piece w0 + lane / HB, head qh0 + lane % HB
-        float lsl = kMaskedScore;
+        for (int j = 0; j < HB; ++j)
+#pragma unroll
+          for (int k = 0; k < C::DPL; ++k) acc[m][j][k] = 0.f;
+      for (int i0 = 0; i0 < nitems; i0 += PC) {
+        // item i -> (sequence sel, range w); slot w + b_sel.  Items past the
+        // list reuse its last slot (a readable address) and are not live.
+        const int nround = min(PC, nitems - i0);
+        auto item = [&](int i, int& sel) __attribute__((always_inline)) {
+          const int ic = i0 + min(i, nround - 1);
+          sel = ic >= cnt[0] ? 1 : 0;
+          return wf[sel] + (ic - (sel ? cnt[0] : 0));
+        };
+        // live items of the round as a bit mask; with at least as many blocks
+        // as ranges every range is non-empty, otherwise lane i checks item i
+        uint64_t livemask;
+        if (none_empty) {
+          livemask = nround >= 64 ? ~0ull : ((1ull << nround) - 1);
+        } else {
+          int sl;
+          const int wl = item(lane, sl);
+          livemask = __ballot(lane < nround && range_start64(wl + 1, total, nwg) > range_start64(wl, total, nwg));
+        }
+        int lsel;
+        float lsl;
         {
-          const int64_t w = w0 + (lane % (PC * HB)) / HB;
-          const bool live = lane < PC * HB && w <= wl && range_start64(w + 1, total, nwg) > range_start64(w, total, nwg);
-          const int hh = g * p.G + min(qh0 + lane % HB, p.G - 1);
-          const float l = atomic_ld(p.part_lse + ((live ? w : wf) + b) * p.Hq + hh);
-          lsl = live ? l : kMaskedScore;
+          const int il = (lane % (PC * HB)) / HB;
+          const int slot = item(il, lsel) + bs[lsel];
+          const int hh = g * p.G + min(qh0 + hj, p.G - 1);
+          const float l = atomic_ld(p.part_lse + (int64_t)slot * p.Hq + hh);
+          lsl = (lane < PC * HB && ((livemask >> il) & 1)) ? l : kMaskedScore;
         }
         float ov[PC][HB][C::DPL];
 #pragma unroll
         for (int i = 0; i < PC; ++i) {
-          const int64_t slot = min(w0 + i, wl) + b;
+          int sel;
+          const uint32_t slot = (uint32_t)(item(i, sel) + bs[sel]);
 #pragma unroll
           for (int j = 0; j < HB; ++j) {
-            const int hh = g * p.G + min(qh0 + j, p.G - 1);
+            const uint32_t hh = (uint32_t)(g * p.G + min(qh0 + j, p.G - 1));
 #pragma unroll
-            for (int k = 0; k < C::DPL; ++k) ov[i][j][k] = atomic_ld(p.part_o + (slot * p.Hq + hh) * D + lane + 64 * k);
+            for (int k = 0; k < C::DPL; ++k)
+              ov[i][j][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                  rs, ((slot * (uint32_t)p.Hq + hh) * D + lane + 64 * k) * 4, 0, kDeviceScope));
           }
         }
+        // running maximum and weight sum of head hj, per sequence, over the
+        // lanes that hold that head (lane bits above log2(HB))
+        static_assert(HB == 4, "the reductions below run over the lanes that share lane % 4");
+        float Mn[2], sc[2];
 #pragma unroll
-        for (int j = 0; j < HB; ++j) {
-          float ls[PC];
+        for (int m = 0; m < 2; ++m) {
+          const float x = max_mod4(lsel == m ? lsl : kMaskedScore);
+          Mn[m] = fmaxf(M[m], x);
+          sc[m] = __builtin_amdgcn_exp2f(M[m] - Mn[m]);
+        }
+        const float wt = lsl == kMaskedScore ? 0.f : __builtin_amdgcn_exp2f(lsl - (lsel ? Mn[1] : Mn[0]));
 #pragma unroll
-          for (int i = 0; i < PC; ++i) ls[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsl), i * HB + j));
-          float Mn = M[j];
+        for (int m = 0; m < 2; ++m) {
+          const float x = sum_mod4(lsel == m ? wt : 0.f);
+          W[m] = W[m] * sc[m] + x;
+          M[m] = Mn[m];
+        }
 #pragma unroll
-          for (int i = 0; i < PC; ++i) Mn = fmaxf(Mn, ls[i]);
-          const float sc = __builtin_amdgcn_exp2f(M[j] - Mn);
-          wsum[j] *= sc;
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int k = 0; k < C::DPL; ++k) acc[j][k] *= sc;
+          for (int j = 0; j < HB; ++j) {
+            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[m]), j));
 #pragma unroll
-          for (int i = 0; i < PC; ++i) {
-            // pieces that do not exist are selected away, never multiplied by 0
-            const bool use = ls[i] != kMaskedScore;
-            const float wt = use ? __builtin_amdgcn_exp2f(ls[i] - Mn) : 0.f;
-            wsum[j] += wt;
-#pragma unroll
-            for (int k = 0; k < C::DPL; ++k) acc[j][k] = use ? acc[j][k] + wt * ov[i][j][k] : acc[j][k];
+            for (int k = 0; k < C::DPL; ++k) acc[m][j][k] *= f;
           }
-          M[j] = Mn;
+#pragma unroll
+        for (int i = 0; i < PC; ++i) {
+          // uniform: items that do not exist are skipped, never weighted by 0
+          if (!((livemask >> i) & 1)) continue;
+          const int sel = i0 + i >= cnt[0] ? 1 : 0;
+#pragma unroll
+          for (int j = 0; j < HB; ++j) {
+            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), i * HB + j));
+#pragma unroll
+            for (int k = 0; k < C::DPL; ++k) {
+              if (sel) acc[1][j][k] = fmaf(f, ov[i][j][k], acc[1][j][k]);
+              else acc[0][j][k] = fmaf(f, ov[i][j][k], acc[0][j][k]);
+            }
+          }
         }
       }
 #pragma unroll
-      for (int j = 0; j < HB; ++j) {
-        if (qh0 + j >= p.G) break;
-        const int hh = g * p.G + qh0 + j;
-        const float inv = 1.0f / wsum[j];
-        const int64_t orow = ((int64_t)t * p.Hq + hh) * D;
+      for (int m = 0; m < 2; ++m) {
+        if (m >= nm) break;
 #pragma unroll
-        for (int k = 0; k < C::DPL; ++k) {
-          if constexpr (BF16) {
-            reinterpret_cast<__bf16*>(p.out)[orow + lane + 64 * k] = (__bf16)(acc[j][k] * inv);
-          } else {
-            static_cast<float*>(p.out)[orow + lane + 64 * k] = acc[j][k] * inv;
+        for (int j = 0; j < HB; ++j) {
+          if (qh0 + j >= p.G) break;
+          const int hh = g * p.G + qh0 + j;
+          const float Wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(W[m]), j));
+          const float Mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M[m]), j));
+          const float inv = 1.0f / Wj;
+          const int64_t orow = ((int64_t)t[m] * p.Hq + hh) * D;
+#pragma unroll
+          for (int k = 0; k < C::DPL; ++k) {
+            if constexpr (BF16) {
+              reinterpret_cast<__bf16*>(p.out)[orow + lane + 64 * k] = (__bf16)(acc[m][j][k] * inv);
+            } else {
+              static_cast<float*>(p.out)[orow + lane + 64 * k] = acc[m][j][k] * inv;
+            }
           }
+          if (p.lse && lane == 0) p.lse[(int64_t)t[m] * p.Hq + hh] = (Mj + __builtin_amdgcn_logf(Wj)) * kLn2;
         }
-        if (p.lse && lane == 0) p.lse[(int64_t)t * p.Hq + hh] = (M[j] + __builtin_amdgcn_logf(wsum[j])) * kLn2;
       }
     }
   }
@@ -409,15 +501,19 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   using W = DecodeWave<D, BF16>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int B = p.B;
-  int* sstart = reinterpret_cast<int*>(smem);        // [B + 1] block prefix
-  int* sflag = sstart + ((B + 1 + 3) & ~3);          // [4]    broadcast slots
-  int* tbl = sflag + 4;                              // [kTblWin] physical blocks of the range window
+  int* slens = reinterpret_cast<int*>(smem);         // [B]      seqlens_k
+  int* sstart = slens + ((B + 3) & ~3);              // [B + 1]  exclusive block prefix
+  int* tbl = sstart + ((B + 1 + 3) & ~3);            // [kTblWin] physical blocks of the range
   char* slabs = reinterpret_cast<char*>(tbl + kTblWin);
   __shared__ int wtot[8];
 
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int w = blockIdx.x, hg = blockIdx.y, nwg = p.nwg;
+
+  // ---- seqlens_k into LDS ---------------------------------------------------
+  for (int b = tid; b < B; b += nthr) slens[b] = p.lens_k[b];
+  __syncthreads();
 
   // ---- exclusive prefix of ceil(Lk_b / 16) over the batch, in LDS ---------
   {
@@ -426,14 +522,9 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     int run = 0;
     for (int i = 0; i < per; ++i) {
       const int b = b0 + i;
-      if (b < B) run += (p.lens_k[b] + 15) >> 4;
+      if (b < B) run += (slens[b] + 15) >> 4;
     }
-    int x = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
+    const int x = wave_inclusive_sum(run);
     if (lane == 63) wtot[wave] = x;
     __syncthreads();
     int base = 0;
@@ -443,7 +534,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       const int b = b0 + i;
       if (b < B) {
         sstart[b] = acc;
-        acc += (p.lens_k[b] + 15) >> 4;
+        acc += (slens[b] + 15) >> 4;
       }
     }
     if (tid == nthr - 1) sstart[B] = acc;
@@ -511,8 +602,8 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     const int hi = seg_hi(seg);
     const int end = min(min(pos + C::NBS, s1), hi);
     st.b = sb;
-    st.t = p.cu_q[sb];
-    st.Lk = p.lens_k[sb];
+    st.t = sb;   // one query row per sequence: cu_seqlens_q[b] = b
+    st.Lk = slens[sb];
     st.lblk = pos - s0;
     st.nblk = end - pos;
     st.gblk = pos;
@@ -547,20 +638,26 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   auto publish = [&]() __attribute__((always_inline)) {
     if (split_b0 < 0) return;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's partial stores are complete
-    auto count = [&](int b, int n) __attribute__((always_inline)) {
-      int done = 0;
-      if (lane == 0) {
-        int* cnt = p.counters + (int64_t)b * p.Hkv + g;
-        done = __hip_atomic_fetch_add(cnt, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + n;
-        if (done == sstart[b + 1] - sstart[b])
-          __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-      }
-      return __builtin_amdgcn_readfirstlane(done) == sstart[b + 1] - sstart[b];
-    };
-    const bool last0 = count(split_b0, split_n0);
-    const bool last1 = split_b1 >= 0 && count(split_b1, split_n1);
-    if (last0) wv.merge(p.cu_q[split_b0], split_b0, sstart[split_b0], sstart[split_b0 + 1], total, nwg);
-    if (last1) wv.merge(p.cu_q[split_b1], split_b1, sstart[split_b1], sstart[split_b1 + 1], total, nwg);
+    // lane 0 counts the first split sequence, lane 1 the second: one atomic
+    // instruction, one round trip
+    const int mb = lane == 0 ? split_b0 : split_b1;
+    const int mn = lane == 0 ? split_n0 : split_n1;
+    bool done = false;
+    if (lane < 2 && mb >= 0) {
+      int* cnt = p.counters + (int64_t)mb * p.Hkv + g;
+      const int need = sstart[mb + 1] - sstart[mb];
+      done = __hip_atomic_fetch_add(cnt, mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mn == need;
+      if (done) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+    }
+    const uint64_t lastm = __ballot(done);
+    int nm = 0, mt[2], mbs[2], ms0[2], ms1[2];
+    if (lastm & 1) {
+      mt[nm] = split_b0; mbs[nm] = split_b0; ms0[nm] = sstart[split_b0]; ms1[nm] = sstart[split_b0 + 1]; ++nm;
+    }
+    if (lastm & 2) {
+      mt[nm] = split_b1; mbs[nm] = split_b1; ms0[nm] = sstart[split_b1]; ms1[nm] = sstart[split_b1 + 1]; ++nm;
+    }
+    if (nm > 0) wv.merge(nm, mt, mbs, ms0, ms1, total, nwg);
   };
 
   // Stream segments [s_begin, s_end) through the two-buffer pipeline.
@@ -616,7 +713,8 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 template <int D, bool BF16>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   using C = DCfg<D>;
-  const size_t lds = (size_t)(((p.B + 1 + 3) & ~3) + 4 + kTblWin) * sizeof(int) + (size_t)p.hpw * C::SLAB;
+  static_assert(C::SLAB == D * 40, "decode_slab_bytes must match the slab layout");
+  const size_t lds = decode_lds_bytes(p.B, p.hpw, C::SLAB);
   // dynamic LDS above the default limit must be requested; grow it as needed
   static size_t lds_granted = 0;
   if (lds > lds_granted) {

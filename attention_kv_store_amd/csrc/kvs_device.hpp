@@ -60,11 +60,54 @@ __device__ __forceinline__ f32x4 mfma16x16x4_f32(float a, float b, const f32x4& 
 // ---- cross-lane ------------------------------------------------------------
 // Combine a value with the one in lane (lane ^ 32).  ds_bpermute through the
 // LDS crossbar; one instruction per call.
-__device__ __forceinline__ float max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
-// Value of lane (lane ^ 16) via the LDS crossbar swizzle (no LDS storage used).
-__device__ __forceinline__ float xor16(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+// Cross-lane combines on the VALU (gfx950 permlane swaps): with both operands
+// the same register, the pair returned holds this lane's value and the value
+// of lane ^ 16 (resp. lane ^ 32), in an order that depends on the lane, so it
+// is only ever combined symmetrically.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Value of lane (l & ~15) | ((l - n) & 15): a rotation inside each row of 16
+// lanes (DPP row_ror, n in 1..15).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  static_assert(N >= 1 && N <= 15, "row_ror takes 1..15");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+// Max / sum over the 16 lanes that share lane % 4.
+__device__ __forceinline__ float max_mod4(float x) {
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<8>(x));
+  return max_xor32(max_xor16(x));
+}
+__device__ __forceinline__ float sum_mod4(float x) {
+  x += row_ror<4>(x);
+  x += row_ror<8>(x);
+  return sum_xor32(sum_xor16(x));
+}
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts inside rows
+// of 16, then the last lane of a row added to the rows after it).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
 }
 
 // ---- memory --------------------------------------------------------------

@@ -48,6 +48,15 @@ struct AttnParams {
   int32_t* counters;      // [B, Hkv]         finished-block counts; zero between calls
 };
 
+// Decode LDS bytes per workgroup: seqlens_k, block prefix, the table entries
+// of the workgroup's range, then one V^T slab per wave.
+constexpr int kDecodeTblWin = 2048;          // most blocks in one workgroup's range
+inline size_t decode_lds_bytes(int B, int hpw, int slab_bytes) {
+  const size_t ints = (size_t)((B + 3) & ~3) + (size_t)((B + 1 + 3) & ~3) + kDecodeTblWin;
+  return ints * sizeof(int) + (size_t)hpw * slab_bytes;
+}
+inline int decode_slab_bytes(int D) { return D * 40; }
+
 hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s);
