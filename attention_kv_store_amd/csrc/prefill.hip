@@ -78,17 +78,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hgrp = (int)(L / (uint32_t)p.NV);
   // reversed so the last (heaviest, under a causal mask) tiles start first
   const int vt = p.NV - 1 - (int)(L - (uint32_t)hgrp * (uint32_t)p.NV);
-  int lo = 0, hi = p.B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.cu_q[mid] / TW + mid <= vt) lo = mid; else hi = mid - 1;
+  const int tw_shift = 5 + (p.TPW >> 1);   // log2(TW): TPW is 1, 2 or 4
+  // b = the last sequence with cu_q[b] / TW + b <= vt (monotone in b, true at
+  // b = 0).  A 64-ary search: every lane tests one candidate and the ballot
+  // count is the answer, so a batch of up to 64 sequences costs a single round
+  // trip to memory, which also brings cu_q[b + 1] and seqlens_k[b].
+  int lo = 0, nrange = p.B;
+  while (nrange > 64) {
+    const int step = (nrange + 63) >> 6;
+    const int cand = lo + lane * step;
+    const bool ok = cand < lo + nrange && (p.cu_q[min(cand, p.B - 1)] >> tw_shift) + cand <= vt;
+    lo += (__popcll(__ballot(ok)) - 1) * step;
+    nrange = min(step, p.B - lo);
   }
-  const int b = lo;
-  const int q0 = p.cu_q[b];
-  const int Lq = p.cu_q[b + 1] - q0;
-  const int tile = vt - (q0 / TW + b);
+  int b, q0, Lq, Lk;
+  {
+    const int cand = min(lo + lane, p.B - 1);
+    const int cq = p.cu_q[cand], cq1 = p.cu_q[cand + 1], lk = p.lens_k[cand];
+    const bool ok = lane < nrange && (cq >> tw_shift) + lo + lane <= vt;
+    const int sel = __popcll(__ballot(ok)) - 1;
+    b = lo + sel;
+    q0 = __builtin_amdgcn_readlane(cq, sel);
+    Lq = __builtin_amdgcn_readlane(cq1, sel) - q0;
+    Lk = __builtin_amdgcn_readlane(lk, sel);
+  }
+  const int tile = vt - ((q0 >> tw_shift) + b);
   if (tile >= (Lq + TW - 1) / TW) return;  // surplus virtual tile (whole workgroup)
-  const int Lk = p.lens_k[b];
   const int cached = Lk - Lq;
   const int tok0 = tile * TW;
   const int tlast = min(tok0 + TW, Lq) - 1;
@@ -141,53 +156,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // ---- staging helpers ----------------------------------------------------
-  int pg_cur[C::NPG], pg_nxt[C::NPG];
-  auto load_pages = [&](int t, int* pg) {
-#pragma unroll
-    for (int i = 0; i < C::NPG; ++i) {
-      const int page = t * C::NPG + i;
-      pg[i] = page < npages ? trow[page] : 0;
-    }
+  // Block-table entries of tile t: lane i holds entry t * NPG + (i % NPG)
+  // (index clamped to the sequence's last page; issue_loads replaces entries
+  // past it by block 0).  A vector load, so waiting for it is counted with the
+  // other global loads and never holds up an LDS read, and nothing uses the
+  // value before the next tile.
+  auto load_pages = [&](int t) -> int {
+    return trow[min(t * C::NPG + (lane & (C::NPG - 1)), npages - 1)];
   };
+  const int64_t page_stride = (int64_t)kPage * kv_tok_stride;   // elements per block
+  // Chunk it of a K row-major tile: key row j = (it * 256 + tid) / CPR of the
+  // tile (its page index is the same across a wave), 16-byte chunk ch.
+  auto kpage_idx = [&](int it) -> int {
+    return __builtin_amdgcn_readfirstlane(((it * 256 + tid) / C::CPR) >> 4);
+  };
+  int64_t koff[C::KIT];
+#pragma unroll
+  for (int it = 0; it < C::KIT; ++it) {
+    const int c = it * 256 + tid;
+    const int j = (c / C::CPR) & (C::BN - 1), ch = c % C::CPR;
+    koff[it] = (int64_t)(j & 15) * kv_tok_stride + ch * (16 / C::ESZ);
+  }
+  // bf16 V items: 4 keys x 8 d, keys kq*4 .. kq*4+3 of page kq / 4
+  const int vkq = tid % (C::BN / 4), vdch = (tid / (C::BN / 4)) % (D / 8);
+  int64_t voff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) voff[r] = (int64_t)((vkq & 3) * 4 + r) * kv_tok_stride + vdch * 8;
   u32x4 kreg[C::KIT];
   u32x4 vreg[C::VREGS];
-  auto row_ptr = [&](const E* base, int kv0, int j, const int* pg) -> const E* {
-    const int pos = kv0 + j;
-    return base + ((int64_t)pg[j >> 4] * kPage + (pos & 15)) * kv_tok_stride;
-  };
-  auto issue_loads = [&](int t, const int* pg) {
-    const int kv0 = t * C::BN;
+  auto issue_loads = [&](int pgv, int t) {
+    // raw loads; readable either way: a row past nkeys lies in an owned block
+    // or, past the last owned page, in block 0
+    int pg[C::NPG];
+#pragma unroll
+    for (int i = 0; i < C::NPG; ++i) {
+      const int e = __builtin_amdgcn_readlane(pgv, i);
+      pg[i] = t * C::NPG + i < npages ? e : 0;
+    }
 #pragma unroll
     for (int it = 0; it < C::KIT; ++it) {
-      const int c = it * 256 + tid;
-      const int j = c / C::CPR, ch = c % C::CPR;
-      // raw load, masked when written to LDS (see write_stage); readable
-      // either way: a row past nkeys lies in an owned block or, past the last
-      // owned page, in block 0 (pg entries default to 0)
-      kreg[it] = ld16(row_ptr(kbase, kv0, j & (C::BN - 1), pg) + ch * (16 / C::ESZ));
+      const int pi = kpage_idx(it);
+      int pk = pg[0];
+#pragma unroll
+      for (int i = 1; i < C::NPG; ++i) pk = pi == i ? pg[i] : pk;   // uniform
+      kreg[it] = ld16(kbase + pk * page_stride + koff[it]);
     }
     if constexpr (BF16) {
+      static_assert(C::VIT == 1, "one V item per thread");
+      const int q = vkq >> 2;
+      int pv = pg[0];
 #pragma unroll
-      for (int iv = 0; iv < C::VIT; ++iv) {
-        const int it = iv * 256 + tid;
-        const int kq = it % (C::BN / 4), dch = it / (C::BN / 4);
+      for (int i = 1; i < C::NPG; ++i) pv = q == i ? pg[i] : pv;
+      const E* vb = vbase + pv * page_stride;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = kq * 4 + r;
-          vreg[iv * 4 + r] = ld16(row_ptr(vbase, kv0, j, pg) + (dch % (D / 8)) * 8);
-        }
-      }
+      for (int r = 0; r < 4; ++r) vreg[r] = ld16(vb + voff[r]);
     } else {
 #pragma unroll
       for (int it = 0; it < C::VIT; ++it) {
-        const int c = it * 256 + tid;
-        const int j = c / C::CPR, ch = c % C::CPR;
-        vreg[it] = ld16(row_ptr(vbase, kv0, j & (C::BN - 1), pg) + ch * 4);
+        const int pi = kpage_idx(it);
+        int pk = pg[0];
+#pragma unroll
+        for (int i = 1; i < C::NPG; ++i) pk = pi == i ? pg[i] : pk;
+        vreg[it] = ld16(vbase + pk * page_stride + koff[it]);
       }
     }
   };
-  // Writes tile t's registers to LDS buffer `buf`; rows at or past nkeys are
-  // zeroed here (only the last tile has any).
+  // Writes tile t's registers to LDS buffer `buf`.  V rows at or past nkeys
+  // are zeroed (only the last tile has any): P is 0 there but V may hold
+  // anything.  K rows there stay as loaded: tiles that have them always take
+  // the masked path, which selects their scores away.
   auto write_stage = [&](int buf, int t) {
     char* Ks = smem + buf * C::STAGE;
     char* Vs = Ks + C::KTILE;
@@ -197,26 +234,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int it = 0; it < C::KIT; ++it) {
       const int c = it * 256 + tid;
-      const bool keep = !tail || kv0 + c / C::CPR < nkeys;
-      if (c < C::KCH) st16(Ks + (c / C::CPR) * C::KROW + (c % C::CPR) * 16, keep ? kreg[it] : zero);
+      if (c < C::KCH) st16(Ks + (c / C::CPR) * C::KROW + (c % C::CPR) * 16, kreg[it]);
     }
     if constexpr (BF16) {
       // transpose 4 keys x 8 d into 8 rows (one per d) of 4 keys
-#pragma unroll
-      for (int iv = 0; iv < C::VIT; ++iv) {
-        const int it = iv * 256 + tid;
-        if (it >= C::VITEMS) continue;
-        const int kq = it % (C::BN / 4), dch = it / (C::BN / 4);
+      if (tid < C::VITEMS) {
         u32x4 w[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (!tail || kv0 + kq * 4 + r < nkeys) ? vreg[iv * 4 + r] : zero;
+        for (int r = 0; r < 4; ++r) w[r] = vreg[r];
+        if (tail) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[r] = kv0 + vkq * 4 + r < nkeys ? w[r] : zero;
+        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const uint32_t lo01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u);
           const uint32_t lo23 = __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u);
           const uint32_t hi01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u);
           const uint32_t hi23 = __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u);
-          char* r0 = Vs + (dch * 8 + 2 * m) * C::VROW + kq * 8;
+          char* r0 = Vs + (vdch * 8 + 2 * m) * C::VROW + vkq * 8;
           *reinterpret_cast<u32x2*>(r0) = u32x2{lo01, lo23};
           *reinterpret_cast<u32x2*>(r0 + C::VROW) = u32x2{hi01, hi23};
         }
@@ -244,9 +280,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
 
   // ---- prologue -----------------------------------------------------------
-  load_pages(0, pg_cur);
-  if (ntiles > 1) load_pages(1, pg_nxt);
-  issue_loads(0, pg_cur);
+  int pg_nxt = load_pages(0);
+  issue_loads(pg_nxt, 0);
+  pg_nxt = load_pages(1);
   write_stage(0, 0);
   __syncthreads();
 
@@ -254,10 +290,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int kv0 = t * C::BN;
     const bool has_next = t + 1 < ntiles;
     if (has_next) {
-      issue_loads(t + 1, pg_nxt);
-#pragma unroll
-      for (int i = 0; i < C::NPG; ++i) pg_cur[i] = pg_nxt[i];
-      if (t + 2 < ntiles) load_pages(t + 2, pg_nxt);
+      issue_loads(pg_nxt, t + 1);
+      pg_nxt = load_pages(t + 2);
     }
 
     const bool skip = !wave_live || (p.causal && kv0 > cached + wt0 + 31);

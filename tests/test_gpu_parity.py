@@ -166,6 +166,19 @@ def test_scale_sign_and_size(dtype, scale, decode):
     _check(b, out, lse, tol=tol)
 
 
+@pytest.mark.parametrize("B", [65, 130, 300])
+def test_prefill_many_sequences(B):
+    """More than 64 sequences: the tile map searches the batch in several
+    64-way levels."""
+    rng = np.random.default_rng(700 + B)
+    q = [int(x) for x in rng.integers(1, 41, size=B)]
+    c = [int(x) for x in rng.integers(0, 25, size=B)]
+    b = _mk(700 + B, q, [a + x for a, x in zip(q, c)], Hq=8, Hkv=2, D=64, dtype="bf16", causal=True,
+            name=f"prefill-B{B}")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
 # --------------------------------------------------------------- decode ---
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
@@ -183,6 +196,16 @@ def test_decode_group_sizes(heads):
     Hq, Hkv = heads
     k = [5, 77, 160, 1024, 513]
     b = _mk(551 + Hq, [1] * len(k), k, Hq=Hq, Hkv=Hkv, D=64, dtype="bf16", causal=True, name=f"decode-G{Hq}/{Hkv}")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
+@pytest.mark.parametrize("B", [65, 300, 1000])
+def test_decode_many_sequences(B):
+    """More than 64 sequences: the block prefix spans several waves."""
+    rng = np.random.default_rng(800 + B)
+    k = [int(x) for x in rng.integers(1, 400, size=B)]
+    b = _mk(800 + B, [1] * B, k, Hq=8, Hkv=2, D=64, dtype="bf16", causal=True, name=f"decode-B{B}")
     out, lse = _run(b)
     _check(b, out, lse)
 
