@@ -171,10 +171,13 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     p.HW = p.G % 4 == 0 ? 4 : (p.G % 2 == 0 ? 2 : 1);
     p.TPW = 4 / p.HW;
     p.NHG = p.Hq / p.HW;
-    const int64_t TW = 32 * p.TPW;
-    const int64_t NV = T / TW + B;
-    if (NV * p.NHG > (int64_t)UINT32_MAX) return fail(KVS_ERR_UNSUPPORTED, "prefill grid too large");
-    p.NV = (int32_t)NV;
+    // cu_seqlens_q / seqlens_k ride in LDS while two workgroups still fit in
+    // a CU's 160 KiB; the persistent grid (two workgroups per CU) is sized at
+    // launch
+    p.pgrid = 0;
+    const size_t half_cu = 80 * 1024 - 256;
+    p.meta_lds = kvs::prefill_lds_bytes((int)D, q->dtype == KVS_BF16, (int)B, 1) <= half_cu ? 1 : 0;
+    if (B > (1 << 24)) return fail(KVS_ERR_UNSUPPORTED, "prefill batch too large");
     return KVS_OK;
   }
 
@@ -207,6 +210,25 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     plan->ws_cnt_off = plan->ws_lse_off + align_up(slots * Hq * sizeof(float), 256);
     plan->ws_bytes = plan->ws_cnt_off + align_up((size_t)B * Hkv * sizeof(int32_t), 256);
   }
+  return KVS_OK;
+}
+
+// ---- compute units of the current device (cached per device) ---------------
+std::mutex g_cu_mu;
+std::vector<int> g_cus;
+
+kvs_status device_cus(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_cu_mu);
+  if ((size_t)dev >= g_cus.size()) g_cus.resize(dev + 1, 0);
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return fail(KVS_ERR_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed");
+    g_cus[dev] = n;
+  }
+  *out = g_cus[dev];
   return KVS_OK;
 }
 
@@ -259,10 +281,13 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
                  plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg);
     return KVS_OK;
   }
+  int cus = 0;
+  KVS_TRY(device_cus(&cus));
+  p.pgrid = 2 * cus;
   const hipError_t e = kvs::launch_prefill(p, plan.dt, plan.D, stream);
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
-  set_dispatch("prefill_%s_d%d grid=%u (NV=%d x NHG=%d) heads/wg=%d tokens/wg=%d", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
-               plan.D, (unsigned)(p.NV * p.NHG), p.NV, p.NHG, p.HW, 32 * p.TPW);
+  set_dispatch("prefill_%s_d%d grid=%d (persistent) head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d",
+               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.pgrid, p.NHG, p.HW, 32 * p.TPW, p.meta_lds);
   return KVS_OK;
 }
 

@@ -87,6 +87,14 @@ __device__ __forceinline__ float row_ror(float x) {
   static_assert(N >= 1 && N <= 15, "row_ror takes 1..15");
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
 }
+// Max over all 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, row_ror<1>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<8>(x));
+  return max_xor32(max_xor16(x));
+}
 // Max / sum over the 16 lanes that share lane % 4.
 __device__ __forceinline__ float max_mod4(float x) {
   x = fmaxf(x, row_ror<4>(x));

@@ -37,7 +37,8 @@ struct AttnParams {
   int32_t HW;             // query heads per workgroup (divides G)
   int32_t TPW;            // 32-token blocks per workgroup (HW * TPW == 4 waves)
   int32_t NHG;            // head groups = Hq / HW
-  int32_t NV;             // virtual tiles per head group = T / (32 * TPW) + B
+  int32_t pgrid;          // persistent workgroups (two per CU)
+  int32_t meta_lds;       // 1: cu_seqlens_q and seqlens_k are staged in LDS
   // decode work plan: the batch's key blocks, flattened sequence-major, are cut
   // into `nwg` equal contiguous ranges, one per workgroup; a workgroup holds the
   // waves of `hpw` consecutive KV heads.
@@ -56,6 +57,18 @@ inline size_t decode_lds_bytes(int B, int hpw, int slab_bytes) {
   return ints * sizeof(int) + (size_t)hpw * slab_bytes;
 }
 inline int decode_slab_bytes(int D) { return D * 40; }
+
+// Prefill LDS bytes per workgroup: two K/V stages, then cu_seqlens_q and
+// seqlens_k when staged.
+inline size_t prefill_stage_bytes(int D, bool bf16) {
+  const int BN = bf16 ? 64 : 32, ESZ = bf16 ? 2 : 4;
+  const int KROW = D * ESZ + 16;
+  const int VROW = bf16 ? (BN * 2 + 8) : (D * 4 + 16);
+  return (size_t)BN * KROW + (size_t)(bf16 ? D * VROW : BN * VROW);
+}
+inline size_t prefill_lds_bytes(int D, bool bf16, int B, int meta_lds) {
+  return 2 * prefill_stage_bytes(D, bf16) + (meta_lds ? (size_t)(2 * B + 1) * sizeof(int) : 0);
+}
 
 hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s);

@@ -9,7 +9,8 @@
 // that share one KV head are served by the same workgroup so each K/V tile is
 // loaded once for the whole group (§15).
 //
-// Layout of the work (one workgroup = 4 waves):
+// Layout of the work (one workgroup = 4 waves; a persistent grid walks the
+// items, see prefill_kernel):
 //  * A wave owns 32 query rows of ONE query head: rows = tokens
 //    [wt0, wt0 + 32) of one sequence.  The 4 waves are HW heads x TPW token
 //    blocks of the same KV head (HW * TPW = 4; HW divides the group size).
@@ -22,10 +23,9 @@
 //    MFMA (8 keys of one d per lane) is two 8-byte LDS reads.  fp32: the 32x32x2
 //    MFMA takes one element per lane, so V stays row-major.
 //  * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//    issued before the current tile's math, the block-table entries two tiles
-//    ahead.  Rows past the last key a workgroup needs are zero-filled, never
-//    loaded, so tail rows and table entries past a sequence's last block are
-//    never touched.
+//    issued before the current tile's math.  Rows past the last key an item
+//    needs are never trusted: V is zeroed there and K scores are masked, and
+//    table entries past a sequence's last block are never used.
 //  * Causal (bottom-right, with cached prefix c = Lk - Lq): tiles wholly above
 //    a wave's rows are skipped; only tiles crossing the diagonal are masked.
 #include <type_traits>
@@ -58,140 +58,177 @@ struct PCfg {
   static constexpr int VREGS = BF16 ? VIT * 4 : VIT;
   static constexpr int NDB = D / 32;           // 32-wide d blocks of the output
 };
+static_assert(PCfg<128, true>::STAGE == 69632 / 2 && PCfg<64, true>::STAGE * 2 == 2 * (64 * 144 + 64 * 136),
+              "stage layout");
 
-// Two workgroups per CU (two waves per SIMD): one workgroup's barrier and
-// load waits overlap the other's math.
+// Persistent work loop, two workgroups per CU (two waves per SIMD): one
+// workgroup's barrier and load waits overlap the other's math.
+//
+// An item is (sequence b, token tile of TW rows, head group); items are
+// enumerated tile-major from the last token tile down, so under a causal mask
+// the heaviest items come first, and dealt to the workgroups in snake order
+// (round r: workgroup w takes item r*G + w, or r*G + G-1-w in odd rounds),
+// which evens out the work.  A workgroup walks its items as ONE stream of
+// (item, key tile) steps: the next step's K/V loads -- also the first tile of
+// the next item -- are issued before the current step's math, block-table
+// entries one step earlier, and the next item's Q rows as soon as the last
+// score tile of the current item is formed, so moving to a new item costs
+// about what moving to a new key tile does.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(AttnParams p) {
   using C = PCfg<D, BF16>;
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_nt[4];
 
   const int tid = threadIdx.x;
   // wave-uniform by construction; readfirstlane lets the compiler see it, so
   // every per-wave decision below is a scalar branch
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
-
-  // ---- workgroup -> (sequence, token tile, head group) -------------------
+  const int B = p.B;
   const int TW = 32 * p.TPW;
-  const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int hgrp = (int)(L / (uint32_t)p.NV);
-  // reversed so the last (heaviest, under a causal mask) tiles start first
-  const int vt = p.NV - 1 - (int)(L - (uint32_t)hgrp * (uint32_t)p.NV);
   const int tw_shift = 5 + (p.TPW >> 1);   // log2(TW): TPW is 1, 2 or 4
-  // b = the last sequence with cu_q[b] / TW + b <= vt (monotone in b, true at
-  // b = 0).  A 64-ary search: every lane tests one candidate and the ballot
-  // count is the answer, so a batch of up to 64 sequences costs a single round
-  // trip to memory, which also brings cu_q[b + 1] and seqlens_k[b].
-  int lo = 0, nrange = p.B;
-  while (nrange > 64) {
-    const int step = (nrange + 63) >> 6;
-    const int cand = lo + lane * step;
-    const bool ok = cand < lo + nrange && (p.cu_q[min(cand, p.B - 1)] >> tw_shift) + cand <= vt;
-    lo += (__popcll(__ballot(ok)) - 1) * step;
-    nrange = min(step, p.B - lo);
-  }
-  int b, q0, Lq, Lk;
-  {
-    const int cand = min(lo + lane, p.B - 1);
-    const int cq = p.cu_q[cand], cq1 = p.cu_q[cand + 1], lk = p.lens_k[cand];
-    const bool ok = lane < nrange && (cq >> tw_shift) + lo + lane <= vt;
-    const int sel = __popcll(__ballot(ok)) - 1;
-    b = lo + sel;
-    q0 = __builtin_amdgcn_readlane(cq, sel);
-    Lq = __builtin_amdgcn_readlane(cq1, sel) - q0;
-    Lk = __builtin_amdgcn_readlane(lk, sel);
-  }
-  const int tile = vt - ((q0 >> tw_shift) + b);
-  if (tile >= (Lq + TW - 1) / TW) return;  // surplus virtual tile (whole workgroup)
-  const int cached = Lk - Lq;
-  const int tok0 = tile * TW;
-  const int tlast = min(tok0 + TW, Lq) - 1;
-  const int nkeys = p.causal ? min(Lk, cached + tlast + 1) : Lk;
-  const int ntiles = (nkeys + C::BN - 1) / C::BN;
-  const int npages = (nkeys + 15) >> 4;
-
   const int hw = wave % p.HW, tb = wave / p.HW;
-  const int h = hgrp * p.HW + hw;
-  const int g = h / p.G;
-  const int wt0 = tok0 + tb * 32;
-  const bool wave_live = wt0 < Lq;
-  const int qrow = wt0 + n;                 // this lane's query row in the sequence
-  const int qpos = cached + qrow;           // its position among the keys
-
-  const int32_t* trow = p.table + (int64_t)b * p.MB;
   const int64_t kv_tok_stride = (int64_t)p.Hkv * D;   // elements between token rows
+  const int64_t page_stride = (int64_t)kPage * kv_tok_stride;   // elements per block
 
-  using E = typename std::conditional<BF16, uint16_t, float>::type;
-  const E* kbase = static_cast<const E*>(p.k) + (int64_t)g * D;
-  const E* vbase = static_cast<const E*>(p.v) + (int64_t)g * D;
-
-  // ---- Q fragment (B operand of S^T = K . Q^T), loaded once -------------
-  // bf16 32x32x16: lane holds Q[row n][ks*16 + hh*8 .. +8] for k-step ks.
-  // fp32 32x32x2: lane holds Q[row n][hh*D/2 + ks] for k-step ks.
-  // The sign of the scale is moved into Q (an exact sign flip), so the score
-  // multiplier c is >= 0 and a row maximum of raw scores is also the maximum of
-  // the scaled ones.
-  constexpr int QF = BF16 ? D / 16 : D / 2;
-  typename std::conditional<BF16, u32x4, float>::type qf[QF];
-  const float c = fabsf(p.scale_log2);
+  // ---- batch metadata: cu_seqlens_q and seqlens_k staged in LDS (when the
+  // planner has room for them), and the most token tiles of any sequence ----
+  const bool staged = p.meta_lds != 0;
+  int* s_cq = reinterpret_cast<int*>(smem + 2 * C::STAGE);   // [B + 1]
+  int* s_lk = s_cq + B + 1;                                   // [B]
   {
-    const bool ok = wave_live && qrow < Lq;
-    const uint32_t flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-    const E* qp = static_cast<const E*>(p.q) + ((int64_t)(q0 + (ok ? qrow : 0)) * p.Hq + h) * D;
-    if constexpr (BF16) {
-#pragma unroll
-      for (int ks = 0; ks < QF; ++ks) {
-        const u32x4 w = ld16_keep(qp + ks * 16 + hh * 8, ok);  // row clamped to 0 if !ok
-        qf[ks] = u32x4{w[0] ^ flip, w[1] ^ flip, w[2] ^ flip, w[3] ^ flip};
+    float ntmax = 0.f;
+    for (int b = tid; b < B; b += 256) {
+      const int a = p.cu_q[b], z = p.cu_q[b + 1], lk = p.lens_k[b];
+      if (staged) {
+        s_cq[b] = a;
+        s_lk[b] = lk;
+        if (b == B - 1) s_cq[B] = z;
       }
-    } else {
-#pragma unroll
-      for (int c4 = 0; c4 < QF / 4; ++c4) {
-        const u32x4 w = ld16_keep(qp + hh * (D / 2) + c4 * 4, ok);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(w[e] ^ (flip << 16));
-      }
+      ntmax = fmaxf(ntmax, (float)((z - a + TW - 1) >> tw_shift));
     }
+    ntmax = wave_max(ntmax);
+    if (lane == 0) s_nt[wave] = (int)ntmax;
+    __syncthreads();
   }
+  const int NT = __builtin_amdgcn_readfirstlane(max(max(s_nt[0], s_nt[1]), max(s_nt[2], s_nt[3])));
+  const int64_t BH = (int64_t)B * p.NHG;
+  const int64_t NI = (int64_t)NT * BH;
+  const int G = gridDim.x, w = blockIdx.x;
+  const int64_t nrounds = (NI + G - 1) / G;
+
+  // ---- items --------------------------------------------------------------
+  struct Item {
+    int r;             // round of this workgroup's item sequence (nrounds: none)
+    int b, hgrp, tile;
+    int q0, Lq, Lk;
+    int nkeys, ntiles, npages;
+  };
+  auto meta = [&](int b, int& q0, int& q1, int& lk) __attribute__((always_inline)) {
+    // uniform values: readfirstlane keeps the item state in scalar registers
+    if (staged) {
+      q0 = __builtin_amdgcn_readfirstlane(s_cq[b]);
+      q1 = __builtin_amdgcn_readfirstlane(s_cq[b + 1]);
+      lk = __builtin_amdgcn_readfirstlane(s_lk[b]);
+    } else {
+      q0 = __builtin_amdgcn_readfirstlane(p.cu_q[b]);
+      q1 = __builtin_amdgcn_readfirstlane(p.cu_q[b + 1]);
+      lk = __builtin_amdgcn_readfirstlane(p.lens_k[b]);
+    }
+  };
+  // first non-empty item of round r or later
+  auto item_from = [&](int r) __attribute__((always_inline)) {
+    Item it;
+    it.ntiles = 0;
+    for (; r < nrounds; ++r) {
+      const int64_t u = (int64_t)r * G + ((r & 1) ? G - 1 - w : w);
+      if (u >= NI) continue;
+      const int64_t pair = u % BH;
+      const int tile = NT - 1 - (int)(u / BH);
+      const int b = (int)(pair / p.NHG), hgrp = (int)(pair % p.NHG);
+      int q0, q1, lk;
+      meta(b, q0, q1, lk);
+      const int Lq = q1 - q0;
+      if (tile * TW >= Lq) continue;   // this sequence has fewer token tiles
+      const int cached = lk - Lq;
+      const int tlast = min(tile * TW + TW, Lq) - 1;
+      it.b = b;
+      it.hgrp = hgrp;
+      it.tile = tile;
+      it.q0 = q0;
+      it.Lq = Lq;
+      it.Lk = lk;
+      it.nkeys = p.causal ? min(lk, cached + tlast + 1) : lk;
+      it.ntiles = (it.nkeys + C::BN - 1) / C::BN;
+      it.npages = (it.nkeys + 15) >> 4;
+      break;
+    }
+    it.r = r;
+    return it;
+  };
+  // a step of the stream: key tile t of item it (it.ntiles == 0: none)
+  struct Step {
+    Item it;
+    int t;
+  };
+  auto advance = [&](const Step& s) __attribute__((always_inline)) {
+    Step x = s;
+    if (s.it.ntiles == 0) return x;
+    if (s.t + 1 < s.it.ntiles) {
+      x.t = s.t + 1;
+    } else {
+      x.it = item_from(s.it.r + 1);
+      x.t = 0;
+    }
+    return x;
+  };
+  auto kv_base = [&](const Item& it, const void* base) __attribute__((always_inline)) {
+    const int g = (it.hgrp * p.HW) / p.G;   // HW divides G: one KV head per item
+    return static_cast<const E*>(base) + (int64_t)g * D;
+  };
 
   // ---- staging helpers ----------------------------------------------------
-  // Block-table entries of tile t: lane i holds entry t * NPG + (i % NPG)
+  // Block-table entries of step s: lane i holds entry t * NPG + (i % NPG)
   // (index clamped to the sequence's last page; issue_loads replaces entries
   // past it by block 0).  A vector load, so waiting for it is counted with the
-  // other global loads and never holds up an LDS read, and nothing uses the
-  // value before the next tile.
-  auto load_pages = [&](int t) -> int {
-    return trow[min(t * C::NPG + (lane & (C::NPG - 1)), npages - 1)];
+  // other global loads and never holds up an LDS read.
+  auto load_pages = [&](const Step& s) -> int {
+    if (s.it.ntiles == 0) return 0;
+    const int32_t* trow = p.table + (int64_t)s.it.b * p.MB;
+    return trow[min(s.t * C::NPG + (lane & (C::NPG - 1)), s.it.npages - 1)];
   };
-  const int64_t page_stride = (int64_t)kPage * kv_tok_stride;   // elements per block
   // Chunk it of a K row-major tile: key row j = (it * 256 + tid) / CPR of the
   // tile (its page index is the same across a wave), 16-byte chunk ch.
   auto kpage_idx = [&](int it) -> int {
     return __builtin_amdgcn_readfirstlane(((it * 256 + tid) / C::CPR) >> 4);
   };
-  int64_t koff[C::KIT];
+  // per-lane element offsets inside a block (< 16 * Hkv * D, so 32 bits)
+  uint32_t koff[C::KIT];
 #pragma unroll
   for (int it = 0; it < C::KIT; ++it) {
-    const int c = it * 256 + tid;
-    const int j = (c / C::CPR) & (C::BN - 1), ch = c % C::CPR;
-    koff[it] = (int64_t)(j & 15) * kv_tok_stride + ch * (16 / C::ESZ);
+    const int cch = it * 256 + tid;
+    const int j = (cch / C::CPR) & (C::BN - 1), ch = cch % C::CPR;
+    koff[it] = (uint32_t)((j & 15) * (int)kv_tok_stride + ch * (16 / C::ESZ));
   }
   // bf16 V items: 4 keys x 8 d, keys kq*4 .. kq*4+3 of page kq / 4
   const int vkq = tid % (C::BN / 4), vdch = (tid / (C::BN / 4)) % (D / 8);
-  int64_t voff[4];
+  uint32_t voff[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) voff[r] = (int64_t)((vkq & 3) * 4 + r) * kv_tok_stride + vdch * 8;
+  for (int r = 0; r < 4; ++r) voff[r] = (uint32_t)(((vkq & 3) * 4 + r) * (int)kv_tok_stride + vdch * 8);
   u32x4 kreg[C::KIT];
   u32x4 vreg[C::VREGS];
-  auto issue_loads = [&](int pgv, int t) {
+  auto issue_loads = [&](int pgv, const Step& s) {
     // raw loads; readable either way: a row past nkeys lies in an owned block
     // or, past the last owned page, in block 0
+    const E* kbase = kv_base(s.it, p.k);
+    const E* vbase = kv_base(s.it, p.v);
     int pg[C::NPG];
 #pragma unroll
     for (int i = 0; i < C::NPG; ++i) {
       const int e = __builtin_amdgcn_readlane(pgv, i);
-      pg[i] = t * C::NPG + i < npages ? e : 0;
+      pg[i] = s.t * C::NPG + i < s.it.npages ? e : 0;
     }
 #pragma unroll
     for (int it = 0; it < C::KIT; ++it) {
@@ -221,37 +258,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  // Writes tile t's registers to LDS buffer `buf`.  V rows at or past nkeys
-  // are zeroed (only the last tile has any): P is 0 there but V may hold
+  // Writes step s's registers to LDS buffer `buf`.  V rows at or past nkeys
+  // are zeroed (only an item's last tile has any): P is 0 there but V may hold
   // anything.  K rows there stay as loaded: tiles that have them always take
   // the masked path, which selects their scores away.
-  auto write_stage = [&](int buf, int t) {
+  auto write_stage = [&](int buf, const Step& s) {
     char* Ks = smem + buf * C::STAGE;
     char* Vs = Ks + C::KTILE;
-    const int kv0 = t * C::BN;
+    const int kv0 = s.t * C::BN;
+    const int nkeys = s.it.nkeys;
     const bool tail = kv0 + C::BN > nkeys;
     const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
     for (int it = 0; it < C::KIT; ++it) {
-      const int c = it * 256 + tid;
-      if (c < C::KCH) st16(Ks + (c / C::CPR) * C::KROW + (c % C::CPR) * 16, kreg[it]);
+      const int cch = it * 256 + tid;
+      if (cch < C::KCH) st16(Ks + (cch / C::CPR) * C::KROW + (cch % C::CPR) * 16, kreg[it]);
     }
     if constexpr (BF16) {
       // transpose 4 keys x 8 d into 8 rows (one per d) of 4 keys
       if (tid < C::VITEMS) {
-        u32x4 w[4];
+        u32x4 wv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = vreg[r];
+        for (int r = 0; r < 4; ++r) wv[r] = vreg[r];
         if (tail) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) w[r] = kv0 + vkq * 4 + r < nkeys ? w[r] : zero;
+          for (int r = 0; r < 4; ++r) wv[r] = kv0 + vkq * 4 + r < nkeys ? wv[r] : zero;
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const uint32_t lo01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u);
-          const uint32_t lo23 = __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u);
-          const uint32_t hi01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u);
-          const uint32_t hi23 = __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u);
+          const uint32_t lo01 = __builtin_amdgcn_perm(wv[1][m], wv[0][m], 0x05040100u);
+          const uint32_t lo23 = __builtin_amdgcn_perm(wv[3][m], wv[2][m], 0x05040100u);
+          const uint32_t hi01 = __builtin_amdgcn_perm(wv[1][m], wv[0][m], 0x07060302u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(wv[3][m], wv[2][m], 0x07060302u);
           char* r0 = Vs + (vdch * 8 + 2 * m) * C::VROW + vkq * 8;
           *reinterpret_cast<u32x2*>(r0) = u32x2{lo01, lo23};
           *reinterpret_cast<u32x2*>(r0 + C::VROW) = u32x2{hi01, hi23};
@@ -260,9 +298,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
 #pragma unroll
       for (int it = 0; it < C::VIT; ++it) {
-        const int c = it * 256 + tid;
-        const bool keep = !tail || kv0 + c / C::CPR < nkeys;
-        if (c < C::KCH) st16(Vs + (c / C::CPR) * C::VROW + (c % C::CPR) * 16, keep ? vreg[it] : zero);
+        const int cch = it * 256 + tid;
+        const bool keep = !tail || kv0 + cch / C::CPR < nkeys;
+        if (cch < C::KCH) st16(Vs + (cch / C::CPR) * C::VROW + (cch % C::CPR) * 16, keep ? vreg[it] : zero);
+      }
+    }
+  };
+
+  // ---- Q fragment (B operand of S^T = K . Q^T) of an item ----------------
+  // bf16 32x32x16: lane holds Q[row n][ks*16 + hh*8 .. +8] for k-step ks.
+  // fp32 32x32x2: lane holds Q[row n][hh*D/2 + ks] for k-step ks.
+  // The sign of the scale is moved into Q (an exact sign flip), so the score
+  // multiplier c is >= 0 and a row maximum of raw scores is also the maximum of
+  // the scaled ones.
+  constexpr int QF = BF16 ? D / 16 : D / 2;
+  typename std::conditional<BF16, u32x4, float>::type qf[QF];
+  const float c = fabsf(p.scale_log2);
+  const uint32_t flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  auto load_q = [&](const Item& it) __attribute__((always_inline)) {
+    const int qrow = it.tile * TW + tb * 32 + n;
+    const bool ok = qrow < it.Lq;
+    const int h = it.hgrp * p.HW + hw;
+    const E* qp = static_cast<const E*>(p.q) + ((int64_t)(it.q0 + (ok ? qrow : 0)) * p.Hq + h) * D;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int ks = 0; ks < QF; ++ks) {
+        const u32x4 wq = ld16(qp + ks * 16 + hh * 8);   // row clamped to the item's first if !ok
+        qf[ks] = u32x4{wq[0] ^ flip, wq[1] ^ flip, wq[2] ^ flip, wq[3] ^ flip};
+      }
+    } else {
+#pragma unroll
+      for (int c4 = 0; c4 < QF / 4; ++c4) {
+        const u32x4 wq = ld16(qp + hh * (D / 2) + c4 * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(wq[e] ^ (flip << 16));
       }
     }
   };
@@ -279,25 +348,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
 
-  // ---- prologue -----------------------------------------------------------
-  int pg_nxt = load_pages(0);
-  issue_loads(pg_nxt, 0);
-  pg_nxt = load_pages(1);
-  write_stage(0, 0);
+  // ---- prologue: the first step -------------------------------------------
+  Step cur;
+  cur.it = item_from(0);
+  cur.t = 0;
+  if (cur.it.ntiles == 0) return;   // no item for this workgroup (whole workgroup)
+  Step nx1 = advance(cur);
+  Step nx2 = advance(nx1);
+  load_q(cur.it);
+  int pg_nxt = load_pages(cur);
+  issue_loads(pg_nxt, cur);
+  pg_nxt = load_pages(nx1);
+  write_stage(0, cur);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int kv0 = t * C::BN;
-    const bool has_next = t + 1 < ntiles;
+  for (int buf = 0;; buf ^= 1) {
+    const Item& it = cur.it;
+    const int t = cur.t;
+    const bool has_next = nx1.it.ntiles != 0;
+    const bool item_end = t + 1 == it.ntiles;   // last key tile of this item
     if (has_next) {
-      issue_loads(pg_nxt, t + 1);
-      pg_nxt = load_pages(t + 2);
+      issue_loads(pg_nxt, nx1);
+      pg_nxt = load_pages(nx2);
     }
 
+    const int kv0 = t * C::BN;
+    const int cached = it.Lk - it.Lq;
+    const int wt0 = it.tile * TW + tb * 32;
+    const bool wave_live = wt0 < it.Lq;
+    const int qpos = cached + wt0 + n;   // this lane's row's position among the keys
     const bool skip = !wave_live || (p.causal && kv0 > cached + wt0 + 31);
+    bool q_next = !(item_end && has_next);   // true once the next item's Q is on its way
     if (!skip) {
-      const bool need_mask = p.causal ? (kv0 + C::BN - 1 > cached + wt0) : (kv0 + C::BN > Lk);
-      const char* Ks = smem + (t & 1) * C::STAGE;
+      const bool need_mask = p.causal ? (kv0 + C::BN - 1 > cached + wt0) : (kv0 + C::BN > it.Lk);
+      const char* Ks = smem + buf * C::STAGE;
       const char* Vs = Ks + C::KTILE;
       constexpr int NKB = C::BN / 32;
       f32x16 s[NKB];
@@ -318,13 +402,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
         }
       }
+      // Q of this item is no longer needed: bring in the next item's
+      if (!q_next) {
+        load_q(nx1.it);
+        q_next = true;
+      }
       // Tile maximum.  Unmasked tiles take it over raw scores (c >= 0) and fold
       // the scale into the exponent's fma; tiles that cross the causal
       // diagonal or the key tail scale first and select masked keys away.
       float mt = kMaskedScore;
       if (need_mask) {
         // key offset of register r inside a 32-key block: (r/4)*8 + hh*4 + r%4
-        const int lim = (p.causal ? qpos + 1 : Lk) - kv0 - hh * 4;   // visible iff offset < lim
+        const int lim = (p.causal ? qpos + 1 : it.Lk) - kv0 - hh * 4;   // visible iff offset < lim
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -405,50 +494,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
+    if (!q_next) load_q(nx1.it);
 
-    if (has_next) write_stage((t + 1) & 1, t + 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: O / l, lse = (m + log2 l) ln 2 ---------------------------
-  if (!wave_live || qrow >= Lq) return;
-  const float l_tot = sum_xor32(l_run);
-  const float inv = 1.0f / l_tot;
-  const int64_t orow = ((int64_t)(q0 + qrow) * p.Hq + h) * D;
+    if (item_end) {
+      // ---- epilogue of the item: O / l, lse = (m + log2 l) ln 2 -----------
+      const int qrow = wt0 + n;
+      if (wave_live && qrow < it.Lq) {
+        const int h = it.hgrp * p.HW + hw;
+        const float l_tot = sum_xor32(l_run);
+        const float inv = 1.0f / l_tot;
+        const int64_t orow = ((int64_t)(it.q0 + qrow) * p.Hq + h) * D;
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
+        for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = db * 32 + g4 * 8 + hh * 4;
-      const float a0 = o[db][g4 * 4 + 0] * inv, a1 = o[db][g4 * 4 + 1] * inv;
-      const float a2 = o[db][g4 * 4 + 2] * inv, a3 = o[db][g4 * 4 + 3] * inv;
-      if constexpr (BF16) {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + orow + d) =
-            u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-      } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow + d) = f32x4{a0, a1, a2, a3};
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d = db * 32 + g4 * 8 + hh * 4;
+            const float a0 = o[db][g4 * 4 + 0] * inv, a1 = o[db][g4 * 4 + 1] * inv;
+            const float a2 = o[db][g4 * 4 + 2] * inv, a3 = o[db][g4 * 4 + 3] * inv;
+            if constexpr (BF16) {
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + orow + d) =
+                  u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+            } else {
+              *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow + d) = f32x4{a0, a1, a2, a3};
+            }
+          }
+        }
+        if (p.lse && hh == 0) p.lse[(int64_t)(it.q0 + qrow) * p.Hq + h] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
       }
+      m_run = kMaskedScore;
+      l_run = 0.f;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
     }
+
+    if (has_next) write_stage(buf ^ 1, nx1);
+    __syncthreads();
+    if (!has_next) break;
+    cur = nx1;
+    nx1 = nx2;
+    nx2 = advance(nx2);
   }
-  if (p.lse && hh == 0) p.lse[(int64_t)(q0 + qrow) * p.Hq + h] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 template <int D, bool BF16>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
-  using C = PCfg<D, BF16>;
-  const unsigned grid = (unsigned)p.NV * (unsigned)p.NHG;
-  const size_t lds = 2 * C::STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
+  const size_t lds = prefill_lds_bytes(D, BF16, p.B, p.meta_lds);
+  // dynamic LDS above the default limit must be requested; grow it as needed
+  static size_t lds_granted = 0;
+  if (lds > lds_granted) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
       return e;
     }
-    attr_set = true;
+    lds_granted = lds;
   }
-  hipLaunchKernelGGL((prefill_kernel<D, BF16>), dim3(grid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, BF16>), dim3(p.pgrid), dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
