@@ -118,6 +118,23 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
   return x;
 }
 
+// ---- LDS transposing read (gfx950) -----------------------------------------
+// In each group of 16 lanes, lane i receives 16-bit element i % 4 of the 8-byte
+// rows addressed by lanes i/4, i/4 + 4, i/4 + 8 and i/4 + 12 of its group, in
+// that order (checked on the device).
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// 16-byte copy from global memory straight into LDS (gfx950): lane l's 16
+// bytes land at lds_block + 16 * l; lds_block must be the same on every lane.
+__device__ __forceinline__ void copy16_to_lds(const void* src, char* lds_block) {
+  __builtin_amdgcn_global_load_lds(src, lds_block, 16, 0, 0);
+}
+
 // ---- memory --------------------------------------------------------------
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 // Load unconditionally (the address must be readable either way) and keep the

@@ -61,10 +61,8 @@ inline int decode_slab_bytes(int D) { return D * 40; }
 // Prefill LDS bytes per workgroup: two K/V stages, then cu_seqlens_q and
 // seqlens_k when staged.
 inline size_t prefill_stage_bytes(int D, bool bf16) {
-  const int BN = bf16 ? 64 : 32, ESZ = bf16 ? 2 : 4;
-  const int KROW = D * ESZ + 16;
-  const int VROW = bf16 ? (BN * 2 + 8) : (D * 4 + 16);
-  return (size_t)BN * KROW + (size_t)(bf16 ? D * VROW : BN * VROW);
+  // bf16: 64-key K and V tiles, unpadded rows; fp32: 32-key tiles, rows padded by 16 bytes
+  return bf16 ? (size_t)2 * 64 * D * 2 : (size_t)2 * 32 * (D * 4 + 16);
 }
 inline size_t prefill_lds_bytes(int D, bool bf16, int B, int meta_lds) {
   return 2 * prefill_stage_bytes(D, bf16) + (meta_lds ? (size_t)(2 * B + 1) * sizeof(int) : 0);

@@ -42,24 +42,31 @@ template <int D, bool BF16>
 struct PCfg {
   static constexpr int BN = BF16 ? 64 : 32;   // keys per tile
   static constexpr int ESZ = BF16 ? 2 : 4;    // element bytes
-  static constexpr int KROW = D * ESZ + 16;   // padded K row in LDS (bytes)
-  // bf16: one V^T row holds one d for the BN keys; fp32: one V row per key
-  static constexpr int VROW = BF16 ? (BN * 2 + 8) : (D * 4 + 16);
+  // bf16: K and V tiles are row-major without padding, filled by 16-byte
+  // global-to-LDS copies; the 16-byte chunks of a row are XOR-swizzled by key
+  // so that the score-operand reads and the transposing V reads hit distinct
+  // banks.  fp32: padded rows written from registers.
+  static constexpr int KROW = BF16 ? D * 2 : D * 4 + 16;   // bytes per K row in LDS
+  static constexpr int VROW = BF16 ? D * 2 : D * 4 + 16;   // bytes per V row in LDS
   static constexpr int KTILE = BN * KROW;
-  static constexpr int VTILE = BF16 ? D * VROW : BN * VROW;
+  static constexpr int VTILE = BN * VROW;
   static constexpr int STAGE = KTILE + VTILE;
   static constexpr int NPG = BN / 16;          // pages per tile
   static constexpr int CPR = D * ESZ / 16;     // 16-byte chunks per token row
-  static constexpr int KCH = BN * CPR;         // K chunks per tile
-  static constexpr int KIT = (KCH + 255) / 256;
-  // bf16 V items: 4 keys x 8 d (four 16-byte chunks); fp32 V: plain chunks
-  static constexpr int VITEMS = BF16 ? (BN / 4) * (D / 8) : KCH;
-  static constexpr int VIT = (VITEMS + 255) / 256;
-  static constexpr int VREGS = BF16 ? VIT * 4 : VIT;
+  static constexpr int KCH = BN * CPR;         // chunks per tile and operand
+  static constexpr int KIT = (KCH + 255) / 256;  // chunks per thread and operand
   static constexpr int NDB = D / 32;           // 32-wide d blocks of the output
+  // bf16 chunk slot of logical chunk c of key row `key`: c ^ swizzle(key)
+  __host__ __device__ static constexpr int kswz(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+  __host__ __device__ static constexpr int vswz(int key) { return D == 128 ? ((key & 3) << 1) : (key & 2); }
 };
-static_assert(PCfg<128, true>::STAGE == 69632 / 2 && PCfg<64, true>::STAGE * 2 == 2 * (64 * 144 + 64 * 136),
-              "stage layout");
+static_assert(PCfg<128, true>::STAGE == 32768 && PCfg<64, true>::STAGE == 16384, "stage layout");
+static_assert(PCfg<128, true>::KIT * 4 * 64 == PCfg<128, true>::KCH && PCfg<64, true>::KIT * 4 * 64 == PCfg<64, true>::KCH,
+              "each wave copies KIT whole 1 KiB blocks of a tile");
+
+// Source of the key rows past an item's last key: a zero row, so V is exactly
+// 0 there (P is 0 too, but V could hold anything) and K is harmless.
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[128];
 
 // Persistent work loop, two workgroups per CU (two waves per SIMD): one
 // workgroup's barrier and load waits overlap the other's math.
@@ -67,8 +74,8 @@ static_assert(PCfg<128, true>::STAGE == 69632 / 2 && PCfg<64, true>::STAGE * 2 =
 // An item is (sequence b, token tile of TW rows, head group); items are
 // enumerated tile-major from the last token tile down, so under a causal mask
 // the heaviest items come first, and dealt to the workgroups in snake order
-// (round r: workgroup w takes item r*G + w, or r*G + G-1-w in odd rounds),
-// which evens out the work.  A workgroup walks its items as ONE stream of
+// (round r: workgroup w takes item r*G + w, in odd rounds the mirror image of
+// w among the workgroups of its XCD), which evens out the work.  A workgroup walks its items as ONE stream of
 // (item, key tile) steps: the next step's K/V loads -- also the first tile of
 // the next item -- are issued before the current step's math, block-table
 // entries one step earlier, and the next item's Q rows as soon as the last
@@ -117,6 +124,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t BH = (int64_t)B * p.NHG;
   const int64_t NI = (int64_t)NT * BH;
   const int G = gridDim.x, w = blockIdx.x;
+  const int rev_w = (G & 7) == 0 ? (w & 7) + 8 * (G / 8 - 1 - (w >> 3)) : G - 1 - w;
   const int64_t nrounds = (NI + G - 1) / G;
 
   // ---- items --------------------------------------------------------------
@@ -143,7 +151,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     Item it;
     it.ntiles = 0;
     for (; r < nrounds; ++r) {
-      const int64_t u = (int64_t)r * G + ((r & 1) ? G - 1 - w : w);
+      // odd rounds reverse the order within each XCD's workgroups (w % 8 is
+      // the XCD a workgroup runs on), so an item's (sequence, head group)
+      // pair stays on one XCD and its K/V re-reads hit that XCD's L2
+      const int64_t u = (int64_t)r * G + ((r & 1) ? rev_w : w);
       if (u >= NI) continue;
       const int64_t pair = u % BH;
       const int tile = NT - 1 - (int)(u / BH);
@@ -204,7 +215,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto kpage_idx = [&](int it) -> int {
     return __builtin_amdgcn_readfirstlane(((it * 256 + tid) / C::CPR) >> 4);
   };
-  // per-lane element offsets inside a block (< 16 * Hkv * D, so 32 bits)
+  // fp32 path: chunk it of a row-major tile (key row (it * 256 + tid) / CPR)
+  // is loaded into registers and written to padded LDS rows; per-lane element
+  // offsets inside a block (< 16 * Hkv * D, so 32 bits)
   uint32_t koff[C::KIT];
 #pragma unroll
   for (int it = 0; it < C::KIT; ++it) {
@@ -212,16 +225,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int j = (cch / C::CPR) & (C::BN - 1), ch = cch % C::CPR;
     koff[it] = (uint32_t)((j & 15) * (int)kv_tok_stride + ch * (16 / C::ESZ));
   }
-  // bf16 V items: 4 keys x 8 d, keys kq*4 .. kq*4+3 of page kq / 4
-  const int vkq = tid % (C::BN / 4), vdch = (tid / (C::BN / 4)) % (D / 8);
-  uint32_t voff[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) voff[r] = (uint32_t)(((vkq & 3) * 4 + r) * (int)kv_tok_stride + vdch * 8);
-  u32x4 kreg[C::KIT];
-  u32x4 vreg[C::VREGS];
-  auto issue_loads = [&](int pgv, const Step& s) {
-    // raw loads; readable either way: a row past nkeys lies in an owned block
-    // or, past the last owned page, in block 0
+  u32x4 kreg[BF16 ? 1 : C::KIT];
+  u32x4 vreg[BF16 ? 1 : C::KIT];
+  // K/V of step s: bf16 -> 16-byte global-to-LDS copies straight into stage
+  // `buf` (each wave writes KIT whole 1 KiB blocks of each tile; key rows at
+  // or past nkeys copy the zero row); fp32 -> registers, see write_stage.
+  // Raw addresses stay readable: a row past nkeys lies in an owned block or,
+  // past the last owned page, in block 0.
+  auto issue_loads = [&](int pgv, const Step& s, int buf) {
     const E* kbase = kv_base(s.it, p.k);
     const E* vbase = kv_base(s.it, p.v);
     int pg[C::NPG];
@@ -230,80 +241,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int e = __builtin_amdgcn_readlane(pgv, i);
       pg[i] = s.t * C::NPG + i < s.it.npages ? e : 0;
     }
-#pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int pi = kpage_idx(it);
-      int pk = pg[0];
-#pragma unroll
-      for (int i = 1; i < C::NPG; ++i) pk = pi == i ? pg[i] : pk;   // uniform
-      kreg[it] = ld16(kbase + pk * page_stride + koff[it]);
-    }
     if constexpr (BF16) {
-      static_assert(C::VIT == 1, "one V item per thread");
-      const int q = vkq >> 2;
-      int pv = pg[0];
+      char* Kd = smem + buf * C::STAGE;
+      char* Vd = Kd + C::KTILE;
+      const int kv0 = s.t * C::BN;
+      const E* zero = reinterpret_cast<const E*>(g_zero_row);
 #pragma unroll
-      for (int i = 1; i < C::NPG; ++i) pv = q == i ? pg[i] : pv;
-      const E* vb = vbase + pv * page_stride;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[r] = ld16(vb + voff[r]);
-    } else {
-#pragma unroll
-      for (int it = 0; it < C::VIT; ++it) {
-        const int pi = kpage_idx(it);
+      for (int j = 0; j < C::KIT; ++j) {
+        const int blk = wave * C::KIT + j;   // 1 KiB block of each tile
+        const int pch = blk * 64 + lane;      // 16-byte chunk slot in the tile
+        const int key = pch / C::CPR, slot = pch % C::CPR;
+        const int pi = __builtin_amdgcn_readfirstlane(key >> 4);   // same page across the block
         int pk = pg[0];
 #pragma unroll
         for (int i = 1; i < C::NPG; ++i) pk = pi == i ? pg[i] : pk;
+        const bool live = kv0 + key < s.it.nkeys;
+        const int64_t row = pk * page_stride + (key & 15) * kv_tok_stride;
+        const int ck = (slot ^ C::kswz(key)) * 8, cv = (slot ^ C::vswz(key)) * 8;
+        copy16_to_lds(live ? kbase + row + ck : zero + ck, Kd + blk * 1024);
+        copy16_to_lds(live ? vbase + row + cv : zero + cv, Vd + blk * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < C::KIT; ++it) {
+        const int pi = kpage_idx(it);
+        int pk = pg[0];
+#pragma unroll
+        for (int i = 1; i < C::NPG; ++i) pk = pi == i ? pg[i] : pk;   // uniform
+        kreg[it] = ld16(kbase + pk * page_stride + koff[it]);
         vreg[it] = ld16(vbase + pk * page_stride + koff[it]);
       }
     }
   };
-  // Writes step s's registers to LDS buffer `buf`.  V rows at or past nkeys
-  // are zeroed (only an item's last tile has any): P is 0 there but V may hold
-  // anything.  K rows there stay as loaded: tiles that have them always take
-  // the masked path, which selects their scores away.
+  // fp32: writes step s's registers to LDS buffer `buf`.  V rows at or past
+  // nkeys are zeroed (only an item's last tile has any): P is 0 there but V
+  // may hold anything.  K rows there stay as loaded: tiles that have them
+  // always take the masked path, which selects their scores away.
   auto write_stage = [&](int buf, const Step& s) {
-    char* Ks = smem + buf * C::STAGE;
-    char* Vs = Ks + C::KTILE;
-    const int kv0 = s.t * C::BN;
-    const int nkeys = s.it.nkeys;
-    const bool tail = kv0 + C::BN > nkeys;
-    const u32x4 zero = {0, 0, 0, 0};
+    if constexpr (!BF16) {
+      char* Ks = smem + buf * C::STAGE;
+      char* Vs = Ks + C::KTILE;
+      const int kv0 = s.t * C::BN;
+      const bool tail = kv0 + C::BN > s.it.nkeys;
+      const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int cch = it * 256 + tid;
-      if (cch < C::KCH) st16(Ks + (cch / C::CPR) * C::KROW + (cch % C::CPR) * 16, kreg[it]);
-    }
-    if constexpr (BF16) {
-      // transpose 4 keys x 8 d into 8 rows (one per d) of 4 keys
-      if (tid < C::VITEMS) {
-        u32x4 wv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wv[r] = vreg[r];
-        if (tail) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) wv[r] = kv0 + vkq * 4 + r < nkeys ? wv[r] : zero;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t lo01 = __builtin_amdgcn_perm(wv[1][m], wv[0][m], 0x05040100u);
-          const uint32_t lo23 = __builtin_amdgcn_perm(wv[3][m], wv[2][m], 0x05040100u);
-          const uint32_t hi01 = __builtin_amdgcn_perm(wv[1][m], wv[0][m], 0x07060302u);
-          const uint32_t hi23 = __builtin_amdgcn_perm(wv[3][m], wv[2][m], 0x07060302u);
-          char* r0 = Vs + (vdch * 8 + 2 * m) * C::VROW + vkq * 8;
-          *reinterpret_cast<u32x2*>(r0) = u32x2{lo01, lo23};
-          *reinterpret_cast<u32x2*>(r0 + C::VROW) = u32x2{hi01, hi23};
-        }
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < C::VIT; ++it) {
+      for (int it = 0; it < C::KIT; ++it) {
         const int cch = it * 256 + tid;
-        const bool keep = !tail || kv0 + cch / C::CPR < nkeys;
-        if (cch < C::KCH) st16(Vs + (cch / C::CPR) * C::VROW + (cch % C::CPR) * 16, keep ? vreg[it] : zero);
+        if (cch < C::KCH) {
+          const bool keep = !tail || kv0 + cch / C::CPR < s.it.nkeys;
+          st16(Ks + (cch / C::CPR) * C::KROW + (cch % C::CPR) * 16, kreg[it]);
+          st16(Vs + (cch / C::CPR) * C::VROW + (cch % C::CPR) * 16, keep ? vreg[it] : zero);
+        }
       }
     }
   };
+  // bf16 transposing V reads: lane (16-lane group g16, i = lane % 16) reads
+  // the 8-byte row of key  base + 4 * (g16 / 2) + i / 4  and d  32 db +
+  // 16 (g16 % 2) + 4 (i % 4); the group then holds V^T for 16 d x 4 keys.
+  // The key base is a multiple of 4, so the row's swizzle depends on i / 4.
+  const int tr_i = lane & 15, tr_g = lane >> 4;
+  const int tr_row = (4 * (tr_g >> 1) + (tr_i >> 2)) * C::VROW + (tr_i & 1) * 8;
+  const int tr_c = 2 * (tr_g & 1) + ((tr_i & 3) >> 1), tr_sw = C::vswz(tr_i >> 2);
 
   // ---- Q fragment (B operand of S^T = K . Q^T) of an item ----------------
   // bf16 32x32x16: lane holds Q[row n][ks*16 + hh*8 .. +8] for k-step ks.
@@ -320,18 +318,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool ok = qrow < it.Lq;
     const int h = it.hgrp * p.HW + hw;
     const E* qp = static_cast<const E*>(p.q) + ((int64_t)(it.q0 + (ok ? qrow : 0)) * p.Hq + h) * D;
+    // the sign flip is a separate (uniform) step so a prefetch of Q is not
+    // waited for where it is issued
     if constexpr (BF16) {
 #pragma unroll
-      for (int ks = 0; ks < QF; ++ks) {
-        const u32x4 wq = ld16(qp + ks * 16 + hh * 8);   // row clamped to the item's first if !ok
-        qf[ks] = u32x4{wq[0] ^ flip, wq[1] ^ flip, wq[2] ^ flip, wq[3] ^ flip};
+      for (int ks = 0; ks < QF; ++ks) qf[ks] = ld16(qp + ks * 16 + hh * 8);   // row clamped to the item's first if !ok
+      if (flip) {
+#pragma unroll
+        for (int ks = 0; ks < QF; ++ks) qf[ks] = u32x4{qf[ks][0] ^ flip, qf[ks][1] ^ flip, qf[ks][2] ^ flip, qf[ks][3] ^ flip};
       }
     } else {
 #pragma unroll
       for (int c4 = 0; c4 < QF / 4; ++c4) {
         const u32x4 wq = ld16(qp + hh * (D / 2) + c4 * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(wq[e] ^ (flip << 16));
+        for (int e = 0; e < 4; ++e) qf[c4 * 4 + e] = __uint_as_float(wq[e]);
+      }
+      if (flip) {
+#pragma unroll
+        for (int e = 0; e < QF; ++e) qf[e] = -qf[e];
       }
     }
   };
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   Step nx2 = advance(nx1);
   load_q(cur.it);
   int pg_nxt = load_pages(cur);
-  issue_loads(pg_nxt, cur);
+  issue_loads(pg_nxt, cur, 0);
   pg_nxt = load_pages(nx1);
   write_stage(0, cur);
   __syncthreads();
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool has_next = nx1.it.ntiles != 0;
     const bool item_end = t + 1 == it.ntiles;   // last key tile of this item
     if (has_next) {
-      issue_loads(pg_nxt, nx1);
+      issue_loads(pg_nxt, nx1, buf ^ 1);
       pg_nxt = load_pages(nx2);
     }
 
@@ -390,9 +395,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         s[kb] = f32x16{};
         const char* krow = Ks + (kb * 32 + n) * C::KROW;
         if constexpr (BF16) {
+          // logical chunk 2 ks + hh of key kb*32 + n (whose swizzle is n's)
+          const int kx = hh ^ C::kswz(n);
 #pragma unroll
           for (int ks = 0; ks < D / 16; ++ks)
-            s[kb] = mfma32x32x16_bf16(*reinterpret_cast<const u32x4*>(krow + ks * 32 + hh * 16), qf[ks], s[kb]);
+            s[kb] = mfma32x32x16_bf16(*reinterpret_cast<const u32x4*>(krow + ((2 * ks) ^ kx) * 16), qf[ks], s[kb]);
         } else {
 #pragma unroll
           for (int c4 = 0; c4 < D / 8; ++c4) {
@@ -474,12 +481,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                               pack_bf16x2(s[kb][8 * pp + 2], s[kb][8 * pp + 3]),
                               pack_bf16x2(s[kb][8 * pp + 4], s[kb][8 * pp + 5]),
                               pack_bf16x2(s[kb][8 * pp + 6], s[kb][8 * pp + 7])};
-            const int key0 = kb * 32 + 16 * pp + 4 * hh;
+            // k slot e of this MFMA is key kb*32 + 16 pp + 4 hh + (e % 4) + 8 (e / 4):
+            // two transposing reads, keys +0..3 and +8..11 of the lane's group
+            const char* vk = Vs + (kb * 32 + 16 * pp) * C::VROW + tr_row;
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-              const char* vr = Vs + (db * 32 + n) * C::VROW + key0 * 2;
-              const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr);
-              const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + 16);
+              const int cs = ((4 * db + tr_c) ^ tr_sw) * 16;
+              const u32x2 lo2 = lds_read_tr16(vk + cs);
+              const u32x2 hi2 = lds_read_tr16(vk + 8 * C::VROW + cs);
               o[db] = mfma32x32x16_bf16(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pb, o[db]);
             }
           }
