@@ -19,7 +19,7 @@ from typing import Optional
 from . import _lib
 from ._lib import KVS_BF16, KVS_F32, KVS_I32, KvsError, KvsHints, describe, last_dispatch  # noqa: F401
 
-__all__ = ["kv_store_paged", "attn_varlen_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
+__all__ = ["kv_store_paged", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
 
 
 def _dtype_code(t) -> int:
@@ -80,9 +80,10 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
     """Exact paged varlen attention.  Returns ``(out, lse)`` (lse is None when
     ``return_lse`` is False and no ``lse`` tensor was given).
 
-    Uses the allocation-free ``attn_varlen_paged_ex`` entry point with a
-    torch-allocated workspace, or the one passed in, which must have been
-    zero-filled before its first use (see ``workspace_size``)."""
+    Uses the allocation-free ``attn_varlen_paged_ex`` entry point with the
+    workspace passed in, which must have been zero-filled before its first use
+    and be at least ``workspace_size`` bytes (the library checks), or else a
+    torch-allocated one of the size needed."""
     import torch
 
     lib = _lib.load()
@@ -91,20 +92,55 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
     if lse is None and return_lse:
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
     h = _hints(max_seqlen_q, max_seqlen_k, num_splits)
+    ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
+    d = [_desc(q), _desc(k_cache), _desc(v_cache), _desc(block_table), _desc(cu_seqlens_q), _desc(seqlens_k)]
+    st = lib.attn_varlen_paged_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)),
+                                  _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
+                                  _stream(q))
+    _lib.check(st)
+    return out, lse
+
+
+def _workspace(lib, q, k_cache, block_table, h, workspace):
+    """(pointer, bytes, tensor) of the decode workspace: the caller's as given (the
+    library checks its size), else a new zero-filled one of the size needed.
+    A workspace is zero-filled once: the decode counters in it must start at
+    zero, and every call leaves them at zero, so it may be kept and reused."""
+    if workspace is not None:
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
     dq, dk, dt_ = _desc(q), _desc(k_cache), _desc(block_table)
     need = lib.attn_varlen_paged_workspace_size(_ref(dq), _ref(dk), _ref(dt_), ctypes.byref(h))
     if need == ctypes.c_size_t(-1).value:
         raise KvsError(_lib.KVS_ERR_INVALID, lib.kvs_last_error().decode())
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        # zero-filled once: the decode counters in it must start at zero (and
-        # every call leaves them at zero, so a caller may keep and reuse it)
-        workspace = torch.zeros(int(need), dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
-    ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
-    d = [dq, dk, _desc(v_cache), dt_, _desc(cu_seqlens_q), _desc(seqlens_k)]
-    st = lib.attn_varlen_paged_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)),
-                                  _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
-                                  _stream(q))
+    if not need:
+        return None, 0, None
+    import torch
+
+    workspace = torch.zeros(int(need), dtype=torch.uint8, device=q.device)
+    return workspace.data_ptr(), int(need), workspace
+
+
+def attn_decode_append_paged(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale: float,
+                             out=None, lse=None, *, return_lse: bool = True, max_seqlen_k: int = 0,
+                             num_splits: int = 0, workspace=None):
+    """One decode step in one launch: writes row b of ``k_new`` / ``v_new`` as
+    key ``seqlens_k[b] - 1`` of sequence b (its slot taken from the block
+    table) and attends query row b over the sequence's ``seqlens_k[b]`` keys.
+    Same result as ``kv_store_paged`` then ``attn_varlen_paged`` with
+    ``cu_seqlens_q = 0..B``.  Returns ``(out, lse)``."""
+    import torch
+
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    h = _hints(1, max_seqlen_k, num_splits)
+    ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
+    d = [_desc(q), _desc(k_new), _desc(v_new), _desc(k_cache), _desc(v_cache), _desc(block_table),
+         _desc(seqlens_k)]
+    st = lib.attn_decode_append_paged(*[_ref(x) for x in d], ctypes.c_float(scale), _ref(_desc(out)),
+                                      _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes, _stream(q))
     _lib.check(st)
     return out, lse
 

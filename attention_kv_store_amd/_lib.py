@@ -24,6 +24,7 @@ EXPORTS = (
     "attn_varlen_paged",
     "attn_varlen_paged_workspace_size",
     "attn_varlen_paged_ex",
+    "attn_decode_append_paged",
     "kvs_last_error",
     "kvs_last_dispatch",
     "kvs_release_workspace",
@@ -79,6 +80,9 @@ def load(path: str = LIB_PATH):
     lib.attn_varlen_paged_ex.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P,
                                          ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
     lib.attn_varlen_paged_ex.restype = st
+    lib.attn_decode_append_paged.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, P,
+                                             ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
+    lib.attn_decode_append_paged.restype = st
     lib.kvs_last_error.argtypes = []
     lib.kvs_last_error.restype = ctypes.c_char_p
     lib.kvs_last_dispatch.argtypes = []

@@ -96,18 +96,19 @@ struct Plan {
   int D = 0;
   bool decode = false;
   size_t ws_bytes = 0;   // scratch needed (decode with >1 split)
+  size_t ws_po_off = 0;  // byte offset of part_o inside the scratch
   size_t ws_lse_off = 0; // byte offset of part_lse inside the scratch
-  size_t ws_cnt_off = 0; // byte offset of the per-sequence counters
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Validates shapes (not device values) and fills the plan.  `v_cache`,
-// `cu`, `lk`, `out`, `lse` may be NULL when only sizing the workspace.
+// `cu`, `lk`, `out`, `lse` may be NULL when only sizing the workspace; `cu`
+// is NULL in append mode (one query row per sequence).
 kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
                      const kvs_tensor* table, const kvs_tensor* cu, const kvs_tensor* lk, float scale,
                      int causal, const kvs_tensor* out, const kvs_tensor* lse, const kvs_hints* hints,
-                     bool sizing_only, Plan* plan) {
+                     bool sizing_only, Plan* plan, bool append = false) {
   KVS_TRY(check_tensor(q, "q", kFloatTypes, 3));
   KVS_TRY(check_tensor(k_cache, "k_cache", kFloatTypes, 4));
   KVS_TRY(check_tensor(table, "block_table", kIntTypes, 2));
@@ -129,9 +130,13 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     for (int i = 0; i < 4; ++i)
       if (v_cache->shape[i] != k_cache->shape[i]) return fail(KVS_ERR_INVALID, "v_cache shape != k_cache shape");
     if (v_cache->dtype != q->dtype) return fail(KVS_ERR_INVALID, "v_cache dtype != q dtype");
-    KVS_TRY(check_tensor(cu, "cu_seqlens_q", kIntTypes, 1));
+    if (!append) {
+      KVS_TRY(check_tensor(cu, "cu_seqlens_q", kIntTypes, 1));
+      if (cu->shape[0] != B + 1) return fail(KVS_ERR_INVALID, "cu_seqlens_q has %lld entries, expected B+1=%lld", (long long)cu->shape[0], (long long)(B + 1));
+    } else if (T != B) {
+      return fail(KVS_ERR_INVALID, "append mode needs one query row per sequence (q has %lld rows for %lld sequences)", (long long)T, (long long)B);
+    }
     KVS_TRY(check_tensor(lk, "seqlens_k", kIntTypes, 1));
-    if (cu->shape[0] != B + 1) return fail(KVS_ERR_INVALID, "cu_seqlens_q has %lld entries, expected B+1=%lld", (long long)cu->shape[0], (long long)(B + 1));
     if (lk->shape[0] != B) return fail(KVS_ERR_INVALID, "seqlens_k has %lld entries, expected B=%lld", (long long)lk->shape[0], (long long)B);
     KVS_TRY(check_tensor(out, "out", kFloatTypes, 3));
     if (out->dtype != q->dtype) return fail(KVS_ERR_INVALID, "out dtype != q dtype");
@@ -159,6 +164,7 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   p.Hq = (int32_t)Hq;
   p.Hkv = (int32_t)Hkv;
   p.MB = (int32_t)MB;
+  p.NB = (int32_t)NB;
   p.G = (int32_t)(Hq / Hkv);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal ? 1 : 0;
@@ -205,10 +211,18 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   if (kvs::decode_lds_bytes((int)B, hpw, kvs::decode_slab_bytes((int)D)) > kLdsBudget)
     return fail(KVS_ERR_UNSUPPORTED, "decode batch too large for one workgroup's LDS (B=%lld)", (long long)B);
   if (nwg > 1) {
+    // The counters sit at the same place for every shape: the first
+    // kvs::kDecodeCounterBytes of the workspace, counter (b, g) at index
+    // b * Hkv + g.  Every call leaves the ones it used at zero, so calls of
+    // any shapes may follow one another on one workspace (a layout that moved
+    // with the shape would meet another call's partial outputs there).
+    if (B * Hkv > (int64_t)(kvs::kDecodeCounterBytes / sizeof(int32_t)))
+      return fail(KVS_ERR_UNSUPPORTED, "split decode supports B * Hkv <= %zu (got %lld)",
+                  kvs::kDecodeCounterBytes / sizeof(int32_t), (long long)(B * Hkv));
     const size_t slots = (size_t)nwg + B;
-    plan->ws_lse_off = align_up(slots * Hq * D * sizeof(float), 256);
-    plan->ws_cnt_off = plan->ws_lse_off + align_up(slots * Hq * sizeof(float), 256);
-    plan->ws_bytes = plan->ws_cnt_off + align_up((size_t)B * Hkv * sizeof(int32_t), 256);
+    plan->ws_po_off = kvs::kDecodeCounterBytes;
+    plan->ws_lse_off = plan->ws_po_off + align_up(slots * Hq * D * sizeof(float), 256);
+    plan->ws_bytes = plan->ws_lse_off + align_up(slots * Hq * sizeof(float), 256);
   }
   return KVS_OK;
 }
@@ -271,9 +285,9 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
       if (!ws || ws_bytes < plan.ws_bytes)
         return fail(KVS_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", plan.ws_bytes, ws_bytes);
       if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(KVS_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-      p.part_o = static_cast<float*>(ws);
+      p.counters = static_cast<int32_t*>(ws);
+      p.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.ws_po_off);
       p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.ws_lse_off);
-      p.counters = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.ws_cnt_off);
     }
     const hipError_t e = kvs::launch_decode(p, plan.dt, plan.D, stream);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
@@ -357,6 +371,37 @@ size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k
                 &plan) != KVS_OK)
     return (size_t)-1;
   return plan.ws_bytes;
+}
+
+kvs_status attn_decode_append_paged(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                    kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
+                                    const kvs_tensor* seqlens_k, float scale, kvs_tensor* out, kvs_tensor* lse,
+                                    const kvs_hints* hints, void* workspace, size_t workspace_bytes,
+                                    kvs_stream_t stream) {
+  g_err.clear();
+  if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
+    return fail(KVS_ERR_INVALID, "hints must be non-negative");
+  Plan plan;
+  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, nullptr, seqlens_k, scale, 1, out, lse, hints, false,
+                    &plan, true));
+  KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3));
+  KVS_TRY(check_tensor(v_new, "v_new", kFloatTypes, 3));
+  for (int i = 0; i < 3; ++i)
+    if (v_new->shape[i] != k_new->shape[i]) return fail(KVS_ERR_INVALID, "v_new shape != k_new shape");
+  if (k_new->dtype != q->dtype || v_new->dtype != q->dtype) return fail(KVS_ERR_INVALID, "k_new / v_new dtype != q dtype");
+  if (k_new->shape[0] != q->shape[0] || k_new->shape[1] != k_cache->shape[2] || k_new->shape[2] != k_cache->shape[3])
+    return fail(KVS_ERR_INVALID, "k_new must be [B, Hkv, D] = [%lld, %lld, %lld]", (long long)q->shape[0],
+                (long long)k_cache->shape[2], (long long)k_cache->shape[3]);
+  kvs::AttnParams& p = plan.p;
+  p.k_new = k_new->data;
+  p.v_new = v_new->data;
+  p.k_cache_w = k_cache->data;
+  p.v_cache_w = v_cache->data;
+  p.append = 1;
+  KVS_TRY(run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream)));
+  set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
+               plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg);
+  return KVS_OK;
 }
 
 kvs_status attn_varlen_paged_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,

@@ -43,6 +43,7 @@
 //    the compiler can count outstanding loads exactly and a prefetch is never
 //    waited on early.  Addresses past a sequence's end stay readable: tail
 //    rows lie in an owned block, and blocks past a step's end read block 0.
+#include <atomic>
 #include <type_traits>
 
 #include "kvs_device.hpp"
@@ -112,7 +113,7 @@ struct Step {
   int last;   // last step of the piece
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool APPEND>
 struct DecodeWave {
   using C = DCfg<D>;
   using E = typename std::conditional<BF16, uint16_t, float>::type;
@@ -182,6 +183,87 @@ struct DecodeWave {
     u32x4 v[C::NBS][2 * C::VIL];
     u32x4 q[C::KI];
   };
+  // First element of sequence b's new K (V) row of this wave's KV head.
+  __device__ __forceinline__ const E* new_row(const void* base, int b) const {
+    return static_cast<const E*>(base) + ((int64_t)b * p.Hkv + g) * D;
+  }
+
+  // ---- append: the cache writes ---------------------------------------------
+  // Workgroup w writes the new rows of sequences w, w + nwg, w + 2 nwg, ...
+  // (its wave g the rows of KV head g) during its set-up, so the stores are
+  // issued before its stream of loads starts.  One wave instruction covers RPI
+  // rows: lane = row * CH + piece, one 16-byte piece per lane.  Rows whose
+  // length or table entry lies outside the cache are skipped.
+  static constexpr int EPP = 16 / (int)sizeof(E);   // elements per 16-byte piece
+  static constexpr int CH = D / EPP;                // pieces per row of one KV head
+  static constexpr int RPI = 64 / CH;               // rows per wave instruction
+  struct NewRows {
+    u32x4 k, v;
+    int kl;   // key index Lk - 1 (-1: no row for this lane)
+    int pj;   // physical block holding it
+  };
+  __device__ __forceinline__ NewRows append_load(int b0, int stride, const int* slens) const {
+    NewRows r;
+    r.kl = -1;
+    r.pj = -1;
+    const int b = b0 + (lane / CH) * stride;
+    if (b < p.B) {
+      const int Lk = slens[b];
+      if (Lk >= 1 && Lk <= p.MB * kPage) {
+        const int c = lane % CH;
+        r.kl = Lk - 1;
+        r.pj = p.table[(int64_t)b * p.MB + (r.kl >> 4)];
+        r.k = ld16(new_row(p.k_new, b) + c * EPP);
+        r.v = ld16(new_row(p.v_new, b) + c * EPP);
+      }
+    }
+    return r;
+  }
+  __device__ __forceinline__ void append_store(const NewRows& r) const {
+    if (r.kl >= 0 && r.pj >= 0 && r.pj < p.NB) {
+      const int64_t at = ((int64_t)r.pj * kPage + (r.kl & 15)) * tok_stride + (int64_t)g * D + (lane % CH) * EPP;
+      st16(static_cast<E*>(p.k_cache_w) + at, r.k);
+      st16(static_cast<E*>(p.v_cache_w) + at, r.v);
+    }
+  }
+  // stores the rows `first` holds (those of sequences w + nwg * (lane / CH)),
+  // then loads and stores the workgroup's remaining rows, if any
+  __device__ __forceinline__ void append_rows(const NewRows& first, int w, int nwg, const int* slens) const {
+    append_store(first);
+    for (int b0 = w + nwg * RPI; b0 < p.B; b0 += nwg * RPI) append_store(append_load(b0, nwg, slens));
+  }
+
+  // K and V loads of one step.  With SUB, key kl is read from the new row
+  // (kn, vn) instead of the cache (the cache slot is written in this launch).
+  template <bool SUB>
+  __device__ __forceinline__ void load_kv(const Step& st, const int* phys, Buf& bf, int kl, const E* kn,
+                                          const E* vn) {
+    const int kp = lane & 7;
+#pragma unroll
+    for (int j = 0; j < C::NBS; ++j) {
+      const E* kblk = kbase + (int64_t)phys[j] * kPage * tok_stride;
+      const E* vblk = vbase + (int64_t)phys[j] * kPage * tok_stride;
+      const int key0 = (st.lblk + j) * 16;
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i) {
+        const E* ka = kblk + col * tok_stride + i * 32 + grp * 8;
+        if constexpr (SUB) ka = key0 + col == kl ? kn + i * 32 + grp * 8 : ka;
+        bf.k[j][i] = ld16(ka);
+      }
+#pragma unroll
+      for (int it = 0; it < C::VIL; ++it) {
+        const int dch = (lane >> 3) + 8 * it;
+        const E* va0 = vblk + (2 * kp) * tok_stride + dch * 8;
+        const E* va1 = vblk + (2 * kp + 1) * tok_stride + dch * 8;
+        if constexpr (SUB) {
+          va0 = key0 + 2 * kp == kl ? vn + dch * 8 : va0;
+          va1 = key0 + 2 * kp + 1 == kl ? vn + dch * 8 : va1;
+        }
+        bf.v[j][2 * it] = ld16(va0);
+        bf.v[j][2 * it + 1] = ld16(va1);
+      }
+    }
+  }
 
   // Raw, unconditional loads of one step into `bf` (phys[j] = physical block of
   // the step's j-th block, 0 for blocks past its end).
@@ -190,19 +272,19 @@ struct DecodeWave {
     const E* qp = static_cast<const E*>(p.q) + ((int64_t)(st.b < 0 ? 0 : st.t) * p.Hq + hq) * D;
 #pragma unroll
     for (int i = 0; i < C::KI; ++i) bf.q[i] = ld16(qp + i * 32 + grp * 8);
-    const int kp = lane & 7;
-#pragma unroll
-    for (int j = 0; j < C::NBS; ++j) {
-      const E* kblk = kbase + (int64_t)phys[j] * kPage * tok_stride;
-      const E* vblk = vbase + (int64_t)phys[j] * kPage * tok_stride;
-#pragma unroll
-      for (int i = 0; i < C::KI; ++i) bf.k[j][i] = ld16(kblk + col * tok_stride + i * 32 + grp * 8);
-#pragma unroll
-      for (int it = 0; it < C::VIL; ++it) {
-        const int dch = (lane >> 3) + 8 * it;
-        bf.v[j][2 * it] = ld16(vblk + (2 * kp) * tok_stride + dch * 8);
-        bf.v[j][2 * it + 1] = ld16(vblk + (2 * kp + 1) * tok_stride + dch * 8);
+    if constexpr (APPEND) {
+      // append: the step holding key kl = Lk - 1 (one step per sequence, a
+      // wave-uniform branch) reads that key from the new row; the cache slot
+      // is written elsewhere in the same launch
+      const int kl = st.Lk - 1;
+      const bool app = st.b >= 0 && (kl >> 4) >= st.lblk && (kl >> 4) < st.lblk + C::NBS;
+      if (app) {
+        load_kv<true>(st, phys, bf, kl, new_row(p.k_new, st.b), new_row(p.v_new, st.b));
+      } else {
+        load_kv<false>(st, phys, bf, 0, nullptr, nullptr);
       }
+    } else {
+      load_kv<false>(st, phys, bf, 0, nullptr, nullptr);
     }
   }
 
@@ -271,6 +353,16 @@ struct DecodeWave {
     const float* kb = reinterpret_cast<const float*>(kbase);
     const float* vb = reinterpret_cast<const float*>(vbase);
     const int kend = min(st.Lk, (st.lblk + st.nblk) * 16);
+    // append: key kl = Lk - 1 comes from the new row
+    const int kl = st.Lk - 1;
+    const float* kn = nullptr;
+    const float* vn = nullptr;
+    bool app = false;
+    if constexpr (APPEND) {
+      app = (kl >> 4) >= st.lblk && (kl >> 4) < st.lblk + st.nblk;   // uniform
+      kn = reinterpret_cast<const float*>(new_row(p.k_new, st.b));
+      vn = reinterpret_cast<const float*>(new_row(p.v_new, st.b));
+    }
 #pragma unroll
     for (int j = 0; j < C::NBS; ++j) {
       if (j >= st.nblk) break;
@@ -280,7 +372,9 @@ struct DecodeWave {
       f32x4 s[1] = {f32x4{}};
 #pragma unroll
       for (int c4 = 0; c4 < QF / 4; ++c4) {
-        const u32x4 w = ld16(kblk + col * tok_stride + grp * QF + c4 * 4);
+        const float* ka = kblk + col * tok_stride + grp * QF + c4 * 4;
+        if constexpr (APPEND) ka = (app && kb0 + col == kl) ? kn + grp * QF + c4 * 4 : ka;
+        const u32x4 w = ld16(ka);
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[0] = mfma16x16x4_f32(__uint_as_float(w[e]), qv[c4 * 4 + e], s[0]);
       }
@@ -291,7 +385,8 @@ struct DecodeWave {
         const bool ok = kb0 + key < kend;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          const float v = vblk[key * tok_stride + db * 16 + col];
+          float v = vblk[key * tok_stride + db * 16 + col];
+          if constexpr (APPEND) v = (app && kb0 + key == kl) ? vn[db * 16 + col] : v;
           o[db] = mfma16x16x4_f32(ok ? v : 0.f, s[0][r], o[db]);
         }
       }
@@ -348,157 +443,126 @@ struct DecodeWave {
     if (grp == 0) atomic_st(p.part_lse + prow, lse2);
   }
 
-  // Merge the pieces of up to two sequences (nm of them; query rows t[m],
-  // blocks [s0[m], s1[m]) on the flattened axis) for this wave's query heads.
-  // The pieces of sequence b are the partial slots w + b of the workgroups w
-  // whose ranges meet its blocks; the pieces of both sequences form one list
-  // of items.  Heads go HB at a time and items PC at a time.  In a round, lane
-  // i loads the lse of (item i / HB, head j = i % HB) and every lane loads its
-  // d = lane + 64 k of each (item, head) output, all before any is used (one
-  // memory round trip).  The lanes of head j then hold that head's running
-  // maximum M and weight sum W per sequence (cross-lane reductions), and each
-  // output element adds its items with independent fmas:
+  // Merge the pieces of sequence b (query row b, blocks [sb0, sb1) on the
+  // flattened axis) for this wave's query heads.  The pieces are the partial
+  // slots w + b of the workgroups w whose ranges meet the sequence's blocks.
+  // Heads go HB at a time and pieces PC at a time counted from the first
+  // piece, so the rounding is the same whichever workgroup ends up merging
+  // the sequence (and whether it merges another one too).  In a round,
+  // lane i loads the lse of (piece i / HB, head j = i % HB) and every lane
+  // loads its d = lane + 64 k of each (piece, head) output, all before any is
+  // used (one memory round trip).  The lanes of head j then hold that head's
+  // running maximum M and weight sum W (cross-lane reductions), and each
+  // output element adds the round's pieces with independent fmas:
   //   M' = max(M, max_i lse_i),  W' = W 2^(M - M') + sum_i 2^(lse_i - M'),
   //   acc' = acc 2^(M - M') + sum_i 2^(lse_i - M') O_i,   out = acc / W.
-  __device__ __forceinline__ void merge(int nm, const int* t, const int* bs, const int* s0, const int* s1, int total,
-                                        int nwg) {
+  __device__ __forceinline__ void merge(int b, int sb0, int sb1, int total, int nwg) {
     constexpr int HB = 4;
     constexpr int PC = D == 64 ? 16 : 8;
-    int wf[2], cnt[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int mm = m < nm ? m : 0;
-      // ranges holding the first and the last block of the sequence
-      wf[m] = (int)udiv_small((uint64_t)(s0[mm] + 1) * (uint32_t)nwg - 1, (uint32_t)total);
-      const int wl = (int)udiv_small((uint64_t)s1[mm] * (uint32_t)nwg - 1, (uint32_t)total);
-      cnt[m] = m < nm ? wl - wf[m] + 1 : 0;
-    }
-    const int nitems = cnt[0] + cnt[1];
+    static_assert(HB == 4, "the reductions below run over the lanes that share lane % 4");
     const bool none_empty = total >= nwg;   // then every range holds at least one block
     const __amdgpu_buffer_rsrc_t rs = raw_rsrc(p.part_o, part_bytes());
     const int hj = lane % HB;                // the head whose running state this lane holds
-    for (int qh0 = 0; qh0 < p.G; qh0 += HB) {
-      float M[2] = {kMaskedScore, kMaskedScore}, W[2] = {0.f, 0.f};
-      float acc[2][HB][C::DPL];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
+    {
+      // ranges holding the first and the last block of the sequence
+      const int wf = (int)udiv_small((uint64_t)(sb0 + 1) * (uint32_t)nwg - 1, (uint32_t)total);
+      const int wl = (int)udiv_small((uint64_t)sb1 * (uint32_t)nwg - 1, (uint32_t)total);
+      const int npc = wl - wf + 1;
+      for (int qh0 = 0; qh0 < p.G; qh0 += HB) {
+        float M = kMaskedScore, W = 0.f;
+        float acc[HB][C::DPL];
 #pragma unroll
         for (int j = 0; j < HB; ++j)
 #pragma unroll
-          for (int k = 0; k < C::DPL; ++k) acc[m][j][k] = 0.f;
-      for (int i0 = 0; i0 < nitems; i0 += PC) {
-        // item i -> (sequence sel, range w); slot w + b_sel.  Items past the
-        // list reuse its last slot (a readable address) and are not live.
-        const int nround = min(PC, nitems - i0);
-        auto item = [&](int i, int& sel) __attribute__((always_inline)) {
-          const int ic = i0 + min(i, nround - 1);
-          sel = ic >= cnt[0] ? 1 : 0;
-          return wf[sel] + (ic - (sel ? cnt[0] : 0));
-        };
-        // live items of the round as a bit mask; with at least as many blocks
-        // as ranges every range is non-empty, otherwise lane i checks item i
-        uint64_t livemask;
-        if (none_empty) {
-          livemask = nround >= 64 ? ~0ull : ((1ull << nround) - 1);
-        } else {
-          int sl;
-          const int wl = item(lane, sl);
-          livemask = __ballot(lane < nround && range_start64(wl + 1, total, nwg) > range_start64(wl, total, nwg));
-        }
-        int lsel;
-        float lsl;
-        {
-          const int il = (lane % (PC * HB)) / HB;
-          const int slot = item(il, lsel) + bs[lsel];
-          const int hh = g * p.G + min(qh0 + hj, p.G - 1);
-          const float l = atomic_ld(p.part_lse + (int64_t)slot * p.Hq + hh);
-          lsl = (lane < PC * HB && ((livemask >> il) & 1)) ? l : kMaskedScore;
-        }
-        float ov[PC][HB][C::DPL];
-#pragma unroll
-        for (int i = 0; i < PC; ++i) {
-          int sel;
-          const uint32_t slot = (uint32_t)(item(i, sel) + bs[sel]);
-#pragma unroll
-          for (int j = 0; j < HB; ++j) {
-            const uint32_t hh = (uint32_t)(g * p.G + min(qh0 + j, p.G - 1));
-#pragma unroll
-            for (int k = 0; k < C::DPL; ++k)
-              ov[i][j][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                  rs, ((slot * (uint32_t)p.Hq + hh) * D + lane + 64 * k) * 4, 0, kDeviceScope));
+          for (int k = 0; k < C::DPL; ++k) acc[j][k] = 0.f;
+        for (int i0 = 0; i0 < npc; i0 += PC) {
+          // piece i of the round -> its range; pieces past the sequence's last
+          // reuse that one's slot (a readable address) and are not live
+          const int nround = min(PC, npc - i0);
+          auto range = [&](int i) __attribute__((always_inline)) { return wf + i0 + min(i, nround - 1); };
+          // live pieces of the round as a bit mask; with at least as many
+          // blocks as ranges every range is non-empty, otherwise lane i checks
+          // piece i
+          uint64_t livemask;
+          if (none_empty) {
+            livemask = nround >= 64 ? ~0ull : ((1ull << nround) - 1);
+          } else {
+            const int wr = range(lane);
+            livemask = __ballot(lane < nround && range_start64(wr + 1, total, nwg) > range_start64(wr, total, nwg));
           }
-        }
-        // running maximum and weight sum of head hj, per sequence, over the
-        // lanes that hold that head (lane bits above log2(HB))
-        static_assert(HB == 4, "the reductions below run over the lanes that share lane % 4");
-        float Mn[2], sc[2];
+          float lsl;
+          {
+            const int il = (lane % (PC * HB)) / HB;
+            const int slot = range(il) + b;
+            const int hh = g * p.G + min(qh0 + hj, p.G - 1);
+            const float l = atomic_ld(p.part_lse + (int64_t)slot * p.Hq + hh);
+            lsl = (lane < PC * HB && ((livemask >> il) & 1)) ? l : kMaskedScore;
+          }
+          float ov[PC][HB][C::DPL];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float x = max_mod4(lsel == m ? lsl : kMaskedScore);
-          Mn[m] = fmaxf(M[m], x);
-          sc[m] = __builtin_amdgcn_exp2f(M[m] - Mn[m]);
-        }
-        const float wt = lsl == kMaskedScore ? 0.f : __builtin_amdgcn_exp2f(lsl - (lsel ? Mn[1] : Mn[0]));
+          for (int i = 0; i < PC; ++i) {
+            const uint32_t slot = (uint32_t)(range(i) + b);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float x = sum_mod4(lsel == m ? wt : 0.f);
-          W[m] = W[m] * sc[m] + x;
-          M[m] = Mn[m];
-        }
+            for (int j = 0; j < HB; ++j) {
+              const uint32_t hh = (uint32_t)(g * p.G + min(qh0 + j, p.G - 1));
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+              for (int k = 0; k < C::DPL; ++k)
+                ov[i][j][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rs, ((slot * (uint32_t)p.Hq + hh) * D + lane + 64 * k) * 4, 0, kDeviceScope));
+            }
+          }
+          // running maximum and weight sum of head hj over the lanes that hold
+          // that head (lane bits above log2(HB))
+          const float Mn = fmaxf(M, max_mod4(lsl));
+          const float sc = __builtin_amdgcn_exp2f(M - Mn);
+          const float wt = lsl == kMaskedScore ? 0.f : __builtin_amdgcn_exp2f(lsl - Mn);
+          W = W * sc + sum_mod4(wt);
+          M = Mn;
 #pragma unroll
           for (int j = 0; j < HB; ++j) {
-            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[m]), j));
+            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), j));
 #pragma unroll
-            for (int k = 0; k < C::DPL; ++k) acc[m][j][k] *= f;
+            for (int k = 0; k < C::DPL; ++k) acc[j][k] *= f;
           }
 #pragma unroll
-        for (int i = 0; i < PC; ++i) {
-          // uniform: items that do not exist are skipped, never weighted by 0
-          if (!((livemask >> i) & 1)) continue;
-          const int sel = i0 + i >= cnt[0] ? 1 : 0;
+          for (int i = 0; i < PC; ++i) {
+            // uniform: pieces that do not exist are skipped, never weighted by 0
+            if (!((livemask >> i) & 1)) continue;
 #pragma unroll
-          for (int j = 0; j < HB; ++j) {
-            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), i * HB + j));
+            for (int j = 0; j < HB; ++j) {
+              const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), i * HB + j));
 #pragma unroll
-            for (int k = 0; k < C::DPL; ++k) {
-              if (sel) acc[1][j][k] = fmaf(f, ov[i][j][k], acc[1][j][k]);
-              else acc[0][j][k] = fmaf(f, ov[i][j][k], acc[0][j][k]);
+              for (int k = 0; k < C::DPL; ++k) acc[j][k] = fmaf(f, ov[i][j][k], acc[j][k]);
             }
           }
         }
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m >= nm) break;
 #pragma unroll
         for (int j = 0; j < HB; ++j) {
           if (qh0 + j >= p.G) break;
           const int hh = g * p.G + qh0 + j;
-          const float Wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(W[m]), j));
-          const float Mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M[m]), j));
+          const float Wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(W), j));
+          const float Mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), j));
           const float inv = 1.0f / Wj;
-          const int64_t orow = ((int64_t)t[m] * p.Hq + hh) * D;
+          const int64_t orow = ((int64_t)b * p.Hq + hh) * D;
 #pragma unroll
           for (int k = 0; k < C::DPL; ++k) {
             if constexpr (BF16) {
-              reinterpret_cast<__bf16*>(p.out)[orow + lane + 64 * k] = (__bf16)(acc[m][j][k] * inv);
+              reinterpret_cast<__bf16*>(p.out)[orow + lane + 64 * k] = (__bf16)(acc[j][k] * inv);
             } else {
-              static_cast<float*>(p.out)[orow + lane + 64 * k] = acc[m][j][k] * inv;
+              static_cast<float*>(p.out)[orow + lane + 64 * k] = acc[j][k] * inv;
             }
           }
-          if (p.lse && lane == 0) p.lse[(int64_t)t[m] * p.Hq + hh] = (Mj + __builtin_amdgcn_logf(Wj)) * kLn2;
+          if (p.lse && lane == 0) p.lse[(int64_t)b * p.Hq + hh] = (Mj + __builtin_amdgcn_logf(Wj)) * kLn2;
         }
       }
     }
   }
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool APPEND>
 __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   using C = DCfg<D>;
-  using W = DecodeWave<D, BF16>;
+  using W = DecodeWave<D, BF16, APPEND>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int B = p.B;
   int* slens = reinterpret_cast<int*>(smem);         // [B]      seqlens_k
@@ -542,7 +606,16 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   }
   const int total = sstart[B];
   const int r0 = (int)(((int64_t)w * total) / nwg), r1 = (int)(((int64_t)(w + 1) * total) / nwg);
-  if (r0 >= r1) return;  // empty range (whole workgroup)
+  const int g = hg * p.hpw + wave;
+  W wv(p, g, slabs + wave * C::SLAB);
+  // append: this workgroup's first new rows are loaded now, with the table
+  // window below, and stored once it has arrived
+  typename W::NewRows nr;
+  if constexpr (APPEND) nr = wv.append_load(w, nwg, slens);
+  if (r0 >= r1) {  // empty range (whole workgroup)
+    if constexpr (APPEND) wv.append_rows(nr, w, nwg, slens);
+    return;
+  }
 
   auto seq_of = [&](int gb) __attribute__((always_inline)) {  // largest b with sstart[b] <= gb
     int lo = 0, hi = B - 1;
@@ -553,9 +626,6 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     return lo;
   };
 
-  const int g = hg * p.hpw + wave;
-  W wv(p, g, slabs + wave * C::SLAB);
-
   // The range's table entries, once, in LDS (the planner keeps a range within
   // kTblWin blocks).
   for (int i = tid; i < r1 - r0; i += nthr) {
@@ -564,6 +634,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     tbl[i] = p.table[(int64_t)b * p.MB + (gb - sstart[b])];
   }
   __syncthreads();
+  if constexpr (APPEND) wv.append_rows(nr, w, nwg, slens);
 
   // Segments of the range, in processing order: the piece of the last sequence
   // Z (its head, unless it starts in this range), the piece of the first
@@ -650,14 +721,13 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       if (done) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
     }
     const uint64_t lastm = __ballot(done);
-    int nm = 0, mt[2], mbs[2], ms0[2], ms1[2];
-    if (lastm & 1) {
-      mt[nm] = split_b0; mbs[nm] = split_b0; ms0[nm] = sstart[split_b0]; ms1[nm] = sstart[split_b0 + 1]; ++nm;
+    // one query row per sequence: sequence b's output row is b
+#pragma nounroll
+    for (int m = 0; m < 2; ++m) {
+      if (!((lastm >> m) & 1)) continue;
+      const int mb = m == 0 ? split_b0 : split_b1;
+      wv.merge(mb, sstart[mb], sstart[mb + 1], total, nwg);
     }
-    if (lastm & 2) {
-      mt[nm] = split_b1; mbs[nm] = split_b1; ms0[nm] = sstart[split_b1]; ms1[nm] = sstart[split_b1 + 1]; ++nm;
-    }
-    if (nm > 0) wv.merge(nm, mt, mbs, ms0, ms1, total, nwg);
   };
 
   // Stream segments [s_begin, s_end) through the two-buffer pipeline.
@@ -710,29 +780,38 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   if (nseg > nsplit_seg) stream(nsplit_seg, nseg);
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool APPEND>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   using C = DCfg<D>;
   static_assert(C::SLAB == D * 40, "decode_slab_bytes must match the slab layout");
   const size_t lds = decode_lds_bytes(p.B, p.hpw, C::SLAB);
   // dynamic LDS above the default limit must be requested; grow it as needed
-  static size_t lds_granted = 0;
-  if (lds > lds_granted) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16>),
+  // (per instantiation; atomic so that concurrent first calls are safe)
+  static std::atomic<size_t> lds_granted{0};
+  if (lds > lds_granted.load(std::memory_order_relaxed)) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
       return e;
     }
-    lds_granted = lds;
+    size_t cur = lds_granted.load(std::memory_order_relaxed);
+    while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
+    }
   }
-  hipLaunchKernelGGL((decode_kernel<D, BF16>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
   return hipGetLastError();
 }
 
+template <bool APPEND>
+static hipError_t launch_decode_a(const AttnParams& p, DType dt, int D, hipStream_t s) {
+  if (dt == DType::BF16)
+    return D == 64 ? launch_decode_t<64, true, APPEND>(p, s) : launch_decode_t<128, true, APPEND>(p, s);
+  return D == 64 ? launch_decode_t<64, false, APPEND>(p, s) : launch_decode_t<128, false, APPEND>(p, s);
+}
+
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s) {
-  if (dt == DType::BF16) return D == 64 ? launch_decode_t<64, true>(p, s) : launch_decode_t<128, true>(p, s);
-  return D == 64 ? launch_decode_t<64, false>(p, s) : launch_decode_t<128, false>(p, s);
+  return p.append ? launch_decode_a<true>(p, dt, D, s) : launch_decode_a<false>(p, dt, D, s);
 }
 
 }  // namespace kvs

@@ -47,7 +47,20 @@ struct AttnParams {
   float* part_o;          // [nwg + B, Hq, D] fp32 partial outputs (normalised)
   float* part_lse;        // [nwg + B, Hq]    fp32 partial lse (base 2)
   int32_t* counters;      // [B, Hkv]         finished-block counts; zero between calls
+  // decode with append: the new K/V row of sequence b ([B, Hkv, D]) is its
+  // key seqlens_k[b] - 1; it is read from here (not from the cache) and
+  // written to the cache at that key's slot
+  const void* k_new;
+  const void* v_new;
+  void* k_cache_w;
+  void* v_cache_w;
+  int32_t append;
+  int32_t NB;             // cache blocks (the append writes only slots inside the pool)
 };
+
+// Split decode counts finished blocks per (sequence, KV head) in the first
+// bytes of its workspace, at a place that does not depend on the shape.
+constexpr size_t kDecodeCounterBytes = size_t(1) << 22;   // 2^20 counters
 
 // Decode LDS bytes per workgroup: seqlens_k, block prefix, the table entries
 // of the workgroup's range, then one V^T slab per wave.

@@ -28,6 +28,7 @@
 //    table entries past a sequence's last block are never used.
 //  * Causal (bottom-right, with cached prefix c = Lk - Lq): tiles wholly above
 //    a wave's rows are skipped; only tiles crossing the diagonal are masked.
+#include <atomic>
 #include <type_traits>
 
 #include "kvs_device.hpp"
@@ -60,7 +61,9 @@ struct PCfg {
   __host__ __device__ static constexpr int kswz(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
   __host__ __device__ static constexpr int vswz(int key) { return D == 128 ? ((key & 3) << 1) : (key & 2); }
 };
-static_assert(PCfg<128, true>::STAGE == 32768 && PCfg<64, true>::STAGE == 16384, "stage layout");
+static_assert(PCfg<128, true>::STAGE == 32768 && PCfg<64, true>::STAGE == 16384 &&
+                  PCfg<128, false>::STAGE == 2 * 32 * (128 * 4 + 16),
+              "the host's prefill_stage_bytes must match the stage layout");
 static_assert(PCfg<128, true>::KIT * 4 * 64 == PCfg<128, true>::KCH && PCfg<64, true>::KIT * 4 * 64 == PCfg<64, true>::KCH,
               "each wave copies KIT whole 1 KiB blocks of a tile");
 
@@ -549,15 +552,18 @@ template <int D, bool BF16>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const size_t lds = prefill_lds_bytes(D, BF16, p.B, p.meta_lds);
   // dynamic LDS above the default limit must be requested; grow it as needed
-  static size_t lds_granted = 0;
-  if (lds > lds_granted) {
+  // (per instantiation; atomic so that concurrent first calls are safe)
+  static std::atomic<size_t> lds_granted{0};
+  if (lds > lds_granted.load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
       return e;
     }
-    lds_granted = lds;
+    size_t cur = lds_granted.load(std::memory_order_relaxed);
+    while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
+    }
   }
   hipLaunchKernelGGL((prefill_kernel<D, BF16>), dim3(p.pgrid), dim3(256), lds, s, p);
   return hipGetLastError();

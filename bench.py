@@ -3,8 +3,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-One step is one pass of the whole path over one batch: kv_store_paged of the
-batch's new K/V rows, then attn_varlen_paged.  The headline workload is the
+One step is one pass of the whole path over one batch: the batch's new K/V
+rows stored into the paged cache, then attention over it.  For the decode
+batch that is one attn_decode_append_paged call (store and attention in one
+launch; the two-call form, kv_store_paged then attn_varlen_paged, is timed
+beside it); for prefill it is the two calls.  The headline workload is the
 paged decode batch (64 sequences x 1 query row, contexts uniform in
 [128, 2048], 32 query / 8 KV heads, head dim 64, bf16, 16-token pages,
 shuffled blocks); its metric is K+V bytes read per second.  The causal prefill
@@ -12,7 +15,9 @@ batch (16 x 512 tokens, 32/8 heads, head dim 128, bf16) is measured the same
 way and reported under "prefill" in attention TFLOP/s.
 
 Timing follows the device-event method of Transformer 추론 커널 (3/10), §26:
-warm-up launches, then K back-to-back steps between two events on the stream.
+warm-up launches, then K back-to-back steps between two events on the stream;
+the steps are replayed from captured HIP graphs, so the host's time to issue
+each call does not enter the figure (--eager times plain launches instead).
 Each step uses the next of R replicas (separate device copies of the same
 batch) so that the 256 MB Infinity Cache cannot hold the working set.
 Prints one JSON line on stdout; progress goes to stderr.
@@ -49,7 +54,7 @@ def _src_sha(name: str) -> str:
 
 # kernel symbol (as rocprofv3 names it) and source file of each timed workload
 COUNTED = {
-    "paged_decode_bf16": ("kvs::decode_kernel<64, true>", "decode.hip"),
+    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true>", "decode.hip"),
     "causal_prefill_bf16": ("kvs::prefill_kernel<128, true>", "prefill.hip"),
 }
 
@@ -157,32 +162,88 @@ class Workload:
         self.kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q,
                                    db.seqlens_k, db.scale, db.causal, out=out, lse=lse, workspace=self.ws[r])
 
+    def append_attend(self, i):
+        r = i % len(self.reps)
+        db, kn, vn, _, out, lse = self.reps[r]
+        self.kvs.attn_decode_append_paged(db.q, kn, vn, db.k_cache, db.v_cache, db.block_table, db.seqlens_k,
+                                          db.scale, out=out, lse=lse, workspace=self.ws[r])
 
-def time_steps(w: Workload, steps: int, warmup: int):
-    """K timed steps between two events; per-phase events inside the region
-    give the attention call's own average duration on the same stream."""
+
+def _graph_len(steps: int, cap: int = 100) -> int:
+    """Steps per captured graph: the largest divisor of ``steps`` up to ``cap``,
+    so that whole replays time exactly ``steps`` steps."""
+    return max(d for d in range(1, min(steps, cap) + 1) if steps % d == 0)
+
+
+def time_steps(w: Workload, steps: int, warmup: int, fused: bool = False, eager: bool = False):
+    """Time exactly ``steps`` steps on one stream.
+
+    The steps are captured into a HIP graph (G steps per graph, G dividing
+    ``steps``) and the graph is replayed steps / G times between two events, so
+    the figure is the device's time per step, not the host's time to issue it;
+    a serving loop issues decode steps the same way ("장부가 커널 인자로 바뀌는
+    지점과 CUDA graph").  A second graph holding only the attention launches of
+    the same steps gives that launch's average duration.  With ``fused`` a step
+    is the one attn_decode_append_paged launch, and the two figures coincide.
+
+    With ``eager`` the steps are plain launches instead, with events around
+    each attention call (host issue time included where it exceeds the
+    device's).
+
+    Returns (ms per step, ms per attention launch, wall seconds)."""
     import torch
 
+    store = (lambda i: None) if fused else w.store
+    attend = w.append_attend if fused else w.attend
     for i in range(warmup):
-        w.store(i)
-        w.attend(i)
+        store(i)
+        attend(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(steps):
-        w.store(i)
-        ev[i][0].record()
-        w.attend(i)
-        ev[i][1].record()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / steps
-    attn = [a.elapsed_time(b) for a, b in ev]
-    attn_ms = sum(attn) / steps
+    if eager:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            store(i)
+            ev[i][0].record()
+            attend(i)
+            ev[i][1].record()
+        end.record()
+        torch.cuda.synchronize()
+        return (start.elapsed_time(end) / steps, sum(a.elapsed_time(b) for a, b in ev) / steps,
+                time.perf_counter() - t0)
+    G = _graph_len(steps)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(G):
+                fn(i)
+        return g
+
+    def run(g):
+        for _ in range(2):                      # replay warm-up
+            g.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for _ in range(steps // G):
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps, time.perf_counter() - t0
+
+    g_step = capture(lambda i: (store(i), attend(i)))
+    ms_step, wall = run(g_step)
+    if fused:
+        attn_ms = ms_step
+    else:
+        g_attn = capture(attend)
+        attn_ms, _ = run(g_attn)
+        del g_attn
+    del g_step
     return ms_step, attn_ms, wall
 
 
@@ -220,6 +281,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time plain launches instead of graph replays")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--counter-command", default="", help="command line recorded with --summarize-counters")
@@ -243,12 +305,15 @@ def main():
     dec = paged_decode_bf16()
     log(f"decode batch: B={dec.B} sum(Lk)={int(dec.k_lens.sum())} K+V={kv_bytes(dec)/1e6:.1f} MB")
     w = Workload(dec, args.replicas)
-    ms, attn_ms, wall = time_steps(w, args.steps, args.warmup)
-    dispatch = kvs.last_dispatch()
     kvb = kv_bytes(dec)
+    sms, sattn_ms, _ = time_steps(w, args.steps, args.warmup, eager=args.eager)
+    sdispatch = kvs.last_dispatch()
+    log(f"decode, two calls: {sms*1e3:.2f} us/step, attention {sattn_ms*1e3:.2f} us ({sdispatch})")
+    ms, attn_ms, wall = time_steps(w, args.steps, args.warmup, fused=True, eager=args.eager)
+    dispatch = kvs.last_dispatch()
     value = kvb / (ms * 1e-3) / 1e9
     achieved = kvb / (attn_ms * 1e-3) / 1e9
-    log(f"decode: {ms*1e3:.2f} us/step, attention {attn_ms*1e3:.2f} us -> {achieved:.0f} GB/s ({dispatch})")
+    log(f"decode, fused: {ms*1e3:.2f} us/step, launch {attn_ms*1e3:.2f} us -> {achieved:.0f} GB/s ({dispatch})")
     traffic = _traffic("decode.hip", "paged_decode_bf16")
     line = {
         "metric": "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
@@ -268,12 +333,19 @@ def main():
             "batch_sequences": dec.B, "query_rows": dec.T, "context_min": int(dec.k_lens.min()),
             "context_max": int(dec.k_lens.max()), "context_sum": int(dec.k_lens.sum()),
             "q_heads": dec.Hq, "kv_heads": dec.Hkv, "head_dim": dec.D, "page_size": 16,
-            "replicas": args.replicas, "step": "kv_store_paged(new rows) + attn_varlen_paged",
+            "replicas": args.replicas,
+            "step": "attn_decode_append_paged (new K/V rows stored and attended in one launch)",
+            "timing": "eager launches" if args.eager else f"HIP graph replays ({_graph_len(args.steps)} steps per graph)",
             "dispatch": dispatch,
+        },
+        "two_calls": {
+            "step": "kv_store_paged(new rows) + attn_varlen_paged",
+            "ms_per_step": round(sms, 6), "value": round(kvb / (sms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "attention_us": round(sattn_ms * 1e3, 3), "dispatch": sdispatch,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": COUNTED["paged_decode_bf16"][0] + " (the one launch of each attn_varlen_paged call)",
+            "kernel": COUNTED["paged_decode_bf16"][0] + " (the one launch of each attn_decode_append_paged call)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -291,7 +363,7 @@ def main():
         pre = causal_prefill_bf16()
         wp = Workload(pre, args.replicas)
         psteps = max(1, args.steps // 4)
-        pms, pattn, _ = time_steps(wp, psteps, max(1, args.warmup // 4))
+        pms, pattn, _ = time_steps(wp, psteps, max(1, args.warmup // 4), eager=args.eager)
         pdisp = kvs.last_dispatch()
         fl = attention_flops(pre)
         tf = fl / (pattn * 1e-3) / 1e12

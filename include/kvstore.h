@@ -158,10 +158,13 @@ size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k
  * Same computation and argument meaning.  `workspace` is a device buffer of at
  * least attn_varlen_paged_workspace_size(q, k_cache, block_table, hints) bytes,
  * 256-byte aligned (may be NULL when that size is 0).  It must be zero-filled
- * before its first use with this library; every call leaves it in a state
- * valid for the next call (its counters back at zero), so zero it once and
- * reuse it.  Two calls that overlap in time must not share it.  Allocates
- * nothing.  `hints` may be NULL.
+ * before its first use with this library.  Its first 4 MiB hold the split
+ * decode's per-(sequence, KV head) counters at a place that does not depend on
+ * the shapes, and every call leaves them at zero, so one workspace, zeroed
+ * once, serves any sequence of calls of any shapes (each needing no more than
+ * its size).  Two calls that overlap in time must not share it.  Allocates
+ * nothing.  `hints` may be NULL.  A split decode (more than one range) needs
+ * B * Hkv <= 2^20, else KVS_ERR_UNSUPPORTED.
  */
 kvs_status attn_varlen_paged_ex(const kvs_tensor* q,
                                 const kvs_tensor* k_cache, const kvs_tensor* v_cache,
@@ -173,6 +176,47 @@ kvs_status attn_varlen_paged_ex(const kvs_tensor* q,
                                 const kvs_hints* hints,
                                 void* workspace, size_t workspace_bytes,
                                 kvs_stream_t stream);
+
+/*
+ * attn_decode_append_paged -- one decode step in one launch: each sequence's
+ * new key/value row is appended to the cache and the sequence's query row
+ * attends over all of its keys, the new one included.
+ *
+ * The result, in `out`, `lse` and the caches, is that of
+ *   kv_store_paged(k_new, v_new, slots, k_cache, v_cache)   with
+ *     slots[b] = block_table[b][(Lk_b - 1) / 16] * 16 + (Lk_b - 1) % 16,
+ *   then attn_varlen_paged_ex(q, ..., cu_seqlens_q = {0, 1, .., B}, seqlens_k,
+ *     scale, causal = 1, out, lse, hints, workspace, ...)
+ * -- store before attention ("Transformer 추론 커널 (3/10)", §2), with the new
+ * token's K/V as key Lk_b - 1 (decode adds one token per sequence to the paged
+ * cache: "tiny-vLLM ...", entry 5).  The
+ * launch reads the new row from k_new / v_new rather than from the cache, so
+ * the store and the attention need no ordering between them.
+ *
+ *   q            [B, Hq, D]  f32 or bf16, one query row per sequence
+ *   k_new/v_new  [B, Hkv, D] same dtype; row b is sequence b's new token
+ *   k_cache/v_cache [NB, 16, Hkv, D]; the slot of key Lk_b - 1 is written
+ *   block_table  i32 [B, MB];  seqlens_k  i32 [B] (Lk_b counts the new token)
+ *   out, lse, hints, workspace: as for attn_varlen_paged_ex (the workspace
+ *     size is attn_varlen_paged_workspace_size(q, k_cache, block_table, hints))
+ * Preconditions on device values: 1 <= Lk_b <= 16 * MB and every table entry
+ * that is read lies in [0, NB); the slots of different sequences differ, and
+ * no sequence reads, as one of its keys, a slot that another sequence's new
+ * row is written to (as with the two separate calls, whose order would decide
+ * what such a read sees).
+ * Same support limits and errors as the decode path of attn_varlen_paged.
+ * Allocates nothing.
+ */
+kvs_status attn_decode_append_paged(const kvs_tensor* q,
+                                    const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                    kvs_tensor* k_cache, kvs_tensor* v_cache,
+                                    const kvs_tensor* block_table,
+                                    const kvs_tensor* seqlens_k,
+                                    float scale,
+                                    kvs_tensor* out, kvs_tensor* lse,
+                                    const kvs_hints* hints,
+                                    void* workspace, size_t workspace_bytes,
+                                    kvs_stream_t stream);
 
 /* Text of the calling thread's last non-OK status ("" if none).  The pointer is
  * valid until that thread's next library call. */

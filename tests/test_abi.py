@@ -97,9 +97,9 @@ def test_workspace_sizing_and_check(lib):
     h = L.KvsHints()
     h.num_splits = 4
     need = lib.attn_varlen_paged_workspace_size(ref(a["q"]), ref(a["k"]), ref(a["table"]), ctypes.byref(h))
-    # (4 ranges + 4 sequences) slots x 8 heads x 64 floats, their lse, and one
-    # counter per (sequence, KV head), each part 256-byte aligned
-    assert need == 8 * 8 * 64 * 4 + 256 + 256
+    # the fixed 4 MiB counter area, then (4 ranges + 4 sequences) slots x 8
+    # heads x 64 floats and their lse, each part 256-byte aligned
+    assert need == (1 << 22) + 8 * 8 * 64 * 4 + 256
     st = _call_ex(lib, a, hints=h, ws=FAKE, ws_bytes=need - 1)
     assert st == L.KVS_ERR_WORKSPACE
     h.num_splits = 1
@@ -112,11 +112,69 @@ def test_workspace_sizing_and_check(lib):
     assert lib.attn_varlen_paged_workspace_size(ref(bad), ref(a["k"]), ref(a["table"]), None) == ctypes.c_size_t(-1).value
 
 
+def test_split_counter_limit(lib):
+    # split decode keeps one counter per (sequence, KV head) in a fixed 4 MiB area
+    a = _attn_args(T_=8192, Hq=256, Hkv=256, B=8192, MB=2, NB=8)
+    a["out"] = T([8192, 256, 64])
+    a["lse"] = None
+    h = L.KvsHints()
+    h.num_splits = 4
+    assert _call_ex(lib, a, hints=h) == L.KVS_ERR_UNSUPPORTED
+    assert "B * Hkv" in lib.kvs_last_error().decode()
+
+
 def test_negative_hints_rejected(lib):
     a = _attn_args()
     h = L.KvsHints()
     h.num_splits = -1
     assert _call_ex(lib, a, hints=h) == L.KVS_ERR_INVALID
+
+
+def _append_args(B=4, Hq=8, Hkv=2, D=64, NB=8, MB=2, dtype=L.KVS_BF16):
+    return dict(q=T([B, Hq, D], dtype), kn=T([B, Hkv, D], dtype), vn=T([B, Hkv, D], dtype),
+                k=T([NB, 16, Hkv, D], dtype), v=T([NB, 16, Hkv, D], dtype), table=T([B, MB], L.KVS_I32),
+                lk=T([B], L.KVS_I32), out=T([B, Hq, D], dtype), lse=T([B, Hq], L.KVS_F32))
+
+
+def _call_append(lib, a, hints=None, ws=None, ws_bytes=0, scale=0.125):
+    return lib.attn_decode_append_paged(ref(a["q"]), ref(a["kn"]), ref(a["vn"]), ref(a["k"]), ref(a["v"]),
+                                        ref(a["table"]), ref(a["lk"]), ctypes.c_float(scale), ref(a["out"]),
+                                        ref(a.get("lse")), ctypes.byref(hints) if hints else None, ws, ws_bytes,
+                                        None)
+
+
+@pytest.mark.parametrize("mutate,expect,msg", [
+    (lambda a: a.update(q=T([5, 8, 64]), out=T([5, 8, 64]), lse=T([5, 8], L.KVS_F32)), L.KVS_ERR_INVALID,
+     "one query row per sequence"),
+    (lambda a: a.update(kn=T([4, 2, 32]), vn=T([4, 2, 32])), L.KVS_ERR_INVALID, "k_new must be"),
+    (lambda a: a.update(kn=T([4, 4, 64]), vn=T([4, 4, 64])), L.KVS_ERR_INVALID, "k_new must be"),
+    (lambda a: a.update(kn=T([3, 2, 64]), vn=T([3, 2, 64])), L.KVS_ERR_INVALID, "k_new must be"),
+    (lambda a: a.update(vn=T([4, 2, 32])), L.KVS_ERR_INVALID, "v_new shape"),
+    (lambda a: a.update(kn=T([4, 2, 64], L.KVS_F32), vn=T([4, 2, 64], L.KVS_F32)), L.KVS_ERR_INVALID, "dtype"),
+    (lambda a: a.update(kn=None), L.KVS_ERR_INVALID, "k_new"),
+    (lambda a: a.update(vn=T([4, 2, 64], data=0)), L.KVS_ERR_INVALID, "NULL"),
+    (lambda a: a.update(v=T([9, 16, 2, 64])), L.KVS_ERR_INVALID, "v_cache shape"),
+    (lambda a: a.update(lk=T([3], L.KVS_I32)), L.KVS_ERR_INVALID, "seqlens_k"),
+    (lambda a: a.update(lse=T([4, 7], L.KVS_F32)), L.KVS_ERR_INVALID, "lse"),
+    (lambda a: a.update(q=T([4, 34, 64]), out=T([4, 34, 64]), lse=None), L.KVS_ERR_UNSUPPORTED, "16 query heads"),
+])
+def test_append_validation(lib, mutate, expect, msg):
+    a = _append_args()
+    mutate(a)
+    assert _call_append(lib, a) == expect
+    assert msg in lib.kvs_last_error().decode()
+
+
+def test_append_workspace_check(lib):
+    # the fused call takes the same workspace as the decode path of attn_varlen_paged_ex
+    a = _append_args(B=4, MB=128)
+    h = L.KvsHints()
+    h.num_splits = 4
+    need = lib.attn_varlen_paged_workspace_size(ref(a["q"]), ref(a["k"]), ref(a["table"]), ctypes.byref(h))
+    assert need > 0
+    assert _call_append(lib, a, hints=h, ws=FAKE, ws_bytes=need - 1) == L.KVS_ERR_WORKSPACE
+    h.num_splits = -2
+    assert _call_append(lib, a, hints=h) == L.KVS_ERR_INVALID
 
 
 @pytest.mark.parametrize("mutate,expect,msg", [

@@ -210,6 +210,55 @@ def test_decode_many_sequences(B):
     _check(b, out, lse)
 
 
+@pytest.mark.parametrize("splits", [0, 64, 300])
+def test_decode_split_results_reproducible(splits):
+    """Split sequences are merged by whichever workgroup finishes last; the
+    merge groups a sequence's pieces the same way whoever merges it, so
+    repeated calls give the same bits."""
+    from tests.gpu_side import to_device
+    rng = np.random.default_rng(571)
+    k = [int(x) for x in rng.integers(1, 3000, size=40)]
+    b = _mk(571 + splits, [1] * len(k), k, Hq=8, Hkv=2, D=64, dtype="bf16", causal=True)
+    db = to_device(b)
+    import attention_kv_store_amd as kvs
+    first = None
+    for _ in range(6):
+        out, lse = kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q,
+                                         db.seqlens_k, db.scale, True, num_splits=splits)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (out.clone(), lse.clone())
+            _check(b, out, lse)
+        else:
+            assert torch.equal(out, first[0]) and torch.equal(lse, first[1])
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace, zeroed once, serves decode calls of different batch sizes,
+    head counts and split counts in any order (the split counters sit at a
+    fixed place and every call leaves them at zero)."""
+    import attention_kv_store_amd as kvs
+    from tests.gpu_side import run_append, to_device, to_device_before_append
+    rng = np.random.default_rng(591)
+    cases = []
+    for i, (B, Hq, Hkv) in enumerate([(10, 8, 2), (64, 32, 8), (3, 4, 1), (200, 8, 2)]):
+        k = [int(x) for x in rng.integers(1, 1500, size=B)]
+        cases.append(_mk(591 + i, [1] * B, k, Hq=Hq, Hkv=Hkv, D=64, dtype="bf16", causal=True, name=f"ws-{i}"))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    order = [(0, 7), (1, 64), (0, 300), (2, 0), (3, 32), (1, 5), (0, 7), (3, 512), (2, 64), (1, 0)]
+    for n, (ci, splits) in enumerate(order):
+        b = cases[ci]
+        if n % 3 == 2:
+            db, kn, vn = to_device_before_append(b)
+            out, lse = run_append(db, kn, vn, num_splits=splits, workspace=ws)
+        else:
+            db = to_device(b)
+            out, lse = kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q,
+                                             db.seqlens_k, db.scale, True, num_splits=splits, workspace=ws)
+            torch.cuda.synchronize()
+        _check(b, out, lse)
+
+
 def test_decode_plain_entry_point():
     """The plain call (library-owned scratch) gives the same bits as _ex."""
     import attention_kv_store_amd as kvs
@@ -226,6 +275,154 @@ def test_decode_plain_entry_point():
     torch.cuda.synchronize()
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
     kvs.release_workspace()
+
+
+# ------------------------------------------------ fused decode append ----
+def _pool_matches_oracle(batch, k_cache, v_cache):
+    """Every slot the batch owns holds the oracle store's bits; the rest stay NaN."""
+    from tests.gpu_side import cache_bits
+    from tests.oracle_side import oracle_pool
+    kc, vc = oracle_pool(batch, dtype=np.float32)
+    for dev, ref in ((k_cache, kc), (v_cache, vc)):
+        got = cache_bits(dev)
+        ref_bits = (ref.view(np.uint32) >> 16).astype(np.uint16) if batch.dtype == "bf16" else ref.view(np.uint32)
+        owned = ~np.isnan(ref)
+        assert np.array_equal(got[owned], ref_bits[owned])
+        assert np.isnan(dev.float().cpu().numpy()[~owned]).all()
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("splits", [0, 1, 7, 64])
+def test_decode_append_matches_store_then_attention(dtype, D, splits):
+    """The fused call equals kv_store_paged then attn_varlen_paged: out and lse
+    against the oracle (whose pool holds the new rows), the written cache bit for
+    bit, and the same bits as the two-call path."""
+    from tests.gpu_side import run_append, to_device, to_device_before_append
+    k = [1, 15, 16, 17, 64, 65, 300, 1000, 2048, 129]
+    b = _mk(900 + D + splits, [1] * len(k), k, Hq=8, Hkv=2, D=D, dtype=dtype, causal=True,
+            name=f"append-{dtype}-{D}-s{splits}")
+    db, kn, vn = to_device_before_append(b)
+    out, lse = run_append(db, kn, vn, num_splits=splits)
+    _check(b, out, lse)
+    _pool_matches_oracle(b, db.k_cache, db.v_cache)
+    out2, lse2 = _run(b, num_splits=splits)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    ref = to_device(b)
+    assert torch.equal(db.k_cache.view(torch.uint8), ref.k_cache.view(torch.uint8))
+    assert torch.equal(db.v_cache.view(torch.uint8), ref.v_cache.view(torch.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_decode_append_steps(dtype):
+    """Several decode steps in a row, each appending one token per sequence and
+    crossing block boundaries; after every step out/lse match the oracle, and
+    after the last the pool equals the oracle store of all tokens."""
+    import dataclasses
+
+    from tests.gpu_side import run_append, to_device_before_append
+    from tests.oracle_side import oracle_attention, oracle_pool
+    base = np.array([0, 14, 15, 16, 31, 47, 200])
+    S = 5
+    final = _mk(950, [1] * len(base), base + S, Hq=8, Hkv=2, D=64, dtype=dtype, causal=True,
+                name=f"append-steps-{dtype}")
+    # the device pool starts with tokens 0 .. base-1 of every sequence
+    db, _, _ = to_device_before_append(_prefix_batch(final, base + 1))
+    pool = oracle_pool(final)
+    rng = np.random.default_rng(951)
+    dt = db.q.dtype
+    for s in range(S):
+        lens = (base + s + 1).astype(np.int32)
+        q = rng.standard_normal(final.q.shape, dtype=np.float32)
+        if dtype == "bf16":
+            q = torch.from_numpy(q).to(torch.bfloat16).float().numpy()
+        rows = final.cu_seqlens_k[:-1] + lens - 1
+        kn = torch.from_numpy(final.k_tokens[rows]).to(dt).cuda()
+        vn = torch.from_numpy(final.v_tokens[rows]).to(dt).cuda()
+        db.q = torch.from_numpy(q).to(dt).cuda()
+        db.seqlens_k = torch.from_numpy(lens).cuda()
+        out, lse = run_append(db, kn, vn)
+        step = dataclasses.replace(final, q=q, k_lens=lens, name=f"append-steps-{dtype}-{s}")
+        ro, rl = oracle_attention(step, pool=pool)
+        go, gl = out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+        assert np.isfinite(go).all() and np.isfinite(gl).all()
+        eo, el = np.max(np.abs(go - ro)), np.max(np.abs(gl - rl))
+        print(f"[{step.name}] max|dout|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+        assert eo <= TOL[dtype] and el <= TOL[dtype]
+    _pool_matches_oracle(final, db.k_cache, db.v_cache)
+
+
+def _prefix_batch(batch, lens):
+    """The same batch cut to ``lens`` keys per sequence (one new row each),
+    drawn from the same token rows and slots."""
+    import dataclasses
+    lens = np.asarray(lens, np.int64)
+    keep = np.concatenate([np.arange(int(batch.cu_seqlens_k[b]), int(batch.cu_seqlens_k[b]) + int(lens[b]))
+                           for b in range(batch.B)])
+    cu_k = np.zeros(batch.B + 1, np.int64)
+    cu_k[1:] = np.cumsum(lens)
+    return dataclasses.replace(batch, k_lens=lens.astype(np.int32), cu_seqlens_k=cu_k.astype(np.int32),
+                               k_tokens=batch.k_tokens[keep], v_tokens=batch.v_tokens[keep],
+                               slots=batch.slots[keep])
+
+
+def test_decode_append_named_workload():
+    """The 64-sequence bf16 decode workload through the fused call."""
+    from tests.gpu_side import run_append, to_device_before_append
+    from workloads import NAMED
+    b = NAMED["paged_decode_bf16"]()
+    db, kn, vn = to_device_before_append(b)
+    out, lse = run_append(db, kn, vn)
+    _check(b, out, lse)
+    _pool_matches_oracle(b, db.k_cache, db.v_cache)
+
+
+# ------------------------------------------------------- graph capture ----
+@pytest.mark.parametrize("mode", ["fused_decode", "decode", "prefill"])
+def test_graph_replay_matches_eager(mode):
+    """The calls captured into a HIP graph: every replay, with eager work and
+    synchronisations between replays, gives the eager call's bits."""
+    import attention_kv_store_amd as kvs
+    from tests.gpu_side import to_device, to_device_before_append
+    if mode == "prefill":
+        b = _mk(981, [40, 17, 64], [40, 30, 100], Hq=8, Hkv=2, D=128, dtype="bf16", causal=True)
+    else:
+        k = [int(x) for x in np.random.default_rng(982).integers(1, 2000, size=24)]
+        b = _mk(982, [1] * len(k), k, Hq=8, Hkv=2, D=64, dtype="bf16", causal=True)
+    if mode == "fused_decode":
+        db, kn, vn = to_device_before_append(b)
+    else:
+        db = to_device(b)
+    need = kvs.workspace_size(db.q, db.k_cache, db.block_table, num_splits=32)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(db.q)
+    lse = torch.empty(db.q.shape[0], db.q.shape[1], dtype=torch.float32, device="cuda")
+
+    def call(o, l):
+        if mode == "fused_decode":
+            kvs.attn_decode_append_paged(db.q, kn, vn, db.k_cache, db.v_cache, db.block_table, db.seqlens_k,
+                                         db.scale, out=o, lse=l, num_splits=32, workspace=ws)
+        else:
+            kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q, db.seqlens_k,
+                                  db.scale, True, out=o, lse=l, num_splits=32, workspace=ws)
+
+    call(out, lse)
+    torch.cuda.synchronize()
+    _check(b, out, lse)
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, lse)
+    o2, l2 = torch.empty_like(out), torch.empty_like(lse)
+    for _ in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+        call(o2, l2)                  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o2, ref_o) and torch.equal(l2, ref_l)
 
 
 # ------------------------------------------------------ one-hot probes ----
