@@ -208,7 +208,12 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   // partial outputs are addressed with 32-bit byte offsets
   if ((double)(nwg + B) * Hq * D * sizeof(float) >= 2147483648.0)
     return fail(KVS_ERR_UNSUPPORTED, "decode partial buffer would exceed 2 GiB (num_splits %lld)", (long long)nwg);
-  if (kvs::decode_lds_bytes((int)B, hpw, kvs::decode_slab_bytes((int)D)) > kLdsBudget)
+  const int slab = kvs::decode_slab_bytes((int)D);
+  // (the whole table is copied in 16-byte pieces: it must be 16-byte aligned)
+  p.dsmall = B <= kvs::kDecodeSmallB && B * MB <= kvs::kDecodeSmallTbl &&
+             reinterpret_cast<uintptr_t>(table->data) % 16 == 0 &&
+             kvs::decode_lds_bytes((int)B, kvs::decode_tbl_ints((int)B, (int)MB, true), hpw, slab) <= kLdsBudget;
+  if (kvs::decode_lds_bytes((int)B, kvs::decode_tbl_ints((int)B, (int)MB, p.dsmall), hpw, slab) > kLdsBudget)
     return fail(KVS_ERR_UNSUPPORTED, "decode batch too large for one workgroup's LDS (B=%lld)", (long long)B);
   if (nwg > 1) {
     // The counters sit at the same place for every shape: the first
@@ -291,8 +296,8 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
     }
     const hipError_t e = kvs::launch_decode(p, plan.dt, plan.D, stream);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-    set_dispatch("decode_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
-                 plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg);
+    set_dispatch("decode_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
+                 plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window");
     return KVS_OK;
   }
   int cus = 0;
@@ -399,8 +404,9 @@ kvs_status attn_decode_append_paged(const kvs_tensor* q, const kvs_tensor* k_new
   p.v_cache_w = v_cache->data;
   p.append = 1;
   KVS_TRY(run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream)));
-  set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
-               plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg);
+  set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s",
+               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg,
+               p.dsmall ? "whole" : "window");
   return KVS_OK;
 }
 

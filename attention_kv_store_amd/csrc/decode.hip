@@ -199,24 +199,37 @@ struct DecodeWave {
   static constexpr int RPI = 64 / CH;               // rows per wave instruction
   struct NewRows {
     u32x4 k, v;
+    int b;    // sequence of this lane's row (>= B: none)
     int kl;   // key index Lk - 1 (-1: no row for this lane)
     int pj;   // physical block holding it
   };
-  __device__ __forceinline__ NewRows append_load(int b0, int stride, const int* slens) const {
+  // the rows of sequences b0 + stride * (lane / CH) (needs no lengths)
+  __device__ __forceinline__ NewRows append_fetch(int b0, int stride) const {
     NewRows r;
+    r.b = b0 + (lane / CH) * stride;
     r.kl = -1;
     r.pj = -1;
-    const int b = b0 + (lane / CH) * stride;
-    if (b < p.B) {
-      const int Lk = slens[b];
+    if (r.b < p.B) {
+      r.k = ld16(new_row(p.k_new, r.b) + (lane % CH) * EPP);
+      r.v = ld16(new_row(p.v_new, r.b) + (lane % CH) * EPP);
+    }
+    return r;
+  }
+  // their slots: the length from LDS, the table entry from the staged whole
+  // table (tbl_all) or else from memory
+  __device__ __forceinline__ void append_locate(NewRows& r, const int* slens, const int* tbl_all) const {
+    if (r.b < p.B) {
+      const int Lk = slens[r.b];
       if (Lk >= 1 && Lk <= p.MB * kPage) {
-        const int c = lane % CH;
         r.kl = Lk - 1;
-        r.pj = p.table[(int64_t)b * p.MB + (r.kl >> 4)];
-        r.k = ld16(new_row(p.k_new, b) + c * EPP);
-        r.v = ld16(new_row(p.v_new, b) + c * EPP);
+        const int64_t at = (int64_t)r.b * p.MB + (r.kl >> 4);
+        r.pj = tbl_all ? tbl_all[at] : p.table[at];
       }
     }
+  }
+  __device__ __forceinline__ NewRows append_load(int b0, int stride, const int* slens) const {
+    NewRows r = append_fetch(b0, stride);
+    append_locate(r, slens, nullptr);
     return r;
   }
   __device__ __forceinline__ void append_store(const NewRows& r) const {
@@ -567,51 +580,75 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   const int B = p.B;
   int* slens = reinterpret_cast<int*>(smem);         // [B]      seqlens_k
   int* sstart = slens + ((B + 3) & ~3);              // [B + 1]  exclusive block prefix
-  int* tbl = sstart + ((B + 1 + 3) & ~3);            // [kTblWin] physical blocks of the range
-  char* slabs = reinterpret_cast<char*>(tbl + kTblWin);
+  // small batch: the whole table [B * MB]; else the range's window [kTblWin]
+  const bool small = p.dsmall != 0;
+  int* tbl = sstart + ((B + 1 + 3) & ~3);
+  char* slabs = reinterpret_cast<char*>(tbl + decode_tbl_ints(B, p.MB, small));
   __shared__ int wtot[8];
 
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int w = blockIdx.x, hg = blockIdx.y, nwg = p.nwg;
+  const int g = hg * p.hpw + wave;
+  W wv(p, g, slabs + wave * C::SLAB);
+  typename W::NewRows nr;
 
-  // ---- seqlens_k into LDS ---------------------------------------------------
-  for (int b = tid; b < B; b += nthr) slens[b] = p.lens_k[b];
-  __syncthreads();
-
-  // ---- exclusive prefix of ceil(Lk_b / 16) over the batch, in LDS ---------
-  {
-    const int per = (B + nthr - 1) / nthr;
-    const int b0 = tid * per;
-    int run = 0;
-    for (int i = 0; i < per; ++i) {
-      const int b = b0 + i;
-      if (b < B) run += (slens[b] + 15) >> 4;
-    }
-    const int x = wave_inclusive_sum(run);
-    if (lane == 63) wtot[wave] = x;
-    __syncthreads();
-    int base = 0;
-    for (int i = 0; i < wave; ++i) base += wtot[i];
-    int acc = base + x - run;
-    for (int i = 0; i < per; ++i) {
-      const int b = b0 + i;
-      if (b < B) {
-        sstart[b] = acc;
-        acc += (slens[b] + 15) >> 4;
+  if (small) {
+    // ---- one memory round trip: this workgroup's first new rows (append),
+    // seqlens_k and the whole block table; wave 0 forms the block prefix with
+    // one in-register scan (B <= 64)
+    if constexpr (APPEND) nr = wv.append_fetch(w, nwg);
+    const int nt = B * p.MB;
+    for (int c = tid; c < (nt >> 2); c += nthr) st16(tbl + 4 * c, ld16(p.table + 4 * c));
+    for (int i = (nt & ~3) + tid; i < nt; i += nthr) tbl[i] = p.table[i];
+    if (wave == 0) {
+      const int L = lane < B ? p.lens_k[lane] : 0;
+      const int nb = (L + 15) >> 4;
+      const int x = wave_inclusive_sum(nb);
+      if (lane < B) {
+        slens[lane] = L;
+        sstart[lane] = x - nb;
       }
+      if (lane == B - 1) sstart[B] = x;
     }
-    if (tid == nthr - 1) sstart[B] = acc;
     __syncthreads();
+    if constexpr (APPEND) wv.append_locate(nr, slens, tbl);
+  } else {
+    // ---- seqlens_k into LDS ---------------------------------------------------
+    for (int b = tid; b < B; b += nthr) slens[b] = p.lens_k[b];
+    __syncthreads();
+
+    // ---- exclusive prefix of ceil(Lk_b / 16) over the batch, in LDS ---------
+    {
+      const int per = (B + nthr - 1) / nthr;
+      const int b0 = tid * per;
+      int run = 0;
+      for (int i = 0; i < per; ++i) {
+        const int b = b0 + i;
+        if (b < B) run += (slens[b] + 15) >> 4;
+      }
+      const int x = wave_inclusive_sum(run);
+      if (lane == 63) wtot[wave] = x;
+      __syncthreads();
+      int base = 0;
+      for (int i = 0; i < wave; ++i) base += wtot[i];
+      int acc = base + x - run;
+      for (int i = 0; i < per; ++i) {
+        const int b = b0 + i;
+        if (b < B) {
+          sstart[b] = acc;
+          acc += (slens[b] + 15) >> 4;
+        }
+      }
+      if (tid == nthr - 1) sstart[B] = acc;
+      __syncthreads();
+    }
+    // append: this workgroup's first new rows are loaded now, with the table
+    // window below, and stored once it has arrived
+    if constexpr (APPEND) nr = wv.append_load(w, nwg, slens);
   }
   const int total = sstart[B];
   const int r0 = (int)(((int64_t)w * total) / nwg), r1 = (int)(((int64_t)(w + 1) * total) / nwg);
-  const int g = hg * p.hpw + wave;
-  W wv(p, g, slabs + wave * C::SLAB);
-  // append: this workgroup's first new rows are loaded now, with the table
-  // window below, and stored once it has arrived
-  typename W::NewRows nr;
-  if constexpr (APPEND) nr = wv.append_load(w, nwg, slens);
   if (r0 >= r1) {  // empty range (whole workgroup)
     if constexpr (APPEND) wv.append_rows(nr, w, nwg, slens);
     return;
@@ -627,13 +664,15 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   };
 
   // The range's table entries, once, in LDS (the planner keeps a range within
-  // kTblWin blocks).
-  for (int i = tid; i < r1 - r0; i += nthr) {
-    const int gb = r0 + i;
-    const int b = seq_of(gb);
-    tbl[i] = p.table[(int64_t)b * p.MB + (gb - sstart[b])];
+  // kTblWin blocks); a small batch has the whole table there already.
+  if (!small) {
+    for (int i = tid; i < r1 - r0; i += nthr) {
+      const int gb = r0 + i;
+      const int b = seq_of(gb);
+      tbl[i] = p.table[(int64_t)b * p.MB + (gb - sstart[b])];
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if constexpr (APPEND) wv.append_rows(nr, w, nwg, slens);
 
   // Segments of the range, in processing order: the piece of the last sequence
@@ -686,7 +725,8 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   auto phys_of = [&](const Step& st, int* ph) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < C::NBS; ++j)
-      ph[j] = __builtin_amdgcn_readfirstlane(j < st.nblk ? tbl[st.gblk - r0 + j] : 0);
+      ph[j] = __builtin_amdgcn_readfirstlane(
+          j < st.nblk ? tbl[small ? st.b * p.MB + st.lblk + j : st.gblk - r0 + j] : 0);
   };
   auto finish_piece = [&](const Step& st) __attribute__((always_inline)) {
     const int s0 = sstart[st.b], s1 = sstart[st.b + 1];
@@ -784,7 +824,7 @@ template <int D, bool BF16, bool APPEND>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   using C = DCfg<D>;
   static_assert(C::SLAB == D * 40, "decode_slab_bytes must match the slab layout");
-  const size_t lds = decode_lds_bytes(p.B, p.hpw, C::SLAB);
+  const size_t lds = decode_lds_bytes(p.B, decode_tbl_ints(p.B, p.MB, p.dsmall != 0), p.hpw, C::SLAB);
   // dynamic LDS above the default limit must be requested; grow it as needed
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};

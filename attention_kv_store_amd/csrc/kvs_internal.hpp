@@ -56,6 +56,7 @@ struct AttnParams {
   void* v_cache_w;
   int32_t append;
   int32_t NB;             // cache blocks (the append writes only slots inside the pool)
+  int32_t dsmall;         // decode: 1 = small batch, whole block table staged in LDS
 };
 
 // Split decode counts finished blocks per (sequence, KV head) in the first
@@ -65,8 +66,14 @@ constexpr size_t kDecodeCounterBytes = size_t(1) << 22;   // 2^20 counters
 // Decode LDS bytes per workgroup: seqlens_k, block prefix, the table entries
 // of the workgroup's range, then one V^T slab per wave.
 constexpr int kDecodeTblWin = 2048;          // most blocks in one workgroup's range
-inline size_t decode_lds_bytes(int B, int hpw, int slab_bytes) {
-  const size_t ints = (size_t)((B + 3) & ~3) + (size_t)((B + 1 + 3) & ~3) + kDecodeTblWin;
+// Small batches (B <= 64 and at most kDecodeSmallTbl table entries) stage the
+// whole block table instead of a workgroup's window: one memory round trip
+// then sets a workgroup up.
+constexpr int kDecodeSmallB = 64;
+constexpr int kDecodeSmallTbl = 16384;
+__host__ __device__ inline int decode_tbl_ints(int B, int MB, bool small) { return small ? ((B * MB + 3) & ~3) : kDecodeTblWin; }
+inline size_t decode_lds_bytes(int B, int tbl_ints, int hpw, int slab_bytes) {
+  const size_t ints = (size_t)((B + 3) & ~3) + (size_t)((B + 1 + 3) & ~3) + (size_t)tbl_ints;
   return ints * sizeof(int) + (size_t)hpw * slab_bytes;
 }
 inline int decode_slab_bytes(int D) { return D * 40; }

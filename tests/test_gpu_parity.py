@@ -233,6 +233,41 @@ def test_decode_split_results_reproducible(splits):
             assert torch.equal(out, first[0]) and torch.equal(lse, first[1])
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_table_paths_agree(fused):
+    """A small batch stages its whole block table; a table that is not 16-byte
+    aligned, or too large, takes the per-range window instead.  The paths give
+    the same bits, and both match the oracle."""
+    import attention_kv_store_amd as kvs
+    from tests.gpu_side import run_append, to_device, to_device_before_append
+    k = [1, 15, 16, 17, 64, 65, 300, 1000, 2048, 129, 777, 31]
+    b = _mk(611, [1] * len(k), k, Hq=8, Hkv=2, D=64, dtype="bf16", causal=True, name="table-paths")
+    if fused:
+        db, kn, vn = to_device_before_append(b)
+    else:
+        db = to_device(b)
+    res = {}
+    base = db.block_table
+    shifted = torch.empty(base.numel() + 1, dtype=torch.int32, device="cuda")[1:].view(base.shape)
+    shifted.copy_(base)
+    wide = torch.zeros(base.shape[0], 2048, dtype=torch.int32, device="cuda")
+    wide[:, :base.shape[1]] = base
+    for name, tab, want in (("aligned", base, "table=whole"), ("shifted", shifted, "table=window"),
+                            ("wide", wide, "table=window")):
+        if fused:
+            out, lse = kvs.attn_decode_append_paged(db.q, kn, vn, db.k_cache, db.v_cache, tab, db.seqlens_k,
+                                                    db.scale, num_splits=64)
+        else:
+            out, lse = kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, tab, db.cu_seqlens_q, db.seqlens_k,
+                                             db.scale, True, num_splits=64)
+        torch.cuda.synchronize()
+        assert want in kvs.last_dispatch(), kvs.last_dispatch()
+        _check(b, out, lse)
+        res[name] = (out, lse)
+    for name in ("shifted", "wide"):
+        assert torch.equal(res[name][0], res["aligned"][0]) and torch.equal(res[name][1], res["aligned"][1])
+
+
 def test_workspace_reused_across_shapes():
     """One workspace, zeroed once, serves decode calls of different batch sizes,
     head counts and split counts in any order (the split counters sit at a
