@@ -456,118 +456,173 @@ struct DecodeWave {
     if (grp == 0) atomic_st(p.part_lse + prow, lse2);
   }
 
-  // Merge the pieces of sequence b (query row b, blocks [sb0, sb1) on the
-  // flattened axis) for this wave's query heads.  The pieces are the partial
-  // slots w + b of the workgroups w whose ranges meet the sequence's blocks.
-  // Heads go HB at a time and pieces PC at a time counted from the first
-  // piece, so the rounding is the same whichever workgroup ends up merging
-  // the sequence (and whether it merges another one too).  In a round,
-  // lane i loads the lse of (piece i / HB, head j = i % HB) and every lane
-  // loads its d = lane + 64 k of each (piece, head) output, all before any is
-  // used (one memory round trip).  The lanes of head j then hold that head's
+  // ---- merge of split sequences ---------------------------------------------
+  // The pieces of sequence b (query row b, blocks [sb0, sb1) on the flattened
+  // axis) are the partial slots w + b of the workgroups w whose ranges meet
+  // its blocks.  A merging wave works through units -- HB heads by PC pieces,
+  // the pieces counted from the sequence's first -- and loads the next unit
+  // while it combines the current one.  In a unit, lane i loads the lse of
+  // (piece i / HB, head j = i % HB) and every lane loads its d = lane + 64 k of
+  // each (piece, head) output.  The lanes of head j then hold that head's
   // running maximum M and weight sum W (cross-lane reductions), and each
-  // output element adds the round's pieces with independent fmas:
+  // output element adds the unit's pieces with independent fmas:
   //   M' = max(M, max_i lse_i),  W' = W 2^(M - M') + sum_i 2^(lse_i - M'),
   //   acc' = acc 2^(M - M') + sum_i 2^(lse_i - M') O_i,   out = acc / W.
-  __device__ __forceinline__ void merge(int b, int sb0, int sb1, int total, int nwg) {
-    constexpr int HB = 4;
-    constexpr int PC = D == 64 ? 16 : 8;
-    static_assert(HB == 4, "the reductions below run over the lanes that share lane % 4");
-    const bool none_empty = total >= nwg;   // then every range holds at least one block
-    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(p.part_o, part_bytes());
-    const int hj = lane % HB;                // the head whose running state this lane holds
+  // A sequence's arithmetic is the same whichever workgroup merges it and
+  // whatever else that wave merges, so repeated calls give the same bits.
+  static constexpr int HB = 4;
+  static constexpr int PC = D == 64 ? 16 : 8;
+  struct MUnit {
+    int b;     // sequence (< 0: no unit)
+    int wf;    // range holding its first block
+    int npc;   // its pieces
+    int qh0;   // first head of the unit (within the wave's G)
+    int i0;    // first piece of the unit
+  };
+  struct MBuf {
+    float ov[PC][HB][C::DPL];
+    float lsl;        // this lane's lse (piece i / HB, head i % HB), or masked
+    uint64_t live;    // live pieces of the unit
+  };
+  __device__ __forceinline__ MUnit merge_first(int b, int sb0, int sb1, int total, int nwg) const {
+    MUnit u;
+    u.b = b;
+    // ranges holding the first and the last block of the sequence
+    u.wf = (int)udiv_small((uint64_t)(sb0 + 1) * (uint32_t)nwg - 1, (uint32_t)total);
+    const int wl = (int)udiv_small((uint64_t)sb1 * (uint32_t)nwg - 1, (uint32_t)total);
+    u.npc = wl - u.wf + 1;
+    u.qh0 = 0;
+    u.i0 = 0;
+    return u;
+  }
+  __device__ __forceinline__ void merge_load(const MUnit& u, MBuf& mb, int total, int nwg,
+                                             __amdgpu_buffer_rsrc_t rs) const {
+    if (u.b < 0) return;
+    // piece i of the unit -> its range; pieces past the sequence's last reuse
+    // that one's slot (a readable address) and are not live
+    const int nround = min(PC, u.npc - u.i0);
+    auto range = [&](int i) __attribute__((always_inline)) { return u.wf + u.i0 + min(i, nround - 1); };
+    // with at least as many blocks as ranges every range is non-empty,
+    // otherwise lane i checks piece i
+    if (total >= nwg) {
+      mb.live = nround >= 64 ? ~0ull : ((1ull << nround) - 1);
+    } else {
+      const int wr = range(lane);
+      mb.live = __ballot(lane < nround && range_start64(wr + 1, total, nwg) > range_start64(wr, total, nwg));
+    }
     {
-      // ranges holding the first and the last block of the sequence
-      const int wf = (int)udiv_small((uint64_t)(sb0 + 1) * (uint32_t)nwg - 1, (uint32_t)total);
-      const int wl = (int)udiv_small((uint64_t)sb1 * (uint32_t)nwg - 1, (uint32_t)total);
-      const int npc = wl - wf + 1;
-      for (int qh0 = 0; qh0 < p.G; qh0 += HB) {
-        float M = kMaskedScore, W = 0.f;
-        float acc[HB][C::DPL];
+      const int il = (lane % (PC * HB)) / HB;
+      const int hh = g * p.G + min(u.qh0 + lane % HB, p.G - 1);
+      const float l = atomic_ld(p.part_lse + (int64_t)(range(il) + u.b) * p.Hq + hh);
+      mb.lsl = (lane < PC * HB && ((mb.live >> il) & 1)) ? l : kMaskedScore;
+    }
+#pragma unroll
+    for (int i = 0; i < PC; ++i) {
+      const uint32_t slot = (uint32_t)(range(i) + u.b);
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        const uint32_t hh = (uint32_t)(g * p.G + min(u.qh0 + j, p.G - 1));
+#pragma unroll
+        for (int k = 0; k < C::DPL; ++k)
+          mb.ov[i][j][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rs, ((slot * (uint32_t)p.Hq + hh) * D + lane + 64 * k) * 4, 0, kDeviceScope));
+      }
+    }
+  }
+  __device__ __forceinline__ void merge_combine(const MBuf& mb, float& M, float& W, float (&acc)[HB][C::DPL]) const {
+    static_assert(HB == 4, "the reductions below run over the lanes that share lane % 4");
+    const float Mn = fmaxf(M, max_mod4(mb.lsl));
+    const float sc = __builtin_amdgcn_exp2f(M - Mn);
+    const float wt = mb.lsl == kMaskedScore ? 0.f : __builtin_amdgcn_exp2f(mb.lsl - Mn);
+    W = W * sc + sum_mod4(wt);
+    M = Mn;
+#pragma unroll
+    for (int j = 0; j < HB; ++j) {
+      const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), j));
+#pragma unroll
+      for (int k = 0; k < C::DPL; ++k) acc[j][k] *= f;
+    }
+#pragma unroll
+    for (int i = 0; i < PC; ++i) {
+      // uniform: pieces that do not exist are skipped, never weighted by 0
+      if (!((mb.live >> i) & 1)) continue;
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), i * HB + j));
+#pragma unroll
+        for (int k = 0; k < C::DPL; ++k) acc[j][k] = fmaf(f, mb.ov[i][j][k], acc[j][k]);
+      }
+    }
+  }
+  __device__ __forceinline__ void merge_store(const MUnit& u, float M, float W, const float (&acc)[HB][C::DPL]) const {
+#pragma unroll
+    for (int j = 0; j < HB; ++j) {
+      if (u.qh0 + j >= p.G) break;
+      const int hh = g * p.G + u.qh0 + j;
+      const float Wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(W), j));
+      const float Mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), j));
+      const float inv = 1.0f / Wj;
+      const int64_t orow = ((int64_t)u.b * p.Hq + hh) * D;
+#pragma unroll
+      for (int k = 0; k < C::DPL; ++k) {
+        if constexpr (BF16) {
+          reinterpret_cast<__bf16*>(p.out)[orow + lane + 64 * k] = (__bf16)(acc[j][k] * inv);
+        } else {
+          static_cast<float*>(p.out)[orow + lane + 64 * k] = acc[j][k] * inv;
+        }
+      }
+      if (p.lse && lane == 0) p.lse[(int64_t)u.b * p.Hq + hh] = (Mj + __builtin_amdgcn_logf(Wj)) * kLn2;
+    }
+  }
+  // Merges sequence b0 (blocks [s00, s10)) and, if nm == 2, sequence b1
+  // (blocks [s01, s11)), the units of both in one pipelined pass.
+  __device__ __forceinline__ void merge(int nm, int b0, int s00, int s10, int b1, int s01, int s11, int total,
+                                        int nwg) {
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(p.part_o, part_bytes());
+    auto next = [&](const MUnit& u) __attribute__((always_inline)) {
+      MUnit n = u;
+      n.i0 += PC;
+      if (n.i0 >= u.npc) {
+        n.i0 = 0;
+        n.qh0 += HB;
+        if (n.qh0 >= p.G) {
+          if (nm == 2 && u.b == b0) {
+            n = merge_first(b1, s01, s11, total, nwg);
+          } else {
+            n.b = -1;
+          }
+        }
+      }
+      return n;
+    };
+    float M = kMaskedScore, W = 0.f;
+    float acc[HB][C::DPL];
+    auto step = [&](const MUnit& cur, const MBuf& mb) __attribute__((always_inline)) {
+      if (cur.i0 == 0) {
+        M = kMaskedScore;
+        W = 0.f;
 #pragma unroll
         for (int j = 0; j < HB; ++j)
 #pragma unroll
           for (int k = 0; k < C::DPL; ++k) acc[j][k] = 0.f;
-        for (int i0 = 0; i0 < npc; i0 += PC) {
-          // piece i of the round -> its range; pieces past the sequence's last
-          // reuse that one's slot (a readable address) and are not live
-          const int nround = min(PC, npc - i0);
-          auto range = [&](int i) __attribute__((always_inline)) { return wf + i0 + min(i, nround - 1); };
-          // live pieces of the round as a bit mask; with at least as many
-          // blocks as ranges every range is non-empty, otherwise lane i checks
-          // piece i
-          uint64_t livemask;
-          if (none_empty) {
-            livemask = nround >= 64 ? ~0ull : ((1ull << nround) - 1);
-          } else {
-            const int wr = range(lane);
-            livemask = __ballot(lane < nround && range_start64(wr + 1, total, nwg) > range_start64(wr, total, nwg));
-          }
-          float lsl;
-          {
-            const int il = (lane % (PC * HB)) / HB;
-            const int slot = range(il) + b;
-            const int hh = g * p.G + min(qh0 + hj, p.G - 1);
-            const float l = atomic_ld(p.part_lse + (int64_t)slot * p.Hq + hh);
-            lsl = (lane < PC * HB && ((livemask >> il) & 1)) ? l : kMaskedScore;
-          }
-          float ov[PC][HB][C::DPL];
-#pragma unroll
-          for (int i = 0; i < PC; ++i) {
-            const uint32_t slot = (uint32_t)(range(i) + b);
-#pragma unroll
-            for (int j = 0; j < HB; ++j) {
-              const uint32_t hh = (uint32_t)(g * p.G + min(qh0 + j, p.G - 1));
-#pragma unroll
-              for (int k = 0; k < C::DPL; ++k)
-                ov[i][j][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    rs, ((slot * (uint32_t)p.Hq + hh) * D + lane + 64 * k) * 4, 0, kDeviceScope));
-            }
-          }
-          // running maximum and weight sum of head hj over the lanes that hold
-          // that head (lane bits above log2(HB))
-          const float Mn = fmaxf(M, max_mod4(lsl));
-          const float sc = __builtin_amdgcn_exp2f(M - Mn);
-          const float wt = lsl == kMaskedScore ? 0.f : __builtin_amdgcn_exp2f(lsl - Mn);
-          W = W * sc + sum_mod4(wt);
-          M = Mn;
-#pragma unroll
-          for (int j = 0; j < HB; ++j) {
-            const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), j));
-#pragma unroll
-            for (int k = 0; k < C::DPL; ++k) acc[j][k] *= f;
-          }
-#pragma unroll
-          for (int i = 0; i < PC; ++i) {
-            // uniform: pieces that do not exist are skipped, never weighted by 0
-            if (!((livemask >> i) & 1)) continue;
-#pragma unroll
-            for (int j = 0; j < HB; ++j) {
-              const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), i * HB + j));
-#pragma unroll
-              for (int k = 0; k < C::DPL; ++k) acc[j][k] = fmaf(f, ov[i][j][k], acc[j][k]);
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < HB; ++j) {
-          if (qh0 + j >= p.G) break;
-          const int hh = g * p.G + qh0 + j;
-          const float Wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(W), j));
-          const float Mj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), j));
-          const float inv = 1.0f / Wj;
-          const int64_t orow = ((int64_t)b * p.Hq + hh) * D;
-#pragma unroll
-          for (int k = 0; k < C::DPL; ++k) {
-            if constexpr (BF16) {
-              reinterpret_cast<__bf16*>(p.out)[orow + lane + 64 * k] = (__bf16)(acc[j][k] * inv);
-            } else {
-              static_cast<float*>(p.out)[orow + lane + 64 * k] = acc[j][k] * inv;
-            }
-          }
-          if (p.lse && lane == 0) p.lse[(int64_t)b * p.Hq + hh] = (Mj + __builtin_amdgcn_logf(Wj)) * kLn2;
-        }
       }
+      merge_combine(mb, M, W, acc);
+      if (cur.i0 + PC >= cur.npc) merge_store(cur, M, W, acc);
+    };
+    MBuf bA, bB;
+    MUnit cur = merge_first(b0, s00, s10, total, nwg);
+    merge_load(cur, bA, total, nwg, rs);
+    for (;;) {
+      MUnit nxt = next(cur);
+      merge_load(nxt, bB, total, nwg, rs);
+      step(cur, bA);
+      if (nxt.b < 0) break;
+      cur = nxt;
+      nxt = next(cur);
+      merge_load(nxt, bA, total, nwg, rs);
+      step(cur, bB);
+      if (nxt.b < 0) break;
+      cur = nxt;
     }
   }
 };
@@ -762,11 +817,10 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     }
     const uint64_t lastm = __ballot(done);
     // one query row per sequence: sequence b's output row is b
-#pragma nounroll
-    for (int m = 0; m < 2; ++m) {
-      if (!((lastm >> m) & 1)) continue;
-      const int mb = m == 0 ? split_b0 : split_b1;
-      wv.merge(mb, sstart[mb], sstart[mb + 1], total, nwg);
+    if (lastm & 3) {
+      const int ba = (lastm & 1) ? split_b0 : split_b1;
+      const int bb = (lastm & 3) == 3 ? split_b1 : ba;   // second sequence, if both are complete
+      wv.merge((lastm & 3) == 3 ? 2 : 1, ba, sstart[ba], sstart[ba + 1], bb, sstart[bb], sstart[bb + 1], total, nwg);
     }
   };
 
