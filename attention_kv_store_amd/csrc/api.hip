@@ -184,6 +184,12 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     const size_t half_cu = 80 * 1024 - 256;
     p.meta_lds = kvs::prefill_lds_bytes((int)D, q->dtype == KVS_BF16, (int)B, 1) <= half_cu ? 1 : 0;
     if (B > (1 << 24)) return fail(KVS_ERR_UNSUPPORTED, "prefill batch too large");
+    // items are (token tile, sequence, head group); no sequence has more than
+    // ceil(T / tile) token tiles, which bounds the item count from above
+    const int64_t tile_rows = 32 * (int64_t)p.TPW;
+    const int64_t items_bound = (T + tile_rows - 1) / tile_rows * B * (int64_t)p.NHG;
+    p.items32 = items_bound < ((int64_t)1 << 31) ? 1 : 0;
+    kvs::fast_div_magic((uint32_t)p.NHG, &p.nhg_m, &p.nhg_l);
     return KVS_OK;
   }
 

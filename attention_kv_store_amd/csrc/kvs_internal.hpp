@@ -39,6 +39,10 @@ struct AttnParams {
   int32_t NHG;            // head groups = Hq / HW
   int32_t pgrid;          // persistent workgroups (two per CU)
   int32_t meta_lds;       // 1: cu_seqlens_q and seqlens_k are staged in LDS
+  // 1: every item index fits in 31 bits; items are then ordered per XCD and
+  // decoded with multiply-high divisions (by NHG with the magic below)
+  int32_t items32;
+  uint32_t nhg_m, nhg_l;
   // decode work plan: the batch's key blocks, flattened sequence-major, are cut
   // into `nwg` equal contiguous ranges, one per workgroup; a workgroup holds the
   // waves of `hpw` consecutive KV heads.
@@ -58,6 +62,17 @@ struct AttnParams {
   int32_t NB;             // cache blocks (the append writes only slots inside the pool)
   int32_t dsmall;         // decode: 1 = small batch, whole block table staged in LDS
 };
+
+// Division by a divisor d (1 <= d < 2^31) fixed for a launch, for dividends
+// n < 2^31: q = (mulhi(n, m) + n) >> l with l = ceil(log2 d) and
+// m = floor(2^(32 + l) / d) - 2^32 + 1 (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, section 4).
+inline void fast_div_magic(uint32_t d, uint32_t* m, uint32_t* l) {
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  *l = s;
+  *m = (uint32_t)(((uint64_t(1) << (32 + s)) / d) - (uint64_t(1) << 32) + 1);
+}
 
 // Split decode counts finished blocks per (sequence, KV head) in the first
 // bytes of its workspace, at a place that does not depend on the shape.

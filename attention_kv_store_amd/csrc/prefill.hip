@@ -66,6 +66,8 @@ static_assert(PCfg<128, true>::STAGE == 32768 && PCfg<64, true>::STAGE == 16384 
               "the host's prefill_stage_bytes must match the stage layout");
 static_assert(PCfg<128, true>::KIT * 4 * 64 == PCfg<128, true>::KCH && PCfg<64, true>::KIT * 4 * 64 == PCfg<64, true>::KCH,
               "each wave copies KIT whole 1 KiB blocks of a tile");
+static_assert(PCfg<128, true>::KIT * 64 == 16 * PCfg<128, true>::CPR && PCfg<64, true>::KIT * 64 == 16 * PCfg<64, true>::CPR,
+              "bf16: wave w copies exactly the 16 keys of page w of a tile");
 
 // Source of the key rows past an item's last key: a zero row, so V is exactly
 // 0 there (P is 0 too, but V could hold anything) and K is harmless.
@@ -128,12 +130,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t NI = (int64_t)NT * BH;
   const int G = gridDim.x, w = blockIdx.x;
   const int rev_w = (G & 7) == 0 ? (w & 7) + 8 * (G / 8 - 1 - (w >> 3)) : G - 1 - w;
-  const int64_t nrounds = (NI + G - 1) / G;
+  // Item order.  A pair (sequence, head group) -- whose token tiles all read
+  // the same keys -- belongs to one XCD (pair % 8; workgroup w runs on XCD
+  // w % 8), and each XCD's workgroups take its pairs a few at a time, all
+  // token tiles of a pair in one round, heaviest (last) tile first; odd
+  // rounds run the other way round, so each workgroup's causal work evens out.
+  // The K/V a round re-reads then fits the XCD's L2.  (items32 = 0: the same
+  // tile-major order over all workgroups with 64-bit indices.)
+  const int X = (G & 7) == 0 ? 8 : 1;
+  const int xcd = w % X, wi = w / X, GX = G / X;
+  const int NPx = (int)((BH - xcd + X - 1) / X);   // pairs of this XCD
+  const int64_t NIx = (int64_t)NPx * NT;           // its items
+  const int64_t nrounds = p.items32 ? (NIx + GX - 1) / GX : (NI + G - 1) / G;
+  // NT < 2^31: q = v / NT by multiply-high (see fast_div_magic)
+  uint32_t nt_l = 0;
+  while ((1u << nt_l) < (uint32_t)NT && nt_l < 31) ++nt_l;
+  const uint32_t nt_m = (uint32_t)((((uint64_t)1) << (32 + nt_l)) / (uint32_t)max(NT, 1) - (((uint64_t)1) << 32) + 1);
 
   // ---- items --------------------------------------------------------------
   struct Item {
     int r;             // round of this workgroup's item sequence (nrounds: none)
     int b, hgrp, tile;
+    int kvh;           // KV head of the head group
     int q0, Lq, Lk;
     int nkeys, ntiles, npages;
   };
@@ -154,14 +172,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     Item it;
     it.ntiles = 0;
     for (; r < nrounds; ++r) {
-      // odd rounds reverse the order within each XCD's workgroups (w % 8 is
-      // the XCD a workgroup runs on), so an item's (sequence, head group)
-      // pair stays on one XCD and its K/V re-reads hit that XCD's L2
-      const int64_t u = (int64_t)r * G + ((r & 1) ? rev_w : w);
-      if (u >= NI) continue;
-      const int64_t pair = u % BH;
-      const int tile = NT - 1 - (int)(u / BH);
-      const int b = (int)(pair / p.NHG), hgrp = (int)(pair % p.NHG);
+      int tile, b, hgrp;
+      if (p.items32) {
+        // this XCD's item v (< 2^31): local pair v / NT, tile counted down
+        const int64_t v64 = (int64_t)r * GX + ((r & 1) ? GX - 1 - wi : wi);
+        if (v64 >= NIx) continue;
+        const uint32_t v = (uint32_t)v64;
+        const uint32_t lp = (__umulhi(v, nt_m) + v) >> nt_l;
+        tile = NT - 1 - (int)(v - lp * (uint32_t)NT);
+        const uint32_t pair = (uint32_t)xcd + (uint32_t)X * lp;
+        const uint32_t bq = (__umulhi(pair, p.nhg_m) + pair) >> p.nhg_l;
+        b = (int)bq;
+        hgrp = (int)(pair - bq * (uint32_t)p.NHG);
+      } else {
+        // tile-major over all workgroups; odd rounds mirror the workgroups
+        // within each XCD, so a pair still stays on one XCD
+        const int64_t u = (int64_t)r * G + ((r & 1) ? rev_w : w);
+        if (u >= NI) continue;
+        const int64_t pair = u % BH;
+        tile = NT - 1 - (int)(u / BH);
+        b = (int)(pair / p.NHG);
+        hgrp = (int)(pair % p.NHG);
+      }
       int q0, q1, lk;
       meta(b, q0, q1, lk);
       const int Lq = q1 - q0;
@@ -170,6 +202,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int tlast = min(tile * TW + TW, Lq) - 1;
       it.b = b;
       it.hgrp = hgrp;
+      it.kvh = (hgrp * p.HW) / p.G;   // HW divides G: one KV head per item
       it.tile = tile;
       it.q0 = q0;
       it.Lq = Lq;
@@ -199,8 +232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return x;
   };
   auto kv_base = [&](const Item& it, const void* base) __attribute__((always_inline)) {
-    const int g = (it.hgrp * p.HW) / p.G;   // HW divides G: one KV head per item
-    return static_cast<const E*>(base) + (int64_t)g * D;
+    return static_cast<const E*>(base) + (int64_t)it.kvh * D;
   };
 
   // ---- staging helpers ----------------------------------------------------
@@ -230,6 +262,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   u32x4 kreg[BF16 ? 1 : C::KIT];
   u32x4 vreg[BF16 ? 1 : C::KIT];
+  // bf16: wave w copies page w of every tile (16 keys).  Per lane and copy j,
+  // the element offset inside the page of its 16-byte chunk, with the chunk
+  // slot swizzled by key: the same for every step.
+  uint32_t kpo[BF16 ? C::KIT : 1], vpo[BF16 ? C::KIT : 1];
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < C::KIT; ++j) {
+      const int pch = j * 64 + lane;            // chunk of the wave's page
+      const int kip = pch / C::CPR, slot = pch % C::CPR;
+      const int key = wave * 16 + kip;          // key row in the tile
+      kpo[j] = (uint32_t)(kip * (int)kv_tok_stride + (slot ^ C::kswz(key)) * 8);
+      vpo[j] = (uint32_t)(kip * (int)kv_tok_stride + (slot ^ C::vswz(key)) * 8);
+    }
+  }
   // K/V of step s: bf16 -> 16-byte global-to-LDS copies straight into stage
   // `buf` (each wave writes KIT whole 1 KiB blocks of each tile; key rows at
   // or past nkeys copy the zero row); fp32 -> registers, see write_stage.
@@ -238,33 +284,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto issue_loads = [&](int pgv, const Step& s, int buf) {
     const E* kbase = kv_base(s.it, p.k);
     const E* vbase = kv_base(s.it, p.v);
-    int pg[C::NPG];
-#pragma unroll
-    for (int i = 0; i < C::NPG; ++i) {
-      const int e = __builtin_amdgcn_readlane(pgv, i);
-      pg[i] = s.t * C::NPG + i < s.it.npages ? e : 0;
-    }
     if constexpr (BF16) {
       char* Kd = smem + buf * C::STAGE;
       char* Vd = Kd + C::KTILE;
+      // this wave's page of the tile (block 0 past the sequence's last page)
+      const int pk = s.t * C::NPG + wave < s.it.npages ? __builtin_amdgcn_readlane(pgv, wave) : 0;
+      const E* kpage = kbase + pk * page_stride;
+      const E* vpage = vbase + pk * page_stride;
       const int kv0 = s.t * C::BN;
+      // keys at or past nkeys (only in an item's last tile) copy the zero row
+      const bool tail = kv0 + wave * 16 + 16 > s.it.nkeys;   // uniform
       const E* zero = reinterpret_cast<const E*>(g_zero_row);
 #pragma unroll
       for (int j = 0; j < C::KIT; ++j) {
         const int blk = wave * C::KIT + j;   // 1 KiB block of each tile
-        const int pch = blk * 64 + lane;      // 16-byte chunk slot in the tile
-        const int key = pch / C::CPR, slot = pch % C::CPR;
-        const int pi = __builtin_amdgcn_readfirstlane(key >> 4);   // same page across the block
-        int pk = pg[0];
-#pragma unroll
-        for (int i = 1; i < C::NPG; ++i) pk = pi == i ? pg[i] : pk;
-        const bool live = kv0 + key < s.it.nkeys;
-        const int64_t row = pk * page_stride + (key & 15) * kv_tok_stride;
-        const int ck = (slot ^ C::kswz(key)) * 8, cv = (slot ^ C::vswz(key)) * 8;
-        copy16_to_lds(live ? kbase + row + ck : zero + ck, Kd + blk * 1024);
-        copy16_to_lds(live ? vbase + row + cv : zero + cv, Vd + blk * 1024);
+        const E* ks = kpage + kpo[j];
+        const E* vs = vpage + vpo[j];
+        if (tail) {
+          const int key = wave * 16 + (j * 64 + lane) / C::CPR;
+          const bool live = kv0 + key < s.it.nkeys;
+          const int slot = (j * 64 + lane) % C::CPR;
+          ks = live ? ks : zero + (slot ^ C::kswz(key)) * 8;
+          vs = live ? vs : zero + (slot ^ C::vswz(key)) * 8;
+        }
+        copy16_to_lds(ks, Kd + blk * 1024);
+        copy16_to_lds(vs, Vd + blk * 1024);
       }
     } else {
+      int pg[C::NPG];
+#pragma unroll
+      for (int i = 0; i < C::NPG; ++i) {
+        const int e = __builtin_amdgcn_readlane(pgv, i);
+        pg[i] = s.t * C::NPG + i < s.it.npages ? e : 0;
+      }
 #pragma unroll
       for (int it = 0; it < C::KIT; ++it) {
         const int pi = kpage_idx(it);
@@ -355,6 +407,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16 o[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
+
+  // ---- epilogue of an item: O / l, lse = (m + log2 l) ln 2, then the state
+  // is reset for the next item.  Lanes n and n + 32 hold the two halves of
+  // row n, 4 consecutive d at a time.  bf16: one exchange between them gives
+  // each lane 8 consecutive d, so each store is 16 bytes and a lane pair
+  // writes 32 contiguous bytes of its row (half as many write requests as
+  // 8-byte stores).
+  auto epilogue = [&](const Item& e) __attribute__((always_inline)) {
+    const int wt0 = e.tile * TW + tb * 32;
+    const int qrow = wt0 + n;
+    // lanes n and n + 32 share row n (and so this condition); the cross-lane
+    // steps below run on all lanes, only the stores are conditional
+    const bool row_ok = wt0 < e.Lq && qrow < e.Lq;
+    const int h = e.hgrp * p.HW + hw;
+    const float l_tot = sum_xor32(l_run);
+    const float inv = 1.0f / l_tot;
+    const int64_t orow = ((int64_t)(e.q0 + (row_ok ? qrow : 0)) * p.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      if constexpr (BF16) {
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          // x: this lane's 4 values of group 2 g2, y: of group 2 g2 + 1; the
+          // swap of x's upper lanes with y's lower lanes leaves lane n (hh 0)
+          // with d 8 (2 g2) + 0..7 and lane n + 32 with d 8 (2 g2 + 1) + 0..7
+          const int r0 = 8 * g2, r1 = 8 * g2 + 4;
+          const uint32_t x0 = pack_bf16x2(o[db][r0 + 0] * inv, o[db][r0 + 1] * inv);
+          const uint32_t x1 = pack_bf16x2(o[db][r0 + 2] * inv, o[db][r0 + 3] * inv);
+          const uint32_t y0 = pack_bf16x2(o[db][r1 + 0] * inv, o[db][r1 + 1] * inv);
+          const uint32_t y1 = pack_bf16x2(o[db][r1 + 2] * inv, o[db][r1 + 3] * inv);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+          const int d = db * 32 + (2 * g2 + hh) * 8;
+          if (row_ok)
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + orow + d) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+        }
+      } else {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + hh * 4;
+          if (row_ok)
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow + d) =
+                f32x4{o[db][g4 * 4 + 0] * inv, o[db][g4 * 4 + 1] * inv, o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv};
+        }
+      }
+    }
+    if (p.lse && hh == 0 && row_ok) p.lse[(int64_t)(e.q0 + qrow) * p.Hq + h] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    m_run = kMaskedScore;
+    l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
+  };
 
   // ---- prologue: the first step -------------------------------------------
   Step cur;
@@ -508,36 +612,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (!q_next) load_q(nx1.it);
 
-    if (item_end) {
-      // ---- epilogue of the item: O / l, lse = (m + log2 l) ln 2 -----------
-      const int qrow = wt0 + n;
-      if (wave_live && qrow < it.Lq) {
-        const int h = it.hgrp * p.HW + hw;
-        const float l_tot = sum_xor32(l_run);
-        const float inv = 1.0f / l_tot;
-        const int64_t orow = ((int64_t)(it.q0 + qrow) * p.Hq + h) * D;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int d = db * 32 + g4 * 8 + hh * 4;
-            const float a0 = o[db][g4 * 4 + 0] * inv, a1 = o[db][g4 * 4 + 1] * inv;
-            const float a2 = o[db][g4 * 4 + 2] * inv, a3 = o[db][g4 * 4 + 3] * inv;
-            if constexpr (BF16) {
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + orow + d) =
-                  u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-            } else {
-              *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow + d) = f32x4{a0, a1, a2, a3};
-            }
-          }
-        }
-        if (p.lse && hh == 0) p.lse[(int64_t)(it.q0 + qrow) * p.Hq + h] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
-      }
-      m_run = kMaskedScore;
-      l_run = 0.f;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) o[db] = f32x16{};
-    }
+    if (item_end) epilogue(it);
 
     if (has_next) write_stage(buf ^ 1, nx1);
     __syncthreads();
