@@ -174,8 +174,11 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   plan->ws_bytes = 0;
 
   if (!plan->decode) {
+    // bf16: one 8-wave workgroup per CU (a K/V tile serves 8 x 32 rows);
+    // fp32: two 4-wave workgroups per CU
+    p.pnw = q->dtype == KVS_BF16 ? 8 : 4;
     p.HW = p.G % 4 == 0 ? 4 : (p.G % 2 == 0 ? 2 : 1);
-    p.TPW = 4 / p.HW;
+    p.TPW = p.pnw / p.HW;
     p.NHG = p.Hq / p.HW;
     // cu_seqlens_q / seqlens_k ride in LDS while two workgroups still fit in
     // a CU's 160 KiB; the persistent grid (two workgroups per CU) is sized at
@@ -308,11 +311,12 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   }
   int cus = 0;
   KVS_TRY(device_cus(&cus));
-  p.pgrid = 2 * cus;
+  p.pgrid = (p.pnw == 8 ? 1 : 2) * cus;
   const hipError_t e = kvs::launch_prefill(p, plan.dt, plan.D, stream);
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
-  set_dispatch("prefill_%s_d%d grid=%d (persistent) head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d",
-               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.pgrid, p.NHG, p.HW, 32 * p.TPW, p.meta_lds);
+  set_dispatch("prefill_%s_d%d grid=%d (persistent) waves/wg=%d head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d",
+               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.pgrid, p.pnw, p.NHG, p.HW, 32 * p.TPW,
+               p.meta_lds);
   return KVS_OK;
 }
 

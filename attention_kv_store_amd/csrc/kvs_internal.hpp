@@ -37,7 +37,8 @@ struct AttnParams {
   int32_t HW;             // query heads per workgroup (divides G)
   int32_t TPW;            // 32-token blocks per workgroup (HW * TPW == 4 waves)
   int32_t NHG;            // head groups = Hq / HW
-  int32_t pgrid;          // persistent workgroups (two per CU)
+  int32_t pgrid;          // persistent workgroups
+  int32_t pnw;            // waves per prefill workgroup (4: two per CU; 8: one per CU)
   int32_t meta_lds;       // 1: cu_seqlens_q and seqlens_k are staged in LDS
   // 1: every item index fits in 31 bits; items are then ordered per XCD and
   // decoded with multiply-high divisions (by NHG with the magic below)

@@ -9,11 +9,11 @@
 // that share one KV head are served by the same workgroup so each K/V tile is
 // loaded once for the whole group (§15).
 //
-// Layout of the work (one workgroup = 4 waves; a persistent grid walks the
-// items, see prefill_kernel):
+// Layout of the work (one workgroup = NW waves, 4 or 8; a persistent grid
+// walks the items, see prefill_kernel):
 //  * A wave owns 32 query rows of ONE query head: rows = tokens
-//    [wt0, wt0 + 32) of one sequence.  The 4 waves are HW heads x TPW token
-//    blocks of the same KV head (HW * TPW = 4; HW divides the group size).
+//    [wt0, wt0 + 32) of one sequence.  The NW waves are HW heads x TPW token
+//    blocks of the same KV head (HW * TPW = NW; HW divides the group size).
 //  * Scores are formed transposed, S^T = K . Q^T, with the 32x32 MFMA.  In the
 //    accumulator layout every lane then holds ONE query row (lane % 32) and 16
 //    of the 32 keys of a block, so row max / row sum are in-lane plus a single
@@ -39,8 +39,9 @@ namespace kvs {
 // Largest growth (base 2) of a row maximum absorbed without rescaling.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, bool BF16>
+template <int D, bool BF16, int NW = 4>
 struct PCfg {
+  static constexpr int NTH = 64 * NW;          // threads per workgroup
   static constexpr int BN = BF16 ? 64 : 32;   // keys per tile
   static constexpr int ESZ = BF16 ? 2 : 4;    // element bytes
   // bf16: K and V tiles are row-major without padding, filled by 16-byte
@@ -55,7 +56,8 @@ struct PCfg {
   static constexpr int NPG = BN / 16;          // pages per tile
   static constexpr int CPR = D * ESZ / 16;     // 16-byte chunks per token row
   static constexpr int KCH = BN * CPR;         // chunks per tile and operand
-  static constexpr int KIT = (KCH + 255) / 256;  // chunks per thread and operand
+  static constexpr int KIT = (KCH + NTH - 1) / NTH;  // chunks per thread and operand
+  static constexpr int KPW = 64 * KIT / CPR;   // bf16: key rows each wave copies
   static constexpr int NDB = D / 32;           // 32-wide d blocks of the output
   // bf16 chunk slot of logical chunk c of key row `key`: c ^ swizzle(key)
   __host__ __device__ static constexpr int kswz(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
@@ -64,10 +66,14 @@ struct PCfg {
 static_assert(PCfg<128, true>::STAGE == 32768 && PCfg<64, true>::STAGE == 16384 &&
                   PCfg<128, false>::STAGE == 2 * 32 * (128 * 4 + 16),
               "the host's prefill_stage_bytes must match the stage layout");
-static_assert(PCfg<128, true>::KIT * 4 * 64 == PCfg<128, true>::KCH && PCfg<64, true>::KIT * 4 * 64 == PCfg<64, true>::KCH,
-              "each wave copies KIT whole 1 KiB blocks of a tile");
-static_assert(PCfg<128, true>::KIT * 64 == 16 * PCfg<128, true>::CPR && PCfg<64, true>::KIT * 64 == 16 * PCfg<64, true>::CPR,
-              "bf16: wave w copies exactly the 16 keys of page w of a tile");
+template <int D, int NW>
+constexpr bool copies_whole_pages() {
+  using C = PCfg<D, true, NW>;
+  return C::KIT * C::NTH == C::KCH && C::KPW * C::CPR == 64 * C::KIT && 16 % C::KPW == 0;
+}
+static_assert(copies_whole_pages<128, 4>() && copies_whole_pages<64, 4>() && copies_whole_pages<128, 8>() &&
+                  copies_whole_pages<64, 8>(),
+              "bf16: each wave copies KIT whole 1 KiB blocks: KPW consecutive keys of one page of a tile");
 
 // Source of the key rows past an item's last key: a zero row, so V is exactly
 // 0 there (P is 0 too, but V could hold anything) and K is harmless.
@@ -86,12 +92,12 @@ __device__ __attribute__((aligned(16))) uint16_t g_zero_row[128];
 // entries one step earlier, and the next item's Q rows as soon as the last
 // score tile of the current item is formed, so moving to a new item costs
 // about what moving to a new key tile does.
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(AttnParams p) {
-  using C = PCfg<D, BF16>;
+template <int D, bool BF16, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(AttnParams p) {
+  using C = PCfg<D, BF16, NW>;
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int s_nt[4];
+  __shared__ int s_nt[NW];
 
   const int tid = threadIdx.x;
   // wave-uniform by construction; readfirstlane lets the compiler see it, so
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int n = lane & 31, hh = lane >> 5;
   const int B = p.B;
   const int TW = 32 * p.TPW;
-  const int tw_shift = 5 + (p.TPW >> 1);   // log2(TW): TPW is 1, 2 or 4
+  const int tw_shift = 5 + __builtin_ctz(p.TPW);   // log2(TW): TPW is a power of two
   const int hw = wave % p.HW, tb = wave / p.HW;
   const int64_t kv_tok_stride = (int64_t)p.Hkv * D;   // elements between token rows
   const int64_t page_stride = (int64_t)kPage * kv_tok_stride;   // elements per block
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int* s_lk = s_cq + B + 1;                                   // [B]
   {
     float ntmax = 0.f;
-    for (int b = tid; b < B; b += 256) {
+    for (int b = tid; b < B; b += C::NTH) {
       const int a = p.cu_q[b], z = p.cu_q[b + 1], lk = p.lens_k[b];
       if (staged) {
         s_cq[b] = a;
@@ -125,7 +131,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (lane == 0) s_nt[wave] = (int)ntmax;
     __syncthreads();
   }
-  const int NT = __builtin_amdgcn_readfirstlane(max(max(s_nt[0], s_nt[1]), max(s_nt[2], s_nt[3])));
+  int nt_all = s_nt[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) nt_all = max(nt_all, s_nt[i]);
+  const int NT = __builtin_amdgcn_readfirstlane(nt_all);
   const int64_t BH = (int64_t)B * p.NHG;
   const int64_t NI = (int64_t)NT * BH;
   const int G = gridDim.x, w = blockIdx.x;
@@ -245,35 +254,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int32_t* trow = p.table + (int64_t)s.it.b * p.MB;
     return trow[min(s.t * C::NPG + (lane & (C::NPG - 1)), s.it.npages - 1)];
   };
-  // Chunk it of a K row-major tile: key row j = (it * 256 + tid) / CPR of the
+  // Chunk it of a K row-major tile: key row j = (it * NTH + tid) / CPR of the
   // tile (its page index is the same across a wave), 16-byte chunk ch.
   auto kpage_idx = [&](int it) -> int {
-    return __builtin_amdgcn_readfirstlane(((it * 256 + tid) / C::CPR) >> 4);
+    return __builtin_amdgcn_readfirstlane(((it * C::NTH + tid) / C::CPR) >> 4);
   };
-  // fp32 path: chunk it of a row-major tile (key row (it * 256 + tid) / CPR)
+  // fp32 path: chunk it of a row-major tile (key row (it * NTH + tid) / CPR)
   // is loaded into registers and written to padded LDS rows; per-lane element
   // offsets inside a block (< 16 * Hkv * D, so 32 bits)
   uint32_t koff[C::KIT];
 #pragma unroll
   for (int it = 0; it < C::KIT; ++it) {
-    const int cch = it * 256 + tid;
+    const int cch = it * C::NTH + tid;
     const int j = (cch / C::CPR) & (C::BN - 1), ch = cch % C::CPR;
     koff[it] = (uint32_t)((j & 15) * (int)kv_tok_stride + ch * (16 / C::ESZ));
   }
   u32x4 kreg[BF16 ? 1 : C::KIT];
   u32x4 vreg[BF16 ? 1 : C::KIT];
-  // bf16: wave w copies page w of every tile (16 keys).  Per lane and copy j,
-  // the element offset inside the page of its 16-byte chunk, with the chunk
-  // slot swizzled by key: the same for every step.
+  // bf16: wave w copies keys [w KPW, w KPW + KPW) of every tile, all in page
+  // w KPW / 16.  Per lane and copy j, the element offset inside that page of
+  // its 16-byte chunk, with the chunk slot swizzled by key: the same for
+  // every step.
   uint32_t kpo[BF16 ? C::KIT : 1], vpo[BF16 ? C::KIT : 1];
   if constexpr (BF16) {
 #pragma unroll
     for (int j = 0; j < C::KIT; ++j) {
-      const int pch = j * 64 + lane;            // chunk of the wave's page
-      const int kip = pch / C::CPR, slot = pch % C::CPR;
-      const int key = wave * 16 + kip;          // key row in the tile
-      kpo[j] = (uint32_t)(kip * (int)kv_tok_stride + (slot ^ C::kswz(key)) * 8);
-      vpo[j] = (uint32_t)(kip * (int)kv_tok_stride + (slot ^ C::vswz(key)) * 8);
+      const int pch = j * 64 + lane;            // chunk of the wave's keys
+      const int slot = pch % C::CPR;
+      const int key = wave * C::KPW + pch / C::CPR;   // key row in the tile
+      kpo[j] = (uint32_t)((key & 15) * (int)kv_tok_stride + (slot ^ C::kswz(key)) * 8);
+      vpo[j] = (uint32_t)((key & 15) * (int)kv_tok_stride + (slot ^ C::vswz(key)) * 8);
     }
   }
   // K/V of step s: bf16 -> 16-byte global-to-LDS copies straight into stage
@@ -288,12 +298,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       char* Kd = smem + buf * C::STAGE;
       char* Vd = Kd + C::KTILE;
       // this wave's page of the tile (block 0 past the sequence's last page)
-      const int pk = s.t * C::NPG + wave < s.it.npages ? __builtin_amdgcn_readlane(pgv, wave) : 0;
+      const int pgi = (wave * C::KPW) >> 4;
+      const int pk = s.t * C::NPG + pgi < s.it.npages ? __builtin_amdgcn_readlane(pgv, pgi) : 0;
       const E* kpage = kbase + pk * page_stride;
       const E* vpage = vbase + pk * page_stride;
       const int kv0 = s.t * C::BN;
       // keys at or past nkeys (only in an item's last tile) copy the zero row
-      const bool tail = kv0 + wave * 16 + 16 > s.it.nkeys;   // uniform
+      const bool tail = kv0 + wave * C::KPW + C::KPW > s.it.nkeys;   // uniform
       const E* zero = reinterpret_cast<const E*>(g_zero_row);
 #pragma unroll
       for (int j = 0; j < C::KIT; ++j) {
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const E* ks = kpage + kpo[j];
         const E* vs = vpage + vpo[j];
         if (tail) {
-          const int key = wave * 16 + (j * 64 + lane) / C::CPR;
+          const int key = wave * C::KPW + (j * 64 + lane) / C::CPR;
           const bool live = kv0 + key < s.it.nkeys;
           const int slot = (j * 64 + lane) % C::CPR;
           ks = live ? ks : zero + (slot ^ C::kswz(key)) * 8;
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
       for (int it = 0; it < C::KIT; ++it) {
-        const int cch = it * 256 + tid;
+        const int cch = it * C::NTH + tid;
         if (cch < C::KCH) {
           const bool keep = !tail || kv0 + cch / C::CPR < s.it.nkeys;
           st16(Ks + (cch / C::CPR) * C::KROW + (cch % C::CPR) * 16, kreg[it]);
@@ -623,14 +634,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, int NW>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const size_t lds = prefill_lds_bytes(D, BF16, p.B, p.meta_lds);
   // dynamic LDS above the default limit must be requested; grow it as needed
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
   if (lds > lds_granted.load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16, NW>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
@@ -640,13 +651,16 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<D, BF16>), dim3(p.pgrid), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, BF16, NW>), dim3(p.pgrid), dim3(64 * NW), lds, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s) {
-  if (dt == DType::BF16) return D == 64 ? launch_prefill_t<64, true>(p, s) : launch_prefill_t<128, true>(p, s);
-  return D == 64 ? launch_prefill_t<64, false>(p, s) : launch_prefill_t<128, false>(p, s);
+  if (dt == DType::BF16) {
+    if (p.pnw == 8) return D == 64 ? launch_prefill_t<64, true, 8>(p, s) : launch_prefill_t<128, true, 8>(p, s);
+    return D == 64 ? launch_prefill_t<64, true, 4>(p, s) : launch_prefill_t<128, true, 4>(p, s);
+  }
+  return D == 64 ? launch_prefill_t<64, false, 4>(p, s) : launch_prefill_t<128, false, 4>(p, s);
 }
 
 }  // namespace kvs
