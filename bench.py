@@ -55,7 +55,7 @@ def _src_sha(name: str) -> str:
 # kernel symbol (as rocprofv3 names it) and source file of each timed workload
 COUNTED = {
     "paged_decode_bf16": ("kvs::decode_kernel<64, true, true>", "decode.hip"),
-    "causal_prefill_bf16": ("kvs::prefill_kernel<128, true>", "prefill.hip"),
+    "causal_prefill_bf16": ("kvs::prefill_kernel<128, true, 8>", "prefill.hip"),
 }
 
 
@@ -190,7 +190,9 @@ def time_steps(w: Workload, steps: int, warmup: int, fused: bool = False, eager:
     each attention call (host issue time included where it exceeds the
     device's).
 
-    Returns (ms per step, ms per attention launch, wall seconds)."""
+    Returns (ms per step, ms per attention launch, wall seconds, stats) where
+    stats holds the median and p95 over the graph replays of the per-step
+    time (None for eager timing)."""
     import torch
 
     store = (lambda i: None) if fused else w.store
@@ -212,7 +214,7 @@ def time_steps(w: Workload, steps: int, warmup: int, fused: bool = False, eager:
         end.record()
         torch.cuda.synchronize()
         return (start.elapsed_time(end) / steps, sum(a.elapsed_time(b) for a, b in ev) / steps,
-                time.perf_counter() - t0)
+                time.perf_counter() - t0, None)
     G = _graph_len(steps)
 
     def capture(fn):
@@ -226,25 +228,90 @@ def time_steps(w: Workload, steps: int, warmup: int, fused: bool = False, eager:
         for _ in range(2):                      # replay warm-up
             g.replay()
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nrep = steps // G
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
         t0 = time.perf_counter()
-        start.record()
-        for _ in range(steps // G):
+        ev[0].record()
+        for r in range(nrep):
             g.replay()
-        end.record()
+            ev[r + 1].record()
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / steps, time.perf_counter() - t0
+        per = sorted(ev[r].elapsed_time(ev[r + 1]) / G for r in range(nrep))
+        stats = {"replays": nrep, "steps_per_replay": G, "median_ms_per_step": round(per[nrep // 2], 6),
+                 "p95_ms_per_step": round(per[min(nrep - 1, int(0.95 * nrep))], 6)}
+        return ev[0].elapsed_time(ev[nrep]) / steps, time.perf_counter() - t0, stats
 
     g_step = capture(lambda i: (store(i), attend(i)))
-    ms_step, wall = run(g_step)
+    ms_step, wall, stats = run(g_step)
     if fused:
         attn_ms = ms_step
     else:
         g_attn = capture(attend)
-        attn_ms, _ = run(g_attn)
+        attn_ms, _, astats = run(g_attn)
+        stats["attention_median_ms"] = astats["median_ms_per_step"]
         del g_attn
     del g_step
-    return ms_step, attn_ms, wall
+    return ms_step, attn_ms, wall, stats
+
+
+def measure_peaks():
+    """Rates this GPU sustains, to set beside the published peaks: a 1 GiB
+    device-to-device copy (bytes read + written per second) and a bf16 MFMA
+    loop with no memory traffic (kvs_mfma_peak_launch)."""
+    import torch
+
+    from attention_kv_store_amd import _lib
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    t_copy = timed(lambda: b.copy_(a), 10)
+    copy_gbs = 2 * n / t_copy / 1e9
+    del a, b
+    lib = _lib.load()
+    src = torch.randn(256, device="cuda").to(torch.bfloat16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters = 8 * cus, 2048
+    dst = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def mfma():
+        _lib.check(lib.kvs_mfma_peak_launch(src.data_ptr(), dst.data_ptr(), wgs, iters, stream))
+
+    t_mfma = timed(mfma, 5)
+    flops = wgs * 4 * 4 * iters * 32768
+    return {"copy_GBs": round(copy_gbs, 1), "bf16_mfma_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "how": "1 GiB device copy (read + write bytes); bf16 32x32x16 MFMA loop, "
+                   f"{wgs} workgroups x 4 waves x 4 chains x {iters} MFMAs, no memory traffic"}
+
+
+def environment():
+    import platform
+    import subprocess
+
+    import torch
+
+    env = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None), "host": platform.node(),
+           "host_cpus": len(os.sched_getaffinity(0))}
+    try:
+        env["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                                    text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        env["git"] = None
+    return env
 
 
 def cpu_baseline(batch, target_s: float = 10.0):
@@ -306,10 +373,17 @@ def main():
     log(f"decode batch: B={dec.B} sum(Lk)={int(dec.k_lens.sum())} K+V={kv_bytes(dec)/1e6:.1f} MB")
     w = Workload(dec, args.replicas)
     kvb = kv_bytes(dec)
-    sms, sattn_ms, _ = time_steps(w, args.steps, args.warmup, eager=args.eager)
+    # the first call of the process (module load and first dispatch), by itself
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    w.append_attend(0)
+    c1.record()
+    torch.cuda.synchronize()
+    cold_ms = c0.elapsed_time(c1)
+    sms, sattn_ms, _, sstats = time_steps(w, args.steps, args.warmup, eager=args.eager)
     sdispatch = kvs.last_dispatch()
     log(f"decode, two calls: {sms*1e3:.2f} us/step, attention {sattn_ms*1e3:.2f} us ({sdispatch})")
-    ms, attn_ms, wall = time_steps(w, args.steps, args.warmup, fused=True, eager=args.eager)
+    ms, attn_ms, wall, stats = time_steps(w, args.steps, args.warmup, fused=True, eager=args.eager)
     dispatch = kvs.last_dispatch()
     value = kvb / (ms * 1e-3) / 1e9
     achieved = kvb / (attn_ms * 1e-3) / 1e9
@@ -341,8 +415,10 @@ def main():
         "two_calls": {
             "step": "kv_store_paged(new rows) + attn_varlen_paged",
             "ms_per_step": round(sms, 6), "value": round(kvb / (sms * 1e-3) / 1e9, 2), "unit": "GB/s",
-            "attention_us": round(sattn_ms * 1e3, 3), "dispatch": sdispatch,
+            "attention_us": round(sattn_ms * 1e3, 3), "dispatch": sdispatch, "replay_stats": sstats,
         },
+        "replay_stats": stats,
+        "cold_first_call_ms": round(cold_ms, 3),
         "roofline": {
             "bound": "hbm",
             "kernel": COUNTED["paged_decode_bf16"][0] + " (the one launch of each attn_decode_append_paged call)",
@@ -358,12 +434,20 @@ def main():
     }
     del w
     torch.cuda.empty_cache()
+    # the same decode steps on one replica: K/V may then stay in the 256 MB
+    # Infinity Cache between steps (labelled warm; the headline rotates replicas)
+    w1 = Workload(dec, 1)
+    wms, _, _, _ = time_steps(w1, max(100, args.steps // 4), max(1, args.warmup // 4), fused=True, eager=args.eager)
+    line["warm_one_replica"] = {"ms_per_step": round(wms, 6), "value": round(kvb / (wms * 1e-3) / 1e9, 2),
+                                "unit": "GB/s", "note": "1 replica: K/V can stay in the Infinity Cache"}
+    del w1
+    torch.cuda.empty_cache()
 
     if not args.no_prefill:
         pre = causal_prefill_bf16()
         wp = Workload(pre, args.replicas)
         psteps = max(1, args.steps // 4)
-        pms, pattn, _ = time_steps(wp, psteps, max(1, args.warmup // 4), eager=args.eager)
+        pms, pattn, _, pstats = time_steps(wp, psteps, max(1, args.warmup // 4), eager=args.eager)
         pdisp = kvs.last_dispatch()
         fl = attention_flops(pre)
         tf = fl / (pattn * 1e-3) / 1e12
@@ -376,10 +460,18 @@ def main():
             "flops_per_launch": fl, "avg_launch_us": round(pattn * 1e3, 3),
             "ms_per_step": round(pms, 6), "steps": psteps,
             "traffic": _traffic("prefill.hip", "causal_prefill_bf16"),
-            "dispatch": pdisp,
+            "dispatch": pdisp, "replay_stats": pstats,
         }
         del wp
         torch.cuda.empty_cache()
+
+    peaks = measure_peaks()
+    line["measured_peaks"] = peaks
+    line["roofline"]["frac_of_measured_copy"] = round(achieved / peaks["copy_GBs"], 4)
+    if "prefill" in line:
+        line["prefill"]["frac_of_measured_mfma"] = round(line["prefill"]["achieved"] / peaks["bf16_mfma_TFLOPs"], 4)
+    line["env"] = environment()
+    log(f"measured peaks: {peaks}")
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

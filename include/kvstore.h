@@ -230,6 +230,18 @@ const char* kvs_last_dispatch(void);
  * device.  Synchronises the device first (the buffer may be in use). */
 kvs_status kvs_release_workspace(void);
 
+/*
+ * kvs_mfma_peak_launch -- device calibration for the benchmark, not part of
+ * the attention path: enqueues `workgroups` workgroups of 4 waves, each wave
+ * running 4 independent chains of `iters` 32x32x16 bf16 MFMAs (32768 FLOP
+ * each) with no memory traffic in the loop; a caller times it with events to
+ * get the bf16 MFMA rate this GPU sustains (FLOP = workgroups * 4 * 4 * iters
+ * * 32768).  `src`: 512 readable bytes, 16-byte aligned (operand data);
+ * `dst`: workgroups * 256 floats written.  KVS_ERR_INVALID on a bad argument
+ * (kvs_last_error is not set), KVS_ERR_HIP if the launch fails.
+ */
+kvs_status kvs_mfma_peak_launch(const void* src, void* dst, int workgroups, int iters, kvs_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
