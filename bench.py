@@ -254,6 +254,41 @@ def time_steps(w: Workload, steps: int, warmup: int, fused: bool = False, eager:
     return ms_step, attn_ms, wall, stats
 
 
+def runner_replays(dec, args):
+    """Replay time of DecodeGraphRunner's 64-row bucket for 64 real rows and
+    for 50 real rows padded with 14 dummy rows (one key each)."""
+    import torch
+
+    from attention_kv_store_amd.graph_runner import DecodeGraphRunner
+    from tests.gpu_side import to_device
+
+    db = to_device(dec)
+    rows = dec.new_token_rows()
+    kn = torch.from_numpy(dec.k_tokens[rows]).to(torch.bfloat16).cuda()
+    vn = torch.from_numpy(dec.v_tokens[rows]).to(torch.bfloat16).cuda()
+    runner = DecodeGraphRunner(db.k_cache, db.v_cache, dec.poison_block, [16, 32, 64], dec.MB, Hq=dec.Hq,
+                               scale=dec.scale)
+    res = {}
+    for B in (64, 50):
+        runner.step(db.q[:B], kn[:B], vn[:B], db.block_table[:B], db.seqlens_k[:B])
+        g = runner.graphs[runner.bucket_for(B)]
+        n = max(50, args.steps // 20)
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"rows_{B}_bucket_64_us"] = round(e0.elapsed_time(e1) / n * 1e3, 3)
+    res["note"] = "one replica (cache-resident between replays); the headline rotates 4 replicas"
+    del runner, db
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_peaks():
     """Rates this GPU sustains, to set beside the published peaks: a 1 GiB
     device-to-device copy (bytes read + written per second) and a bf16 MFMA
@@ -442,6 +477,12 @@ def main():
                                 "unit": "GB/s", "note": "1 replica: K/V can stay in the Infinity Cache"}
     del w1
     torch.cuda.empty_cache()
+
+    # graph runner (decode steps replayed from per-bucket graphs): the first 50
+    # sequences of the batch padded to the 64-row bucket with dummy rows, and
+    # all 64 -- replays only (inputs already in the bucket's buffers)
+    line["graph_runner"] = runner_replays(dec, args)
+    log(f"graph runner: {line['graph_runner']}")
 
     if not args.no_prefill:
         pre = causal_prefill_bf16()

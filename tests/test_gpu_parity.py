@@ -412,6 +412,83 @@ def test_decode_append_named_workload():
     _pool_matches_oracle(b, db.k_cache, db.v_cache)
 
 
+# ------------------------------------------------------- graph runner -----
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_graph_runner_buckets(dtype):
+    """Decode steps replayed from per-bucket graphs: a batch padded to the next
+    bucket with dummy rows in a reserved block gives the oracle's out / lse
+    for its real rows and writes exactly their new rows into the cache; then
+    a smaller batch through another bucket, one token longer."""
+    import dataclasses
+
+    from attention_kv_store_amd.graph_runner import DecodeGraphRunner
+    from tests.gpu_side import cache_bits, to_device_before_append
+    from tests.oracle_side import oracle_attention, oracle_pool
+    rng = np.random.default_rng(621)
+    # step 2 appends key k + 1: keep it inside the sequence's last allocated
+    # block (k + 1 not a multiple of 16), as a block manager would otherwise
+    # hand out a new block first
+    k = [int(x) - (1 if (int(x) + 1) % 16 == 0 else 0) for x in rng.integers(2, 900, size=37)]
+    b = _mk(621, [1] * 37, [x + 1 for x in k], Hq=8, Hkv=2, D=64, dtype=dtype, causal=True,
+            extra_table_cols=3, name=f"runner-{dtype}")
+    # pool holding keys 0 .. k-1 of every sequence; step 1 appends key k
+    db, _, _ = to_device_before_append(_prefix_batch(b, np.array(k) + 1))
+    runner = DecodeGraphRunner(db.k_cache, db.v_cache, b.poison_block, [16, 32, 64], b.MB, Hq=8,
+                               scale=b.scale, num_splits=7)
+    before = cache_bits(db.k_cache).copy()
+    rows = b.cu_seqlens_k[:-1] + np.array(k)
+    dt = db.q.dtype
+    kn = torch.from_numpy(b.k_tokens[rows]).to(dt).cuda()
+    vn = torch.from_numpy(b.v_tokens[rows]).to(dt).cuda()
+    out, lse = runner.step(db.q, kn, vn, db.block_table, torch.from_numpy((np.array(k) + 1).astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    step1 = dataclasses.replace(b, k_lens=(np.array(k) + 1).astype(np.int32))
+    pool = oracle_pool(b)
+    ro, rl = oracle_attention(step1, pool=pool)
+    go, gl = out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    eo, el = np.max(np.abs(go - ro)), np.max(np.abs(gl - rl))
+    print(f"[runner-{dtype} B=37 -> bucket 64] max|dout|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    assert eo <= TOL[dtype] and el <= TOL[dtype]
+    # the cache: the 37 new rows written, nothing else outside the reserved block changed
+    after = cache_bits(db.k_cache)
+    changed = np.argwhere((after != before).reshape(b.num_blocks * 16, -1).any(axis=1)).ravel()
+    written = set(int(x) for x in b.slots[rows])
+    assert set(int(x) for x in changed) - {b.poison_block * 16} <= written
+    kc, _ = oracle_pool(_prefix_batch(b, np.array(k) + 1), dtype=np.float32)
+    flat = after.reshape(b.num_blocks * 16, -1)
+    ref = (kc.view(np.uint32) >> 16).astype(np.uint16) if dtype == "bf16" else kc.view(np.uint32)
+    ref = ref.reshape(b.num_blocks * 16, -1)
+    for sl in written:
+        assert np.array_equal(flat[sl], ref[sl])
+    # a second step: the first 10 sequences, one key longer, through bucket 16
+    k2 = np.array(k[:10]) + 1
+    b2 = _mk(622, [1] * 10, list(k2 + 1), Hq=8, Hkv=2, D=64, dtype=dtype, causal=True)
+    q2 = torch.from_numpy(b2.q).to(dt).cuda()
+    kn2 = torch.from_numpy(b2.k_tokens[b2.new_token_rows()]).to(dt).cuda()
+    vn2 = torch.from_numpy(b2.v_tokens[b2.new_token_rows()]).to(dt).cuda()
+    table2 = db.block_table[:10]
+    # the new row of sequence s lands at key k2[s]; its block is in sequence s's table
+    out2, lse2 = runner.step(q2, kn2, vn2, table2, torch.from_numpy((k2 + 1).astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    # oracle: the first 10 sequences' keys 0 .. k2 (key k2 = the new row)
+    kt = np.concatenate([np.concatenate([b.k_tokens[b.cu_seqlens_k[s]:b.cu_seqlens_k[s] + k2[s]],
+                                         b2.k_tokens[b2.new_token_rows()][s:s + 1]]) for s in range(10)])
+    vt = np.concatenate([np.concatenate([b.v_tokens[b.cu_seqlens_k[s]:b.cu_seqlens_k[s] + k2[s]],
+                                         b2.v_tokens[b2.new_token_rows()][s:s + 1]]) for s in range(10)])
+    cu = np.zeros(11, np.int64)
+    cu[1:] = np.cumsum(k2 + 1)
+    slots = np.concatenate([b.block_table[s, np.arange(k2[s] + 1) // 16] * 16 + np.arange(k2[s] + 1) % 16
+                            for s in range(10)])
+    b3 = dataclasses.replace(b2, block_table=b.block_table[:10], num_blocks=b.num_blocks, poison_block=b.poison_block,
+                             k_lens=(k2 + 1).astype(np.int32), cu_seqlens_k=cu.astype(np.int32), k_tokens=kt,
+                             v_tokens=vt, slots=slots.astype(np.int32))
+    ro2, rl2 = oracle_attention(b3)
+    go2, gl2 = out2.float().cpu().numpy().astype(np.float64), lse2.cpu().numpy().astype(np.float64)
+    eo2, el2 = np.max(np.abs(go2 - ro2)), np.max(np.abs(gl2 - rl2))
+    print(f"[runner-{dtype} B=10 -> bucket 16] max|dout|={eo2:.3e} max|dlse|={el2:.3e}", flush=True)
+    assert eo2 <= TOL[dtype] and el2 <= TOL[dtype]
+
+
 # ------------------------------------------------------- graph capture ----
 @pytest.mark.parametrize("mode", ["fused_decode", "decode", "prefill"])
 def test_graph_replay_matches_eager(mode):
