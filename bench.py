@@ -506,6 +506,27 @@ def main():
         del wp
         torch.cuda.empty_cache()
 
+    if not args.no_prefill:
+        # a mixed serving step in one launch: 2 prompts x 256 new tokens and 30
+        # decode rows over 128..2048-token contexts (M = 542 rows); it runs on
+        # the prefill/extend kernel (T != B)
+        from workloads import mixed_prefill_decode_bf16
+        mix = mixed_prefill_decode_bf16()
+        wm = Workload(mix, args.replicas)
+        msteps = max(1, args.steps // 4)
+        mms, mattn, _, mstats = time_steps(wm, msteps, max(1, args.warmup // 4), eager=args.eager)
+        line["mixed"] = {
+            "workload": "mixed_prefill_decode_bf16", "query_rows": mix.T, "sequences": mix.B,
+            "avg_launch_us": round(mattn * 1e3, 3),
+            "TFLOPs": round(attention_flops(mix) / (mattn * 1e-3) / 1e12, 3),
+            "kv_GBs": round(kv_bytes(mix) / (mattn * 1e-3) / 1e9, 2),
+            "flops_per_launch": attention_flops(mix), "kv_bytes_per_launch": kv_bytes(mix),
+            "dispatch": kvs.last_dispatch(), "replay_stats": mstats,
+        }
+        log(f"mixed: {line['mixed']}")
+        del wm
+        torch.cuda.empty_cache()
+
     peaks = measure_peaks()
     line["measured_peaks"] = peaks
     line["roofline"]["frac_of_measured_copy"] = round(achieved / peaks["copy_GBs"], 4)

@@ -599,7 +599,8 @@ def _sample_rows(batch, per_seq=4, seed=0):
     return sorted(set(int(r) for r in rows))
 
 
-@pytest.mark.parametrize("name", ["paged_decode_bf16", "causal_prefill_bf16", "extend_prefill_bf16"])
+@pytest.mark.parametrize("name", ["paged_decode_bf16", "causal_prefill_bf16", "extend_prefill_bf16",
+                                  "mixed_prefill_decode_bf16"])
 def test_named_workload_sampled(name):
     from workloads import NAMED
     b = NAMED[name]()

@@ -251,12 +251,29 @@ def long_prefill_bf16(seed: int = 5, L: int = 32768) -> PagedBatch:
                       extra_blocks=4, name="long_prefill_bf16")
 
 
+def mixed_prefill_decode_bf16(seed: int = 6, n_prefill: int = 2, prefill_len: int = 256, n_decode: int = 30,
+                              lo: int = 128, hi: int = 2048) -> PagedBatch:
+    """One batch mixing both phases, as a serving step schedules them: n_prefill
+    prompts of prefill_len new tokens (no cached prefix) and n_decode sequences
+    with one new token each over contexts U{lo..hi} (the new token included);
+    M = 2 x 256 + 30 x 1 = 542 query rows at the defaults.  Heads and D as the
+    causal prefill workload (32 / 8, D 128)."""
+    def draw(rng):
+        k_dec = rng.integers(lo, hi + 1, size=n_decode)
+        q = np.concatenate([np.full(n_prefill, prefill_len), np.ones(n_decode, np.int64)])
+        k = np.concatenate([np.full(n_prefill, prefill_len), k_dec])
+        return q, k
+    return make_batch(seed, Hq=32, Hkv=8, D=128, dtype="bf16", causal=True, len_draw=draw,
+                      name="mixed_prefill_decode_bf16")
+
+
 NAMED = {
     "tiny_varlen_fp32": tiny_varlen_fp32,
     "paged_decode_bf16": paged_decode_bf16,
     "causal_prefill_bf16": causal_prefill_bf16,
     "extend_prefill_bf16": extend_prefill_bf16,
     "long_prefill_bf16": long_prefill_bf16,
+    "mixed_prefill_decode_bf16": mixed_prefill_decode_bf16,
 }
 
 
