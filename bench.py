@@ -384,6 +384,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time plain launches instead of graph replays")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline decode and prefill workloads (no warm, graph-runner, mixed or peak "
+                         "figures): the profiler runs use it so each kernel name covers one workload")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--counter-command", default="", help="command line recorded with --summarize-counters")
@@ -469,20 +472,22 @@ def main():
     }
     del w
     torch.cuda.empty_cache()
-    # the same decode steps on one replica: K/V may then stay in the 256 MB
-    # Infinity Cache between steps (labelled warm; the headline rotates replicas)
-    w1 = Workload(dec, 1)
-    wms, _, _, _ = time_steps(w1, max(100, args.steps // 4), max(1, args.warmup // 4), fused=True, eager=args.eager)
-    line["warm_one_replica"] = {"ms_per_step": round(wms, 6), "value": round(kvb / (wms * 1e-3) / 1e9, 2),
-                                "unit": "GB/s", "note": "1 replica: K/V can stay in the Infinity Cache"}
-    del w1
-    torch.cuda.empty_cache()
+    if not args.no_extras:
+        # the same decode steps on one replica: K/V may then stay in the 256 MB
+        # Infinity Cache between steps (labelled warm; the headline rotates replicas)
+        w1 = Workload(dec, 1)
+        wms, _, _, _ = time_steps(w1, max(100, args.steps // 4), max(1, args.warmup // 4), fused=True,
+                                  eager=args.eager)
+        line["warm_one_replica"] = {"ms_per_step": round(wms, 6), "value": round(kvb / (wms * 1e-3) / 1e9, 2),
+                                    "unit": "GB/s", "note": "1 replica: K/V can stay in the Infinity Cache"}
+        del w1
+        torch.cuda.empty_cache()
 
-    # graph runner (decode steps replayed from per-bucket graphs): the first 50
-    # sequences of the batch padded to the 64-row bucket with dummy rows, and
-    # all 64 -- replays only (inputs already in the bucket's buffers)
-    line["graph_runner"] = runner_replays(dec, args)
-    log(f"graph runner: {line['graph_runner']}")
+        # graph runner (decode steps replayed from per-bucket graphs): the first 50
+        # sequences of the batch padded to the 64-row bucket with dummy rows, and
+        # all 64 -- replays only (inputs already in the bucket's buffers)
+        line["graph_runner"] = runner_replays(dec, args)
+        log(f"graph runner: {line['graph_runner']}")
 
     if not args.no_prefill:
         pre = causal_prefill_bf16()
@@ -506,7 +511,7 @@ def main():
         del wp
         torch.cuda.empty_cache()
 
-    if not args.no_prefill:
+    if not args.no_prefill and not args.no_extras:
         # a mixed serving step in one launch: 2 prompts x 256 new tokens and 30
         # decode rows over 128..2048-token contexts (M = 542 rows); it runs on
         # the prefill/extend kernel (T != B)
@@ -527,13 +532,14 @@ def main():
         del wm
         torch.cuda.empty_cache()
 
-    peaks = measure_peaks()
-    line["measured_peaks"] = peaks
-    line["roofline"]["frac_of_measured_copy"] = round(achieved / peaks["copy_GBs"], 4)
-    if "prefill" in line:
-        line["prefill"]["frac_of_measured_mfma"] = round(line["prefill"]["achieved"] / peaks["bf16_mfma_TFLOPs"], 4)
+    if not args.no_extras:
+        peaks = measure_peaks()
+        line["measured_peaks"] = peaks
+        line["roofline"]["frac_of_measured_copy"] = round(achieved / peaks["copy_GBs"], 4)
+        if "prefill" in line:
+            line["prefill"]["frac_of_measured_mfma"] = round(line["prefill"]["achieved"] / peaks["bf16_mfma_TFLOPs"], 4)
+        log(f"measured peaks: {peaks}")
     line["env"] = environment()
-    log(f"measured peaks: {peaks}")
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
