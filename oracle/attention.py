@@ -19,6 +19,12 @@ The pages fix what is computed:
   bookkeeping (장부가 커널 인자로 바뀌는 지점과 CUDA graph, "장부에서 텐서로"):
   query length = extend length, key length = the whole length so far.
 * lse (reading): natural log of the sum over visible keys of exp(scale q.k).
+* Sliding window (reading).  The pages list it as one of the mask variants a
+  kernel dispatch must cover and a test must exercise (Transformer 추론 커널
+  (3/10), §19 and §24) without defining it.  Plain reading: with window W >= 1
+  (causal only) the row at position p sees keys max(0, p - W + 1) .. p, the W
+  most recent positions, its own included.  A one-row decode sits at position
+  Lk - 1 and so sees the last W keys.
 """
 from __future__ import annotations
 
@@ -62,14 +68,18 @@ def _validate(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, block_s
 
 
 def attention_oracle(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
-                     scale: float, causal: bool, *, rows: Optional[Sequence[int]] = None,
-                     row_block: int = 2048, block_size: int = BLOCK_SIZE):
+                     scale: float, causal: bool, *, window: int = 0,
+                     rows: Optional[Sequence[int]] = None, row_block: int = 2048,
+                     block_size: int = BLOCK_SIZE):
     """Exact attention, float64.
 
     Arguments mirror the library call: ``q [T, Hq, D]``, ``k_cache``/``v_cache``
     ``[NB, 16, Hkv, D]``, ``block_table int [B, MB]``, ``cu_seqlens_q int [B+1]``,
     ``seqlens_k int [B]``.  Inputs of any float dtype are upcast to float64
     (exact for fp32 and bf16 values).
+
+    ``window`` > 0 narrows the causal mask to the last ``window`` positions of
+    each row (its own included); 0 means no window.
 
     ``rows`` optionally restricts the work to a subset of query tokens (global
     indices into q); rows are independent, so each is still the full definition.
@@ -82,6 +92,9 @@ def attention_oracle(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
     lk_all = np.asarray(seqlens_k, dtype=np.int64)
     _validate(q, k_cache, v_cache, block_table, cu, lk_all, block_size)
+    window = int(window)
+    if window < 0 or (window and not causal):
+        raise ValueError("window must be >= 0, and a window needs the causal mask")
     T, Hq, D = q.shape
     Hkv = k_cache.shape[2]
     G = Hq // Hkv
@@ -107,20 +120,25 @@ def attention_oracle(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
         for c0 in range(0, sel.size, row_block):
             rws = sel[c0:c0 + row_block]
             i = rws - r0                         # row index within the sequence
-            # keys beyond the last visible one of this row block are -inf for
-            # every row in it, so they may be left out without changing anything
+            # keys past the last visible one of this row block, and keys before
+            # the window of its first row, are -inf for every row in it, so they
+            # may be left out without changing anything
             ncols = lk if not (causal and lq > 1) else min(lk, cached + int(i.max()) + 1)
-            visible = np.ones((rws.size, ncols), dtype=bool)
+            k0 = max(0, cached + int(i.min()) - window + 1) if window else 0
+            j = np.arange(k0, ncols)
+            visible = np.ones((rws.size, ncols - k0), dtype=bool)
             if causal and lq > 1:
-                visible = np.arange(ncols)[None, :] <= (cached + i)[:, None]
+                visible = j[None, :] <= (cached + i)[:, None]
+            if window:
+                visible &= j[None, :] >= (cached + i - window + 1)[:, None]
             for h in range(Hq):
                 g = h // G
-                S = scale * (q[rws, h, :] @ Kb[:ncols, g, :].T)      # [rows, keys]
+                S = scale * (q[rws, h, :] @ Kb[k0:ncols, g, :].T)    # [rows, keys]
                 S = np.where(visible, S, -np.inf)
                 m = S.max(axis=1)
                 P = np.exp(S - m[:, None])
                 l = P.sum(axis=1)
-                out[rws, h, :] = (P @ Vb[:ncols, g, :]) / l[:, None]
+                out[rws, h, :] = (P @ Vb[k0:ncols, g, :]) / l[:, None]
                 lse[rws, h] = m + np.log(l)
     return out, lse
 

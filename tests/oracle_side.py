@@ -18,11 +18,12 @@ def oracle_pool(batch: PagedBatch, dtype=np.float64):
                            batch.slots[rows], kc, vc)
 
 
-def oracle_attention(batch: PagedBatch, rows=None, pool=None, causal=None):
+def oracle_attention(batch: PagedBatch, rows=None, pool=None, causal=None, window=None):
     kc, vc = pool if pool is not None else oracle_pool(batch)
     return attention_oracle(batch.q, kc, vc, batch.block_table, batch.cu_seqlens_q,
                             batch.k_lens, batch.scale,
-                            batch.causal if causal is None else causal, rows=rows)
+                            batch.causal if causal is None else causal,
+                            window=batch.window if window is None else window, rows=rows)
 
 
 def gather_loop(cache, table_row, length):

@@ -25,11 +25,15 @@ MUTATIONS = {
     "lse drops max": ("lse[rws, h] = m + np.log(l)", "lse[rws, h] = np.log(l)"),
     "no normalisation": ("/ l[:, None]", "/ 1.0"),
     "scale dropped": ("S = scale * (", "S = ("),
-    "k/v swapped": ("(P @ Vb[:ncols, g, :])", "(P @ Kb[:ncols, g, :])"),
+    "k/v swapped": ("(P @ Vb[k0:ncols, g, :])", "(P @ Kb[k0:ncols, g, :])"),
     "block row index": ("cache[blocks, t % block_size]", "cache[blocks, t // block_size % block_size]"),
     "page index": ("[t // block_size]", "[t % block_size]"),
-    "transposed q/k": ("(q[rws, h, :] @ Kb[:ncols, g, :].T)", "(Kb[:rws.size, g, :] @ q[rws, h, :].T).T[:, :ncols]"),
+    "transposed q/k": ("(q[rws, h, :] @ Kb[k0:ncols, g, :].T)", "(Kb[:rws.size, g, :] @ q[rws, h, :].T).T[:, k0:ncols]"),
     "max not subtracted in lse": ("P = np.exp(S - m[:, None])", "P = np.exp(S)"),
+    "window off by one": (">= (cached + i - window + 1)[:, None]", ">= (cached + i - window)[:, None]"),
+    "window from top-left": (">= (cached + i - window + 1)[:, None]", ">= (i - window + 1)[:, None]"),
+    "window ignored": ("            if window:\n", "            if False:\n"),
+    "window start of the last row": ("cached + int(i.min()) - window + 1", "cached + int(i.max()) - window + 1"),
 }
 
 
@@ -82,6 +86,18 @@ def _battery(attn):
             n = 16 + i + 1
             if abs(lse[i, 0] - math.log(n)) > 1e-12 or np.max(np.abs(out[i, 0] - V[:n, 0].mean(0))) > 1e-12:
                 return False
+        # sliding window: brute force over the band, decode and extend rows
+        for W in (1, 3, 20):
+            b = make_batch(8, [17, 1, 4], [25, 20, 30], Hq=2, Hkv=1, D=4, dtype="fp32", causal=True, window=W)
+            kc, vc = oracle_pool(b)
+            out, lse = attn(b.q, kc, vc, b.block_table, b.cu_seqlens_q, b.k_lens, b.scale, True, window=W)
+            for s in range(b.B):
+                r0, r1 = int(b.cu_seqlens_q[s]), int(b.cu_seqlens_q[s + 1])
+                ks = b.k_tokens[b.cu_seqlens_k[s]:b.cu_seqlens_k[s + 1]]
+                vs = b.v_tokens[b.cu_seqlens_k[s]:b.cu_seqlens_k[s + 1]]
+                bo, bl = _brute(b.q[r0:r1], ks, vs, r1 - r0, int(b.k_lens[s]), b.scale, True, 2, dps=25, window=W)
+                if not (np.max(np.abs(out[r0:r1] - bo)) <= 1e-12 and np.max(np.abs(lse[r0:r1] - bl)) <= 1e-12):
+                    return False
         return True
     except Exception:
         return False

@@ -148,8 +148,9 @@ def test_block_table_permutation():
 
 
 # ---------------------------------------------------------------- P6 ------
-def _brute(q, k_rows, v_rows, lq, lk, scale, causal, G, dps=50):
-    """mpmath loops: softmax(scale q.k + mask) V for one sequence, all heads."""
+def _brute(q, k_rows, v_rows, lq, lk, scale, causal, G, dps=50, window=0):
+    """mpmath loops: softmax(scale q.k + mask) V for one sequence, all heads.
+    ``window`` > 0: the row at position p sees keys max(0, p - window + 1) .. p."""
     import mpmath as mp
 
     mp.mp.dps = dps
@@ -159,17 +160,19 @@ def _brute(q, k_rows, v_rows, lq, lk, scale, causal, G, dps=50):
     lse = np.zeros((lq, Hq))
     for i in range(lq):
         last = (c + i) if (causal and lq > 1) else (lk - 1)
+        first = max(0, c + i - window + 1) if window else 0
+        keys = range(first, last + 1)
         for h in range(Hq):
             g = h // G
-            sc = []
-            for j in range(last + 1):
+            sc = {}
+            for j in keys:
                 acc = mp.mpf(0)
                 for d in range(D):
                     acc += mp.mpf(float(q[i, h, d])) * mp.mpf(float(k_rows[j, g, d]))
-                sc.append(mp.mpf(scale) * acc)
-            z = mp.fsum(mp.exp(x) for x in sc)
+                sc[j] = mp.mpf(scale) * acc
+            z = mp.fsum(mp.exp(sc[j]) for j in keys)
             for d in range(D):
-                num = mp.fsum(mp.exp(sc[j]) * mp.mpf(float(v_rows[j, g, d])) for j in range(last + 1))
+                num = mp.fsum(mp.exp(sc[j]) * mp.mpf(float(v_rows[j, g, d])) for j in keys)
                 out[i, h, d] = float(num / z)
             lse[i, h] = float(mp.log(z))
     return out, lse
@@ -426,3 +429,145 @@ def test_validation_errors():
         attention_oracle(b.q[:, :3], kc, vc, b.block_table, b.cu_seqlens_q, b.k_lens, b.scale, True)
     with pytest.raises(ValueError):
         attention_oracle(b.q, kc, vc, b.block_table, np.array([0, 3, 4]), b.k_lens, b.scale, True)
+
+
+# ---------------------------------------------------------------- W1-W6 ----
+# Sliding window (reading: with window W the row at position p sees keys
+# max(0, p - W + 1) .. p; a one-row decode sits at position Lk - 1).
+def _rows_and_positions(b):
+    for s in range(b.B):
+        lq, lk = int(b.q_lens[s]), int(b.k_lens[s])
+        for i in range(lq):
+            yield s, int(b.cu_seqlens_q[s]) + i, lk - lq + i
+
+
+def test_window_one_is_own_row():
+    """W = 1: a row sees its own position only, so out = v_p bitwise and
+    lse = scale q.k_p -- for prefill rows, extend rows and decode rows alike."""
+    b = _mk(51, [17, 1, 5, 1], [17, 33, 40, 1], Hq=4, Hkv=2, D=8, window=1)
+    out, lse = oracle_attention(b)
+    G = b.Hq // b.Hkv
+    for s, r, p in _rows_and_positions(b):
+        kt = b.k_tokens[int(b.cu_seqlens_k[s]) + p].astype(np.float64)
+        vt = b.v_tokens[int(b.cu_seqlens_k[s]) + p].astype(np.float64)
+        for h in range(b.Hq):
+            assert np.array_equal(out[r, h], vt[h // G])
+            ref = b.scale * float(np.dot(b.q[r, h].astype(np.float64), kt[h // G]))
+            assert abs(lse[r, h] - ref) <= 1e-15 * max(1.0, abs(ref))
+
+
+def test_window_two_closed_form():
+    """W = 2: a row at p >= 1 sees keys p - 1 and p.  With s = scale q.k the
+    weight of key p is the logistic 1 / (1 + e^(s_{p-1} - s_p)) and
+    lse = ln(e^(s_{p-1}) + e^(s_p)); the row at position 0 sees key 0 alone."""
+    b = _mk(52, [18, 1, 3], [18, 50, 16], Hq=2, Hkv=1, D=8, window=2)
+    out, lse = oracle_attention(b)
+    for s, r, p in _rows_and_positions(b):
+        base = int(b.cu_seqlens_k[s])
+        for h in range(b.Hq):
+            qv = b.q[r, h].astype(np.float64)
+            sp = b.scale * float(np.dot(qv, b.k_tokens[base + p, 0].astype(np.float64)))
+            vp = b.v_tokens[base + p, 0].astype(np.float64)
+            if p == 0:
+                ref_o, ref_l = vp, sp
+            else:
+                s1 = b.scale * float(np.dot(qv, b.k_tokens[base + p - 1, 0].astype(np.float64)))
+                w = 1.0 / (1.0 + math.exp(s1 - sp))
+                ref_o = w * vp + (1.0 - w) * b.v_tokens[base + p - 1, 0].astype(np.float64)
+                ref_l = max(s1, sp) + math.log1p(math.exp(-abs(s1 - sp)))
+            assert np.max(np.abs(out[r, h] - ref_o)) <= 1e-13
+            assert abs(lse[r, h] - ref_l) <= 1e-13
+
+
+@pytest.mark.parametrize("W", [3, 16, 17])
+def test_window_zero_query_is_window_mean(W):
+    """Q = 0 makes every visible score 0: out is the plain mean of the V rows of
+    positions max(0, p - W + 1) .. p and lse = ln(min(p + 1, W))."""
+    b = _mk(53, [9, 40, 1], [9, 60, 35], Hq=4, Hkv=2, D=8, window=W)
+    b.q[:] = 0.0
+    out, lse = oracle_attention(b)
+    G = b.Hq // b.Hkv
+    for s, r, p in _rows_and_positions(b):
+        V = b.v_tokens[int(b.cu_seqlens_k[s]):int(b.cu_seqlens_k[s + 1])].astype(np.float64)
+        lo = max(0, p - W + 1)
+        for h in range(b.Hq):
+            assert np.max(np.abs(out[r, h] - V[lo:p + 1, h // G].mean(axis=0))) <= TOL
+            assert abs(lse[r, h] - math.log(p + 1 - lo)) <= TOL
+
+
+@pytest.mark.parametrize("W", [1, 5, 16, 17, 33, 1000])
+def test_window_torch_sdpa_float64(W):
+    """CPU torch SDPA in float64 with an explicit band mask (j <= p and
+    j >= p - W + 1) and enable_gqa."""
+    import torch
+    import torch.nn.functional as F
+
+    b = _mk(54, [17, 9, 40, 1, 1], [17, 30, 64, 77, 5], Hq=8, Hkv=2, D=16, window=W)
+    kc, vc = oracle_pool(b)
+    out, lse = oracle_attention(b, pool=(kc, vc))
+    for s in range(b.B):
+        lq, lk = int(b.q_lens[s]), int(b.k_lens[s])
+        r0 = int(b.cu_seqlens_q[s])
+        K = torch.from_numpy(gather_loop(kc, b.block_table[s], lk)).permute(1, 0, 2)[None]
+        V = torch.from_numpy(gather_loop(vc, b.block_table[s], lk)).permute(1, 0, 2)[None]
+        Q = torch.from_numpy(b.q[r0:r0 + lq].astype(np.float64)).permute(1, 0, 2)[None]
+        pos = (lk - lq + torch.arange(lq))[:, None]
+        j = torch.arange(lk)[None, :]
+        mask = (j <= pos) & (j >= pos - W + 1)
+        ref = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=b.scale, enable_gqa=True)
+        assert np.max(np.abs(out[r0:r0 + lq] - ref[0].permute(1, 0, 2).numpy())) <= 1e-12
+
+
+@pytest.mark.parametrize("case", [
+    dict(seed=55, q=[17, 9], k=[17, 30], W=4),
+    dict(seed=56, q=[1, 1, 20], k=[19, 3, 33], W=16),
+    dict(seed=57, q=[5, 2], k=[40, 18], W=17),
+])
+def test_window_bruteforce_mpmath(case):
+    """The windowed oracle equals the 50-digit brute force with the same band."""
+    b = _mk(case["seed"], case["q"], case["k"], Hq=4, Hkv=2, D=4, window=case["W"])
+    out, lse = oracle_attention(b)
+    for s in range(b.B):
+        r0, r1 = int(b.cu_seqlens_q[s]), int(b.cu_seqlens_q[s + 1])
+        ks = b.k_tokens[b.cu_seqlens_k[s]:b.cu_seqlens_k[s + 1]]
+        vs = b.v_tokens[b.cu_seqlens_k[s]:b.cu_seqlens_k[s + 1]]
+        bo, bl = _brute(b.q[r0:r1], ks, vs, r1 - r0, int(b.k_lens[s]), b.scale, True, 2, window=case["W"])
+        assert np.max(np.abs(out[r0:r1] - bo)) <= TOL
+        assert np.max(np.abs(lse[r0:r1] - bl)) <= TOL
+
+
+def test_window_wider_than_every_row_is_causal():
+    """A window that covers every row's whole prefix (W >= Lk) changes nothing:
+    the band is then the causal mask itself."""
+    b = _mk(58, [17, 1, 9], [17, 40, 64], Hq=4, Hkv=2, D=8)
+    kc, vc = oracle_pool(b)
+    o0, l0 = oracle_attention(b, pool=(kc, vc), window=0)
+    o1, l1 = oracle_attention(b, pool=(kc, vc), window=64)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_window_keys_outside_the_band_are_never_read():
+    """Poisoning (NaN) the K/V rows below every row's window start leaves the
+    result finite and unchanged."""
+    W = 8
+    b = _mk(59, [5, 1], [40, 37], Hq=2, Hkv=1, D=8, window=W)
+    kc, vc = oracle_pool(b)
+    out0, lse0 = oracle_attention(b, pool=(kc, vc))
+    kc2, vc2 = kc.copy(), vc.copy()
+    for s in range(b.B):
+        lq, lk = int(b.q_lens[s]), int(b.k_lens[s])
+        for t in range(max(0, lk - lq - W + 1)):
+            blk = int(b.block_table[s, t // BLOCK_SIZE])
+            kc2[blk, t % BLOCK_SIZE] = np.nan
+            vc2[blk, t % BLOCK_SIZE] = np.nan
+    out1, lse1 = oracle_attention(b, pool=(kc2, vc2))
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+def test_window_needs_causal():
+    b = _mk(60, [3], [3], Hq=2, Hkv=1, D=8, causal=False)
+    kc, vc = oracle_pool(b)
+    with pytest.raises(ValueError):
+        attention_oracle(b.q, kc, vc, b.block_table, b.cu_seqlens_q, b.k_lens, b.scale, False, window=2)
+    with pytest.raises(ValueError):
+        attention_oracle(b.q, kc, vc, b.block_table, b.cu_seqlens_q, b.k_lens, b.scale, True, window=-1)

@@ -59,6 +59,7 @@ class PagedBatch:
     slots: np.ndarray          # int32 [sum k_lens], slot of every key token
     name: str = ""
     meta: dict = field(default_factory=dict)
+    window: int = 0            # sliding window (causal only): row at position p sees keys p-window+1 .. p; 0 = none
 
     # ---- derived views -------------------------------------------------
     @property
@@ -126,6 +127,7 @@ def make_batch(
     len_draw=None,
     name: str = "",
     shared_prefix_blocks: int = 0,
+    window: int = 0,
 ) -> PagedBatch:
     """Draw one batch.
 
@@ -206,6 +208,7 @@ def make_batch(
         cu_seqlens_q=cu_q.astype(np.int32), cu_seqlens_k=cu_k.astype(np.int32),
         block_table=table.astype(np.int32), num_blocks=NB, poison_block=poison,
         q=q, k_tokens=k_tok, v_tokens=v_tok, slots=slots.astype(np.int32), name=name,
+        window=int(window),
     )
 
 
@@ -282,9 +285,13 @@ def attention_flops(batch: PagedBatch) -> int:
     (2*D for the score, 2*D for the weighted sum of V).  Masked pairs and the
     softmax's exp/max/rescale are not counted."""
     pairs = 0
+    W = int(batch.window)
     for b in range(batch.B):
         lq, lk = int(batch.q_lens[b]), int(batch.k_lens[b])
-        if batch.causal and lq > 1:
+        if W:
+            pos = np.arange(lk - lq, lk, dtype=np.int64)   # row positions
+            pairs += int(np.minimum(pos + 1, W).sum())
+        elif batch.causal and lq > 1:
             c = lk - lq
             pairs += lq * c + lq * (lq + 1) // 2
         else:
@@ -293,9 +300,14 @@ def attention_flops(batch: PagedBatch) -> int:
 
 
 def kv_bytes(batch: PagedBatch) -> int:
-    """K and V bytes that attention must read once: every visible key row of every KV head."""
+    """K and V bytes that attention must read once: every key row some query row
+    sees, of every KV head (with a window: keys from the first row's window start)."""
     esize = 2 if batch.dtype == "bf16" else 4
-    return int(2 * int(batch.k_lens.sum()) * batch.Hkv * batch.D * esize)
+    keys = batch.k_lens.astype(np.int64)
+    if batch.window:
+        first = np.maximum(0, keys - batch.q_lens.astype(np.int64) - int(batch.window) + 1)
+        keys = keys - first
+    return int(2 * int(keys.sum()) * batch.Hkv * batch.D * esize)
 
 
 def io_bytes(batch: PagedBatch) -> int:
