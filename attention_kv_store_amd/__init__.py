@@ -4,7 +4,10 @@ Python names mirror the C ABI (include/kvstore.h):
 
 * ``kv_store_paged(k_new, v_new, slot_mapping, k_cache, v_cache)``
 * ``attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
-  scale, causal, out=None, lse=None, ...)``
+  scale, causal, out=None, lse=None, ...)`` (``window=W`` selects the
+  sliding-window entry point ``attn_varlen_paged_window_ex``)
+* ``attn_decode_append_paged(q, k_new, v_new, k_cache, v_cache, block_table,
+  seqlens_k, scale, ...)`` (``window=W``: ``attn_decode_append_paged_window``)
 
 They take torch tensors on the current HIP device (torch supplies memory and
 the stream) and enqueue the library's kernels on torch's current stream.  The
@@ -76,16 +79,20 @@ def workspace_size(q, k_cache, block_table, *, max_seqlen_q=0, max_seqlen_k=0, n
 def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale: float,
                       causal: bool = True, out=None, lse=None, *, return_lse: bool = True,
                       max_seqlen_q: int = 0, max_seqlen_k: int = 0, num_splits: int = 0,
-                      workspace=None):
+                      workspace=None, window: int = 0):
     """Exact paged varlen attention.  Returns ``(out, lse)`` (lse is None when
     ``return_lse`` is False and no ``lse`` tensor was given).
 
     Uses the allocation-free ``attn_varlen_paged_ex`` entry point with the
     workspace passed in, which must have been zero-filled before its first use
     and be at least ``workspace_size`` bytes (the library checks), or else a
-    torch-allocated one of the size needed."""
+    torch-allocated one of the size needed.  ``window`` > 0 (needs ``causal``)
+    calls ``attn_varlen_paged_window_ex``: the row at position p sees keys
+    p - window + 1 .. p."""
     import torch
 
+    if window and not causal:
+        raise ValueError("a sliding window needs the causal mask")
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(q)
@@ -94,9 +101,14 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
     h = _hints(max_seqlen_q, max_seqlen_k, num_splits)
     ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
     d = [_desc(q), _desc(k_cache), _desc(v_cache), _desc(block_table), _desc(cu_seqlens_q), _desc(seqlens_k)]
-    st = lib.attn_varlen_paged_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)),
-                                  _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
-                                  _stream(q))
+    if window:
+        st = lib.attn_varlen_paged_window_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(window),
+                                             _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr,
+                                             ws_bytes, _stream(q))
+    else:
+        st = lib.attn_varlen_paged_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)),
+                                      _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
+                                      _stream(q))
     _lib.check(st)
     return out, lse
 
@@ -122,12 +134,13 @@ def _workspace(lib, q, k_cache, block_table, h, workspace):
 
 def attn_decode_append_paged(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale: float,
                              out=None, lse=None, *, return_lse: bool = True, max_seqlen_k: int = 0,
-                             num_splits: int = 0, workspace=None):
+                             num_splits: int = 0, workspace=None, window: int = 0):
     """One decode step in one launch: writes row b of ``k_new`` / ``v_new`` as
     key ``seqlens_k[b] - 1`` of sequence b (its slot taken from the block
-    table) and attends query row b over the sequence's ``seqlens_k[b]`` keys.
-    Same result as ``kv_store_paged`` then ``attn_varlen_paged`` with
-    ``cu_seqlens_q = 0..B``.  Returns ``(out, lse)``."""
+    table) and attends query row b over the sequence's ``seqlens_k[b]`` keys
+    (the last ``window`` of them when ``window`` > 0).  Same result as
+    ``kv_store_paged`` then ``attn_varlen_paged`` with ``cu_seqlens_q = 0..B``.
+    Returns ``(out, lse)``."""
     import torch
 
     lib = _lib.load()
@@ -139,8 +152,13 @@ def attn_decode_append_paged(q, k_new, v_new, k_cache, v_cache, block_table, seq
     ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
     d = [_desc(q), _desc(k_new), _desc(v_new), _desc(k_cache), _desc(v_cache), _desc(block_table),
          _desc(seqlens_k)]
-    st = lib.attn_decode_append_paged(*[_ref(x) for x in d], ctypes.c_float(scale), _ref(_desc(out)),
-                                      _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes, _stream(q))
+    if window:
+        st = lib.attn_decode_append_paged_window(*[_ref(x) for x in d], ctypes.c_float(scale), int(window),
+                                                 _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr,
+                                                 ws_bytes, _stream(q))
+    else:
+        st = lib.attn_decode_append_paged(*[_ref(x) for x in d], ctypes.c_float(scale), _ref(_desc(out)),
+                                          _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes, _stream(q))
     _lib.check(st)
     return out, lse
 

@@ -25,6 +25,8 @@ EXPORTS = (
     "attn_varlen_paged_workspace_size",
     "attn_varlen_paged_ex",
     "attn_decode_append_paged",
+    "attn_varlen_paged_window_ex",
+    "attn_decode_append_paged_window",
     "kvs_last_error",
     "kvs_last_dispatch",
     "kvs_release_workspace",
@@ -84,6 +86,12 @@ def load(path: str = LIB_PATH):
     lib.attn_decode_append_paged.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, P,
                                              ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
     lib.attn_decode_append_paged.restype = st
+    lib.attn_varlen_paged_window_ex.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, P, P,
+                                                ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
+    lib.attn_varlen_paged_window_ex.restype = st
+    lib.attn_decode_append_paged_window.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, P, P,
+                                                    ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
+    lib.attn_decode_append_paged_window.restype = st
     lib.kvs_last_error.argtypes = []
     lib.kvs_last_error.restype = ctypes.c_char_p
     lib.kvs_last_dispatch.argtypes = []

@@ -3,6 +3,7 @@
 // call, so every error path can be exercised on a machine without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -108,7 +109,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
                      const kvs_tensor* table, const kvs_tensor* cu, const kvs_tensor* lk, float scale,
                      int causal, const kvs_tensor* out, const kvs_tensor* lse, const kvs_hints* hints,
-                     bool sizing_only, Plan* plan, bool append = false) {
+                     bool sizing_only, Plan* plan, bool append = false, int window = 0) {
   KVS_TRY(check_tensor(q, "q", kFloatTypes, 3));
   KVS_TRY(check_tensor(k_cache, "k_cache", kFloatTypes, 4));
   KVS_TRY(check_tensor(table, "block_table", kIntTypes, 2));
@@ -148,6 +149,14 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     }
     if (!std::isfinite(scale)) return fail(KVS_ERR_INVALID, "scale must be finite");
   }
+  if (window < 0 || (window > 0 && !causal)) return fail(KVS_ERR_INVALID, "window must be >= 1 and needs the causal mask");
+  if (window > 0) {
+    // every key index is below 16 * MB, so a wider window is the same mask;
+    // with both below 2^30 the kernels' window arithmetic stays in 32 bits
+    if (16 * MB > (int64_t(1) << 30))
+      return fail(KVS_ERR_UNSUPPORTED, "a sliding window needs 16 * MB <= 2^30 (MB = %lld)", (long long)MB);
+    window = (int)std::min<int64_t>(window, 16 * MB);
+  }
 
   kvs::AttnParams& p = plan->p;
   p = kvs::AttnParams{};
@@ -168,6 +177,7 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   p.G = (int32_t)(Hq / Hkv);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal ? 1 : 0;
+  p.window = window;
   plan->dt = q->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32;
   plan->D = (int)D;
   plan->decode = (T == B);
@@ -292,6 +302,10 @@ kvs_status get_plain_workspace(size_t need, void** out) {
   return KVS_OK;
 }
 
+std::string window_note(const kvs::AttnParams& p) {
+  return p.window > 0 ? " sliding_window=" + std::to_string(p.window) : std::string();
+}
+
 kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   kvs::AttnParams& p = plan.p;
   if (plan.decode) {
@@ -305,8 +319,8 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
     }
     const hipError_t e = kvs::launch_decode(p, plan.dt, plan.D, stream);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-    set_dispatch("decode_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
-                 plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window");
+    set_dispatch("decode_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
+                 plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window", window_note(p).c_str());
     return KVS_OK;
   }
   int cus = 0;
@@ -314,9 +328,9 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   p.pgrid = (p.pnw == 8 ? 1 : 2) * cus;
   const hipError_t e = kvs::launch_prefill(p, plan.dt, plan.D, stream);
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
-  set_dispatch("prefill_%s_d%d grid=%d (persistent) waves/wg=%d head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d",
+  set_dispatch("prefill_%s_d%d grid=%d (persistent) waves/wg=%d head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d%s",
                plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.pgrid, p.pnw, p.NHG, p.HW, 32 * p.TPW,
-               p.meta_lds);
+               p.meta_lds, window_note(p).c_str());
   return KVS_OK;
 }
 
@@ -388,17 +402,19 @@ size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k
   return plan.ws_bytes;
 }
 
-kvs_status attn_decode_append_paged(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
-                                    kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
-                                    const kvs_tensor* seqlens_k, float scale, kvs_tensor* out, kvs_tensor* lse,
-                                    const kvs_hints* hints, void* workspace, size_t workspace_bytes,
-                                    kvs_stream_t stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                         kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
+                         const kvs_tensor* seqlens_k, float scale, int window, kvs_tensor* out, kvs_tensor* lse,
+                         const kvs_hints* hints, void* workspace, size_t workspace_bytes, kvs_stream_t stream) {
   if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
     return fail(KVS_ERR_INVALID, "hints must be non-negative");
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, nullptr, seqlens_k, scale, 1, out, lse, hints, false,
-                    &plan, true));
+                    &plan, true, window));
   KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3));
   KVS_TRY(check_tensor(v_new, "v_new", kFloatTypes, 3));
   for (int i = 0; i < 3; ++i)
@@ -414,10 +430,35 @@ kvs_status attn_decode_append_paged(const kvs_tensor* q, const kvs_tensor* k_new
   p.v_cache_w = v_cache->data;
   p.append = 1;
   KVS_TRY(run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream)));
-  set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s",
+  set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s",
                plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg,
-               p.dsmall ? "whole" : "window");
+               p.dsmall ? "whole" : "window", window_note(p).c_str());
   return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvs_status attn_decode_append_paged(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                    kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
+                                    const kvs_tensor* seqlens_k, float scale, kvs_tensor* out, kvs_tensor* lse,
+                                    const kvs_hints* hints, void* workspace, size_t workspace_bytes,
+                                    kvs_stream_t stream) {
+  g_err.clear();
+  return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, 0, out, lse, hints,
+                       workspace, workspace_bytes, stream);
+}
+
+kvs_status attn_decode_append_paged_window(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                           kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
+                                           const kvs_tensor* seqlens_k, float scale, int32_t window, kvs_tensor* out,
+                                           kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                           size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  if (window < 1) return fail(KVS_ERR_INVALID, "window must be >= 1 (got %d)", (int)window);
+  return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, window, out, lse, hints,
+                       workspace, workspace_bytes, stream);
 }
 
 kvs_status attn_varlen_paged_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
@@ -431,6 +472,21 @@ kvs_status attn_varlen_paged_ex(const kvs_tensor* q, const kvs_tensor* k_cache, 
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, hints,
                     false, &plan));
+  return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                       const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
+                                       const kvs_tensor* seqlens_k, float scale, int32_t window, kvs_tensor* out,
+                                       kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                       size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
+    return fail(KVS_ERR_INVALID, "hints must be non-negative");
+  if (window < 1) return fail(KVS_ERR_INVALID, "window must be >= 1 (got %d)", (int)window);
+  Plan plan;
+  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, 1, out, lse, hints, false,
+                    &plan, false, window));
   return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -7,7 +7,8 @@
 // (same page, §16), with the running-statistics update of §12.
 //
 // Work split.  The key blocks of the whole batch, laid end to end in sequence
-// order (sequence b owns ceil(Lk_b / 16) of them), are cut into `nwg` equal
+// order (sequence b owns ceil(Lk_b / 16) of them; under a sliding window only
+// those from the window's first block on), are cut into `nwg` equal
 // contiguous ranges, one per workgroup, so every workgroup streams the same
 // number of bytes whatever the length mix, and the grid is sized to be
 // resident in one round (8 waves per CU on 256 CUs).  A range covers the tail
@@ -78,6 +79,11 @@ __device__ __forceinline__ int64_t udiv_small(uint64_t x, uint32_t d) {
   if ((x >> 32) == 0) return (int64_t)((uint32_t)x / d);
   return (int64_t)(x / d);
 }
+// Sliding window W > 0: a sequence of L keys attends to keys L - W .. L - 1
+// only, so only its blocks from (L - W) / 16 on enter the flattened axis.
+__device__ __forceinline__ int first_block(int L, int W) { return W > 0 ? max(0, L - W) >> 4 : 0; }
+__device__ __forceinline__ int seq_blocks(int L, int W) { return ((L + 15) >> 4) - first_block(L, W); }
+
 // Start of range w on the flattened block axis: floor(w * total / nwg).
 __device__ __forceinline__ int64_t range_start64(int64_t w, int total, int nwg) {
   return udiv_small((uint64_t)w * (uint32_t)total, (uint32_t)nwg);
@@ -144,18 +150,20 @@ struct DecodeWave {
   }
 
   // s[j][r] holds the score of key k0 + 16 j + 4 grp + r for query column col;
-  // on return it holds exp2(scaled score - running max).  Keys at or past
-  // kend get a masked score by select (their K may be garbage).
+  // on return it holds exp2(scaled score - running max).  Keys outside
+  // [klo, kend) get a masked score by select (their K may be garbage).  Every
+  // step holds at least one key of that range.
   template <int NB>
-  __device__ __forceinline__ void softmax_update(f32x4 (&s)[NB], int k0, int kend) {
+  __device__ __forceinline__ void softmax_update(f32x4 (&s)[NB], int k0, int kend, int klo) {
     float mt = kMaskedScore;
-    const bool tail = k0 + 16 * NB > kend;
+    const bool edge = k0 + 16 * NB > kend || k0 < klo;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float x = s[j][r] * p.scale_log2;
-        if (tail) x = (k0 + 16 * j + grp * 4 + r < kend) ? x : kMaskedScore;
+        const int key = k0 + 16 * j + grp * 4 + r;
+        if (edge) x = (key < kend && key >= klo) ? x : kMaskedScore;
         s[j][r] = x;
         mt = fmaxf(mt, x);
       }
@@ -301,10 +309,14 @@ struct DecodeWave {
     }
   }
 
+  // first key of sequence st.b that the query row sees (the window's start)
+  __device__ __forceinline__ int first_key(const Step& st) const { return p.window > 0 ? max(0, st.Lk - p.window) : 0; }
+
   __device__ __forceinline__ void compute(const Step& st, const Buf& bf) {
     const int k0 = st.lblk * 16;
     const int kend = min(st.Lk, (st.lblk + st.nblk) * 16);
-    const bool tail = k0 + 16 * C::NBS > kend;
+    const int klo = first_key(st);
+    const bool edge = k0 + 16 * C::NBS > kend || k0 < klo;
     const u32x4 zero = {0, 0, 0, 0};
     // V^T into the slab: word (V[2kp][d], V[2kp+1][d]) at row d, key pair kp.
     // The slab is private to this wave and LDS operations of one wave execute
@@ -313,8 +325,9 @@ struct DecodeWave {
 #pragma unroll
     for (int j = 0; j < C::NBS; ++j) {
       const int kp = lane & 7;
-      const bool v0_ok = !tail || k0 + 16 * j + 2 * kp < kend;
-      const bool v1_ok = !tail || k0 + 16 * j + 2 * kp + 1 < kend;
+      const int kv = k0 + 16 * j + 2 * kp;
+      const bool v0_ok = !edge || (kv < kend && kv >= klo);
+      const bool v1_ok = !edge || (kv + 1 < kend && kv + 1 >= klo);
 #pragma unroll
       for (int it = 0; it < C::VIL; ++it) {
         const int dch = (lane >> 3) + 8 * it;
@@ -338,7 +351,7 @@ struct DecodeWave {
 #pragma unroll
       for (int i = 0; i < C::KI; ++i) s[j] = mfma16x16x32_bf16(bf.k[j][i], q[i], s[j]);
     }
-    softmax_update<C::NBS>(s, k0, kend);
+    softmax_update<C::NBS>(s, k0, kend, klo);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int j = 0; j < C::NBS; ++j) {
@@ -366,6 +379,7 @@ struct DecodeWave {
     const float* kb = reinterpret_cast<const float*>(kbase);
     const float* vb = reinterpret_cast<const float*>(vbase);
     const int kend = min(st.Lk, (st.lblk + st.nblk) * 16);
+    const int klo = first_key(st);
     // append: key kl = Lk - 1 comes from the new row
     const int kl = st.Lk - 1;
     const float* kn = nullptr;
@@ -391,11 +405,11 @@ struct DecodeWave {
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[0] = mfma16x16x4_f32(__uint_as_float(w[e]), qv[c4 * 4 + e], s[0]);
       }
-      softmax_update<1>(s, kb0, kend);
+      softmax_update<1>(s, kb0, kend, klo);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = grp * 4 + r;
-        const bool ok = kb0 + key < kend;
+        const bool ok = kb0 + key < kend && kb0 + key >= klo;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
           float v = vblk[key * tok_stride + db * 16 + col];
@@ -658,7 +672,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     for (int i = (nt & ~3) + tid; i < nt; i += nthr) tbl[i] = p.table[i];
     if (wave == 0) {
       const int L = lane < B ? p.lens_k[lane] : 0;
-      const int nb = (L + 15) >> 4;
+      const int nb = seq_blocks(L, p.window);
       const int x = wave_inclusive_sum(nb);
       if (lane < B) {
         slens[lane] = L;
@@ -673,14 +687,14 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     for (int b = tid; b < B; b += nthr) slens[b] = p.lens_k[b];
     __syncthreads();
 
-    // ---- exclusive prefix of ceil(Lk_b / 16) over the batch, in LDS ---------
+    // ---- exclusive prefix of the blocks per sequence over the batch, in LDS --
     {
       const int per = (B + nthr - 1) / nthr;
       const int b0 = tid * per;
       int run = 0;
       for (int i = 0; i < per; ++i) {
         const int b = b0 + i;
-        if (b < B) run += (slens[b] + 15) >> 4;
+        if (b < B) run += seq_blocks(slens[b], p.window);
       }
       const int x = wave_inclusive_sum(run);
       if (lane == 63) wtot[wave] = x;
@@ -692,7 +706,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
         const int b = b0 + i;
         if (b < B) {
           sstart[b] = acc;
-          acc += (slens[b] + 15) >> 4;
+          acc += seq_blocks(slens[b], p.window);
         }
       }
       if (tid == nthr - 1) sstart[B] = acc;
@@ -724,7 +738,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     for (int i = tid; i < r1 - r0; i += nthr) {
       const int gb = r0 + i;
       const int b = seq_of(gb);
-      tbl[i] = p.table[(int64_t)b * p.MB + (gb - sstart[b])];
+      tbl[i] = p.table[(int64_t)b * p.MB + (gb - sstart[b]) + first_block(slens[b], p.window)];
     }
     __syncthreads();
   }
@@ -769,7 +783,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     st.b = sb;
     st.t = sb;   // one query row per sequence: cu_seqlens_q[b] = b
     st.Lk = slens[sb];
-    st.lblk = pos - s0;
+    st.lblk = pos - s0 + first_block(st.Lk, p.window);
     st.nblk = end - pos;
     st.gblk = pos;
     st.first = pos == max(seg_lo(seg), s0) ? 1 : 0;

@@ -33,6 +33,9 @@ struct AttnParams {
   int32_t G;              // Hq / Hkv
   float scale_log2;       // scale * log2(e): scores are kept in base-2 units
   int32_t causal;
+  // sliding window (needs causal): the row at position p sees keys
+  // p - window + 1 .. p; 0 = no window
+  int32_t window;
   // prefill work map
   int32_t HW;             // query heads per workgroup (divides G)
   int32_t TPW;            // 32-token blocks per workgroup (HW * TPW == 4 waves)

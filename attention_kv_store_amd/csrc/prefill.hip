@@ -28,6 +28,11 @@
 //    table entries past a sequence's last block are never used.
 //  * Causal (bottom-right, with cached prefix c = Lk - Lq): tiles wholly above
 //    a wave's rows are skipped; only tiles crossing the diagonal are masked.
+//  * Sliding window W (the WIN instantiations): the row at position p sees
+//    keys p - W + 1 .. p.  An item's key tiles start at the tile holding its
+//    first row's window start; rows before that start are copied as zero rows
+//    (their table entries are never read), tiles wholly below a wave's
+//    windows are skipped, and tiles crossing a window's lower edge are masked.
 #include <atomic>
 #include <type_traits>
 
@@ -92,7 +97,7 @@ __device__ __attribute__((aligned(16))) uint16_t g_zero_row[128];
 // entries one step earlier, and the next item's Q rows as soon as the last
 // score tile of the current item is formed, so moving to a new item costs
 // about what moving to a new key tile does.
-template <int D, bool BF16, int NW>
+template <int D, bool BF16, int NW, bool WIN>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(AttnParams p) {
   using C = PCfg<D, BF16, NW>;
   using E = typename std::conditional<BF16, uint16_t, float>::type;
@@ -163,6 +168,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     int kvh;           // KV head of the head group
     int q0, Lq, Lk;
     int nkeys, ntiles, npages;
+    int klo, t0;       // first key any row of the item sees, its key tile (0 without a window)
   };
   auto meta = [&](int b, int& q0, int& q1, int& lk) __attribute__((always_inline)) {
     // uniform values: readfirstlane keeps the item state in scalar registers
@@ -219,6 +225,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       it.nkeys = p.causal ? min(lk, cached + tlast + 1) : lk;
       it.ntiles = (it.nkeys + C::BN - 1) / C::BN;
       it.npages = (it.nkeys + 15) >> 4;
+      it.klo = WIN ? max(0, cached + tile * TW - p.window + 1) : 0;
+      it.t0 = it.klo / C::BN;
       break;
     }
     it.r = r;
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       x.t = s.t + 1;
     } else {
       x.it = item_from(s.it.r + 1);
-      x.t = 0;
+      x.t = x.it.t0;
     }
     return x;
   };
@@ -246,13 +254,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // ---- staging helpers ----------------------------------------------------
   // Block-table entries of step s: lane i holds entry t * NPG + (i % NPG)
-  // (index clamped to the sequence's last page; issue_loads replaces entries
-  // past it by block 0).  A vector load, so waiting for it is counted with the
-  // other global loads and never holds up an LDS read.
+  // (index clamped to the item's first page -- the one holding klo -- and to
+  // the sequence's last page; issue_loads replaces entries past it by block
+  // 0).  A vector load, so waiting for it is counted with the other global
+  // loads and never holds up an LDS read.
   auto load_pages = [&](const Step& s) -> int {
     if (s.it.ntiles == 0) return 0;
     const int32_t* trow = p.table + (int64_t)s.it.b * p.MB;
-    return trow[min(s.t * C::NPG + (lane & (C::NPG - 1)), s.it.npages - 1)];
+    int e = s.t * C::NPG + (lane & (C::NPG - 1));
+    if constexpr (WIN) e = max(e, s.it.klo >> 4);
+    return trow[min(e, s.it.npages - 1)];
   };
   // Chunk it of a K row-major tile: key row j = (it * NTH + tid) / CPR of the
   // tile (its page index is the same across a wave), 16-byte chunk ch.
@@ -288,7 +299,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   // K/V of step s: bf16 -> 16-byte global-to-LDS copies straight into stage
   // `buf` (each wave writes KIT whole 1 KiB blocks of each tile; key rows at
-  // or past nkeys copy the zero row); fp32 -> registers, see write_stage.
+  // or past nkeys, or before klo, copy the zero row); fp32 -> registers, see
+  // write_stage.
   // Raw addresses stay readable: a row past nkeys lies in an owned block or,
   // past the last owned page, in block 0.
   auto issue_loads = [&](int pgv, const Step& s, int buf) {
@@ -303,17 +315,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const E* kpage = kbase + pk * page_stride;
       const E* vpage = vbase + pk * page_stride;
       const int kv0 = s.t * C::BN;
-      // keys at or past nkeys (only in an item's last tile) copy the zero row
-      const bool tail = kv0 + wave * C::KPW + C::KPW > s.it.nkeys;   // uniform
+      // keys at or past nkeys (only in an item's last tile) and keys before
+      // klo (only in its first tiles) copy the zero row
+      bool edge = kv0 + wave * C::KPW + C::KPW > s.it.nkeys;   // uniform
+      if constexpr (WIN) edge = edge || kv0 + wave * C::KPW < s.it.klo;
       const E* zero = reinterpret_cast<const E*>(g_zero_row);
 #pragma unroll
       for (int j = 0; j < C::KIT; ++j) {
         const int blk = wave * C::KIT + j;   // 1 KiB block of each tile
         const E* ks = kpage + kpo[j];
         const E* vs = vpage + vpo[j];
-        if (tail) {
+        if (edge) {
           const int key = wave * C::KPW + (j * 64 + lane) / C::CPR;
-          const bool live = kv0 + key < s.it.nkeys;
+          const bool live = kv0 + key < s.it.nkeys && (!WIN || kv0 + key >= s.it.klo);
           const int slot = (j * 64 + lane) % C::CPR;
           ks = live ? ks : zero + (slot ^ C::kswz(key)) * 8;
           vs = live ? vs : zero + (slot ^ C::vswz(key)) * 8;
@@ -340,21 +354,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
   // fp32: writes step s's registers to LDS buffer `buf`.  V rows at or past
-  // nkeys are zeroed (only an item's last tile has any): P is 0 there but V
-  // may hold anything.  K rows there stay as loaded: tiles that have them
-  // always take the masked path, which selects their scores away.
+  // nkeys, or before klo, are zeroed (only an item's last or first tiles have
+  // any): P is 0 there but V may hold anything.  K rows there stay as loaded:
+  // tiles that have them always take the masked path, which selects their
+  // scores away.
   auto write_stage = [&](int buf, const Step& s) {
     if constexpr (!BF16) {
       char* Ks = smem + buf * C::STAGE;
       char* Vs = Ks + C::KTILE;
       const int kv0 = s.t * C::BN;
-      const bool tail = kv0 + C::BN > s.it.nkeys;
+      bool edge = kv0 + C::BN > s.it.nkeys;
+      if constexpr (WIN) edge = edge || kv0 < s.it.klo;
       const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
       for (int it = 0; it < C::KIT; ++it) {
         const int cch = it * C::NTH + tid;
         if (cch < C::KCH) {
-          const bool keep = !tail || kv0 + cch / C::CPR < s.it.nkeys;
+          const int key = kv0 + cch / C::CPR;
+          const bool keep = !edge || (key < s.it.nkeys && (!WIN || key >= s.it.klo));
           st16(Ks + (cch / C::CPR) * C::KROW + (cch % C::CPR) * 16, kreg[it]);
           st16(Vs + (cch / C::CPR) * C::VROW + (cch % C::CPR) * 16, keep ? vreg[it] : zero);
         }
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // ---- prologue: the first step -------------------------------------------
   Step cur;
   cur.it = item_from(0);
-  cur.t = 0;
+  cur.t = cur.it.t0;
   if (cur.it.ntiles == 0) return;   // no item for this workgroup (whole workgroup)
   Step nx1 = advance(cur);
   Step nx2 = advance(nx1);
@@ -500,10 +517,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int wt0 = it.tile * TW + tb * 32;
     const bool wave_live = wt0 < it.Lq;
     const int qpos = cached + wt0 + n;   // this lane's row's position among the keys
-    const bool skip = !wave_live || (p.causal && kv0 > cached + wt0 + 31);
+    bool skip = !wave_live || (p.causal && kv0 > cached + wt0 + 31);
+    // a window: the tile lies wholly below every window of the wave's rows
+    if constexpr (WIN) skip = skip || kv0 + C::BN <= cached + wt0 - p.window + 1;
     bool q_next = !(item_end && has_next);   // true once the next item's Q is on its way
     if (!skip) {
-      const bool need_mask = p.causal ? (kv0 + C::BN - 1 > cached + wt0) : (kv0 + C::BN > it.Lk);
+      bool need_mask = p.causal ? (kv0 + C::BN - 1 > cached + wt0) : (kv0 + C::BN > it.Lk);
+      // ... or crosses the lower edge of some row's window
+      if constexpr (WIN) need_mask = need_mask || kv0 < cached + wt0 + 32 - p.window;
       const char* Ks = smem + buf * C::STAGE;
       const char* Vs = Ks + C::KTILE;
       constexpr int NKB = C::BN / 32;
@@ -534,16 +555,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
       // Tile maximum.  Unmasked tiles take it over raw scores (c >= 0) and fold
       // the scale into the exponent's fma; tiles that cross the causal
-      // diagonal or the key tail scale first and select masked keys away.
+      // diagonal, the key tail or a window's lower edge scale first and
+      // select masked keys away.
       float mt = kMaskedScore;
       if (need_mask) {
         // key offset of register r inside a 32-key block: (r/4)*8 + hh*4 + r%4
         const int lim = (p.causal ? qpos + 1 : it.Lk) - kv0 - hh * 4;   // visible iff offset < lim
+        const int lo = WIN ? qpos - p.window + 1 - kv0 - hh * 4 : 0;     // ... and offset >= lo
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float x = ((r >> 2) * 8 + (r & 3) + kb * 32 < lim) ? s[kb][r] * c : kMaskedScore;
+            const int off = (r >> 2) * 8 + (r & 3) + kb * 32;
+            const bool vis = off < lim && (!WIN || off >= lo);
+            const float x = vis ? s[kb][r] * c : kMaskedScore;
             s[kb][r] = x;
             mt = fmaxf(mt, x);
           }
@@ -567,11 +592,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
       float lsum = 0.f;
       if (need_mask) {
+        // With a window a row may have seen no key yet (m_run still the mask
+        // value): its masked scores are then taken against 0, so they give 0.
+        const float m_ref = (WIN && m_run == kMaskedScore) ? 0.f : m_run;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_run);
+            const float e = __builtin_amdgcn_exp2f(s[kb][r] - m_ref);
             s[kb][r] = e;
             lsum += e;
           }
@@ -634,14 +662,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-template <int D, bool BF16, int NW>
+template <int D, bool BF16, int NW, bool WIN>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const size_t lds = prefill_lds_bytes(D, BF16, p.B, p.meta_lds);
   // dynamic LDS above the default limit must be requested; grow it as needed
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
   if (lds > lds_granted.load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16, NW>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16, NW, WIN>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
@@ -651,16 +679,21 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<D, BF16, NW>), dim3(p.pgrid), dim3(64 * NW), lds, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, BF16, NW, WIN>), dim3(p.pgrid), dim3(64 * NW), lds, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s) {
+template <bool WIN>
+static hipError_t launch_prefill_w(const AttnParams& p, DType dt, int D, hipStream_t s) {
   if (dt == DType::BF16) {
-    if (p.pnw == 8) return D == 64 ? launch_prefill_t<64, true, 8>(p, s) : launch_prefill_t<128, true, 8>(p, s);
-    return D == 64 ? launch_prefill_t<64, true, 4>(p, s) : launch_prefill_t<128, true, 4>(p, s);
+    if (p.pnw == 8) return D == 64 ? launch_prefill_t<64, true, 8, WIN>(p, s) : launch_prefill_t<128, true, 8, WIN>(p, s);
+    return D == 64 ? launch_prefill_t<64, true, 4, WIN>(p, s) : launch_prefill_t<128, true, 4, WIN>(p, s);
   }
-  return D == 64 ? launch_prefill_t<64, false, 4>(p, s) : launch_prefill_t<128, false, 4>(p, s);
+  return D == 64 ? launch_prefill_t<64, false, 4, WIN>(p, s) : launch_prefill_t<128, false, 4, WIN>(p, s);
+}
+
+hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s) {
+  return p.window > 0 ? launch_prefill_w<true>(p, dt, D, s) : launch_prefill_w<false>(p, dt, D, s);
 }
 
 }  // namespace kvs

@@ -218,6 +218,49 @@ kvs_status attn_decode_append_paged(const kvs_tensor* q,
                                     void* workspace, size_t workspace_bytes,
                                     kvs_stream_t stream);
 
+/*
+ * attn_varlen_paged_window_ex -- attn_varlen_paged_ex with a sliding-window
+ * causal mask.  The pages list the sliding window among the masks a kernel
+ * dispatch has to cover and a test matrix has to exercise ("Transformer 추론
+ * 커널 (3/10)", §19 and §24); the band taken here is the usual one: with
+ * window W the row at position p (the causal position c_b + i, so a one-row
+ * decode sits at Lk_b - 1) sees keys max(0, p - W + 1) .. p -- its own and the
+ * W - 1 before it.  Same arguments as attn_varlen_paged_ex with `causal`
+ * replaced by `window` (W >= 1, else KVS_ERR_INVALID); same paths, limits,
+ * workspace and errors.  Keys below the first row's window start in a
+ * sequence, and the block-table entries of blocks holding only such keys, are
+ * never read (a caller may have freed those blocks).
+ */
+kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q,
+                                       const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                       const kvs_tensor* block_table,
+                                       const kvs_tensor* cu_seqlens_q,
+                                       const kvs_tensor* seqlens_k,
+                                       float scale, int32_t window,
+                                       kvs_tensor* out, kvs_tensor* lse,
+                                       const kvs_hints* hints,
+                                       void* workspace, size_t workspace_bytes,
+                                       kvs_stream_t stream);
+
+/*
+ * attn_decode_append_paged_window -- attn_decode_append_paged with the
+ * sliding window of attn_varlen_paged_window_ex: sequence b's query row sees
+ * keys max(0, Lk_b - W) .. Lk_b - 1, the new one included.  Same result as
+ * kv_store_paged then attn_varlen_paged_window_ex with cu_seqlens_q = 0..B.
+ * W >= 1, else KVS_ERR_INVALID.  Table entries below block
+ * max(0, Lk_b - W) / 16 are never read.
+ */
+kvs_status attn_decode_append_paged_window(const kvs_tensor* q,
+                                           const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                           kvs_tensor* k_cache, kvs_tensor* v_cache,
+                                           const kvs_tensor* block_table,
+                                           const kvs_tensor* seqlens_k,
+                                           float scale, int32_t window,
+                                           kvs_tensor* out, kvs_tensor* lse,
+                                           const kvs_hints* hints,
+                                           void* workspace, size_t workspace_bytes,
+                                           kvs_stream_t stream);
+
 /* Text of the calling thread's last non-OK status ("" if none).  The pointer is
  * valid until that thread's next library call. */
 const char* kvs_last_error(void);

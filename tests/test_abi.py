@@ -213,3 +213,52 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+# ---- sliding window entry points ----------------------------------------------
+def _call_window(lib, a, window, hints=None):
+    return lib.attn_varlen_paged_window_ex(ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["table"]), ref(a["cu"]),
+                                           ref(a["lk"]), ctypes.c_float(0.125), window, ref(a["out"]),
+                                           ref(a.get("lse")), ctypes.byref(hints) if hints else None, None, 0, None)
+
+
+def _call_append_window(lib, a, window):
+    return lib.attn_decode_append_paged_window(ref(a["q"]), ref(a["kn"]), ref(a["vn"]), ref(a["k"]), ref(a["v"]),
+                                               ref(a["table"]), ref(a["lk"]), ctypes.c_float(0.125), window,
+                                               ref(a["out"]), ref(a.get("lse")), None, None, 0, None)
+
+
+@pytest.mark.parametrize("window", [0, -1, -100])
+def test_window_must_be_positive(lib, window):
+    assert _call_window(lib, _attn_args(), window) == L.KVS_ERR_INVALID
+    assert "window must be >= 1" in lib.kvs_last_error().decode()
+    assert _call_append_window(lib, _append_args(), window) == L.KVS_ERR_INVALID
+    assert "window must be >= 1" in lib.kvs_last_error().decode()
+
+
+def test_window_entries_validate_like_the_others(lib):
+    a = _attn_args()
+    a.update(out=T([8, 3, 64]))
+    assert _call_window(lib, a, 16) == L.KVS_ERR_INVALID
+    assert "out shape" in lib.kvs_last_error().decode()
+    h = L.KvsHints()
+    h.num_splits = -1
+    assert _call_window(lib, _attn_args(), 16, hints=h) == L.KVS_ERR_INVALID
+    a = _append_args()
+    a.update(kn=T([4, 2, 32]), vn=T([4, 2, 32]))
+    assert _call_append_window(lib, a, 16) == L.KVS_ERR_INVALID
+    assert "k_new must be" in lib.kvs_last_error().decode()
+
+
+def test_binding_window_needs_causal():
+    import attention_kv_store_amd as kvs
+    with pytest.raises(ValueError):
+        kvs.attn_varlen_paged(None, None, None, None, None, None, 0.125, False, window=4)
+
+
+def test_window_context_limit(lib):
+    # 16 * MB above 2^30 keys: the window arithmetic would leave 32 bits
+    a = _attn_args(B=1, MB=(1 << 26) + 1, T_=8)
+    a.update(cu=T([2], L.KVS_I32), lk=T([1], L.KVS_I32))
+    assert _call_window(lib, a, 16) == L.KVS_ERR_UNSUPPORTED
+    assert "16 * MB <= 2^30" in lib.kvs_last_error().decode()

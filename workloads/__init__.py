@@ -270,6 +270,23 @@ def mixed_prefill_decode_bf16(seed: int = 6, n_prefill: int = 2, prefill_len: in
                       name="mixed_prefill_decode_bf16")
 
 
+def sliding_window_decode_bf16(seed: int = 7, window: int = 512) -> PagedBatch:
+    """The paged decode workload (64 rows over contexts U{128..2048}, 32 / 8
+    heads, D 64) under a sliding window of ``window`` keys."""
+    b = paged_decode_bf16(seed=seed)
+    b.window = int(window)
+    b.name = "sliding_window_decode_bf16"
+    return b
+
+
+def sliding_window_prefill_bf16(seed: int = 8, B: int = 4, L: int = 4096, window: int = 1024) -> PagedBatch:
+    """B prompts of L tokens (no cached prefix), 32 / 8 heads, D 128, under a
+    sliding window of ``window`` keys: every row past the first ``window``
+    positions sees exactly ``window`` keys."""
+    return make_batch(seed, [L] * B, [L] * B, Hq=32, Hkv=8, D=128, dtype="bf16", causal=True,
+                      window=window, name="sliding_window_prefill_bf16")
+
+
 NAMED = {
     "tiny_varlen_fp32": tiny_varlen_fp32,
     "paged_decode_bf16": paged_decode_bf16,
@@ -277,6 +294,8 @@ NAMED = {
     "extend_prefill_bf16": extend_prefill_bf16,
     "long_prefill_bf16": long_prefill_bf16,
     "mixed_prefill_decode_bf16": mixed_prefill_decode_bf16,
+    "sliding_window_decode_bf16": sliding_window_decode_bf16,
+    "sliding_window_prefill_bf16": sliding_window_prefill_bf16,
 }
 
 
