@@ -119,7 +119,7 @@ struct Step {
   int last;   // last step of the piece
 };
 
-template <int D, bool BF16, bool APPEND>
+template <int D, bool BF16, bool APPEND, bool WIN>
 struct DecodeWave {
   using C = DCfg<D>;
   using E = typename std::conditional<BF16, uint16_t, float>::type;
@@ -156,14 +156,14 @@ struct DecodeWave {
   template <int NB>
   __device__ __forceinline__ void softmax_update(f32x4 (&s)[NB], int k0, int kend, int klo) {
     float mt = kMaskedScore;
-    const bool edge = k0 + 16 * NB > kend || k0 < klo;
+    const bool edge = k0 + 16 * NB > kend || (WIN && k0 < klo);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float x = s[j][r] * p.scale_log2;
         const int key = k0 + 16 * j + grp * 4 + r;
-        if (edge) x = (key < kend && key >= klo) ? x : kMaskedScore;
+        if (edge) x = (key < kend && (!WIN || key >= klo)) ? x : kMaskedScore;
         s[j][r] = x;
         mt = fmaxf(mt, x);
       }
@@ -310,13 +310,13 @@ struct DecodeWave {
   }
 
   // first key of sequence st.b that the query row sees (the window's start)
-  __device__ __forceinline__ int first_key(const Step& st) const { return p.window > 0 ? max(0, st.Lk - p.window) : 0; }
+  __device__ __forceinline__ int first_key(const Step& st) const { return WIN ? max(0, st.Lk - p.window) : 0; }
 
   __device__ __forceinline__ void compute(const Step& st, const Buf& bf) {
     const int k0 = st.lblk * 16;
     const int kend = min(st.Lk, (st.lblk + st.nblk) * 16);
     const int klo = first_key(st);
-    const bool edge = k0 + 16 * C::NBS > kend || k0 < klo;
+    const bool edge = k0 + 16 * C::NBS > kend || (WIN && k0 < klo);
     const u32x4 zero = {0, 0, 0, 0};
     // V^T into the slab: word (V[2kp][d], V[2kp+1][d]) at row d, key pair kp.
     // The slab is private to this wave and LDS operations of one wave execute
@@ -326,8 +326,8 @@ struct DecodeWave {
     for (int j = 0; j < C::NBS; ++j) {
       const int kp = lane & 7;
       const int kv = k0 + 16 * j + 2 * kp;
-      const bool v0_ok = !edge || (kv < kend && kv >= klo);
-      const bool v1_ok = !edge || (kv + 1 < kend && kv + 1 >= klo);
+      const bool v0_ok = !edge || (kv < kend && (!WIN || kv >= klo));
+      const bool v1_ok = !edge || (kv + 1 < kend && (!WIN || kv + 1 >= klo));
 #pragma unroll
       for (int it = 0; it < C::VIL; ++it) {
         const int dch = (lane >> 3) + 8 * it;
@@ -409,7 +409,7 @@ struct DecodeWave {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = grp * 4 + r;
-        const bool ok = kb0 + key < kend && kb0 + key >= klo;
+        const bool ok = kb0 + key < kend && (!WIN || kb0 + key >= klo);
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
           float v = vblk[key * tok_stride + db * 16 + col];
@@ -641,10 +641,11 @@ struct DecodeWave {
   }
 };
 
-template <int D, bool BF16, bool APPEND>
+template <int D, bool BF16, bool APPEND, bool WIN>
 __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   using C = DCfg<D>;
-  using W = DecodeWave<D, BF16, APPEND>;
+  using W = DecodeWave<D, BF16, APPEND, WIN>;
+  const int win = WIN ? p.window : 0;   // sliding window (0: none)
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int B = p.B;
   int* slens = reinterpret_cast<int*>(smem);         // [B]      seqlens_k
@@ -672,7 +673,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     for (int i = (nt & ~3) + tid; i < nt; i += nthr) tbl[i] = p.table[i];
     if (wave == 0) {
       const int L = lane < B ? p.lens_k[lane] : 0;
-      const int nb = seq_blocks(L, p.window);
+      const int nb = seq_blocks(L, win);
       const int x = wave_inclusive_sum(nb);
       if (lane < B) {
         slens[lane] = L;
@@ -694,7 +695,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       int run = 0;
       for (int i = 0; i < per; ++i) {
         const int b = b0 + i;
-        if (b < B) run += seq_blocks(slens[b], p.window);
+        if (b < B) run += seq_blocks(slens[b], win);
       }
       const int x = wave_inclusive_sum(run);
       if (lane == 63) wtot[wave] = x;
@@ -706,7 +707,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
         const int b = b0 + i;
         if (b < B) {
           sstart[b] = acc;
-          acc += seq_blocks(slens[b], p.window);
+          acc += seq_blocks(slens[b], win);
         }
       }
       if (tid == nthr - 1) sstart[B] = acc;
@@ -738,7 +739,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     for (int i = tid; i < r1 - r0; i += nthr) {
       const int gb = r0 + i;
       const int b = seq_of(gb);
-      tbl[i] = p.table[(int64_t)b * p.MB + (gb - sstart[b]) + first_block(slens[b], p.window)];
+      tbl[i] = p.table[(int64_t)b * p.MB + (gb - sstart[b]) + first_block(slens[b], win)];
     }
     __syncthreads();
   }
@@ -783,7 +784,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     st.b = sb;
     st.t = sb;   // one query row per sequence: cu_seqlens_q[b] = b
     st.Lk = slens[sb];
-    st.lblk = pos - s0 + first_block(st.Lk, p.window);
+    st.lblk = pos - s0 + first_block(st.Lk, win);
     st.nblk = end - pos;
     st.gblk = pos;
     st.first = pos == max(seg_lo(seg), s0) ? 1 : 0;
@@ -888,7 +889,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   if (nseg > nsplit_seg) stream(nsplit_seg, nseg);
 }
 
-template <int D, bool BF16, bool APPEND>
+template <int D, bool BF16, bool APPEND, bool WIN>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   using C = DCfg<D>;
   static_assert(C::SLAB == D * 40, "decode_slab_bytes must match the slab layout");
@@ -897,7 +898,7 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
   if (lds > lds_granted.load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND, WIN>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
@@ -907,19 +908,20 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND, WIN>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
   return hipGetLastError();
 }
 
-template <bool APPEND>
+template <bool APPEND, bool WIN>
 static hipError_t launch_decode_a(const AttnParams& p, DType dt, int D, hipStream_t s) {
   if (dt == DType::BF16)
-    return D == 64 ? launch_decode_t<64, true, APPEND>(p, s) : launch_decode_t<128, true, APPEND>(p, s);
-  return D == 64 ? launch_decode_t<64, false, APPEND>(p, s) : launch_decode_t<128, false, APPEND>(p, s);
+    return D == 64 ? launch_decode_t<64, true, APPEND, WIN>(p, s) : launch_decode_t<128, true, APPEND, WIN>(p, s);
+  return D == 64 ? launch_decode_t<64, false, APPEND, WIN>(p, s) : launch_decode_t<128, false, APPEND, WIN>(p, s);
 }
 
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s) {
-  return p.append ? launch_decode_a<true>(p, dt, D, s) : launch_decode_a<false>(p, dt, D, s);
+  if (p.window > 0) return p.append ? launch_decode_a<true, true>(p, dt, D, s) : launch_decode_a<false, true>(p, dt, D, s);
+  return p.append ? launch_decode_a<true, false>(p, dt, D, s) : launch_decode_a<false, false>(p, dt, D, s);
 }
 
 }  // namespace kvs

@@ -54,8 +54,8 @@ def _src_sha(name: str) -> str:
 
 # kernel symbol (as rocprofv3 names it) and source file of each timed workload
 COUNTED = {
-    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true>", "decode.hip"),
-    "causal_prefill_bf16": ("kvs::prefill_kernel<128, true, 8>", "prefill.hip"),
+    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false>", "decode.hip"),
+    "causal_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false>", "prefill.hip"),
 }
 
 
@@ -160,13 +160,15 @@ class Workload:
         r = i % len(self.reps)
         db, _, _, _, out, lse = self.reps[r]
         self.kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q,
-                                   db.seqlens_k, db.scale, db.causal, out=out, lse=lse, workspace=self.ws[r])
+                                   db.seqlens_k, db.scale, db.causal, out=out, lse=lse, workspace=self.ws[r],
+                                   window=self.batch.window)
 
     def append_attend(self, i):
         r = i % len(self.reps)
         db, kn, vn, _, out, lse = self.reps[r]
         self.kvs.attn_decode_append_paged(db.q, kn, vn, db.k_cache, db.v_cache, db.block_table, db.seqlens_k,
-                                          db.scale, out=out, lse=lse, workspace=self.ws[r])
+                                          db.scale, out=out, lse=lse, workspace=self.ws[r],
+                                          window=self.batch.window)
 
 
 def _graph_len(steps: int, cap: int = 100) -> int:
@@ -531,6 +533,39 @@ def main():
         log(f"mixed: {line['mixed']}")
         del wm
         torch.cuda.empty_cache()
+
+    if not args.no_prefill and not args.no_extras:
+        # sliding-window variants: the decode workload under a 512-key window
+        # (fused step) and 4 x 4096-token prompts under a 1024-key window
+        from workloads import sliding_window_decode_bf16, sliding_window_prefill_bf16
+        sw = {}
+        wd = sliding_window_decode_bf16()
+        ww = Workload(wd, args.replicas)
+        dms, _, _, dstats = time_steps(ww, args.steps, args.warmup, fused=True, eager=args.eager)
+        sw["decode"] = {
+            "workload": "sliding_window_decode_bf16", "window": wd.window, "step": "attn_decode_append_paged_window",
+            "avg_launch_us": round(dms * 1e3, 3), "kv_bytes_per_launch": kv_bytes(wd),
+            "GBs": round(kv_bytes(wd) / (dms * 1e-3) / 1e9, 2),
+            "frac": round(kv_bytes(wd) / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "dispatch": kvs.last_dispatch(), "replay_stats": dstats,
+        }
+        del ww
+        torch.cuda.empty_cache()
+        wpf = sliding_window_prefill_bf16()
+        ww = Workload(wpf, args.replicas)
+        psteps = max(1, args.steps // 4)
+        _, wattn, _, wstats = time_steps(ww, psteps, max(1, args.warmup // 4), eager=args.eager)
+        sw["prefill"] = {
+            "workload": "sliding_window_prefill_bf16", "window": wpf.window, "query_rows": wpf.T,
+            "avg_launch_us": round(wattn * 1e3, 3), "flops_per_launch": attention_flops(wpf),
+            "TFLOPs": round(attention_flops(wpf) / (wattn * 1e-3) / 1e12, 3),
+            "frac": round(attention_flops(wpf) / (wattn * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "dispatch": kvs.last_dispatch(), "replay_stats": wstats,
+        }
+        del ww
+        torch.cuda.empty_cache()
+        line["sliding_window"] = sw
+        log(f"sliding window: {sw}")
 
     if not args.no_extras:
         peaks = measure_peaks()
