@@ -14,6 +14,9 @@ define, with no tiling, fusion or reordering beyond that definition:
 * ``kv_store_oracle`` -- the scatter of new K/V rows into their slots
   (Transformer 추론 커널 (3/10), §2 "RoPE + KV cache store" step; slot = block *
   page_size + offset per 장부가 커널 인자로 바뀌는 지점과 CUDA graph, page-table part).
+* ``apply_rope`` / ``kv_store_rope_oracle`` -- the rotary position embedding
+  of Q and K and the "RoPE + KV cache store" step (Transformer 추론 커널 (3/10),
+  §1-§2, §19, §24; formula from RoFormer, section 3.2 -- the pages give none).
 * ``lse_merge`` -- the stable merge of partial results over disjoint key sets
   (Transformer 추론 커널 (3/10), §12 equations for m_new / l_new, and §16).
 
@@ -23,3 +26,4 @@ SDPA.  The readings taken where the pages are silent are listed in the design doc.
 """
 from .attention import attention_oracle, gather_sequence, lse_merge, BLOCK_SIZE  # noqa: F401
 from .store import kv_store_oracle  # noqa: F401
+from .rope import INTERLEAVED, NEOX, apply_rope, kv_store_rope_oracle  # noqa: F401
