@@ -3,6 +3,8 @@
 Python names mirror the C ABI (include/kvstore.h):
 
 * ``kv_store_paged(k_new, v_new, slot_mapping, k_cache, v_cache)``
+* ``kv_store_rope_paged(q, k_new, v_new, positions, slot_mapping, k_cache,
+  v_cache, rotary_dim=0, base=10000.0, style="neox", pos_scale=1.0)``
 * ``attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
   scale, causal, out=None, lse=None, ...)`` (``window=W`` selects the
   sliding-window entry point ``attn_varlen_paged_window_ex``)
@@ -20,9 +22,9 @@ import ctypes
 from typing import Optional
 
 from . import _lib
-from ._lib import KVS_BF16, KVS_F32, KVS_I32, KvsError, KvsHints, describe, last_dispatch  # noqa: F401
+from ._lib import KVS_BF16, KVS_F32, KVS_I32, KvsError, KvsHints, KvsRope, describe, last_dispatch  # noqa: F401
 
-__all__ = ["kv_store_paged", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
+__all__ = ["kv_store_paged", "kv_store_rope_paged", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
 
 
 def _dtype_code(t) -> int:
@@ -56,6 +58,23 @@ def kv_store_paged(k_new, v_new, slot_mapping, k_cache, v_cache) -> None:
     lib = _lib.load()
     d = [_desc(x) for x in (k_new, v_new, slot_mapping, k_cache, v_cache)]
     _lib.check(lib.kv_store_paged(*[_ref(x) for x in d], _stream(k_cache)))
+
+
+def kv_store_rope_paged(q, k_new, v_new, positions, slot_mapping, k_cache, v_cache, *, rotary_dim: int = 0,
+                        base: float = 10000.0, style: str = "neox", pos_scale: float = 1.0) -> None:
+    """The RoPE + KV store step: rotate ``q`` [T, Hq, D] in place (may be None),
+    write RoPE(``k_new``) and ``v_new`` [T, Hkv, D] into ``slot_mapping`` of the
+    pools (negative slots skipped); token t sits at ``positions[t]``.  ``style``
+    is "neox" (pairs i, i + rotary_dim/2) or "interleaved" (pairs 2i, 2i + 1);
+    ``rotary_dim`` 0 means the whole head."""
+    styles = {"neox": _lib.KVS_ROPE_NEOX, "interleaved": _lib.KVS_ROPE_INTERLEAVED}
+    if style not in styles:
+        raise ValueError(f"style must be one of {sorted(styles)}")
+    lib = _lib.load()
+    r = KvsRope()
+    r.rotary_dim, r.style, r.base, r.pos_scale = int(rotary_dim), styles[style], float(base), float(pos_scale)
+    d = [_desc(x) for x in (q, k_new, v_new, positions, slot_mapping, k_cache, v_cache)]
+    _lib.check(lib.kv_store_rope_paged(*[_ref(x) for x in d], ctypes.byref(r), _stream(k_cache)))
 
 
 def _hints(max_seqlen_q=0, max_seqlen_k=0, num_splits=0):

@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "KVS_OK", 1: "KVS_ERR_INVALID", 2: "KVS_ERR_UNSUPPORTED", 3: 
 # every symbol include/kvstore.h declares
 EXPORTS = (
     "kv_store_paged",
+    "kv_store_rope_paged",
     "attn_varlen_paged",
     "attn_varlen_paged_workspace_size",
     "attn_varlen_paged_ex",
@@ -52,6 +53,18 @@ class KvsHints(ctypes.Structure):
     ]
 
 
+KVS_ROPE_NEOX, KVS_ROPE_INTERLEAVED = 0, 1
+
+
+class KvsRope(ctypes.Structure):
+    _fields_ = [
+        ("rotary_dim", ctypes.c_int32),
+        ("style", ctypes.c_int32),
+        ("base", ctypes.c_double),
+        ("pos_scale", ctypes.c_double),
+    ]
+
+
 class KvsError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -76,6 +89,8 @@ def load(path: str = LIB_PATH):
     vp, st = ctypes.c_void_p, ctypes.c_int
     lib.kv_store_paged.argtypes = [P, P, P, P, P, vp]
     lib.kv_store_paged.restype = st
+    lib.kv_store_rope_paged.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(KvsRope), vp]
+    lib.kv_store_rope_paged.restype = st
     lib.attn_varlen_paged.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, vp]
     lib.attn_varlen_paged.restype = st
     lib.attn_varlen_paged_workspace_size.argtypes = [P, P, P, ctypes.POINTER(KvsHints)]

@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvstore.so")
-SOURCES = ["api.hip", "store.hip", "prefill.hip", "decode.hip", "calib.hip"]
+SOURCES = ["api.hip", "store.hip", "rope.hip", "prefill.hip", "decode.hip", "calib.hip"]
 ARCH = "gfx950"
 
 

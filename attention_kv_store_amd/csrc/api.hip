@@ -379,6 +379,69 @@ kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new, cons
   return KVS_OK;
 }
 
+kvs_status kv_store_rope_paged(kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                               const kvs_tensor* positions, const kvs_tensor* slot_mapping, kvs_tensor* k_cache,
+                               kvs_tensor* v_cache, const kvs_rope* rope, kvs_stream_t stream) {
+  g_err.clear();
+  KVS_TRY(check_tensor(k_cache, "k_cache", kFloatTypes, 4));
+  KVS_TRY(check_tensor(v_cache, "v_cache", kFloatTypes, 4));
+  KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3, true));
+  KVS_TRY(check_tensor(v_new, "v_new", kFloatTypes, 3, true));
+  KVS_TRY(check_tensor(positions, "positions", kIntTypes, 1, true));
+  KVS_TRY(check_tensor(slot_mapping, "slot_mapping", kIntTypes, 1, true));
+  if (q) KVS_TRY(check_tensor(q, "q", kFloatTypes, 3, true));
+  if (!rope) return fail(KVS_ERR_INVALID, "rope: parameters are NULL");
+  const int64_t Tn = k_new->shape[0], Hkv = k_cache->shape[2], D = k_cache->shape[3];
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i]) return fail(KVS_ERR_INVALID, "v_cache shape != k_cache shape");
+  for (int i = 0; i < 3; ++i)
+    if (v_new->shape[i] != k_new->shape[i]) return fail(KVS_ERR_INVALID, "v_new shape != k_new shape");
+  if (k_cache->dtype != v_cache->dtype || k_new->dtype != k_cache->dtype || v_new->dtype != k_cache->dtype ||
+      (q && q->dtype != k_cache->dtype))
+    return fail(KVS_ERR_INVALID, "q, k_new, v_new, k_cache and v_cache must share one dtype");
+  if (k_cache->shape[1] != 16) return fail(KVS_ERR_UNSUPPORTED, "page size %lld not supported (only 16)", (long long)k_cache->shape[1]);
+  if (k_new->shape[1] != Hkv || k_new->shape[2] != D)
+    return fail(KVS_ERR_INVALID, "k_new [T, Hkv, D] does not match the pool's [.., .., Hkv, D]");
+  if (q && (q->shape[0] != Tn || q->shape[2] != D || q->shape[1] < 1))
+    return fail(KVS_ERR_INVALID, "q must be [T, Hq, D] with the rows and head dim of k_new");
+  if (positions->shape[0] != Tn) return fail(KVS_ERR_INVALID, "positions has %lld entries for %lld rows", (long long)positions->shape[0], (long long)Tn);
+  if (slot_mapping->shape[0] != Tn) return fail(KVS_ERR_INVALID, "slot_mapping has %lld entries for %lld rows", (long long)slot_mapping->shape[0], (long long)Tn);
+  if (D % 16 || D > 2 * kvs::kRopeMaxPairs) return fail(KVS_ERR_UNSUPPORTED, "rope: head dim %lld not supported (a multiple of 16, at most %d)", (long long)D, 2 * kvs::kRopeMaxPairs);
+  const int64_t rd = rope->rotary_dim ? rope->rotary_dim : D;
+  if (rd < 16 || rd > D || rd % 16) return fail(KVS_ERR_INVALID, "rope: rotary_dim %lld must be a multiple of 16 in [16, D]", (long long)rd);
+  if (rope->style != KVS_ROPE_NEOX && rope->style != KVS_ROPE_INTERLEAVED) return fail(KVS_ERR_INVALID, "rope: unknown style %d", (int)rope->style);
+  if (!(std::isfinite(rope->base) && rope->base > 0) || !(std::isfinite(rope->pos_scale) && rope->pos_scale > 0))
+    return fail(KVS_ERR_INVALID, "rope: base and pos_scale must be finite and positive");
+  if (Tn > INT32_MAX || (q && q->shape[1] > 4096)) return fail(KVS_ERR_UNSUPPORTED, "rope: sizes beyond the kernel's ranges");
+  if (Tn == 0) {
+    set_dispatch("kv_store_rope_paged: empty (nothing enqueued)");
+    return KVS_OK;
+  }
+  kvs::RopeParams p{};
+  p.q = q ? q->data : nullptr;
+  p.k_new = k_new->data;
+  p.v_new = v_new->data;
+  p.pos = static_cast<const int32_t*>(positions->data);
+  p.slots = static_cast<const int32_t*>(slot_mapping->data);
+  p.k_cache = k_cache->data;
+  p.v_cache = v_cache->data;
+  p.T = Tn;
+  p.num_slots = k_cache->shape[0] * 16;
+  p.Hq = q ? (int32_t)q->shape[1] : 0;
+  p.Hkv = (int32_t)Hkv;
+  p.D = (int32_t)D;
+  p.rd = (int32_t)rd;
+  p.style = rope->style;
+  p.inv_scale = 1.0 / rope->pos_scale;
+  for (int i = 0; i < rd / 2; ++i) p.inv_freq[i] = std::pow(rope->base, -2.0 * i / (double)rd);
+  const hipError_t e = kvs::launch_rope_store(p, k_cache->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32,
+                                              reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVS_ERR_HIP, "kv_store_rope_paged launch failed: %s", hipGetErrorString(e));
+  set_dispatch("kv_store_rope_paged rows=%lld q_heads=%d kv_heads=%lld rotary_dim=%lld style=%s", (long long)Tn,
+               p.Hq, (long long)Hkv, (long long)rd, rope->style == KVS_ROPE_NEOX ? "neox" : "interleaved");
+  return KVS_OK;
+}
+
 kvs_status attn_varlen_paged(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
                              const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
                              const kvs_tensor* seqlens_k, float scale, int causal, kvs_tensor* out,

@@ -67,6 +67,25 @@ struct AttnParams {
   int32_t dsmall;         // decode: 1 = small batch, whole block table staged in LDS
 };
 
+// RoPE + KV store: one workgroup per token row; angles from host-side
+// frequencies theta_i = base^(-2 i / rd), i < rd / 2 <= kRopeMaxPairs.
+constexpr int kRopeMaxPairs = 128;
+struct RopeParams {
+  void* q;                // [T, Hq, D], rotated in place (null: K/V only)
+  const void* k_new;      // [T, Hkv, D]
+  const void* v_new;
+  const int32_t* pos;     // [T] positions
+  const int32_t* slots;   // [T] pool slots (negative: row not stored)
+  void* k_cache;          // [NB, 16, Hkv, D]
+  void* v_cache;
+  int64_t T, num_slots;
+  int32_t Hq, Hkv, D;
+  int32_t rd;             // rotated dims per head
+  int32_t style;          // 0: pairs (i, i + rd/2); 1: pairs (2i, 2i + 1)
+  double inv_scale;       // 1 / pos_scale
+  double inv_freq[kRopeMaxPairs];
+};
+
 // Division by a divisor d (1 <= d < 2^31) fixed for a launch, for dividends
 // n < 2^31: q = (mulhi(n, m) + n) >> l with l = ceil(log2 d) and
 // m = floor(2^(32 + l) / d) - 2^32 + 1 (Granlund and Montgomery, "Division by
@@ -108,6 +127,7 @@ inline size_t prefill_lds_bytes(int D, bool bf16, int B, int meta_lds) {
 }
 
 hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);
+hipError_t launch_rope_store(const RopeParams& p, DType dt, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s);
 

@@ -30,11 +30,13 @@ class DecodeGraphRunner:
     reserved_block: a block index of the pool that no sequence uses (the
     dummy rows' table entries point at it and their new rows are stored there);
     buckets: batch sizes to capture (ascending); max_blocks: table width;
-    Hq: query heads; scale: score scale; num_splits: 0 = automatic.
+    Hq: query heads; scale: score scale; num_splits: 0 = automatic;
+    window: sliding window of every captured step (0 = none), see
+    attn_decode_append_paged.
     """
 
     def __init__(self, k_cache, v_cache, reserved_block: int, buckets: Sequence[int], max_blocks: int, Hq: int,
-                 scale: float, num_splits: int = 0):
+                 scale: float, num_splits: int = 0, window: int = 0):
         import torch
 
         if not buckets or list(buckets) != sorted(set(int(b) for b in buckets)) or buckets[0] < 1:
@@ -46,6 +48,7 @@ class DecodeGraphRunner:
         self.buckets = [int(b) for b in buckets]
         self.max_blocks = int(max_blocks)
         self.scale = float(scale)
+        self.window = int(window)
         Hkv, D = k_cache.shape[2], k_cache.shape[3]
         dt, dev = k_cache.dtype, k_cache.device
         self.graphs: Dict[int, torch.cuda.CUDAGraph] = {}
@@ -67,7 +70,7 @@ class DecodeGraphRunner:
             def step(b=b):
                 attn_decode_append_paged(b["q"], b["k_new"], b["v_new"], k_cache, v_cache, b["table"], b["lens"],
                                          self.scale, out=b["out"], lse=b["lse"], num_splits=num_splits,
-                                         workspace=b["ws"])
+                                         workspace=b["ws"], window=self.window)
 
             step()   # warm-up outside the capture (first-call set-up of the library)
             torch.cuda.synchronize()

@@ -83,6 +83,49 @@ kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new,
                           kvs_tensor* k_cache, kvs_tensor* v_cache,
                           kvs_stream_t stream);
 
+/* Layout of the rotary pairs of a head (kv_store_rope_paged). */
+typedef enum { KVS_ROPE_NEOX = 0, KVS_ROPE_INTERLEAVED = 1 } kvs_rope_style;
+
+typedef struct {
+  int32_t rotary_dim;  /* dims rotated per head: a multiple of 16 in [16, D]; 0 = D   */
+  int32_t style;       /* kvs_rope_style: pairs (i, i + rotary_dim/2) or (2i, 2i + 1) */
+  double base;         /* theta_i = base^(-2 i / rotary_dim); finite, > 0             */
+  double pos_scale;    /* angle = (position / pos_scale) * theta_i; finite, > 0       */
+} kvs_rope;
+
+/*
+ * kv_store_rope_paged -- the "RoPE + KV cache store" step in one pass: rotate
+ * q in place, and write the rotated k_new and the unchanged v_new into their
+ * slots.
+ *
+ * A layer's step list applies a rotary position embedding to Q and K right
+ * before attention, fused with the KV-cache write ("Transformer 추론 커널 (3/10)",
+ * §1-§2); its variant, scaling and offset are dispatch and test axes (§19,
+ * §24).  The pages give no formula; the rotation is RoFormer's (Su et al.
+ * 2021, section 3.2): pair i of token t is turned by
+ *   a = (positions[t] / pos_scale) * base^(-2 i / rotary_dim),
+ *   x1' = x1 cos a - x2 sin a,   x2' = x2 cos a + x1 sin a,
+ * with the pairs of `style`; dims at or past rotary_dim are unchanged.
+ * Angles are formed in double precision; the rotation runs in fp32 and the
+ * result is rounded to the tensor dtype (nearest even for bf16).
+ *
+ *   q            [T, Hq, D] f32 or bf16, rotated in place; NULL = no query rows
+ *   k_new, v_new [T, Hkv, D] same dtype (read only)
+ *   positions    i32 [T]: token t's position (any offset is the caller's)
+ *   slot_mapping i32 [T]: pool slot of row t; negative = not stored (q row t
+ *                is still rotated)
+ *   k_cache, v_cache [NB, 16, Hkv, D]: slot s is written with row t's rotated
+ *                K and its V
+ *   rope         rotation parameters (host memory, read during the call)
+ * Supported: D a multiple of 16 up to 256, page size 16.  Preconditions on
+ * device values: no two rows name the same slot; slots >= 16 * NB are skipped.
+ * T == 0 is a no-op.  Allocates nothing.
+ */
+kvs_status kv_store_rope_paged(kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                               const kvs_tensor* positions, const kvs_tensor* slot_mapping,
+                               kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_rope* rope,
+                               kvs_stream_t stream);
+
 /*
  * attn_varlen_paged -- exact softmax attention of packed varlen query rows over
  * a paged K/V cache.

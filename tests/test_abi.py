@@ -262,3 +262,51 @@ def test_window_context_limit(lib):
     a.update(cu=T([2], L.KVS_I32), lk=T([1], L.KVS_I32))
     assert _call_window(lib, a, 16) == L.KVS_ERR_UNSUPPORTED
     assert "16 * MB <= 2^30" in lib.kvs_last_error().decode()
+
+
+# ---- RoPE + store ----------------------------------------------------------------
+def _rope_args(T_=4, Hq=8, Hkv=2, D=64, NB=4, dtype=L.KVS_BF16):
+    return dict(q=T([T_, Hq, D], dtype), kn=T([T_, Hkv, D], dtype), vn=T([T_, Hkv, D], dtype),
+                pos=T([T_], L.KVS_I32), slots=T([T_], L.KVS_I32), k=T([NB, 16, Hkv, D], dtype),
+                v=T([NB, 16, Hkv, D], dtype))
+
+
+def _call_rope(lib, a, rotary_dim=0, style=0, base=10000.0, pos_scale=1.0, rope=True):
+    r = L.KvsRope()
+    r.rotary_dim, r.style, r.base, r.pos_scale = rotary_dim, style, base, pos_scale
+    return lib.kv_store_rope_paged(ref(a["q"]), ref(a["kn"]), ref(a["vn"]), ref(a["pos"]), ref(a["slots"]),
+                                   ref(a["k"]), ref(a["v"]), ctypes.byref(r) if rope else None, None)
+
+
+@pytest.mark.parametrize("kw,mutate,expect,msg", [
+    (dict(rotary_dim=8), None, L.KVS_ERR_INVALID, "rotary_dim"),
+    (dict(rotary_dim=24), None, L.KVS_ERR_INVALID, "rotary_dim"),
+    (dict(rotary_dim=80), None, L.KVS_ERR_INVALID, "rotary_dim"),
+    (dict(style=2), None, L.KVS_ERR_INVALID, "style"),
+    (dict(base=0.0), None, L.KVS_ERR_INVALID, "base and pos_scale"),
+    (dict(base=float("inf")), None, L.KVS_ERR_INVALID, "base and pos_scale"),
+    (dict(pos_scale=-1.0), None, L.KVS_ERR_INVALID, "base and pos_scale"),
+    (dict(rope=False), None, L.KVS_ERR_INVALID, "NULL"),
+    ({}, lambda a: a.update(q=T([4, 8, 64], L.KVS_F32)), L.KVS_ERR_INVALID, "one dtype"),
+    ({}, lambda a: a.update(q=T([5, 8, 64])), L.KVS_ERR_INVALID, "q must be"),
+    ({}, lambda a: a.update(pos=T([3], L.KVS_I32)), L.KVS_ERR_INVALID, "positions"),
+    ({}, lambda a: a.update(slots=T([5], L.KVS_I32)), L.KVS_ERR_INVALID, "slot_mapping"),
+    ({}, lambda a: a.update(kn=T([4, 2, 32]), vn=T([4, 2, 32])), L.KVS_ERR_INVALID, "k_new"),
+    ({}, lambda a: a.update(k=T([4, 8, 2, 64]), v=T([4, 8, 2, 64])), L.KVS_ERR_UNSUPPORTED, "page size"),
+    ({}, lambda a: a.update(q=T([4, 8, 40]), kn=T([4, 2, 40]), vn=T([4, 2, 40]), k=T([4, 16, 2, 40]),
+                            v=T([4, 16, 2, 40])), L.KVS_ERR_UNSUPPORTED, "head dim"),
+    ({}, lambda a: a.update(q=T([4, 8, 512]), kn=T([4, 2, 512]), vn=T([4, 2, 512]), k=T([4, 16, 2, 512]),
+                            v=T([4, 16, 2, 512])), L.KVS_ERR_UNSUPPORTED, "head dim"),
+])
+def test_rope_validation(lib, kw, mutate, expect, msg):
+    a = _rope_args()
+    if mutate:
+        mutate(a)
+    assert _call_rope(lib, a, **kw) == expect
+    assert msg in lib.kvs_last_error().decode()
+
+
+def test_rope_empty_is_noop(lib):
+    a = _rope_args(T_=0)
+    assert _call_rope(lib, a) == L.KVS_OK
+    assert "empty" in lib.kvs_last_dispatch().decode()

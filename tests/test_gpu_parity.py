@@ -414,7 +414,8 @@ def test_decode_append_named_workload():
 
 # ------------------------------------------------------- graph runner -----
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_decode_graph_runner_buckets(dtype):
+@pytest.mark.parametrize("window", [0, 37])
+def test_decode_graph_runner_buckets(dtype, window):
     """Decode steps replayed from per-bucket graphs: a batch padded to the next
     bucket with dummy rows in a reserved block gives the oracle's out / lse
     for its real rows and writes exactly their new rows into the cache; then
@@ -430,11 +431,11 @@ def test_decode_graph_runner_buckets(dtype):
     # hand out a new block first
     k = [int(x) - (1 if (int(x) + 1) % 16 == 0 else 0) for x in rng.integers(2, 900, size=37)]
     b = _mk(621, [1] * 37, [x + 1 for x in k], Hq=8, Hkv=2, D=64, dtype=dtype, causal=True,
-            extra_table_cols=3, name=f"runner-{dtype}")
+            extra_table_cols=3, name=f"runner-{dtype}", window=window)
     # pool holding keys 0 .. k-1 of every sequence; step 1 appends key k
     db, _, _ = to_device_before_append(_prefix_batch(b, np.array(k) + 1))
     runner = DecodeGraphRunner(db.k_cache, db.v_cache, b.poison_block, [16, 32, 64], b.MB, Hq=8,
-                               scale=b.scale, num_splits=7)
+                               scale=b.scale, num_splits=7, window=window)
     before = cache_bits(db.k_cache).copy()
     rows = b.cu_seqlens_k[:-1] + np.array(k)
     dt = db.q.dtype
@@ -462,7 +463,7 @@ def test_decode_graph_runner_buckets(dtype):
         assert np.array_equal(flat[sl], ref[sl])
     # a second step: the first 10 sequences, one key longer, through bucket 16
     k2 = np.array(k[:10]) + 1
-    b2 = _mk(622, [1] * 10, list(k2 + 1), Hq=8, Hkv=2, D=64, dtype=dtype, causal=True)
+    b2 = _mk(622, [1] * 10, list(k2 + 1), Hq=8, Hkv=2, D=64, dtype=dtype, causal=True, window=window)
     q2 = torch.from_numpy(b2.q).to(dt).cuda()
     kn2 = torch.from_numpy(b2.k_tokens[b2.new_token_rows()]).to(dt).cuda()
     vn2 = torch.from_numpy(b2.v_tokens[b2.new_token_rows()]).to(dt).cuda()
