@@ -291,6 +291,59 @@ def runner_replays(dec, args):
     return res
 
 
+def rope_store_line(args):
+    """kv_store_rope_paged at the causal prefill workload's shape (16 x 512 new
+    rows, 32 / 8 heads, D 128) and the decode workload's (64 rows, 32 / 8 heads,
+    D 64), bf16, timed from graph replays over 4 replicas.  Bytes moved: Q read
+    and written, K and V rows read and written, positions and slots read."""
+    import torch
+    import attention_kv_store_amd as kvs
+
+    res = {}
+    for name, T, Hq, Hkv, D in (("prefill_rows", 8192, 32, 8, 128), ("decode_rows", 64, 32, 8, 64)):
+        reps = []
+        NB = (T + 15) // 16 + 1
+        for r in range(4):
+            g = torch.Generator(device="cuda").manual_seed(r)
+            q = torch.randn(T, Hq, D, device="cuda", generator=g).to(torch.bfloat16)
+            kn = torch.randn(T, Hkv, D, device="cuda", generator=g).to(torch.bfloat16)
+            vn = torch.randn(T, Hkv, D, device="cuda", generator=g).to(torch.bfloat16)
+            pos = torch.arange(T, dtype=torch.int32, device="cuda") * 7
+            slots = torch.randperm(NB * 16, device="cuda", generator=g)[:T].to(torch.int32)
+            kc = torch.zeros(NB, 16, Hkv, D, dtype=torch.bfloat16, device="cuda")
+            reps.append((q, kn, vn, pos, slots, kc, torch.zeros_like(kc)))
+
+        def call(i):
+            q, kn, vn, pos, slots, kc, vc = reps[i % 4]
+            kvs.kv_store_rope_paged(q, kn, vn, pos, slots, kc, vc)
+
+        for i in range(8):
+            call(i)
+        torch.cuda.synchronize()
+        n = 100
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                call(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nrep = max(2, args.steps // (4 * n))
+        e0.record()
+        for _ in range(nrep):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / (nrep * n) * 1e3
+        moved = 2 * 2 * T * D * (Hq + 2 * Hkv) + 8 * T
+        res[name] = {"rows": T, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "us": round(us, 3),
+                     "bytes": moved, "GBs": round(moved / (us * 1e-6) / 1e9, 1),
+                     "dispatch": kvs.last_dispatch()}
+        del graph, reps
+        torch.cuda.empty_cache()
+    return res
+
+
 def measure_peaks():
     """Rates this GPU sustains, to set beside the published peaks: a 1 GiB
     device-to-device copy (bytes read + written per second) and a bf16 MFMA
@@ -566,6 +619,10 @@ def main():
         torch.cuda.empty_cache()
         line["sliding_window"] = sw
         log(f"sliding window: {sw}")
+
+    if not args.no_extras:
+        line["rope_store"] = rope_store_line(args)
+        log(f"rope + store: {line['rope_store']}")
 
     if not args.no_extras:
         peaks = measure_peaks()
