@@ -17,6 +17,10 @@ define, with no tiling, fusion or reordering beyond that definition:
 * ``apply_rope`` / ``kv_store_rope_oracle`` -- the rotary position embedding
   of Q and K and the "RoPE + KV cache store" step (Transformer 추론 커널 (3/10),
   §1-§2, §19, §24; formula from RoFormer, section 3.2 -- the pages give none).
+* ``e4m3_encode`` / ``e4m3_decode`` / ``quantize_rows`` / ``kv_store_fp8_oracle``
+  / ``dequantize_pool`` -- the FP8 (OCP E4M3) KV cache with one scale per
+  token row and KV head (Transformer 추론 커널 (3/10), §7, §19, §24 name FP8 KV,
+  quantized layouts and scale layouts; the format is the OCP specification's).
 * ``lse_merge`` -- the stable merge of partial results over disjoint key sets
   (Transformer 추론 커널 (3/10), §12 equations for m_new / l_new, and §16).
 
@@ -27,3 +31,4 @@ SDPA.  The readings taken where the pages are silent are listed in the design doc.
 from .attention import attention_oracle, gather_sequence, lse_merge, BLOCK_SIZE  # noqa: F401
 from .store import kv_store_oracle  # noqa: F401
 from .rope import INTERLEAVED, NEOX, apply_rope, kv_store_rope_oracle  # noqa: F401
+from .fp8 import dequantize_pool, e4m3_decode, e4m3_encode, kv_store_fp8_oracle, quantize_rows  # noqa: F401
