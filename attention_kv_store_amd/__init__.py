@@ -5,6 +5,10 @@ Python names mirror the C ABI (include/kvstore.h):
 * ``kv_store_paged(k_new, v_new, slot_mapping, k_cache, v_cache)``
 * ``kv_store_rope_paged(q, k_new, v_new, positions, slot_mapping, k_cache,
   v_cache, rotary_dim=0, base=10000.0, style="neox", pos_scale=1.0)``
+* ``kv_store_paged_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale,
+  v_scale)`` and ``attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale,
+  block_table, cu_seqlens_q, seqlens_k, scale, causal, ...)``: the FP8 (E4M3)
+  cache with one scale per token row and KV head
 * ``attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
   scale, causal, out=None, lse=None, ...)`` (``window=W`` selects the
   sliding-window entry point ``attn_varlen_paged_window_ex``)
@@ -24,13 +28,15 @@ from typing import Optional
 from . import _lib
 from ._lib import KVS_BF16, KVS_F32, KVS_I32, KvsError, KvsHints, KvsRope, describe, last_dispatch  # noqa: F401
 
-__all__ = ["kv_store_paged", "kv_store_rope_paged", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
+__all__ = ["kv_store_paged", "kv_store_rope_paged", "kv_store_paged_fp8", "attn_varlen_paged_fp8", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
 
 
 def _dtype_code(t) -> int:
     import torch
 
-    m = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16, torch.int32: KVS_I32}
+    m = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16, torch.int32: KVS_I32,
+         # FP8 caches: E4M3 codes, as torch's float8_e4m3fn or as raw bytes
+         torch.float8_e4m3fn: _lib.KVS_FP8_E4M3, torch.uint8: _lib.KVS_FP8_E4M3}
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
@@ -75,6 +81,40 @@ def kv_store_rope_paged(q, k_new, v_new, positions, slot_mapping, k_cache, v_cac
     r.rotary_dim, r.style, r.base, r.pos_scale = int(rotary_dim), styles[style], float(base), float(pos_scale)
     d = [_desc(x) for x in (q, k_new, v_new, positions, slot_mapping, k_cache, v_cache)]
     _lib.check(lib.kv_store_rope_paged(*[_ref(x) for x in d], ctypes.byref(r), _stream(k_cache)))
+
+
+def kv_store_paged_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale) -> None:
+    """Quantize rows of ``k_new`` / ``v_new`` [T, Hkv, D] (f32 / bf16) into the E4M3
+    pools [NB, 16, Hkv, D] (float8_e4m3fn or uint8 codes) at ``slot_mapping``,
+    one fp32 scale per (row, head) into ``k_scale`` / ``v_scale`` [NB, Hkv, 16]."""
+    lib = _lib.load()
+    d = [_desc(x) for x in (k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale)]
+    _lib.check(lib.kv_store_paged_fp8(*[_ref(x) for x in d], _stream(k_cache)))
+
+
+def attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k,
+                          scale: float, causal: bool = True, out=None, lse=None, *, return_lse: bool = True,
+                          num_splits: int = 0, workspace=None, window: int = 0):
+    """Attention over an FP8 cache (values = E4M3(code) * scale of the row and
+    head); q / out bf16.  Decode shapes (one query row per sequence) so far.
+    Returns ``(out, lse)``."""
+    import torch
+
+    if window and not causal:
+        raise ValueError("a sliding window needs the causal mask")
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    h = _hints(0, 0, num_splits)
+    ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
+    d = [_desc(x) for x in (q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k)]
+    st = lib.attn_varlen_paged_fp8_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)), int(window),
+                                      _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
+                                      _stream(q))
+    _lib.check(st)
+    return out, lse
 
 
 def _hints(max_seqlen_q=0, max_seqlen_k=0, num_splits=0):

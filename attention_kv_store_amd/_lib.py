@@ -15,13 +15,15 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvstore.so")
 
 KVS_OK, KVS_ERR_INVALID, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = range(5)
-KVS_F32, KVS_BF16, KVS_I32 = 0, 1, 2
+KVS_F32, KVS_BF16, KVS_I32, KVS_FP8_E4M3 = 0, 1, 2, 3
 STATUS_NAMES = {0: "KVS_OK", 1: "KVS_ERR_INVALID", 2: "KVS_ERR_UNSUPPORTED", 3: "KVS_ERR_WORKSPACE", 4: "KVS_ERR_HIP"}
 
 # every symbol include/kvstore.h declares
 EXPORTS = (
     "kv_store_paged",
     "kv_store_rope_paged",
+    "kv_store_paged_fp8",
+    "attn_varlen_paged_fp8_ex",
     "attn_varlen_paged",
     "attn_varlen_paged_workspace_size",
     "attn_varlen_paged_ex",
@@ -91,6 +93,11 @@ def load(path: str = LIB_PATH):
     lib.kv_store_paged.restype = st
     lib.kv_store_rope_paged.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(KvsRope), vp]
     lib.kv_store_rope_paged.restype = st
+    lib.kv_store_paged_fp8.argtypes = [P, P, P, P, P, P, P, vp]
+    lib.kv_store_paged_fp8.restype = st
+    lib.attn_varlen_paged_fp8_ex.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, ctypes.c_int32,
+                                             P, P, ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
+    lib.attn_varlen_paged_fp8_ex.restype = st
     lib.attn_varlen_paged.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, vp]
     lib.attn_varlen_paged.restype = st
     lib.attn_varlen_paged_workspace_size.argtypes = [P, P, P, ctypes.POINTER(KvsHints)]

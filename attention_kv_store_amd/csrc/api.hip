@@ -44,18 +44,19 @@ const char* dtname(int dt) {
     case KVS_F32: return "f32";
     case KVS_BF16: return "bf16";
     case KVS_I32: return "i32";
+    case KVS_FP8_E4M3: return "fp8_e4m3";
     default: return "?";
   }
 }
 
-int esize(int dt) { return dt == KVS_BF16 ? 2 : 4; }
+int esize(int dt) { return dt == KVS_BF16 ? 2 : (dt == KVS_FP8_E4M3 ? 1 : 4); }
 
 // Checks a descriptor: present, dtype in `allowed` (bitmask of 1 << dtype),
 // rank, dense row-major strides, alignment.  Returns KVS_OK or sets g_err.
 kvs_status check_tensor(const kvs_tensor* t, const char* name, unsigned allowed, int ndim,
                         bool allow_empty = false) {
   if (!t) return fail(KVS_ERR_INVALID, "%s: descriptor is NULL", name);
-  if (t->dtype < 0 || t->dtype > 2 || !(allowed & (1u << t->dtype)))
+  if (t->dtype < 0 || t->dtype > 3 || !(allowed & (1u << t->dtype)))
     return fail(KVS_ERR_INVALID, "%s: dtype %s not allowed here", name, dtname(t->dtype));
   if (t->ndim != ndim) return fail(KVS_ERR_INVALID, "%s: expected %d dims, got %d", name, ndim, t->ndim);
   int64_t numel = 1;
@@ -88,6 +89,7 @@ kvs_status check_tensor(const kvs_tensor* t, const char* name, unsigned allowed,
   } while (0)
 
 constexpr unsigned kFloatTypes = (1u << KVS_F32) | (1u << KVS_BF16);
+constexpr unsigned kCacheTypes = kFloatTypes | (1u << KVS_FP8_E4M3);   // attention may read FP8 caches
 constexpr unsigned kIntTypes = (1u << KVS_I32);
 
 // ---- attention plan --------------------------------------------------------
@@ -111,12 +113,14 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
                      int causal, const kvs_tensor* out, const kvs_tensor* lse, const kvs_hints* hints,
                      bool sizing_only, Plan* plan, bool append = false, int window = 0) {
   KVS_TRY(check_tensor(q, "q", kFloatTypes, 3));
-  KVS_TRY(check_tensor(k_cache, "k_cache", kFloatTypes, 4));
+  KVS_TRY(check_tensor(k_cache, "k_cache", kCacheTypes, 4));
   KVS_TRY(check_tensor(table, "block_table", kIntTypes, 2));
   const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
   const int64_t NB = k_cache->shape[0], page = k_cache->shape[1], Hkv = k_cache->shape[2];
   const int64_t B = table->shape[0], MB = table->shape[1];
-  if (k_cache->dtype != q->dtype) return fail(KVS_ERR_INVALID, "k_cache dtype %s != q dtype %s", dtname(k_cache->dtype), dtname(q->dtype));
+  const bool kv8 = k_cache->dtype == KVS_FP8_E4M3;   // FP8 codes: the queries are bf16
+  if (kv8 ? q->dtype != KVS_BF16 : k_cache->dtype != q->dtype)
+    return fail(KVS_ERR_INVALID, "k_cache dtype %s does not go with q dtype %s", dtname(k_cache->dtype), dtname(q->dtype));
   if (k_cache->shape[3] != D) return fail(KVS_ERR_INVALID, "k_cache head dim %lld != q head dim %lld", (long long)k_cache->shape[3], (long long)D);
   if (page != 16) return fail(KVS_ERR_UNSUPPORTED, "page size %lld not supported (only 16)", (long long)page);
   if (D != 64 && D != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)D);
@@ -127,10 +131,10 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   if (T > INT32_MAX / 2 || Hq > 4096 || NB * 16 > INT32_MAX || B * MB > INT32_MAX)
     return fail(KVS_ERR_UNSUPPORTED, "sizes beyond the 32-bit index ranges the kernels use");
   if (!sizing_only) {
-    KVS_TRY(check_tensor(v_cache, "v_cache", kFloatTypes, 4));
+    KVS_TRY(check_tensor(v_cache, "v_cache", kCacheTypes, 4));
     for (int i = 0; i < 4; ++i)
       if (v_cache->shape[i] != k_cache->shape[i]) return fail(KVS_ERR_INVALID, "v_cache shape != k_cache shape");
-    if (v_cache->dtype != q->dtype) return fail(KVS_ERR_INVALID, "v_cache dtype != q dtype");
+    if (v_cache->dtype != k_cache->dtype) return fail(KVS_ERR_INVALID, "v_cache dtype != k_cache dtype");
     if (!append) {
       KVS_TRY(check_tensor(cu, "cu_seqlens_q", kIntTypes, 1));
       if (cu->shape[0] != B + 1) return fail(KVS_ERR_INVALID, "cu_seqlens_q has %lld entries, expected B+1=%lld", (long long)cu->shape[0], (long long)(B + 1));
@@ -178,6 +182,7 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal ? 1 : 0;
   p.window = window;
+  p.kv8 = kv8 ? 1 : 0;
   plan->dt = q->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32;
   plan->D = (int)D;
   plan->decode = (T == B);
@@ -302,6 +307,11 @@ kvs_status get_plain_workspace(size_t need, void** out) {
   return KVS_OK;
 }
 
+kvs_status no_fp8(const Plan& plan) {
+  if (plan.p.kv8) return fail(KVS_ERR_INVALID, "FP8 caches need their scales: use attn_varlen_paged_fp8_ex");
+  return KVS_OK;
+}
+
 std::string window_note(const kvs::AttnParams& p) {
   return p.window > 0 ? " sliding_window=" + std::to_string(p.window) : std::string();
 }
@@ -319,8 +329,9 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
     }
     const hipError_t e = kvs::launch_decode(p, plan.dt, plan.D, stream);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-    set_dispatch("decode_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
-                 plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window", window_note(p).c_str());
+    set_dispatch("decode_%s%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
+                 p.kv8 ? "_kv_fp8" : "", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window",
+                 window_note(p).c_str());
     return KVS_OK;
   }
   int cus = 0;
@@ -376,6 +387,53 @@ kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new, cons
                                          reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "kv_store_paged launch failed: %s", hipGetErrorString(e));
   set_dispatch("kv_store_paged rows=%lld row_bytes=%lld", (long long)Tn, (long long)row_bytes);
+  return KVS_OK;
+}
+
+kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
+                              kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale, kvs_tensor* v_scale,
+                              kvs_stream_t stream) {
+  g_err.clear();
+  KVS_TRY(check_tensor(k_cache, "k_cache", 1u << KVS_FP8_E4M3, 4));
+  KVS_TRY(check_tensor(v_cache, "v_cache", 1u << KVS_FP8_E4M3, 4));
+  KVS_TRY(check_tensor(k_scale, "k_scale", 1u << KVS_F32, 3));
+  KVS_TRY(check_tensor(v_scale, "v_scale", 1u << KVS_F32, 3));
+  KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3, true));
+  KVS_TRY(check_tensor(v_new, "v_new", kFloatTypes, 3, true));
+  KVS_TRY(check_tensor(slot_mapping, "slot_mapping", kIntTypes, 1, true));
+  const int64_t Tn = k_new->shape[0], NB = k_cache->shape[0], Hkv = k_cache->shape[2], D = k_cache->shape[3];
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i]) return fail(KVS_ERR_INVALID, "v_cache shape != k_cache shape");
+  for (int i = 0; i < 3; ++i)
+    if (v_new->shape[i] != k_new->shape[i]) return fail(KVS_ERR_INVALID, "v_new shape != k_new shape");
+  if (v_new->dtype != k_new->dtype) return fail(KVS_ERR_INVALID, "v_new dtype != k_new dtype");
+  if (k_cache->shape[1] != 16) return fail(KVS_ERR_UNSUPPORTED, "page size %lld not supported (only 16)", (long long)k_cache->shape[1]);
+  if (D != 64 && D != 128) return fail(KVS_ERR_UNSUPPORTED, "head dim %lld not supported (64 or 128)", (long long)D);
+  if (k_new->shape[1] != Hkv || k_new->shape[2] != D)
+    return fail(KVS_ERR_INVALID, "k_new [T, Hkv, D] does not match the pool's [.., .., Hkv, D]");
+  for (const kvs_tensor* t : {k_scale, v_scale})
+    if (t->shape[0] != NB || t->shape[1] != Hkv || t->shape[2] != 16)
+      return fail(KVS_ERR_INVALID, "scales must be [NB, Hkv, 16] = [%lld, %lld, 16]", (long long)NB, (long long)Hkv);
+  if (slot_mapping->shape[0] != Tn) return fail(KVS_ERR_INVALID, "slot_mapping has %lld entries for %lld rows", (long long)slot_mapping->shape[0], (long long)Tn);
+  if (Tn == 0) {
+    set_dispatch("kv_store_paged_fp8: empty (nothing enqueued)");
+    return KVS_OK;
+  }
+  kvs::StoreFp8Params p{};
+  p.k_new = k_new->data;
+  p.v_new = v_new->data;
+  p.slots = static_cast<const int32_t*>(slot_mapping->data);
+  p.k_cache = k_cache->data;
+  p.v_cache = v_cache->data;
+  p.k_scale = static_cast<float*>(k_scale->data);
+  p.v_scale = static_cast<float*>(v_scale->data);
+  p.t_new = Tn;
+  p.num_slots = NB * 16;
+  p.Hkv = (int32_t)Hkv;
+  const hipError_t e = kvs::launch_store_fp8(p, k_new->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32, (int)D,
+                                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVS_ERR_HIP, "kv_store_paged_fp8 launch failed: %s", hipGetErrorString(e));
+  set_dispatch("kv_store_paged_fp8 rows=%lld kv_heads=%lld head_dim=%lld", (long long)Tn, (long long)Hkv, (long long)D);
   return KVS_OK;
 }
 
@@ -450,6 +508,7 @@ kvs_status attn_varlen_paged(const kvs_tensor* q, const kvs_tensor* k_cache, con
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, nullptr,
                     false, &plan));
+  KVS_TRY(no_fp8(plan));
   void* ws = nullptr;
   if (plan.ws_bytes) KVS_TRY(get_plain_workspace(plan.ws_bytes, &ws));
   return run_plan(plan, ws, plan.ws_bytes, reinterpret_cast<hipStream_t>(stream));
@@ -478,6 +537,7 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, nullptr, seqlens_k, scale, 1, out, lse, hints, false,
                     &plan, true, window));
+  KVS_TRY(no_fp8(plan));
   KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3));
   KVS_TRY(check_tensor(v_new, "v_new", kFloatTypes, 3));
   for (int i = 0; i < 3; ++i)
@@ -535,6 +595,33 @@ kvs_status attn_varlen_paged_ex(const kvs_tensor* q, const kvs_tensor* k_cache, 
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, hints,
                     false, &plan));
+  KVS_TRY(no_fp8(plan));
+  return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                    const kvs_tensor* k_scale, const kvs_tensor* v_scale,
+                                    const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
+                                    const kvs_tensor* seqlens_k, float scale, int causal, int32_t window,
+                                    kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                    size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
+    return fail(KVS_ERR_INVALID, "hints must be non-negative");
+  if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
+  KVS_TRY(check_tensor(k_cache, "k_cache", 1u << KVS_FP8_E4M3, 4));
+  KVS_TRY(check_tensor(k_scale, "k_scale", 1u << KVS_F32, 3));
+  KVS_TRY(check_tensor(v_scale, "v_scale", 1u << KVS_F32, 3));
+  const int64_t NB = k_cache->shape[0], Hkv = k_cache->shape[2];
+  for (const kvs_tensor* t : {k_scale, v_scale})
+    if (t->shape[0] != NB || t->shape[1] != Hkv || t->shape[2] != 16)
+      return fail(KVS_ERR_INVALID, "scales must be [NB, Hkv, 16] = [%lld, %lld, 16]", (long long)NB, (long long)Hkv);
+  Plan plan;
+  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, hints,
+                    false, &plan, false, window));
+  plan.p.k_scale = static_cast<const float*>(k_scale->data);
+  plan.p.v_scale = static_cast<const float*>(v_scale->data);
+  if (!plan.decode) return fail(KVS_ERR_UNSUPPORTED, "FP8 caches: only the decode path (one query row per sequence) so far");
   return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -550,6 +637,7 @@ kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q, const kvs_tensor* k_
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, 1, out, lse, hints, false,
                     &plan, false, window));
+  KVS_TRY(no_fp8(plan));
   return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 

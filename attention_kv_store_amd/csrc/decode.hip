@@ -119,18 +119,37 @@ struct Step {
   int last;   // last step of the piece
 };
 
-template <int D, bool BF16, bool APPEND, bool WIN>
+// FP8 (E4M3) codes -> bf16, exactly (every E4M3 value is a bf16 value): the
+// conversion instruction with unit scale, two codes per instruction.
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+  const b2 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return *reinterpret_cast<const uint32_t*>(&r);
+}
+// 8 codes (d, d+1, .., d+7) -> 8 bf16 in the layout of a 16-byte bf16 chunk
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(const u32x2& w) {
+  return u32x4{e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true), e4m3x2_to_bf16x2(w[1], false),
+               e4m3x2_to_bf16x2(w[1], true)};
+}
+
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8>
 struct DecodeWave {
   using C = DCfg<D>;
   using E = typename std::conditional<BF16, uint16_t, float>::type;
+  // K / V elements: E4M3 codes when KV8 (then q and out are bf16)
+  using KE = typename std::conditional<KV8, uint8_t, E>::type;
+  // raw K / V registers of one 8-value chunk: 16 bytes of bf16 or 8 bytes of codes
+  using KRaw = typename std::conditional<KV8, u32x2, u32x4>::type;
+  static_assert(!KV8 || (BF16 && !APPEND), "FP8 caches: bf16 queries, no fused append");
 
   const AttnParams p;   // by value: a reference would pin the kernel arguments to scratch memory
   const int lane, col, grp, g;
   const bool head_ok;
   const int h;
   const int64_t tok_stride;
-  const E* kbase;
-  const E* vbase;
+  const KE* kbase;
+  const KE* vbase;
   char* slab;
 
   float m_run, l_run;
@@ -139,7 +158,7 @@ struct DecodeWave {
   __device__ __forceinline__ DecodeWave(const AttnParams& p_, int g_, char* slab_)
       : p(p_), lane(threadIdx.x & 63), col(lane & 15), grp(lane >> 4), g(g_), head_ok(col < p_.G),
         h(g_ * p_.G + (col < p_.G ? col : 0)), tok_stride((int64_t)p_.Hkv * D),
-        kbase(static_cast<const E*>(p_.k) + (int64_t)g_ * D), vbase(static_cast<const E*>(p_.v) + (int64_t)g_ * D),
+        kbase(static_cast<const KE*>(p_.k) + (int64_t)g_ * D), vbase(static_cast<const KE*>(p_.v) + (int64_t)g_ * D),
         slab(slab_) {}
 
   __device__ __forceinline__ void reset() {
@@ -186,9 +205,13 @@ struct DecodeWave {
   }
 
   // ---- bf16 path -----------------------------------------------------------
-  struct Buf {
-    u32x4 k[C::NBS][C::KI];
-    u32x4 v[C::NBS][2 * C::VIL];
+  struct NoScales {};
+  struct Scales {
+    f32x4 ks[C::NBS], vs[C::NBS];   // scales of the lane's 4 keys (4 grp .. 4 grp + 3)
+  };
+  struct Buf : std::conditional<KV8, Scales, NoScales>::type {
+    KRaw k[C::NBS][C::KI];
+    KRaw v[C::NBS][2 * C::VIL];
     u32x4 q[C::KI];
   };
   // First element of sequence b's new K (V) row of this wave's KV head.
@@ -286,6 +309,30 @@ struct DecodeWave {
     }
   }
 
+  // KV8: the codes of one step (8 bytes per 8-value chunk, the same lane
+  // layout as the bf16 loads) and the scales of the lane's 4 keys.
+  __device__ __forceinline__ void load_kv8(const int* phys, Buf& bf) {
+    const int kp = lane & 7;
+#pragma unroll
+    for (int j = 0; j < C::NBS; ++j) {
+      const KE* kblk = kbase + (int64_t)phys[j] * kPage * tok_stride;
+      const KE* vblk = vbase + (int64_t)phys[j] * kPage * tok_stride;
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i)
+        bf.k[j][i] = *reinterpret_cast<const u32x2*>(kblk + col * tok_stride + i * 32 + grp * 8);
+#pragma unroll
+      for (int it = 0; it < C::VIL; ++it) {
+        const int dch = (lane >> 3) + 8 * it;
+        bf.v[j][2 * it] = *reinterpret_cast<const u32x2*>(vblk + (2 * kp) * tok_stride + dch * 8);
+        bf.v[j][2 * it + 1] = *reinterpret_cast<const u32x2*>(vblk + (2 * kp + 1) * tok_stride + dch * 8);
+      }
+      // scales [NB, Hkv, 16]: this head's 16 keys of the block are contiguous
+      const int64_t so = ((int64_t)phys[j] * p.Hkv + g) * kPage + grp * 4;
+      bf.ks[j] = *reinterpret_cast<const f32x4*>(p.k_scale + so);
+      bf.vs[j] = *reinterpret_cast<const f32x4*>(p.v_scale + so);
+    }
+  }
+
   // Raw, unconditional loads of one step into `bf` (phys[j] = physical block of
   // the step's j-th block, 0 for blocks past its end).
   __device__ __forceinline__ void load(const Step& st, const int* phys, Buf& bf) {
@@ -293,7 +340,9 @@ struct DecodeWave {
     const E* qp = static_cast<const E*>(p.q) + ((int64_t)(st.b < 0 ? 0 : st.t) * p.Hq + hq) * D;
 #pragma unroll
     for (int i = 0; i < C::KI; ++i) bf.q[i] = ld16(qp + i * 32 + grp * 8);
-    if constexpr (APPEND) {
+    if constexpr (KV8) {
+      load_kv8(phys, bf);
+    } else if constexpr (APPEND) {
       // append: the step holding key kl = Lk - 1 (one step per sequence, a
       // wave-uniform branch) reads that key from the new row; the cache slot
       // is written elsewhere in the same launch
@@ -331,8 +380,14 @@ struct DecodeWave {
 #pragma unroll
       for (int it = 0; it < C::VIL; ++it) {
         const int dch = (lane >> 3) + 8 * it;
-        const u32x4 w0 = v0_ok ? bf.v[j][2 * it] : zero;
-        const u32x4 w1 = v1_ok ? bf.v[j][2 * it + 1] : zero;
+        u32x4 w0, w1;
+        if constexpr (KV8) {
+          w0 = v0_ok ? e4m3x8_to_bf16x8(bf.v[j][2 * it]) : zero;
+          w1 = v1_ok ? e4m3x8_to_bf16x8(bf.v[j][2 * it + 1]) : zero;
+        } else {
+          w0 = v0_ok ? bf.v[j][2 * it] : zero;
+          w1 = v1_ok ? bf.v[j][2 * it + 1] : zero;
+        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           char* r0 = slab + j * C::VBLK + (dch * 8 + 2 * m) * C::VROW + kp * 4;
@@ -349,9 +404,30 @@ struct DecodeWave {
     for (int j = 0; j < C::NBS; ++j) {
       s[j] = f32x4{};
 #pragma unroll
-      for (int i = 0; i < C::KI; ++i) s[j] = mfma16x16x32_bf16(bf.k[j][i], q[i], s[j]);
+      for (int i = 0; i < C::KI; ++i) {
+        if constexpr (KV8) s[j] = mfma16x16x32_bf16(e4m3x8_to_bf16x8(bf.k[j][i]), q[i], s[j]);
+        else s[j] = mfma16x16x32_bf16(bf.k[j][i], q[i], s[j]);
+      }
+      // KV8: K = code * scale of its key, so the score is scaled per key
+      if constexpr (KV8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[j][r] *= bf.ks[j][r];
+      }
     }
     softmax_update<C::NBS>(s, k0, kend, klo);
+    if constexpr (KV8) {
+      // V = code * scale of its key: P carries the scale into the PV product
+      // (after l has summed the unscaled P).  Keys outside the range get 0,
+      // not 0 * an unwritten scale.
+#pragma unroll
+      for (int j = 0; j < C::NBS; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 16 * j + grp * 4 + r;
+          const bool ok = !edge || (key < kend && (!WIN || key >= klo));
+          s[j][r] = ok ? s[j][r] * bf.vs[j][r] : 0.f;
+        }
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int j = 0; j < C::NBS; ++j) {
@@ -641,10 +717,10 @@ struct DecodeWave {
   }
 };
 
-template <int D, bool BF16, bool APPEND, bool WIN>
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8>
 __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   using C = DCfg<D>;
-  using W = DecodeWave<D, BF16, APPEND, WIN>;
+  using W = DecodeWave<D, BF16, APPEND, WIN, KV8>;
   const int win = WIN ? p.window : 0;   // sliding window (0: none)
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int B = p.B;
@@ -889,7 +965,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   if (nseg > nsplit_seg) stream(nsplit_seg, nseg);
 }
 
-template <int D, bool BF16, bool APPEND, bool WIN>
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8 = false>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   using C = DCfg<D>;
   static_assert(C::SLAB == D * 40, "decode_slab_bytes must match the slab layout");
@@ -898,7 +974,7 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
   if (lds > lds_granted.load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND, WIN>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND, WIN, KV8>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
@@ -908,7 +984,7 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND, WIN>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND, WIN, KV8>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
   return hipGetLastError();
 }
 
@@ -920,6 +996,10 @@ static hipError_t launch_decode_a(const AttnParams& p, DType dt, int D, hipStrea
 }
 
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s) {
+  if (p.kv8) {   // FP8 caches, bf16 queries, no fused append
+    if (p.window > 0) return D == 64 ? launch_decode_t<64, true, false, true, true>(p, s) : launch_decode_t<128, true, false, true, true>(p, s);
+    return D == 64 ? launch_decode_t<64, true, false, false, true>(p, s) : launch_decode_t<128, true, false, false, true>(p, s);
+  }
   if (p.window > 0) return p.append ? launch_decode_a<true, true>(p, dt, D, s) : launch_decode_a<false, true>(p, dt, D, s);
   return p.append ? launch_decode_a<true, false>(p, dt, D, s) : launch_decode_a<false, false>(p, dt, D, s);
 }

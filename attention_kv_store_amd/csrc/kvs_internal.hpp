@@ -65,6 +65,24 @@ struct AttnParams {
   int32_t append;
   int32_t NB;             // cache blocks (the append writes only slots inside the pool)
   int32_t dsmall;         // decode: 1 = small batch, whole block table staged in LDS
+  // FP8 (E4M3) caches: k / v hold codes, value = code * scale of its (slot, head)
+  int32_t kv8;
+  const float* k_scale;   // [NB, Hkv, 16]
+  const float* v_scale;
+};
+
+// FP8 store: new rows [T, Hkv, D] (f32 / bf16) quantized into E4M3 code pools
+// [NB, 16, Hkv, D] with one fp32 scale per (slot, head) in [NB, Hkv, 16].
+struct StoreFp8Params {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slots;
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;
+  float* v_scale;
+  int64_t t_new, num_slots;
+  int32_t Hkv;
 };
 
 // RoPE + KV store: one workgroup per token row; angles from host-side
@@ -128,6 +146,7 @@ inline size_t prefill_lds_bytes(int D, bool bf16, int B, int meta_lds) {
 
 hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);
 hipError_t launch_rope_store(const RopeParams& p, DType dt, hipStream_t s);
+hipError_t launch_store_fp8(const StoreFp8Params& p, DType in, int D, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s);
 

@@ -6,6 +6,8 @@
 // token row of the [NB, 16, Hkv, D] pool, so the row of all Hkv heads is one
 // contiguous run of Hkv*D elements in both source and destination: the kernel
 // is a row-granular copy with 16-byte lanes (HBM-bound; no arithmetic).
+#include <type_traits>
+
 #include "kvs_device.hpp"
 #include "kvs_internal.hpp"
 
@@ -36,6 +38,114 @@ hipError_t launch_store(const StoreParams& p, DType, hipStream_t s) {
   const int64_t want = (total + 255) / 256;
   const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
   hipLaunchKernelGGL(kv_store_kernel, dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvs
+
+// ---- FP8 (E4M3) store: quantize each (row, KV head) with its own scale ----
+// A 16-lane group takes one token row of one KV head (K or V): its absmax by
+// a 16-lane max, s = absmax / 448 and the codes of x / s, both divisions in
+// fp32 and correctly rounded; the codes go to the row's slot, s to the
+// [NB, Hkv, 16] scale pool.
+namespace kvs {
+
+// Nearest E4M3 code of a finite y (ties to even), saturating at +-448: the
+// OCP E4M3 format (bias 7, subnormal step 2^-9, largest finite 448).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t c;
+  if (a < 0.015625f) {                                  // below 2^-6: multiples of 2^-9
+    c = (uint32_t)__builtin_rintf(a * 512.f);           // exact scaling, ties to even; 8 is 2^-6
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t e = (b >> 23) - 120u;                // E4M3 exponent field: (b >> 23) - 127 + 7
+    const uint32_t mant = b & 0x7FFFFFu;
+    uint32_t m = mant >> 20;                            // 3 kept mantissa bits
+    const uint32_t rest = mant & 0xFFFFFu;
+    m += (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ? 1u : 0u;
+    c = (e << 3) + m;                                   // m == 8 carries into the exponent
+  }
+  return c | sign;
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void kv_store_fp8_kernel(StoreFp8Params p) {
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int EPL = D / 16;                           // values per lane: 16 lanes per row
+  const int64_t gid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  if (gid >= p.t_new * p.Hkv * 2) return;               // whole 16-lane groups
+  const int which = (int)(gid & 1);                     // 0: K, 1: V
+  const int64_t th = gid >> 1;
+  const int h = (int)(th % p.Hkv);
+  const int64_t t = th / p.Hkv;
+  const int32_t slot = p.slots[t];
+  if (slot < 0 || (int64_t)slot >= p.num_slots) return;  // whole group
+  const E* src = static_cast<const E*>(which ? p.v_new : p.k_new) + (t * p.Hkv + h) * D + sub * EPL;
+  float x[EPL];
+  if constexpr (BF16) {
+    uint32_t w[EPL / 2];                                // EPL bf16 values: 8 or 16 bytes
+    if constexpr (EPL == 8) {
+      const u32x4 v = ld16(src);
+      for (int i = 0; i < 4; ++i) w[i] = v[i];
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+      for (int i = 0; i < 2; ++i) w[i] = v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+      x[2 * i] = bf16lo_to_f32(w[i]);
+      x[2 * i + 1] = bf16hi_to_f32(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < EPL / 4; ++c) {
+      const u32x4 v = ld16(src + c * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[c * 4 + i] = __uint_as_float(v[i]);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+  const float s = amax / 448.f;                         // correctly rounded fp32 division
+  uint32_t packed[EPL / 4];
+#pragma unroll
+  for (int q = 0; q < EPL / 4; ++q) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= (s > 0.f ? e4m3_code(x[4 * q + i] / s) : 0u) << (8 * i);
+    packed[q] = w;
+  }
+  uint8_t* dst = static_cast<uint8_t*>(which ? p.v_cache : p.k_cache) + ((int64_t)slot * p.Hkv + h) * D + sub * EPL;
+  if constexpr (EPL == 8) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = packed[0];
+  }
+  if (sub == 0) {
+    float* sc = which ? p.v_scale : p.k_scale;
+    sc[((int64_t)(slot >> 4) * p.Hkv + h) * kPage + (slot & 15)] = s;
+  }
+}
+
+hipError_t launch_store_fp8(const StoreFp8Params& p, DType in, int D, hipStream_t s) {
+  const int64_t threads = p.t_new * p.Hkv * 2 * 16;
+  if (threads == 0) return hipSuccess;
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid);
+  if (in == DType::BF16) {
+    if (D == 64) hipLaunchKernelGGL((kv_store_fp8_kernel<true, 64>), g, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((kv_store_fp8_kernel<true, 128>), g, dim3(256), 0, s, p);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((kv_store_fp8_kernel<false, 64>), g, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((kv_store_fp8_kernel<false, 128>), g, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ typedef enum {
   KVS_ERR_HIP = 4           /* a HIP runtime call or launch failed                       */
 } kvs_status;
 
-typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_I32 = 2 } kvs_dtype;
+typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_I32 = 2, KVS_FP8_E4M3 = 3 } kvs_dtype;   /* FP8: OCP E4M3 codes, 1 byte */
 
 typedef struct {
   void* data;          /* device pointer (16-byte aligned)                 */
@@ -303,6 +303,58 @@ kvs_status attn_decode_append_paged_window(const kvs_tensor* q,
                                            const kvs_hints* hints,
                                            void* workspace, size_t workspace_bytes,
                                            kvs_stream_t stream);
+
+/*
+ * FP8 KV cache.  The pages list FP8 and INT8 KV, and quantized KV layouts,
+ * among the dtypes and layouts a kernel dispatch covers ("Transformer 추론 커널
+ * (3/10)", §19) and quantized KV in the edge-case matrix (§24), and ask that the
+ * quantization group and scale layout be what the kernel expects (§7); they
+ * fix no format.  Here: codes in the OCP E4M3 format (bias 7, subnormal step
+ * 2^-9, largest finite 448, no infinities); the D values of one token row of
+ * one KV head share one fp32 scale s; the value of a code c is E4M3(c) * s.
+ *
+ *   k_cache, v_cache [NB, 16, Hkv, D] dtype KVS_FP8_E4M3 (codes)
+ *   k_scale, v_scale [NB, Hkv, 16] f32: scale of (block, head, row); a head's
+ *                    16 rows of a block are contiguous
+ */
+
+/*
+ * kv_store_paged_fp8 -- quantize new K/V token rows and write them into their
+ * slots: for each row t and KV head h, s = absmax_d |x[t, h, d]| / 448 (0 for an
+ * all-zero row) and code[d] = the E4M3 value nearest to x / s (ties to even,
+ * saturated at +-448), both divisions in fp32, correctly rounded.
+ *
+ *   k_new, v_new   [T_new, Hkv, D], f32 or bf16 (finite values)
+ *   slot_mapping   i32 [T_new]; negative = row skipped; slots >= 16 * NB skipped
+ *   k_cache, v_cache, k_scale, v_scale: as above, written in place
+ * Supported: D in {64, 128}, page size 16.  No two rows may name the same slot.
+ * T_new == 0 is a no-op.  Allocates nothing.
+ */
+kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new,
+                              const kvs_tensor* slot_mapping,
+                              kvs_tensor* k_cache, kvs_tensor* v_cache,
+                              kvs_tensor* k_scale, kvs_tensor* v_scale,
+                              kvs_stream_t stream);
+
+/*
+ * attn_varlen_paged_fp8_ex -- attn_varlen_paged_ex over an FP8 cache: the
+ * same attention with K and V the dequantized values E4M3(code) * scale.
+ * q, out are bf16.  `window` > 0 selects the sliding window of
+ * attn_varlen_paged_window_ex (and needs causal); 0 = none.  Same workspace
+ * rules.  So far only the decode path (one query row per sequence, T == B);
+ * other shapes return KVS_ERR_UNSUPPORTED.  Allocates nothing.
+ */
+kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q,
+                                    const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                    const kvs_tensor* k_scale, const kvs_tensor* v_scale,
+                                    const kvs_tensor* block_table,
+                                    const kvs_tensor* cu_seqlens_q,
+                                    const kvs_tensor* seqlens_k,
+                                    float scale, int causal, int32_t window,
+                                    kvs_tensor* out, kvs_tensor* lse,
+                                    const kvs_hints* hints,
+                                    void* workspace, size_t workspace_bytes,
+                                    kvs_stream_t stream);
 
 /* Text of the calling thread's last non-OK status ("" if none).  The pointer is
  * valid until that thread's next library call. */

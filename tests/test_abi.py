@@ -310,3 +310,82 @@ def test_rope_empty_is_noop(lib):
     a = _rope_args(T_=0)
     assert _call_rope(lib, a) == L.KVS_OK
     assert "empty" in lib.kvs_last_dispatch().decode()
+
+
+# ---- FP8 cache ---------------------------------------------------------------------
+FP8 = L.KVS_FP8_E4M3
+
+
+def _fp8_args(T_=2, B=2, Hq=4, Hkv=2, D=64, NB=8, MB=2):
+    a = _attn_args(T_=T_, B=B, Hq=Hq, Hkv=Hkv, D=D, NB=NB, MB=MB)
+    a.update(k=T([NB, 16, Hkv, D], FP8), v=T([NB, 16, Hkv, D], FP8),
+             ks=T([NB, Hkv, 16], L.KVS_F32), vs=T([NB, Hkv, 16], L.KVS_F32))
+    return a
+
+
+def _call_fp8(lib, a, causal=1, window=0):
+    return lib.attn_varlen_paged_fp8_ex(ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["ks"]), ref(a["vs"]),
+                                        ref(a["table"]), ref(a["cu"]), ref(a["lk"]), ctypes.c_float(0.125), causal,
+                                        window, ref(a["out"]), ref(a.get("lse")), None, None, 0, None)
+
+
+def test_fp8_cache_needs_the_fp8_entry(lib):
+    a = _fp8_args()
+    assert _call_ex(lib, a) == L.KVS_ERR_INVALID
+    assert "attn_varlen_paged_fp8_ex" in lib.kvs_last_error().decode()
+
+
+@pytest.mark.parametrize("mutate,expect,msg", [
+    (lambda a: a.update(ks=T([8, 2, 8], L.KVS_F32)), L.KVS_ERR_INVALID, "scales must be"),
+    (lambda a: a.update(vs=T([8, 3, 16], L.KVS_F32)), L.KVS_ERR_INVALID, "scales must be"),
+    (lambda a: a.update(ks=T([8, 2, 16], L.KVS_BF16)), L.KVS_ERR_INVALID, "k_scale"),
+    (lambda a: a.update(k=T([8, 16, 2, 64]), v=T([8, 16, 2, 64])), L.KVS_ERR_INVALID, "k_cache"),
+    (lambda a: a.update(q=T([2, 4, 64], L.KVS_F32), out=T([2, 4, 64], L.KVS_F32)), L.KVS_ERR_INVALID, "does not go with"),
+    (lambda a: a.update(v=T([8, 16, 2, 64])), L.KVS_ERR_INVALID, "v_cache"),
+])
+def test_fp8_attention_validation(lib, mutate, expect, msg):
+    a = _fp8_args()
+    mutate(a)
+    assert _call_fp8(lib, a) == expect
+    assert msg in lib.kvs_last_error().decode()
+
+
+def test_fp8_window_needs_causal(lib):
+    assert _call_fp8(lib, _fp8_args(), causal=0, window=4) == L.KVS_ERR_INVALID
+    assert _call_fp8(lib, _fp8_args(), window=-2) == L.KVS_ERR_INVALID
+
+
+def test_fp8_prefill_shapes_unsupported(lib):
+    a = _fp8_args(T_=8, B=2)
+    assert _call_fp8(lib, a) == L.KVS_ERR_UNSUPPORTED
+    assert "only the decode path" in lib.kvs_last_error().decode()
+
+
+def _call_store_fp8(lib, a):
+    return lib.kv_store_paged_fp8(ref(a["kn"]), ref(a["vn"]), ref(a["slots"]), ref(a["k"]), ref(a["v"]),
+                                  ref(a["ks"]), ref(a["vs"]), None)
+
+
+def _store_fp8_args(Tn=4, Hkv=2, D=64, NB=4):
+    return dict(kn=T([Tn, Hkv, D]), vn=T([Tn, Hkv, D]), slots=T([Tn], L.KVS_I32), k=T([NB, 16, Hkv, D], FP8),
+                v=T([NB, 16, Hkv, D], FP8), ks=T([NB, Hkv, 16], L.KVS_F32), vs=T([NB, Hkv, 16], L.KVS_F32))
+
+
+@pytest.mark.parametrize("mutate,expect,msg", [
+    (lambda a: a.update(k=T([4, 16, 2, 64])), L.KVS_ERR_INVALID, "k_cache"),
+    (lambda a: a.update(ks=T([4, 2, 15], L.KVS_F32)), L.KVS_ERR_INVALID, "scales must be"),
+    (lambda a: a.update(vn=T([4, 2, 64], L.KVS_F32)), L.KVS_ERR_INVALID, "v_new dtype"),
+    (lambda a: a.update(kn=T([4, 3, 64]), vn=T([4, 3, 64])), L.KVS_ERR_INVALID, "k_new"),
+    (lambda a: a.update(slots=T([5], L.KVS_I32)), L.KVS_ERR_INVALID, "slot_mapping"),
+    (lambda a: a.update(kn=T([4, 2, 96]), vn=T([4, 2, 96]), k=T([4, 16, 2, 96], FP8), v=T([4, 16, 2, 96], FP8)),
+     L.KVS_ERR_UNSUPPORTED, "head dim"),
+])
+def test_fp8_store_validation(lib, mutate, expect, msg):
+    a = _store_fp8_args()
+    mutate(a)
+    assert _call_store_fp8(lib, a) == expect
+    assert msg in lib.kvs_last_error().decode()
+
+
+def test_fp8_store_empty_is_noop(lib):
+    assert _call_store_fp8(lib, _store_fp8_args(Tn=0)) == L.KVS_OK
