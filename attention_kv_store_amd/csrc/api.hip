@@ -232,7 +232,7 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   // partial outputs are addressed with 32-bit byte offsets
   if ((double)(nwg + B) * Hq * D * sizeof(float) >= 2147483648.0)
     return fail(KVS_ERR_UNSUPPORTED, "decode partial buffer would exceed 2 GiB (num_splits %lld)", (long long)nwg);
-  const int slab = kvs::decode_slab_bytes((int)D);
+  const int slab = kvs::decode_slab_bytes((int)D, kv8);
   // (the whole table is copied in 16-byte pieces: it must be 16-byte aligned)
   p.dsmall = B <= kvs::kDecodeSmallB && B * MB <= kvs::kDecodeSmallTbl &&
              reinterpret_cast<uintptr_t>(table->data) % 16 == 0 &&

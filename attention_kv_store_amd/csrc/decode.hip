@@ -52,13 +52,15 @@
 
 namespace kvs {
 
-template <int D>
+template <int D, int NBS_ = 1>
 struct DCfg {
-  // 16-key blocks per step.  One block keeps the bytes in flight near the
-  // bandwidth-latency product: a deeper prefetch only lengthens the memory
-  // queues (and so the latency of every access, including the publication
-  // of partials at the end), without raising the throughput.
-  static constexpr int NBS = 1;
+  // 16-key blocks per step.  For bf16 / fp32 one block keeps the bytes in
+  // flight near the bandwidth-latency product: a deeper prefetch only
+  // lengthens the memory queues (and so the latency of every access,
+  // including the publication of partials at the end), without raising the
+  // throughput.  FP8 codes are half the bytes; kDecodeKv8Blocks sets their
+  // blocks per step.
+  static constexpr int NBS = NBS_;
   static constexpr int KI = D / 32;               // 16x16x32 k-steps over d
   static constexpr int NDB = D / 16;              // 16-wide d blocks of the output
   static constexpr int VROW = 40;                 // bytes per V^T row (16 keys + pad)
@@ -135,7 +137,7 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(const u32x2& w) {
 
 template <int D, bool BF16, bool APPEND, bool WIN, bool KV8>
 struct DecodeWave {
-  using C = DCfg<D>;
+  using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   // K / V elements: E4M3 codes when KV8 (then q and out are bf16)
   using KE = typename std::conditional<KV8, uint8_t, E>::type;
@@ -719,7 +721,7 @@ struct DecodeWave {
 
 template <int D, bool BF16, bool APPEND, bool WIN, bool KV8>
 __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
-  using C = DCfg<D>;
+  using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
   using W = DecodeWave<D, BF16, APPEND, WIN, KV8>;
   const int win = WIN ? p.window : 0;   // sliding window (0: none)
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -967,8 +969,8 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 
 template <int D, bool BF16, bool APPEND, bool WIN, bool KV8 = false>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
-  using C = DCfg<D>;
-  static_assert(C::SLAB == D * 40, "decode_slab_bytes must match the slab layout");
+  using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
+  static_assert(C::SLAB == decode_slab_bytes(D, KV8), "decode_slab_bytes must match the slab layout");
   const size_t lds = decode_lds_bytes(p.B, decode_tbl_ints(p.B, p.MB, p.dsmall != 0), p.hpw, C::SLAB);
   // dynamic LDS above the default limit must be requested; grow it as needed
   // (per instantiation; atomic so that concurrent first calls are safe)

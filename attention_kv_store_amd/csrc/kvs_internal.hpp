@@ -132,7 +132,12 @@ inline size_t decode_lds_bytes(int B, int tbl_ints, int hpw, int slab_bytes) {
   const size_t ints = (size_t)((B + 3) & ~3) + (size_t)((B + 1 + 3) & ~3) + (size_t)tbl_ints;
   return ints * sizeof(int) + (size_t)hpw * slab_bytes;
 }
-inline int decode_slab_bytes(int D) { return D * 40; }
+// 16-key blocks per decode step over FP8 caches (bf16 / fp32: one).  Two
+// blocks (the bf16 step's bytes in flight) measured slower than one: the FP8
+// step is bounded by its instruction chain, not by the bytes it waits for.
+constexpr int kDecodeKv8Blocks = 1;
+// V^T bytes per wave: 16 keys (+ pad) x D per block of a step
+constexpr int decode_slab_bytes(int D, bool kv8) { return D * 40 * (kv8 ? kDecodeKv8Blocks : 1); }
 
 // Prefill LDS bytes per workgroup: two K/V stages, then cu_seqlens_q and
 // seqlens_k when staged.

@@ -291,6 +291,65 @@ def runner_replays(dec, args):
     return res
 
 
+def fp8_decode_line(dec, args):
+    """The decode workload over an FP8 (E4M3) cache: every key row quantized by
+    kv_store_paged_fp8 (one scale per row and KV head), then
+    attn_varlen_paged_fp8 timed from graph replays over 4 replicas.  Bytes
+    read per launch: the codes of every visible key row of K and V plus their
+    fp32 scales."""
+    import torch
+    import attention_kv_store_amd as kvs
+
+    rows = dec.store_rows()
+    reps = []
+    for r in range(4):
+        kc = torch.zeros(dec.pool_shape(), dtype=torch.uint8, device="cuda")
+        vc = torch.zeros_like(kc)
+        ks = torch.zeros(dec.num_blocks, dec.Hkv, 16, dtype=torch.float32, device="cuda")
+        vs = torch.zeros_like(ks)
+        kvs.kv_store_paged_fp8(torch.from_numpy(dec.k_tokens[rows]).to(torch.bfloat16).cuda(),
+                               torch.from_numpy(dec.v_tokens[rows]).to(torch.bfloat16).cuda(),
+                               torch.from_numpy(dec.slots[rows]).cuda(), kc, vc, ks, vs)
+        q = torch.from_numpy(dec.q).to(torch.bfloat16).cuda()
+        meta = [torch.from_numpy(x).cuda() for x in (dec.block_table, dec.cu_seqlens_q, dec.k_lens)]
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device="cuda")
+        ws = torch.zeros(max(kvs.workspace_size(q, kc, meta[0]), 1), dtype=torch.uint8, device="cuda")
+        reps.append((q, kc, vc, ks, vs, meta, out, lse, ws))
+
+    def call(i):
+        q, kc, vc, ks, vs, meta, out, lse, ws = reps[i % 4]
+        kvs.attn_varlen_paged_fp8(q, kc, vc, ks, vs, *meta, dec.scale, True, out=out, lse=lse, workspace=ws)
+
+    for i in range(8):
+        call(i)
+    torch.cuda.synchronize()
+    n = 100
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            call(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    nrep = max(2, args.steps // n)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(nrep):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (nrep * n) * 1e3
+    nkeys = int(dec.k_lens.sum())
+    read = 2 * nkeys * dec.Hkv * (dec.D + 4)        # codes and scales of K and V
+    res = {"workload": "paged_decode_bf16 with an FP8 (E4M3) cache", "avg_launch_us": round(us, 3),
+           "bytes_per_launch": read, "GBs": round(read / (us * 1e-6) / 1e9, 1),
+           "bf16_kv_equivalent_GBs": round(2 * nkeys * dec.Hkv * dec.D * 2 / (us * 1e-6) / 1e9, 1),
+           "dispatch": kvs.last_dispatch()}
+    del graph, reps
+    torch.cuda.empty_cache()
+    return res
+
+
 def rope_store_line(args):
     """kv_store_rope_paged at the causal prefill workload's shape (16 x 512 new
     rows, 32 / 8 heads, D 128) and the decode workload's (64 rows, 32 / 8 heads,
@@ -621,6 +680,8 @@ def main():
         log(f"sliding window: {sw}")
 
     if not args.no_extras:
+        line["fp8_kv_decode"] = fp8_decode_line(dec, args)
+        log(f"fp8 decode: {line['fp8_kv_decode']}")
         line["rope_store"] = rope_store_line(args)
         log(f"rope + store: {line['rope_store']}")
 
