@@ -96,8 +96,7 @@ def attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu
                           scale: float, causal: bool = True, out=None, lse=None, *, return_lse: bool = True,
                           num_splits: int = 0, workspace=None, window: int = 0):
     """Attention over an FP8 cache (values = E4M3(code) * scale of the row and
-    head); q / out bf16.  Decode shapes (one query row per sequence) so far.
-    Returns ``(out, lse)``."""
+    head); q / out bf16.  Returns ``(out, lse)``."""
     import torch
 
     if window and not causal:

@@ -621,7 +621,6 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cac
                     false, &plan, false, window));
   plan.p.k_scale = static_cast<const float*>(k_scale->data);
   plan.p.v_scale = static_cast<const float*>(v_scale->data);
-  if (!plan.decode) return fail(KVS_ERR_UNSUPPORTED, "FP8 caches: only the decode path (one query row per sequence) so far");
   return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 

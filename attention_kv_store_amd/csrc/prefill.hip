@@ -28,6 +28,11 @@
 //    table entries past a sequence's last block are never used.
 //  * Causal (bottom-right, with cached prefix c = Lk - Lq): tiles wholly above
 //    a wave's rows are skipped; only tiles crossing the diagonal are masked.
+//  * FP8 caches (the KV8 instantiations, bf16 queries): each lane loads the
+//    8 codes behind the 16-byte chunk the bf16 copy would have moved (same
+//    element offsets: one code per element) and the scale of its key row,
+//    dequantizes them to bf16 in registers and writes them to the same LDS
+//    place after the step's math; the rest of the kernel is the bf16 one.
 //  * Sliding window W (the WIN instantiations): the row at position p sees
 //    keys p - W + 1 .. p.  An item's key tiles start at the tile holding its
 //    first row's window start; rows before that start are copied as zero rows
@@ -97,8 +102,23 @@ __device__ __attribute__((aligned(16))) uint16_t g_zero_row[128];
 // entries one step earlier, and the next item's Q rows as soon as the last
 // score tile of the current item is formed, so moving to a new item costs
 // about what moving to a new key tile does.
-template <int D, bool BF16, int NW, bool WIN>
+// 8 E4M3 codes times a scale, rounded to bf16 (nearest even): one 16-byte
+// chunk of a bf16 row.  The conversion instruction decodes the OCP E4M3
+// format exactly.
+__device__ __forceinline__ u32x4 e4m3x8_scaled_to_bf16(const u32x2& w, float sc) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const auto f = (h & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w[h >> 1], true)
+                           : __builtin_amdgcn_cvt_pk_f32_fp8(w[h >> 1], false);
+    r[h] = pack_bf16x2(f[0] * sc, f[1] * sc);
+  }
+  return r;
+}
+
+template <int D, bool BF16, int NW, bool WIN, bool KV8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(AttnParams p) {
+  static_assert(!KV8 || BF16, "FP8 caches take bf16 queries");
   using C = PCfg<D, BF16, NW>;
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -282,6 +302,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   u32x4 kreg[BF16 ? 1 : C::KIT];
   u32x4 vreg[BF16 ? 1 : C::KIT];
+  // KV8: codes (8 per chunk) and the scale of the chunk's key row
+  u32x2 k8[KV8 ? C::KIT : 1], v8[KV8 ? C::KIT : 1];
+  float ks8[KV8 ? C::KIT : 1], vs8[KV8 ? C::KIT : 1];
   // bf16: wave w copies keys [w KPW, w KPW + KPW) of every tile, all in page
   // w KPW / 16.  Per lane and copy j, the element offset inside that page of
   // its 16-byte chunk, with the chunk slot swizzled by key: the same for
@@ -306,7 +329,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto issue_loads = [&](int pgv, const Step& s, int buf) {
     const E* kbase = kv_base(s.it, p.k);
     const E* vbase = kv_base(s.it, p.v);
-    if constexpr (BF16) {
+    if constexpr (KV8) {
+      // codes and scales into registers; write_stage dequantizes them into LDS
+      const int pgi = (wave * C::KPW) >> 4;
+      const int pk = s.t * C::NPG + pgi < s.it.npages ? __builtin_amdgcn_readlane(pgv, pgi) : 0;
+      const uint8_t* kpage = static_cast<const uint8_t*>(p.k) + (int64_t)s.it.kvh * D + pk * page_stride;
+      const uint8_t* vpage = static_cast<const uint8_t*>(p.v) + (int64_t)s.it.kvh * D + pk * page_stride;
+      const int64_t so = ((int64_t)pk * p.Hkv + s.it.kvh) * kPage;   // scales [NB, Hkv, 16]
+#pragma unroll
+      for (int j = 0; j < C::KIT; ++j) {
+        const int key = wave * C::KPW + (j * 64 + lane) / C::CPR;   // key row in the tile
+        k8[j] = *reinterpret_cast<const u32x2*>(kpage + kpo[j]);
+        v8[j] = *reinterpret_cast<const u32x2*>(vpage + vpo[j]);
+        ks8[j] = p.k_scale[so + (key & 15)];
+        vs8[j] = p.v_scale[so + (key & 15)];
+      }
+    } else if constexpr (BF16) {
       char* Kd = smem + buf * C::STAGE;
       char* Vd = Kd + C::KTILE;
       // this wave's page of the tile (block 0 past the sequence's last page)
@@ -359,7 +397,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // tiles that have them always take the masked path, which selects their
   // scores away.
   auto write_stage = [&](int buf, const Step& s) {
-    if constexpr (!BF16) {
+    if constexpr (KV8) {
+      // the places the bf16 copies would have written: block wave KIT + j,
+      // 16 bytes per lane; keys past nkeys or before klo are zero
+      char* Kd = smem + buf * C::STAGE;
+      char* Vd = Kd + C::KTILE;
+      const int kv0 = s.t * C::BN;
+      bool edge = kv0 + wave * C::KPW + C::KPW > s.it.nkeys;   // uniform
+      if constexpr (WIN) edge = edge || kv0 + wave * C::KPW < s.it.klo;
+      const u32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < C::KIT; ++j) {
+        const int blk = wave * C::KIT + j;
+        const int key = kv0 + wave * C::KPW + (j * 64 + lane) / C::CPR;
+        const bool live = !edge || (key < s.it.nkeys && (!WIN || key >= s.it.klo));
+        st16(Kd + blk * 1024 + lane * 16, live ? e4m3x8_scaled_to_bf16(k8[j], ks8[j]) : zero);
+        st16(Vd + blk * 1024 + lane * 16, live ? e4m3x8_scaled_to_bf16(v8[j], vs8[j]) : zero);
+      }
+    } else if constexpr (!BF16) {
       char* Ks = smem + buf * C::STAGE;
       char* Vs = Ks + C::KTILE;
       const int kv0 = s.t * C::BN;
@@ -662,14 +717,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-template <int D, bool BF16, int NW, bool WIN>
+template <int D, bool BF16, int NW, bool WIN, bool KV8 = false>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
   const size_t lds = prefill_lds_bytes(D, BF16, p.B, p.meta_lds);
   // dynamic LDS above the default limit must be requested; grow it as needed
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
   if (lds > lds_granted.load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16, NW, WIN>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16, NW, WIN, KV8>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
@@ -679,7 +734,7 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<D, BF16, NW, WIN>), dim3(p.pgrid), dim3(64 * NW), lds, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, BF16, NW, WIN, KV8>), dim3(p.pgrid), dim3(64 * NW), lds, s, p);
   return hipGetLastError();
 }
 
@@ -693,6 +748,11 @@ static hipError_t launch_prefill_w(const AttnParams& p, DType dt, int D, hipStre
 }
 
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s) {
+  if (p.kv8) {   // FP8 caches: bf16 queries, 8-wave workgroups
+    if (p.pnw != 8) return hipErrorInvalidValue;
+    if (p.window > 0) return D == 64 ? launch_prefill_t<64, true, 8, true, true>(p, s) : launch_prefill_t<128, true, 8, true, true>(p, s);
+    return D == 64 ? launch_prefill_t<64, true, 8, false, true>(p, s) : launch_prefill_t<128, true, 8, false, true>(p, s);
+  }
   return p.window > 0 ? launch_prefill_w<true>(p, dt, D, s) : launch_prefill_w<false>(p, dt, D, s);
 }
 

@@ -340,9 +340,9 @@ kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new,
  * attn_varlen_paged_fp8_ex -- attn_varlen_paged_ex over an FP8 cache: the
  * same attention with K and V the dequantized values E4M3(code) * scale.
  * q, out are bf16.  `window` > 0 selects the sliding window of
- * attn_varlen_paged_window_ex (and needs causal); 0 = none.  Same workspace
- * rules.  So far only the decode path (one query row per sequence, T == B);
- * other shapes return KVS_ERR_UNSUPPORTED.  Allocates nothing.
+ * attn_varlen_paged_window_ex (and needs causal); 0 = none.  Same paths
+ * (decode and prefill / extend), shapes, limits and workspace rules as
+ * attn_varlen_paged_ex.  Allocates nothing.
  */
 kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q,
                                     const kvs_tensor* k_cache, const kvs_tensor* v_cache,

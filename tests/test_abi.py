@@ -355,12 +355,6 @@ def test_fp8_window_needs_causal(lib):
     assert _call_fp8(lib, _fp8_args(), window=-2) == L.KVS_ERR_INVALID
 
 
-def test_fp8_prefill_shapes_unsupported(lib):
-    a = _fp8_args(T_=8, B=2)
-    assert _call_fp8(lib, a) == L.KVS_ERR_UNSUPPORTED
-    assert "only the decode path" in lib.kvs_last_error().decode()
-
-
 def _call_store_fp8(lib, a):
     return lib.kv_store_paged_fp8(ref(a["kn"]), ref(a["vn"]), ref(a["slots"]), ref(a["k"]), ref(a["v"]),
                                   ref(a["ks"]), ref(a["vs"]), None)

@@ -95,18 +95,18 @@ def _fp8_batch_pools(b):
     return dev, host
 
 
-def _check_fp8_attention(b, dev, host, rows=None, **kw):
+def _check_fp8_attention(b, dev, host, rows=None, causal=True, **kw):
     import attention_kv_store_amd as kvs
     from oracle import attention_oracle, dequantize_pool
     from tests.gpu_side import to_f64
     q = torch.from_numpy(b.q).to(torch.bfloat16).cuda()
     out, lse = kvs.attn_varlen_paged_fp8(q, dev[0], dev[1], dev[2], dev[3], torch.from_numpy(b.block_table).cuda(),
                                          torch.from_numpy(b.cu_seqlens_q).cuda(), torch.from_numpy(b.k_lens).cuda(),
-                                         b.scale, True, window=b.window, **kw)
+                                         b.scale, causal, window=b.window, **kw)
     torch.cuda.synchronize()
     kq, vq, ks, vs = host
     ro, rl = attention_oracle(b.q, dequantize_pool(kq, ks), dequantize_pool(vq, vs), b.block_table, b.cu_seqlens_q,
-                              b.k_lens, b.scale, True, window=b.window, rows=rows)
+                              b.k_lens, b.scale, causal, window=b.window, rows=rows)
     go, gl = to_f64(out), to_f64(lse)
     if rows is not None:
         ro, rl, go, gl = ro[rows], rl[rows], go[rows], gl[rows]
@@ -150,12 +150,39 @@ def test_fp8_decode_named_workload():
     _check_fp8_attention(b, dev, host)
 
 
-def test_fp8_prefill_not_yet_supported():
-    import attention_kv_store_amd as kvs
+PREFILL_Q = [1, 17, 64, 65, 100, 200, 30, 129]
+PREFILL_K = [1, 17, 64, 65, 300, 200, 500, 129]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("heads", [(8, 2), (32, 8), (4, 4), (12, 4)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill(D, heads, causal):
+    """Prefill and extend rows (cached prefixes over several tiles, a one-row
+    sequence, ragged tails) over an FP8 cache."""
     from workloads import make_batch
-    b = make_batch(1460, [5, 3], [5, 9], Hq=8, Hkv=2, D=64, dtype="bf16")
-    dev, _ = _fp8_batch_pools(b)
-    with pytest.raises(kvs.KvsError, match="only the decode path"):
-        kvs.attn_varlen_paged_fp8(torch.from_numpy(b.q).to(torch.bfloat16).cuda(), dev[0], dev[1], dev[2], dev[3],
-                                  torch.from_numpy(b.block_table).cuda(), torch.from_numpy(b.cu_seqlens_q).cuda(),
-                                  torch.from_numpy(b.k_lens).cuda(), b.scale, True)
+    Hq, Hkv = heads
+    b = make_batch(1470 + D + Hq + causal, PREFILL_Q, PREFILL_K, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", causal=causal,
+                   name=f"prefill-D{D}-{Hq}/{Hkv}-{'causal' if causal else 'full'}")
+    dev, host = _fp8_batch_pools(b)
+    _check_fp8_attention(b, dev, host, causal=causal)
+
+
+@pytest.mark.parametrize("W", [1, 17, 64, 130])
+def test_fp8_prefill_window(W):
+    from workloads import make_batch
+    b = make_batch(1480 + W, PREFILL_Q, PREFILL_K, Hq=8, Hkv=2, D=128, dtype="bf16", window=W,
+                   name=f"prefill-window{W}")
+    dev, host = _fp8_batch_pools(b)
+    _check_fp8_attention(b, dev, host)
+
+
+@pytest.mark.parametrize("name", ["causal_prefill_bf16", "mixed_prefill_decode_bf16"])
+def test_fp8_named_prefill_workloads(name):
+    """The 16 x 512 causal prefill and the mixed 2 x 256 + 30 x 1 batch over an
+    FP8 cache, on sampled rows."""
+    from tests.test_gpu_parity import _sample_rows
+    from workloads import NAMED
+    b = NAMED[name]()
+    dev, host = _fp8_batch_pools(b)
+    _check_fp8_attention(b, dev, host, rows=_sample_rows(b))
