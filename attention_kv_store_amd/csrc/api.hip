@@ -339,9 +339,9 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   p.pgrid = (p.pnw == 8 ? 1 : 2) * cus;
   const hipError_t e = kvs::launch_prefill(p, plan.dt, plan.D, stream);
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
-  set_dispatch("prefill_%s_d%d grid=%d (persistent) waves/wg=%d head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d%s",
-               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.pgrid, p.pnw, p.NHG, p.HW, 32 * p.TPW,
-               p.meta_lds, window_note(p).c_str());
+  set_dispatch("prefill_%s%s_d%d grid=%d (persistent) waves/wg=%d head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d%s",
+               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", p.kv8 ? "_kv_fp8" : "", plan.D, p.pgrid, p.pnw, p.NHG,
+               p.HW, 32 * p.TPW, p.meta_lds, window_note(p).c_str());
   return KVS_OK;
 }
 

@@ -291,27 +291,28 @@ def runner_replays(dec, args):
     return res
 
 
-def fp8_decode_line(dec, args):
-    """The decode workload over an FP8 (E4M3) cache: every key row quantized by
+def fp8_line(batch, args, n=100):
+    """A workload over an FP8 (E4M3) cache: every key row quantized by
     kv_store_paged_fp8 (one scale per row and KV head), then
-    attn_varlen_paged_fp8 timed from graph replays over 4 replicas.  Bytes
-    read per launch: the codes of every visible key row of K and V plus their
-    fp32 scales."""
+    attn_varlen_paged_fp8 timed from graph replays over 4 replicas.  Bytes read
+    per launch: the codes of every visible key row of K and V plus their fp32
+    scales."""
     import torch
     import attention_kv_store_amd as kvs
+    from workloads import attention_flops
 
-    rows = dec.store_rows()
+    rows = batch.store_rows()
     reps = []
     for r in range(4):
-        kc = torch.zeros(dec.pool_shape(), dtype=torch.uint8, device="cuda")
+        kc = torch.zeros(batch.pool_shape(), dtype=torch.uint8, device="cuda")
         vc = torch.zeros_like(kc)
-        ks = torch.zeros(dec.num_blocks, dec.Hkv, 16, dtype=torch.float32, device="cuda")
+        ks = torch.zeros(batch.num_blocks, batch.Hkv, 16, dtype=torch.float32, device="cuda")
         vs = torch.zeros_like(ks)
-        kvs.kv_store_paged_fp8(torch.from_numpy(dec.k_tokens[rows]).to(torch.bfloat16).cuda(),
-                               torch.from_numpy(dec.v_tokens[rows]).to(torch.bfloat16).cuda(),
-                               torch.from_numpy(dec.slots[rows]).cuda(), kc, vc, ks, vs)
-        q = torch.from_numpy(dec.q).to(torch.bfloat16).cuda()
-        meta = [torch.from_numpy(x).cuda() for x in (dec.block_table, dec.cu_seqlens_q, dec.k_lens)]
+        kvs.kv_store_paged_fp8(torch.from_numpy(batch.k_tokens[rows]).to(torch.bfloat16).cuda(),
+                               torch.from_numpy(batch.v_tokens[rows]).to(torch.bfloat16).cuda(),
+                               torch.from_numpy(batch.slots[rows]).cuda(), kc, vc, ks, vs)
+        q = torch.from_numpy(batch.q).to(torch.bfloat16).cuda()
+        meta = [torch.from_numpy(x).cuda() for x in (batch.block_table, batch.cu_seqlens_q, batch.k_lens)]
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device="cuda")
         ws = torch.zeros(max(kvs.workspace_size(q, kc, meta[0]), 1), dtype=torch.uint8, device="cuda")
@@ -319,19 +320,19 @@ def fp8_decode_line(dec, args):
 
     def call(i):
         q, kc, vc, ks, vs, meta, out, lse, ws = reps[i % 4]
-        kvs.attn_varlen_paged_fp8(q, kc, vc, ks, vs, *meta, dec.scale, True, out=out, lse=lse, workspace=ws)
+        kvs.attn_varlen_paged_fp8(q, kc, vc, ks, vs, *meta, batch.scale, batch.causal, out=out, lse=lse,
+                                  workspace=ws)
 
     for i in range(8):
         call(i)
     torch.cuda.synchronize()
-    n = 100
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for i in range(n):
             call(i)
     graph.replay()
     torch.cuda.synchronize()
-    nrep = max(2, args.steps // n)
+    nrep = max(2, args.steps // (4 * n)) if batch.T != batch.B else max(2, args.steps // n)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(nrep):
@@ -339,12 +340,11 @@ def fp8_decode_line(dec, args):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / (nrep * n) * 1e3
-    nkeys = int(dec.k_lens.sum())
-    read = 2 * nkeys * dec.Hkv * (dec.D + 4)        # codes and scales of K and V
-    res = {"workload": "paged_decode_bf16 with an FP8 (E4M3) cache", "avg_launch_us": round(us, 3),
-           "bytes_per_launch": read, "GBs": round(read / (us * 1e-6) / 1e9, 1),
-           "bf16_kv_equivalent_GBs": round(2 * nkeys * dec.Hkv * dec.D * 2 / (us * 1e-6) / 1e9, 1),
-           "dispatch": kvs.last_dispatch()}
+    nkeys = int(batch.k_lens.sum())
+    read = 2 * nkeys * batch.Hkv * (batch.D + 4)        # codes and scales of K and V
+    res = {"workload": f"{batch.name} with an FP8 (E4M3) cache", "avg_launch_us": round(us, 3),
+           "kv_bytes_per_launch": read, "kv_GBs": round(read / (us * 1e-6) / 1e9, 1),
+           "TFLOPs": round(attention_flops(batch) / (us * 1e-6) / 1e12, 1), "dispatch": kvs.last_dispatch()}
     del graph, reps
     torch.cuda.empty_cache()
     return res
@@ -680,8 +680,9 @@ def main():
         log(f"sliding window: {sw}")
 
     if not args.no_extras:
-        line["fp8_kv_decode"] = fp8_decode_line(dec, args)
-        log(f"fp8 decode: {line['fp8_kv_decode']}")
+        from workloads import causal_prefill_bf16 as _cp
+        line["fp8_kv"] = {"decode": fp8_line(dec, args), "prefill": fp8_line(_cp(), args, n=40)}
+        log(f"fp8 cache: {line['fp8_kv']}")
         line["rope_store"] = rope_store_line(args)
         log(f"rope + store: {line['rope_store']}")
 
