@@ -350,6 +350,65 @@ def fp8_line(batch, args, n=100):
     return res
 
 
+def context_sweep(args):
+    """Decode over 64 sequences at contexts 512, 4096 and 16384 (all of one
+    length), 32 / 8 heads, D 128, bf16 -- the decode microbenchmark shape the
+    pages' manifest lists.  Pools filled on the device (torch.randn), block
+    tables random permutations; replicas so that the rotation exceeds the
+    256 MB Infinity Cache.  Timed from graph replays of attn_varlen_paged."""
+    import torch
+    import attention_kv_store_amd as kvs
+
+    B, Hq, Hkv, D = 64, 32, 8, 128
+    res = {}
+    for ctx in (512, 4096, 16384):
+        nblk = B * ctx // 16
+        kv_bytes = 2 * B * ctx * Hkv * D * 2
+        R = max(1, -(-512 * 2**20 // kv_bytes))
+        reps = []
+        g = torch.Generator(device="cuda").manual_seed(ctx)
+        for r in range(R):
+            kc = torch.randn(nblk + 1, 16, Hkv, D, device="cuda", generator=g).to(torch.bfloat16)
+            vc = torch.randn(nblk + 1, 16, Hkv, D, device="cuda", generator=g).to(torch.bfloat16)
+            table = torch.randperm(nblk, device="cuda", generator=g).to(torch.int32).view(B, ctx // 16).contiguous()
+            q = torch.randn(B, Hq, D, device="cuda", generator=g).to(torch.bfloat16)
+            lens = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+            cu = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+            ws = torch.zeros(max(kvs.workspace_size(q, kc, table), 1), dtype=torch.uint8, device="cuda")
+            reps.append((q, kc, vc, table, cu, lens, torch.empty_like(q),
+                         torch.empty(B, Hq, dtype=torch.float32, device="cuda"), ws))
+
+        def call(i):
+            q, kc, vc, table, cu, lens, out, lse, ws = reps[i % R]
+            kvs.attn_varlen_paged(q, kc, vc, table, cu, lens, D ** -0.5, True, out=out, lse=lse, workspace=ws)
+
+        for i in range(4):
+            call(i)
+        torch.cuda.synchronize()
+        n = 40
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                call(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        nrep = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(nrep):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / (nrep * n) * 1e3
+        res[f"context_{ctx}"] = {"us": round(us, 2), "kv_bytes": kv_bytes, "replicas": R,
+                                 "GBs": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+                                 "frac": round(kv_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "dispatch": kvs.last_dispatch()}
+        del graph, reps
+        torch.cuda.empty_cache()
+    return res
+
+
 def rope_store_line(args):
     """kv_store_rope_paged at the causal prefill workload's shape (16 x 512 new
     rows, 32 / 8 heads, D 128) and the decode workload's (64 rows, 32 / 8 heads,
@@ -683,6 +742,8 @@ def main():
         from workloads import causal_prefill_bf16 as _cp
         line["fp8_kv"] = {"decode": fp8_line(dec, args), "prefill": fp8_line(_cp(), args, n=40)}
         log(f"fp8 cache: {line['fp8_kv']}")
+        line["decode_context_sweep"] = context_sweep(args)
+        log(f"decode context sweep: {line['decode_context_sweep']}")
         line["rope_store"] = rope_store_line(args)
         log(f"rope + store: {line['rope_store']}")
 
