@@ -94,7 +94,7 @@ def kv_store_paged_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_
 
 def attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k,
                           scale: float, causal: bool = True, out=None, lse=None, *, return_lse: bool = True,
-                          num_splits: int = 0, workspace=None, window: int = 0):
+                          num_splits: int = 0, workspace=None, window: int = 0, decode_tail: int = 0):
     """Attention over an FP8 cache (values = E4M3(code) * scale of the row and
     head); q / out bf16.  Returns ``(out, lse)``."""
     import torch
@@ -106,7 +106,7 @@ def attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
-    h = _hints(0, 0, num_splits)
+    h = _hints(0, 0, num_splits, decode_tail)
     ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
     d = [_desc(x) for x in (q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k)]
     st = lib.attn_varlen_paged_fp8_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)), int(window),
@@ -116,17 +116,18 @@ def attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu
     return out, lse
 
 
-def _hints(max_seqlen_q=0, max_seqlen_k=0, num_splits=0):
+def _hints(max_seqlen_q=0, max_seqlen_k=0, num_splits=0, decode_tail=0):
     h = KvsHints()
     h.max_seqlen_q = int(max_seqlen_q or 0)
     h.max_seqlen_k = int(max_seqlen_k or 0)
     h.num_splits = int(num_splits or 0)
+    h.decode_tail = int(decode_tail or 0)
     return h
 
 
-def workspace_size(q, k_cache, block_table, *, max_seqlen_q=0, max_seqlen_k=0, num_splits=0) -> int:
+def workspace_size(q, k_cache, block_table, *, max_seqlen_q=0, max_seqlen_k=0, num_splits=0, decode_tail=0) -> int:
     lib = _lib.load()
-    h = _hints(max_seqlen_q, max_seqlen_k, num_splits)
+    h = _hints(max_seqlen_q, max_seqlen_k, num_splits, decode_tail)
     n = lib.attn_varlen_paged_workspace_size(_ref(_desc(q)), _ref(_desc(k_cache)), _ref(_desc(block_table)),
                                              ctypes.byref(h))
     if n == ctypes.c_size_t(-1).value:
@@ -137,7 +138,7 @@ def workspace_size(q, k_cache, block_table, *, max_seqlen_q=0, max_seqlen_k=0, n
 def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale: float,
                       causal: bool = True, out=None, lse=None, *, return_lse: bool = True,
                       max_seqlen_q: int = 0, max_seqlen_k: int = 0, num_splits: int = 0,
-                      workspace=None, window: int = 0):
+                      workspace=None, window: int = 0, decode_tail: int = 0):
     """Exact paged varlen attention.  Returns ``(out, lse)`` (lse is None when
     ``return_lse`` is False and no ``lse`` tensor was given).
 
@@ -146,7 +147,8 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
     and be at least ``workspace_size`` bytes (the library checks), or else a
     torch-allocated one of the size needed.  ``window`` > 0 (needs ``causal``)
     calls ``attn_varlen_paged_window_ex``: the row at position p sees keys
-    p - window + 1 .. p."""
+    p - window + 1 .. p.  ``decode_tail`` = N states that the last N sequences
+    have one query row each (they then run on the decode path)."""
     import torch
 
     if window and not causal:
@@ -156,7 +158,7 @@ def attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
-    h = _hints(max_seqlen_q, max_seqlen_k, num_splits)
+    h = _hints(max_seqlen_q, max_seqlen_k, num_splits, decode_tail)
     ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
     d = [_desc(q), _desc(k_cache), _desc(v_cache), _desc(block_table), _desc(cu_seqlens_q), _desc(seqlens_k)]
     if window:

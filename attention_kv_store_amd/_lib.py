@@ -52,6 +52,7 @@ class KvsHints(ctypes.Structure):
         ("max_seqlen_q", ctypes.c_int32),
         ("max_seqlen_k", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
+        ("decode_tail", ctypes.c_int32),
     ]
 
 

@@ -514,26 +514,17 @@ kvs_status attn_varlen_paged(const kvs_tensor* q, const kvs_tensor* k_cache, con
   return run_plan(plan, ws, plan.ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
-size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k_cache,
-                                        const kvs_tensor* block_table, const kvs_hints* hints) {
-  g_err.clear();
-  Plan plan;
-  if (make_plan(q, k_cache, nullptr, block_table, nullptr, nullptr, 1.0f, 1, nullptr, nullptr, hints, true,
-                &plan) != KVS_OK)
-    return (size_t)-1;
-  return plan.ws_bytes;
-}
-
 }  // extern "C"
 
 namespace {
+
+kvs_status check_hints(const kvs_hints* h);
 
 kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
                          kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
                          const kvs_tensor* seqlens_k, float scale, int window, kvs_tensor* out, kvs_tensor* lse,
                          const kvs_hints* hints, void* workspace, size_t workspace_bytes, kvs_stream_t stream) {
-  if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
-    return fail(KVS_ERR_INVALID, "hints must be non-negative");
+  KVS_TRY(check_hints(hints));
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, nullptr, seqlens_k, scale, 1, out, lse, hints, false,
                     &plan, true, window));
@@ -556,6 +547,108 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
   set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s",
                plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg,
                p.dsmall ? "whole" : "window", window_note(p).c_str());
+  return KVS_OK;
+}
+
+// One attention call's arguments (scales only for FP8 caches).
+struct AttnCall {
+  const kvs_tensor *q, *k, *v, *ks, *vs, *table, *cu, *lk;
+  float scale;
+  int causal, window;
+  kvs_tensor *out, *lse;
+  const kvs_hints* hints;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+kvs_status check_hints(const kvs_hints* h) {
+  if (h && (h->num_splits < 0 || h->max_seqlen_k < 0 || h->max_seqlen_q < 0 || h->decode_tail < 0))
+    return fail(KVS_ERR_INVALID, "hints must be non-negative");
+  return KVS_OK;
+}
+
+kvs_status run_call(const AttnCall& c) {
+  Plan plan;
+  KVS_TRY(make_plan(c.q, c.k, c.v, c.table, c.cu, c.lk, c.scale, c.causal, c.out, c.lse, c.hints, false, &plan,
+                    false, c.window));
+  if (c.ks) {
+    plan.p.k_scale = static_cast<const float*>(c.ks->data);
+    plan.p.v_scale = static_cast<const float*>(c.vs->data);
+  } else {
+    KVS_TRY(no_fp8(plan));
+  }
+  return run_plan(plan, c.ws, c.ws_bytes, c.stream);
+}
+
+// Rows [r0, r0 + n) of a dense descriptor (a view; nothing is copied).
+kvs_tensor rows_of(const kvs_tensor* t, int64_t r0, int64_t n) {
+  kvs_tensor v = *t;
+  int64_t row = 1;
+  for (int i = 1; i < t->ndim; ++i) row *= t->shape[i];
+  v.data = static_cast<char*>(t->data) + r0 * row * esize(t->dtype);
+  v.shape[0] = n;
+  return v;
+}
+
+// The batch split the decode_tail hint asks for: sequences [0, B - N) and
+// rows [0, T - N) go to the prefill/extend path, the last N sequences -- one
+// query row each, rows [T - N, T) -- to the decode path.  *n_out = 0: no
+// split (the hint is absent or 0, every sequence is a decode row, or an lse
+// row view would lose its 16-byte alignment; the call then runs unsplit).
+kvs_status tail_split(const AttnCall& c, int64_t* n_out) {
+  *n_out = 0;
+  const int64_t N = c.hints ? c.hints->decode_tail : 0;
+  if (N <= 0) return KVS_OK;
+  KVS_TRY(check_tensor(c.q, "q", kFloatTypes, 3));
+  KVS_TRY(check_tensor(c.table, "block_table", kIntTypes, 2));
+  const int64_t T = c.q->shape[0], B = c.table->shape[0];
+  if (N > B || B - N > T - N)
+    return fail(KVS_ERR_INVALID, "decode_tail %lld does not fit B=%lld, T=%lld", (long long)N, (long long)B, (long long)T);
+  if (N == B) {
+    if (T != B)
+      return fail(KVS_ERR_INVALID, "decode_tail = B needs one query row per sequence (T=%lld, B=%lld)", (long long)T,
+                  (long long)B);
+    return KVS_OK;
+  }
+  if (c.lse && ((T - N) * c.q->shape[1] * 4) % 16) return KVS_OK;
+  *n_out = N;
+  return KVS_OK;
+}
+
+kvs_status run_hinted(const AttnCall& c) {
+  int64_t N = 0;
+  KVS_TRY(tail_split(c, &N));
+  if (!N) return run_call(c);
+  KVS_TRY(check_tensor(c.out, "out", kFloatTypes, 3));
+  KVS_TRY(check_tensor(c.cu, "cu_seqlens_q", kIntTypes, 1));
+  KVS_TRY(check_tensor(c.lk, "seqlens_k", kIntTypes, 1));
+  if (c.lse) KVS_TRY(check_tensor(c.lse, "lse", 1u << KVS_F32, 2));
+  const int64_t T = c.q->shape[0], B = c.table->shape[0];
+  if (c.out->shape[0] != T || c.cu->shape[0] != B + 1 || c.lk->shape[0] != B || (c.lse && c.lse->shape[0] != T))
+    return fail(KVS_ERR_INVALID, "out, lse, cu_seqlens_q and seqlens_k must cover the T=%lld rows of B=%lld sequences",
+                (long long)T, (long long)B);
+  kvs_hints sub = *c.hints;
+  sub.decode_tail = 0;
+  const int64_t Bp = B - N, Tp = T - N;
+  // prefill / extend part: the first Bp sequences
+  kvs_tensor qp = rows_of(c.q, 0, Tp), op = rows_of(c.out, 0, Tp), tp = rows_of(c.table, 0, Bp);
+  kvs_tensor cp = rows_of(c.cu, 0, Bp + 1), kp = rows_of(c.lk, 0, Bp);
+  kvs_tensor lp = c.lse ? rows_of(c.lse, 0, Tp) : kvs_tensor{};
+  AttnCall pre = c;
+  pre.q = &qp; pre.out = &op; pre.table = &tp; pre.cu = &cp; pre.lk = &kp; pre.lse = c.lse ? &lp : nullptr;
+  pre.hints = &sub;
+  // decode part: the last N sequences, one row each (cu_seqlens_q is not read there)
+  kvs_tensor qd = rows_of(c.q, Tp, N), od = rows_of(c.out, Tp, N), td = rows_of(c.table, Bp, N);
+  kvs_tensor cd = rows_of(c.cu, 0, N + 1), kd = rows_of(c.lk, Bp, N);
+  kvs_tensor ld = c.lse ? rows_of(c.lse, Tp, N) : kvs_tensor{};
+  AttnCall dec = c;
+  dec.q = &qd; dec.out = &od; dec.table = &td; dec.cu = &cd; dec.lk = &kd; dec.lse = c.lse ? &ld : nullptr;
+  dec.hints = &sub;
+  KVS_TRY(run_call(pre));
+  const std::string d1 = g_dispatch;
+  KVS_TRY(run_call(dec));
+  set_dispatch("split (decode_tail %lld): %s | %s", (long long)N, d1.c_str(), g_dispatch.c_str());
   return KVS_OK;
 }
 
@@ -590,13 +683,10 @@ kvs_status attn_varlen_paged_ex(const kvs_tensor* q, const kvs_tensor* k_cache, 
                                 kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                 size_t workspace_bytes, kvs_stream_t stream) {
   g_err.clear();
-  if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
-    return fail(KVS_ERR_INVALID, "hints must be non-negative");
-  Plan plan;
-  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, hints,
-                    false, &plan));
-  KVS_TRY(no_fp8(plan));
-  return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+  KVS_TRY(check_hints(hints));
+  return run_hinted(AttnCall{q, k_cache, v_cache, nullptr, nullptr, block_table, cu_seqlens_q, seqlens_k, scale,
+                             causal, 0, out, lse, hints, workspace, workspace_bytes,
+                             reinterpret_cast<hipStream_t>(stream)});
 }
 
 kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
@@ -606,8 +696,7 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cac
                                     kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                     size_t workspace_bytes, kvs_stream_t stream) {
   g_err.clear();
-  if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
-    return fail(KVS_ERR_INVALID, "hints must be non-negative");
+  KVS_TRY(check_hints(hints));
   if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
   KVS_TRY(check_tensor(k_cache, "k_cache", 1u << KVS_FP8_E4M3, 4));
   KVS_TRY(check_tensor(k_scale, "k_scale", 1u << KVS_F32, 3));
@@ -616,12 +705,9 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cac
   for (const kvs_tensor* t : {k_scale, v_scale})
     if (t->shape[0] != NB || t->shape[1] != Hkv || t->shape[2] != 16)
       return fail(KVS_ERR_INVALID, "scales must be [NB, Hkv, 16] = [%lld, %lld, 16]", (long long)NB, (long long)Hkv);
-  Plan plan;
-  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, hints,
-                    false, &plan, false, window));
-  plan.p.k_scale = static_cast<const float*>(k_scale->data);
-  plan.p.v_scale = static_cast<const float*>(v_scale->data);
-  return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+  return run_hinted(AttnCall{q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k, scale,
+                             causal, window, out, lse, hints, workspace, workspace_bytes,
+                             reinterpret_cast<hipStream_t>(stream)});
 }
 
 kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
@@ -630,14 +716,35 @@ kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q, const kvs_tensor* k_
                                        kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                        size_t workspace_bytes, kvs_stream_t stream) {
   g_err.clear();
-  if (hints && (hints->num_splits < 0 || hints->max_seqlen_k < 0 || hints->max_seqlen_q < 0))
-    return fail(KVS_ERR_INVALID, "hints must be non-negative");
+  KVS_TRY(check_hints(hints));
   if (window < 1) return fail(KVS_ERR_INVALID, "window must be >= 1 (got %d)", (int)window);
+  return run_hinted(AttnCall{q, k_cache, v_cache, nullptr, nullptr, block_table, cu_seqlens_q, seqlens_k, scale, 1,
+                             window, out, lse, hints, workspace, workspace_bytes,
+                             reinterpret_cast<hipStream_t>(stream)});
+}
+
+size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k_cache,
+                                        const kvs_tensor* block_table, const kvs_hints* hints) {
+  g_err.clear();
+  if (check_hints(hints) != KVS_OK) return (size_t)-1;
+  // with the decode_tail hint only the decode part (the last N sequences,
+  // one row each) needs scratch
+  const AttnCall c{q, k_cache, nullptr, nullptr, nullptr, block_table, nullptr, nullptr, 1.0f, 1, 0, nullptr, nullptr,
+                   hints, nullptr, 0, nullptr};
+  int64_t N = 0;
+  if (tail_split(c, &N) != KVS_OK) return (size_t)-1;
+  kvs_tensor qd, td;
+  if (N) {
+    qd = rows_of(q, q->shape[0] - N, N);
+    td = rows_of(block_table, block_table->shape[0] - N, N);
+    q = &qd;
+    block_table = &td;
+  }
   Plan plan;
-  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, 1, out, lse, hints, false,
-                    &plan, false, window));
-  KVS_TRY(no_fp8(plan));
-  return run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream));
+  if (make_plan(q, k_cache, nullptr, block_table, nullptr, nullptr, 1.0f, 1, nullptr, nullptr, hints, true,
+                &plan) != KVS_OK)
+    return (size_t)-1;
+  return plan.ws_bytes;
 }
 
 const char* kvs_last_error(void) { return g_err.c_str(); }

@@ -129,7 +129,7 @@ def _traffic(kernel_src: str, workload: str):
 class Workload:
     """R device replicas of one host batch, plus the step function."""
 
-    def __init__(self, batch, replicas: int):
+    def __init__(self, batch, replicas: int, decode_tail: int = 0):
         import torch
         from tests.gpu_side import to_device
 
@@ -148,7 +148,8 @@ class Workload:
         import attention_kv_store_amd as kvs
         self.kvs = kvs
         db = self.reps[0][0]
-        need = kvs.workspace_size(db.q, db.k_cache, db.block_table)
+        self.decode_tail = int(decode_tail)
+        need = kvs.workspace_size(db.q, db.k_cache, db.block_table, decode_tail=self.decode_tail)
         self.ws = [torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") for _ in range(replicas)]
         torch.cuda.synchronize()
 
@@ -161,7 +162,7 @@ class Workload:
         db, _, _, _, out, lse = self.reps[r]
         self.kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q,
                                    db.seqlens_k, db.scale, db.causal, out=out, lse=lse, workspace=self.ws[r],
-                                   window=self.batch.window)
+                                   window=self.batch.window, decode_tail=self.decode_tail)
 
     def append_attend(self, i):
         r = i % len(self.reps)
@@ -700,6 +701,18 @@ def main():
             "kv_GBs": round(kv_bytes(mix) / (mattn * 1e-3) / 1e9, 2),
             "flops_per_launch": attention_flops(mix), "kv_bytes_per_launch": kv_bytes(mix),
             "dispatch": kvs.last_dispatch(), "replay_stats": mstats,
+        }
+        del wm
+        torch.cuda.empty_cache()
+        # the same batch with its 30 decode rows declared (decode_tail): prefill
+        # kernel on the 2 prompts, decode kernel on the 30 decode rows
+        n_dec = int((mix.q_lens == 1).sum())
+        wm = Workload(mix, args.replicas, decode_tail=n_dec)
+        tms, tattn, _, tstats = time_steps(wm, msteps, max(1, args.warmup // 4), eager=args.eager)
+        line["mixed"]["with_decode_tail"] = {
+            "decode_tail": n_dec, "us_per_call": round(tattn * 1e3, 3),
+            "kv_GBs": round(kv_bytes(mix) / (tattn * 1e-3) / 1e9, 2),
+            "dispatch": kvs.last_dispatch(), "replay_stats": tstats,
         }
         log(f"mixed: {line['mixed']}")
         del wm

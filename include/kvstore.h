@@ -188,6 +188,18 @@ typedef struct {
   int32_t num_splits;    /* decode: number of equal ranges the batch's key blocks are
                             cut into (one workgroup each); 0 = automatic.  Raised
                             if needed so a range holds at most 2048 blocks.       */
+  int32_t decode_tail;   /* N > 0: the caller states that the last N sequences of the
+                            batch have one query row each (a mixed serving batch with
+                            its decode rows last, as a scheduler forms it).  Sequences
+                            [0, B - N) then take the prefill/extend path and the last
+                            N the decode path, two launches on the same stream, which
+                            spreads the decode rows' contexts over the whole device
+                            instead of one work item each.  A wrong statement gives
+                            wrong rows for the sequences it misdescribes (every access
+                            stays inside the given buffers).  N = B needs T == B.
+                            Ignored (one launch) when an lse row view would not be
+                            16-byte aligned.  Only the decode part uses the workspace;
+                            pass the same hints to attn_varlen_paged_workspace_size. */
 } kvs_hints;
 
 /* Bytes of device scratch attn_varlen_paged_ex needs for these shapes and hints

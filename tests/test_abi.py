@@ -383,3 +383,30 @@ def test_fp8_store_validation(lib, mutate, expect, msg):
 
 def test_fp8_store_empty_is_noop(lib):
     assert _call_store_fp8(lib, _store_fp8_args(Tn=0)) == L.KVS_OK
+
+
+# ---- decode_tail hint ----------------------------------------------------------------
+def _hint(**kw):
+    h = L.KvsHints()
+    for k, v in kw.items():
+        setattr(h, k, v)
+    return h
+
+
+@pytest.mark.parametrize("tail,msg", [(-1, "non-negative"), (3, "does not fit"), (2, "one query row per sequence")])
+def test_decode_tail_validation(lib, tail, msg):
+    a = _attn_args(T_=8, B=2)
+    assert _call_ex(lib, a, hints=_hint(decode_tail=tail)) == L.KVS_ERR_INVALID
+    assert msg in lib.kvs_last_error().decode()
+
+
+def test_decode_tail_workspace_is_the_decode_parts():
+    """With the hint, the workspace is sized for the last N sequences alone."""
+    lib = L.load()
+    B, MB, N, T_ = 40, 128, 30, 10 + 30 * 1 + 500
+    q, k, table = T([T_, 32, 128]), T([4096, 16, 8, 128]), T([B, MB], L.KVS_I32)
+    h = _hint(decode_tail=N, num_splits=64)
+    got = lib.attn_varlen_paged_workspace_size(ref(q), ref(k), ref(table), ctypes.byref(h))
+    qd, td = T([N, 32, 128]), T([N, MB], L.KVS_I32, data=FAKE + (B - N) * MB * 4)
+    want = lib.attn_varlen_paged_workspace_size(ref(qd), ref(k), ref(td), ctypes.byref(_hint(num_splits=64)))
+    assert got == want and got > 0

@@ -186,3 +186,12 @@ def test_fp8_named_prefill_workloads(name):
     b = NAMED[name]()
     dev, host = _fp8_batch_pools(b)
     _check_fp8_attention(b, dev, host, rows=_sample_rows(b))
+
+
+def test_fp8_decode_tail():
+    """An FP8 cache under a mixed batch with its decode rows declared."""
+    from workloads import make_batch
+    b = make_batch(1490, [40, 17, 1, 1, 1, 1], [40, 100, 1, 17, 700, 2000], Hq=8, Hkv=2, D=128, dtype="bf16",
+                   name="fp8-decode-tail")
+    dev, host = _fp8_batch_pools(b)
+    _check_fp8_attention(b, dev, host, decode_tail=4)

@@ -616,3 +616,58 @@ def test_long_prefill_sampled():
     out, lse = _run(b)
     rows = [0, 1, 15, 16, 17, 1000, 4095, 4096, 16383, 20000, 32766, 32767]
     _check(b, out, lse, rows=rows)
+
+
+# ------------------------------------------------ mixed batches: decode_tail --
+MIXED_Q = [40, 17, 64, 1, 1, 1, 1, 1, 1]
+MIXED_K = [40, 100, 300, 1, 16, 17, 700, 129, 2000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("splits", [0, 7])
+@pytest.mark.parametrize("with_lse", [True, False])
+def test_decode_tail_matches_oracle(dtype, D, splits, with_lse):
+    """A mixed batch whose last 6 sequences are decode rows, run with
+    decode_tail = 6 (prefill kernel on the first 3, decode kernel on the
+    rest) and with smaller true statements (2, 1): every row matches the
+    oracle."""
+    import attention_kv_store_amd as kvs
+    from tests.gpu_side import run_attention, to_device
+    b = _mk(1500 + D + splits, MIXED_Q, MIXED_K, Hq=8, Hkv=2, D=D, dtype=dtype, causal=True,
+            name=f"tail-{dtype}-{D}-s{splits}")
+    db = to_device(b)
+    for tail in (6, 2, 1):
+        out, lse = run_attention(db, decode_tail=tail, num_splits=splits, return_lse=with_lse)
+        assert kvs.last_dispatch().startswith(f"split (decode_tail {tail})"), kvs.last_dispatch()
+        if with_lse:
+            _check(b, out, lse)
+        else:
+            from tests.gpu_side import to_f64
+            from tests.oracle_side import oracle_attention
+            ro, _ = oracle_attention(b)
+            assert lse is None and np.max(np.abs(to_f64(out) - ro)) <= TOL[dtype]
+
+
+def test_decode_tail_whole_batch_and_window():
+    """decode_tail = B on a decode batch (one launch), and the hint with a
+    sliding window and with an FP8 cache."""
+    import attention_kv_store_amd as kvs
+    from tests.gpu_side import run_attention, to_device
+    b = _mk(1510, [1] * 5, [1, 17, 200, 64, 33], Hq=8, Hkv=2, D=64, dtype="bf16", causal=True)
+    out, lse = run_attention(to_device(b), decode_tail=5)
+    assert not kvs.last_dispatch().startswith("split")
+    _check(b, out, lse)
+    w = _mk(1511, MIXED_Q, MIXED_K, Hq=8, Hkv=2, D=128, dtype="bf16", causal=True, window=33)
+    out, lse = run_attention(to_device(w), decode_tail=6, window=33)
+    assert kvs.last_dispatch().startswith("split")
+    _check(w, out, lse)
+
+
+def test_decode_tail_mixed_named_workload():
+    """The 2 x 256 + 30 x 1 mixed batch with its 30 decode rows declared."""
+    from tests.gpu_side import run_attention, to_device
+    from workloads import mixed_prefill_decode_bf16
+    b = mixed_prefill_decode_bf16()
+    out, lse = run_attention(to_device(b), decode_tail=30)
+    _check(b, out, lse, rows=_sample_rows(b))
