@@ -111,7 +111,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
                      const kvs_tensor* table, const kvs_tensor* cu, const kvs_tensor* lk, float scale,
                      int causal, const kvs_tensor* out, const kvs_tensor* lse, const kvs_hints* hints,
-                     bool sizing_only, Plan* plan, bool append = false, int window = 0) {
+                     bool sizing_only, Plan* plan, bool append = false, int window = 0, int64_t rows_bound = 0) {
   KVS_TRY(check_tensor(q, "q", kFloatTypes, 3));
   KVS_TRY(check_tensor(k_cache, "k_cache", kCacheTypes, 4));
   KVS_TRY(check_tensor(table, "block_table", kIntTypes, 2));
@@ -205,7 +205,10 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     // items are (token tile, sequence, head group); no sequence has more than
     // ceil(T / tile) token tiles, which bounds the item count from above
     const int64_t tile_rows = 32 * (int64_t)p.TPW;
-    const int64_t items_bound = (T + tile_rows - 1) / tile_rows * B * (int64_t)p.NHG;
+    // (rows_bound: the rows of the whole buffer when q is a view of its first
+    // rows, whose sequences a wrong decode_tail statement could run past)
+    const int64_t Tb = rows_bound > T ? rows_bound : T;
+    const int64_t items_bound = (Tb + tile_rows - 1) / tile_rows * B * (int64_t)p.NHG;
     p.items32 = items_bound < ((int64_t)1 << 31) ? 1 : 0;
     kvs::fast_div_magic((uint32_t)p.NHG, &p.nhg_m, &p.nhg_l);
     return KVS_OK;
@@ -560,6 +563,7 @@ struct AttnCall {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  int64_t rows_bound;   // rows of the whole q when q is a row view (0: q's own)
 };
 
 kvs_status check_hints(const kvs_hints* h) {
@@ -571,7 +575,7 @@ kvs_status check_hints(const kvs_hints* h) {
 kvs_status run_call(const AttnCall& c) {
   Plan plan;
   KVS_TRY(make_plan(c.q, c.k, c.v, c.table, c.cu, c.lk, c.scale, c.causal, c.out, c.lse, c.hints, false, &plan,
-                    false, c.window));
+                    false, c.window, c.rows_bound));
   if (c.ks) {
     plan.p.k_scale = static_cast<const float*>(c.ks->data);
     plan.p.v_scale = static_cast<const float*>(c.vs->data);
@@ -603,8 +607,7 @@ kvs_status tail_split(const AttnCall& c, int64_t* n_out) {
   KVS_TRY(check_tensor(c.q, "q", kFloatTypes, 3));
   KVS_TRY(check_tensor(c.table, "block_table", kIntTypes, 2));
   const int64_t T = c.q->shape[0], B = c.table->shape[0];
-  if (N > B || B - N > T - N)
-    return fail(KVS_ERR_INVALID, "decode_tail %lld does not fit B=%lld, T=%lld", (long long)N, (long long)B, (long long)T);
+  if (N > B) return fail(KVS_ERR_INVALID, "decode_tail %lld does not fit B=%lld", (long long)N, (long long)B);
   if (N == B) {
     if (T != B)
       return fail(KVS_ERR_INVALID, "decode_tail = B needs one query row per sequence (T=%lld, B=%lld)", (long long)T,
@@ -638,6 +641,7 @@ kvs_status run_hinted(const AttnCall& c) {
   AttnCall pre = c;
   pre.q = &qp; pre.out = &op; pre.table = &tp; pre.cu = &cp; pre.lk = &kp; pre.lse = c.lse ? &lp : nullptr;
   pre.hints = &sub;
+  pre.rows_bound = T;
   // decode part: the last N sequences, one row each (cu_seqlens_q is not read there)
   kvs_tensor qd = rows_of(c.q, Tp, N), od = rows_of(c.out, Tp, N), td = rows_of(c.table, Bp, N);
   kvs_tensor cd = rows_of(c.cu, 0, N + 1), kd = rows_of(c.lk, Bp, N);
