@@ -671,3 +671,40 @@ def test_decode_tail_mixed_named_workload():
     b = mixed_prefill_decode_bf16()
     out, lse = run_attention(to_device(b), decode_tail=30)
     _check(b, out, lse, rows=_sample_rows(b))
+
+
+# ------------------------------------------------------------ maximum sizes --
+def test_decode_largest_batch():
+    """8192 sequences (the decode path's limit), contexts 1..40, checked on
+    sampled rows, with automatic and forced splits."""
+    from workloads import make_batch
+    rng = np.random.default_rng(1600)
+    k = rng.integers(1, 41, size=8192)
+    b = make_batch(1600, [1] * 8192, list(k), Hq=4, Hkv=2, D=64, dtype="bf16", causal=True, name="decode-8192")
+    rows = sorted(set(rng.integers(0, 8192, size=400).tolist()) | {0, 1, 8190, 8191})
+    for splits in (0, 3000):
+        out, lse = _run(b, num_splits=splits)
+        _check(b, out, lse, rows=rows)
+
+
+@pytest.mark.parametrize("splits", [0, 7, 600])
+def test_decode_very_long_contexts(splits):
+    """Two decode rows over 262144 and 100001 keys: ranges are capped at 2048
+    blocks (the splits are raised to at least 16384 / 2048), and the table
+    window path is taken."""
+    import attention_kv_store_amd as kvs
+    b = _mk(1610, [1, 1], [262144, 100001], Hq=8, Hkv=2, D=64, dtype="bf16", causal=True, name="decode-262144")
+    out, lse = _run(b, num_splits=splits)
+    assert "table=window" in kvs.last_dispatch() or "table=whole" in kvs.last_dispatch()
+    _check(b, out, lse)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("heads", [(16, 1), (32, 1), (32, 2)])
+def test_prefill_largest_groups(dtype, heads):
+    """Prefill and extend with 16 and 32 query heads per KV head."""
+    Hq, Hkv = heads
+    b = _mk(1620 + Hq + Hkv, [40, 1, 70], [40, 90, 200], Hq=Hq, Hkv=Hkv, D=128, dtype=dtype, causal=True,
+            name=f"prefill-groups-{Hq}/{Hkv}")
+    out, lse = _run(b)
+    _check(b, out, lse)
