@@ -73,12 +73,8 @@ def kv_store_rope_paged(q, k_new, v_new, positions, slot_mapping, k_cache, v_cac
     pools (negative slots skipped); token t sits at ``positions[t]``.  ``style``
     is "neox" (pairs i, i + rotary_dim/2) or "interleaved" (pairs 2i, 2i + 1);
     ``rotary_dim`` 0 means the whole head."""
-    styles = {"neox": _lib.KVS_ROPE_NEOX, "interleaved": _lib.KVS_ROPE_INTERLEAVED}
-    if style not in styles:
-        raise ValueError(f"style must be one of {sorted(styles)}")
+    r = _rope(rotary_dim, base, style, pos_scale)
     lib = _lib.load()
-    r = KvsRope()
-    r.rotary_dim, r.style, r.base, r.pos_scale = int(rotary_dim), styles[style], float(base), float(pos_scale)
     d = [_desc(x) for x in (q, k_new, v_new, positions, slot_mapping, k_cache, v_cache)]
     _lib.check(lib.kv_store_rope_paged(*[_ref(x) for x in d], ctypes.byref(r), _stream(k_cache)))
 
@@ -114,6 +110,15 @@ def attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu
                                       _stream(q))
     _lib.check(st)
     return out, lse
+
+
+def _rope(rotary_dim, base, style, pos_scale):
+    styles = {"neox": _lib.KVS_ROPE_NEOX, "interleaved": _lib.KVS_ROPE_INTERLEAVED}
+    if style not in styles:
+        raise ValueError(f"style must be one of {sorted(styles)}")
+    r = KvsRope()
+    r.rotary_dim, r.style, r.base, r.pos_scale = int(rotary_dim), styles[style], float(base), float(pos_scale)
+    return r
 
 
 def _hints(max_seqlen_q=0, max_seqlen_k=0, num_splits=0, decode_tail=0):
@@ -194,12 +199,15 @@ def _workspace(lib, q, k_cache, block_table, h, workspace):
 
 def attn_decode_append_paged(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale: float,
                              out=None, lse=None, *, return_lse: bool = True, max_seqlen_k: int = 0,
-                             num_splits: int = 0, workspace=None, window: int = 0):
+                             num_splits: int = 0, workspace=None, window: int = 0, rope=None):
     """One decode step in one launch: writes row b of ``k_new`` / ``v_new`` as
     key ``seqlens_k[b] - 1`` of sequence b (its slot taken from the block
     table) and attends query row b over the sequence's ``seqlens_k[b]`` keys
     (the last ``window`` of them when ``window`` > 0).  Same result as
     ``kv_store_paged`` then ``attn_varlen_paged`` with ``cu_seqlens_q = 0..B``.
+    ``rope`` (a dict of ``kv_store_rope_paged``'s rotary_dim / base / style /
+    pos_scale) also rotates q and the new keys, sequence b's new token at
+    position ``seqlens_k[b] - 1`` (``q`` itself is not modified).
     Returns ``(out, lse)``."""
     import torch
 
@@ -212,7 +220,13 @@ def attn_decode_append_paged(q, k_new, v_new, k_cache, v_cache, block_table, seq
     ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
     d = [_desc(q), _desc(k_new), _desc(v_new), _desc(k_cache), _desc(v_cache), _desc(block_table),
          _desc(seqlens_k)]
-    if window:
+    if rope is not None:
+        r = _rope(rope.get("rotary_dim", 0), rope.get("base", 10000.0), rope.get("style", "neox"),
+                  rope.get("pos_scale", 1.0))
+        st = lib.attn_decode_append_paged_rope(*[_ref(x) for x in d], ctypes.c_float(scale), int(window),
+                                               ctypes.byref(r), _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h),
+                                               ws_ptr, ws_bytes, _stream(q))
+    elif window:
         st = lib.attn_decode_append_paged_window(*[_ref(x) for x in d], ctypes.c_float(scale), int(window),
                                                  _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr,
                                                  ws_bytes, _stream(q))

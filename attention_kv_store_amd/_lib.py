@@ -30,6 +30,7 @@ EXPORTS = (
     "attn_decode_append_paged",
     "attn_varlen_paged_window_ex",
     "attn_decode_append_paged_window",
+    "attn_decode_append_paged_rope",
     "kvs_last_error",
     "kvs_last_dispatch",
     "kvs_release_workspace",
@@ -115,6 +116,10 @@ def load(path: str = LIB_PATH):
     lib.attn_decode_append_paged_window.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, P, P,
                                                     ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
     lib.attn_decode_append_paged_window.restype = st
+    lib.attn_decode_append_paged_rope.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32,
+                                                  ctypes.POINTER(KvsRope), P, P, ctypes.POINTER(KvsHints), vp,
+                                                  ctypes.c_size_t, vp]
+    lib.attn_decode_append_paged_rope.restype = st
     lib.kvs_last_error.argtypes = []
     lib.kvs_last_error.restype = ctypes.c_char_p
     lib.kvs_last_dispatch.argtypes = []

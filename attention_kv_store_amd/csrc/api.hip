@@ -526,7 +526,8 @@ kvs_status check_hints(const kvs_hints* h);
 kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
                          kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
                          const kvs_tensor* seqlens_k, float scale, int window, kvs_tensor* out, kvs_tensor* lse,
-                         const kvs_hints* hints, void* workspace, size_t workspace_bytes, kvs_stream_t stream) {
+                         const kvs_hints* hints, void* workspace, size_t workspace_bytes, kvs_stream_t stream,
+                         const kvs_rope* rope = nullptr) {
   KVS_TRY(check_hints(hints));
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, nullptr, seqlens_k, scale, 1, out, lse, hints, false,
@@ -546,10 +547,38 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
   p.k_cache_w = k_cache->data;
   p.v_cache_w = v_cache->data;
   p.append = 1;
+  if (rope) {
+    // the pairs of a lane's chunks must stay in the lane: neox halves a
+    // multiple of 32 dims apart, interleaved pairs inside 8-value chunks
+    if (plan.dt != kvs::DType::BF16) return fail(KVS_ERR_UNSUPPORTED, "rope in the fused decode step: bf16 only");
+    const int64_t D = plan.D, rd = rope->rotary_dim ? rope->rotary_dim : D;
+    if (rope->style != KVS_ROPE_NEOX && rope->style != KVS_ROPE_INTERLEAVED)
+      return fail(KVS_ERR_INVALID, "rope: unknown style %d", (int)rope->style);
+    const int64_t step = rope->style == KVS_ROPE_NEOX ? 64 : 16;
+    if (rd < step || rd > D || rd % step)
+      return fail(KVS_ERR_UNSUPPORTED, "rope in the fused decode step: rotary_dim %lld must be a multiple of %lld in [%lld, D]",
+                  (long long)rd, (long long)step, (long long)step);
+    if (!(std::isfinite(rope->base) && rope->base > 0) || !(std::isfinite(rope->pos_scale) && rope->pos_scale > 0))
+      return fail(KVS_ERR_INVALID, "rope: base and pos_scale must be finite and positive");
+    p.rope = 1;
+    p.rope_rd = (int32_t)rd;
+    p.rope_style = rope->style;
+    p.rope_inv_scale = 1.0 / rope->pos_scale;
+    p.rope_l2b = std::log2(rope->base);
+    // the decode LDS grows by the per-wave angle table (the whole-table set-up
+    // gives way to the windowed one if both no longer fit)
+    auto need = [&] {
+      return kvs::decode_lds_bytes(p.B, kvs::decode_tbl_ints(p.B, p.MB, p.dsmall), p.hpw,
+                                   kvs::decode_slab_bytes((int)D, false, true));
+    };
+    constexpr size_t kLdsBudget = 160 * 1024 - 256;
+    if (p.dsmall && need() > kLdsBudget) p.dsmall = 0;
+    if (need() > kLdsBudget) return fail(KVS_ERR_UNSUPPORTED, "decode batch too large for one workgroup's LDS (B=%d)", p.B);
+  }
   KVS_TRY(run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream)));
-  set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s",
+  set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s%s",
                plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg,
-               p.dsmall ? "whole" : "window", window_note(p).c_str());
+               p.dsmall ? "whole" : "window", window_note(p).c_str(), p.rope ? " rope" : "");
   return KVS_OK;
 }
 
@@ -668,6 +697,18 @@ kvs_status attn_decode_append_paged(const kvs_tensor* q, const kvs_tensor* k_new
   g_err.clear();
   return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, 0, out, lse, hints,
                        workspace, workspace_bytes, stream);
+}
+
+kvs_status attn_decode_append_paged_rope(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                         kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
+                                         const kvs_tensor* seqlens_k, float scale, int32_t window, const kvs_rope* rope,
+                                         kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                         size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
+  if (!rope) return fail(KVS_ERR_INVALID, "rope: parameters are NULL");
+  return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, window, out, lse, hints,
+                       workspace, workspace_bytes, stream, rope);
 }
 
 kvs_status attn_decode_append_paged_window(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,

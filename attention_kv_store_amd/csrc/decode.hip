@@ -119,6 +119,7 @@ struct Step {
   int gblk;   // first block of the step on the flattened axis
   int first;  // first step of this sequence's piece
   int last;   // last step of the piece
+  int phys;   // RoPE step: physical block of the step (set with its loads)
 };
 
 // FP8 (E4M3) codes -> bf16, exactly (every E4M3 value is a bf16 value): the
@@ -135,9 +136,23 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(const u32x2& w) {
                e4m3x2_to_bf16x2(w[1], true)};
 }
 
-template <int D, bool BF16, bool APPEND, bool WIN, bool KV8>
-struct DecodeWave {
+// RoPE in the fused decode step: per wave, the cos / sin of the current
+// sequence's angles in LDS, and this lane's frequency theta_lane.
+template <bool ROPE>
+struct DecodeRope {};
+template <>
+struct DecodeRope<true> {
+  float* rcs = nullptr;   // [kRopeLdsPairs] cos, then [kRopeLdsPairs] sin
+  double theta = 0.0;     // base^(-2 lane / rotary_dim) for lane < rotary_dim / 2
+};
+constexpr int kRopeLdsPairs = 64;
+constexpr double kTwoPiHi = 6.283185307179586;       // 2 pi = hi + lo (hi the nearest double)
+constexpr double kTwoPiLo = 2.4492935982947064e-16;
+
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8, bool ROPE = false>
+struct DecodeWave : DecodeRope<ROPE> {
   using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
+  static_assert(!ROPE || (BF16 && APPEND && !KV8), "RoPE: the bf16 fused decode step");
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   // K / V elements: E4M3 codes when KV8 (then q and out are bf16)
   using KE = typename std::conditional<KV8, uint8_t, E>::type;
@@ -360,6 +375,74 @@ struct DecodeWave {
     }
   }
 
+  // ---- RoPE (fused decode step) ---------------------------------------------
+  // The angles of the new token of a sequence of Lk keys (position Lk - 1):
+  // lane i < rotary_dim / 2 forms pair i's angle in double (the product and
+  // its reduction by 2 pi), then cos / sin in fp32, into this wave's LDS.
+  __device__ __forceinline__ void rope_angles(int Lk) {
+    if constexpr (ROPE) {
+      if (lane < (p.rope_rd >> 1)) {
+        const double a = (double)(Lk - 1) * p.rope_inv_scale * this->theta;
+        const double k = rint(a * (1.0 / kTwoPiHi));
+        const double r = fma(-k, kTwoPiHi, a) - k * kTwoPiLo;
+        float sn, cs;
+        sincosf((float)r, &sn, &cs);
+        this->rcs[lane] = cs;
+        this->rcs[kRopeLdsPairs + lane] = sn;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    }
+  }
+  // Rotates this lane's chunks x[i] (value e of chunk i is d = 32 i + 8 grp + e,
+  // the lane layout of both the query and a key row): neox pairs (d, d + rd/2)
+  // are chunks i and i + rd/64 of the same lane, interleaved pairs are
+  // neighbours inside a chunk.  Results are rounded to bf16.
+  __device__ __forceinline__ void rope_rotate(u32x4 (&x)[C::KI]) const {
+    if constexpr (ROPE) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (p.rope_style == 0) {
+        const int ni = p.rope_rd >> 6;
+#pragma unroll
+        for (int i = 0; i < C::KI / 2 + (C::KI == 1 ? 1 : 0); ++i) {
+          if (i >= ni || i + ni >= C::KI) continue;
+          const int j0 = 32 * i + 8 * grp;
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(this->rcs + j0);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(this->rcs + j0 + 4);
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(this->rcs + kRopeLdsPairs + j0);
+          const f32x4 s1 = *reinterpret_cast<const f32x4*>(this->rcs + kRopeLdsPairs + j0 + 4);
+          u32x4& a = x[i];
+          u32x4& b = x[i + ni];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float cl = w < 2 ? c0[2 * w] : c1[2 * w - 4], ch = w < 2 ? c0[2 * w + 1] : c1[2 * w - 3];
+            const float sl = w < 2 ? s0[2 * w] : s1[2 * w - 4], sh = w < 2 ? s0[2 * w + 1] : s1[2 * w - 3];
+            const float a0 = bf16lo_to_f32(a[w]), a1 = bf16hi_to_f32(a[w]);
+            const float b0 = bf16lo_to_f32(b[w]), b1 = bf16hi_to_f32(b[w]);
+            a[w] = pack_bf16x2(fmaf(a0, cl, -b0 * sl), fmaf(a1, ch, -b1 * sh));
+            b[w] = pack_bf16x2(fmaf(b0, cl, a0 * sl), fmaf(b1, ch, a1 * sh));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::KI; ++i) {
+          if (32 * i + 8 * grp >= p.rope_rd) continue;
+          const int j0 = 16 * i + 4 * grp;
+          const f32x4 c = *reinterpret_cast<const f32x4*>(this->rcs + j0);
+          const f32x4 sn = *reinterpret_cast<const f32x4*>(this->rcs + kRopeLdsPairs + j0);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float x1 = bf16lo_to_f32(x[i][w]), x2 = bf16hi_to_f32(x[i][w]);
+            x[i][w] = pack_bf16x2(fmaf(x1, c[w], -x2 * sn[w]), fmaf(x2, c[w], x1 * sn[w]));
+          }
+        }
+      }
+    }
+  }
+  // the cache slot (element offset of this wave's head) of key kl of block phys
+  __device__ __forceinline__ int64_t slot_offset(int phys, int kl) const {
+    return ((int64_t)phys * kPage + (kl & 15)) * tok_stride + (int64_t)g * D;
+  }
+
   // first key of sequence st.b that the query row sees (the window's start)
   __device__ __forceinline__ int first_key(const Step& st) const { return WIN ? max(0, st.Lk - p.window) : 0; }
 
@@ -390,6 +473,14 @@ struct DecodeWave {
           w0 = v0_ok ? bf.v[j][2 * it] : zero;
           w1 = v1_ok ? bf.v[j][2 * it + 1] : zero;
         }
+        if constexpr (ROPE) {
+          // the new token's V row (read from v_new) goes to its cache slot
+          const int kl = st.Lk - 1;
+          if (st.phys >= 0 && st.phys < p.NB) {
+            if (kv == kl) st16(static_cast<E*>(p.v_cache_w) + slot_offset(st.phys, kl) + dch * 8, bf.v[j][2 * it]);
+            if (kv + 1 == kl) st16(static_cast<E*>(p.v_cache_w) + slot_offset(st.phys, kl) + dch * 8, bf.v[j][2 * it + 1]);
+          }
+        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           char* r0 = slab + j * C::VBLK + (dch * 8 + 2 * m) * C::VROW + kp * 4;
@@ -401,14 +492,41 @@ struct DecodeWave {
     u32x4 q[C::KI];
 #pragma unroll
     for (int i = 0; i < C::KI; ++i) q[i] = head_ok ? bf.q[i] : zero;
+    if constexpr (ROPE) rope_rotate(q);
     f32x4 s[C::NBS];
 #pragma unroll
     for (int j = 0; j < C::NBS; ++j) {
       s[j] = f32x4{};
+      if constexpr (ROPE) {
+        // the step holding the new key kl = Lk - 1 (read from k_new): rotate
+        // that key row (lanes col == kl - k0) and write it to its cache slot
+        u32x4 kk[C::KI];
 #pragma unroll
-      for (int i = 0; i < C::KI; ++i) {
-        if constexpr (KV8) s[j] = mfma16x16x32_bf16(e4m3x8_to_bf16x8(bf.k[j][i]), q[i], s[j]);
-        else s[j] = mfma16x16x32_bf16(bf.k[j][i], q[i], s[j]);
+        for (int i = 0; i < C::KI; ++i) kk[i] = bf.k[j][i];
+        const int kl = st.Lk - 1;
+        if (kl >= k0 + 16 * j && kl < k0 + 16 * j + 16) {   // wave-uniform
+          u32x4 kr[C::KI];
+#pragma unroll
+          for (int i = 0; i < C::KI; ++i) kr[i] = kk[i];
+          rope_rotate(kr);
+          if (col == kl - k0 - 16 * j) {
+#pragma unroll
+            for (int i = 0; i < C::KI; ++i) kk[i] = kr[i];
+            if (st.phys >= 0 && st.phys < p.NB) {
+#pragma unroll
+              for (int i = 0; i < C::KI; ++i)
+                st16(static_cast<E*>(p.k_cache_w) + slot_offset(st.phys, kl) + i * 32 + grp * 8, kk[i]);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < C::KI; ++i) s[j] = mfma16x16x32_bf16(kk[i], q[i], s[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::KI; ++i) {
+          if constexpr (KV8) s[j] = mfma16x16x32_bf16(e4m3x8_to_bf16x8(bf.k[j][i]), q[i], s[j]);
+          else s[j] = mfma16x16x32_bf16(bf.k[j][i], q[i], s[j]);
+        }
       }
       // KV8: K = code * scale of its key, so the score is scaled per key
       if constexpr (KV8) {
@@ -719,10 +837,14 @@ struct DecodeWave {
   }
 };
 
-template <int D, bool BF16, bool APPEND, bool WIN, bool KV8>
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8, bool ROPE>
 __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
-  using W = DecodeWave<D, BF16, APPEND, WIN, KV8>;
+  using W = DecodeWave<D, BF16, APPEND, WIN, KV8, ROPE>;
+  // RoPE: the new rows are written by the waves that attend them (rotated),
+  // not during set-up
+  constexpr bool SETUP_APPEND = APPEND && !ROPE;
+  constexpr int RB = ROPE ? 2 * kRopeLdsPairs * (int)sizeof(float) : 0;   // per-wave cos / sin
   const int win = WIN ? p.window : 0;   // sliding window (0: none)
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int B = p.B;
@@ -738,14 +860,18 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int w = blockIdx.x, hg = blockIdx.y, nwg = p.nwg;
   const int g = hg * p.hpw + wave;
-  W wv(p, g, slabs + wave * C::SLAB);
+  W wv(p, g, slabs + wave * (C::SLAB + RB));
+  if constexpr (ROPE) {
+    wv.rcs = reinterpret_cast<float*>(slabs + wave * (C::SLAB + RB) + C::SLAB);
+    if (lane < (p.rope_rd >> 1)) wv.theta = exp2(-(2.0 * lane / p.rope_rd) * p.rope_l2b);
+  }
   typename W::NewRows nr;
 
   if (small) {
     // ---- one memory round trip: this workgroup's first new rows (append),
     // seqlens_k and the whole block table; wave 0 forms the block prefix with
     // one in-register scan (B <= 64)
-    if constexpr (APPEND) nr = wv.append_fetch(w, nwg);
+    if constexpr (SETUP_APPEND) nr = wv.append_fetch(w, nwg);
     const int nt = B * p.MB;
     for (int c = tid; c < (nt >> 2); c += nthr) st16(tbl + 4 * c, ld16(p.table + 4 * c));
     for (int i = (nt & ~3) + tid; i < nt; i += nthr) tbl[i] = p.table[i];
@@ -760,7 +886,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       if (lane == B - 1) sstart[B] = x;
     }
     __syncthreads();
-    if constexpr (APPEND) wv.append_locate(nr, slens, tbl);
+    if constexpr (SETUP_APPEND) wv.append_locate(nr, slens, tbl);
   } else {
     // ---- seqlens_k into LDS ---------------------------------------------------
     for (int b = tid; b < B; b += nthr) slens[b] = p.lens_k[b];
@@ -793,12 +919,12 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     }
     // append: this workgroup's first new rows are loaded now, with the table
     // window below, and stored once it has arrived
-    if constexpr (APPEND) nr = wv.append_load(w, nwg, slens);
+    if constexpr (SETUP_APPEND) nr = wv.append_load(w, nwg, slens);
   }
   const int total = sstart[B];
   const int r0 = (int)(((int64_t)w * total) / nwg), r1 = (int)(((int64_t)(w + 1) * total) / nwg);
   if (r0 >= r1) {  // empty range (whole workgroup)
-    if constexpr (APPEND) wv.append_rows(nr, w, nwg, slens);
+    if constexpr (SETUP_APPEND) wv.append_rows(nr, w, nwg, slens);
     return;
   }
 
@@ -821,7 +947,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     }
     __syncthreads();
   }
-  if constexpr (APPEND) wv.append_rows(nr, w, nwg, slens);
+  if constexpr (SETUP_APPEND) wv.append_rows(nr, w, nwg, slens);
 
   // Segments of the range, in processing order: the piece of the last sequence
   // Z (its head, unless it starts in this range), the piece of the first
@@ -929,20 +1055,29 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       Step cur = gen();
       if (cur.b < 0) return;
       phys_of(cur, ph);
+      if constexpr (ROPE) cur.phys = ph[0];
       wv.load(cur, ph, bA);
       Step nxt = gen();
       for (;;) {
         phys_of(nxt, ph);
+        if constexpr (ROPE) nxt.phys = ph[0];
         wv.load(nxt, ph, bB);
-        if (cur.first) wv.reset();
+        if (cur.first) {
+          wv.reset();
+          if constexpr (ROPE) wv.rope_angles(cur.Lk);
+        }
         wv.compute(cur, bA);
         if (cur.last) finish_piece(cur);
         cur = nxt;
         if (cur.b < 0) break;
         nxt = gen();
         phys_of(nxt, ph);
+        if constexpr (ROPE) nxt.phys = ph[0];
         wv.load(nxt, ph, bA);
-        if (cur.first) wv.reset();
+        if (cur.first) {
+          wv.reset();
+          if constexpr (ROPE) wv.rope_angles(cur.Lk);
+        }
         wv.compute(cur, bB);
         if (cur.last) finish_piece(cur);
         cur = nxt;
@@ -967,16 +1102,18 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   if (nseg > nsplit_seg) stream(nsplit_seg, nseg);
 }
 
-template <int D, bool BF16, bool APPEND, bool WIN, bool KV8 = false>
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8 = false, bool ROPE = false>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
-  static_assert(C::SLAB == decode_slab_bytes(D, KV8), "decode_slab_bytes must match the slab layout");
-  const size_t lds = decode_lds_bytes(p.B, decode_tbl_ints(p.B, p.MB, p.dsmall != 0), p.hpw, C::SLAB);
+  static_assert(C::SLAB + (ROPE ? 2 * kRopeLdsPairs * 4 : 0) == decode_slab_bytes(D, KV8, ROPE),
+                "decode_slab_bytes must match the slab layout");
+  const size_t lds = decode_lds_bytes(p.B, decode_tbl_ints(p.B, p.MB, p.dsmall != 0), p.hpw,
+                                      decode_slab_bytes(D, KV8, ROPE));
   // dynamic LDS above the default limit must be requested; grow it as needed
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
   if (lds > lds_granted.load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND, WIN, KV8>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND, WIN, KV8, ROPE>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
@@ -986,7 +1123,7 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND, WIN, KV8>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND, WIN, KV8, ROPE>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
   return hipGetLastError();
 }
 
@@ -998,6 +1135,11 @@ static hipError_t launch_decode_a(const AttnParams& p, DType dt, int D, hipStrea
 }
 
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s) {
+  if (p.rope) {   // fused decode step with RoPE: bf16 only
+    if (dt != DType::BF16 || !p.append) return hipErrorInvalidValue;
+    if (p.window > 0) return D == 64 ? launch_decode_t<64, true, true, true, false, true>(p, s) : launch_decode_t<128, true, true, true, false, true>(p, s);
+    return D == 64 ? launch_decode_t<64, true, true, false, false, true>(p, s) : launch_decode_t<128, true, true, false, false, true>(p, s);
+  }
   if (p.kv8) {   // FP8 caches, bf16 queries, no fused append
     if (p.window > 0) return D == 64 ? launch_decode_t<64, true, false, true, true>(p, s) : launch_decode_t<128, true, false, true, true>(p, s);
     return D == 64 ? launch_decode_t<64, true, false, false, true>(p, s) : launch_decode_t<128, true, false, false, true>(p, s);

@@ -69,6 +69,12 @@ struct AttnParams {
   int32_t kv8;
   const float* k_scale;   // [NB, Hkv, 16]
   const float* v_scale;
+  // fused decode step with RoPE of q and the new key rows (position Lk - 1)
+  int32_t rope;
+  int32_t rope_rd;        // rotated dims per head
+  int32_t rope_style;     // 0: pairs (i, i + rd/2); 1: pairs (2i, 2i + 1)
+  double rope_inv_scale;  // 1 / pos_scale
+  double rope_l2b;        // log2(base)
 };
 
 // FP8 store: new rows [T, Hkv, D] (f32 / bf16) quantized into E4M3 code pools
@@ -136,8 +142,11 @@ inline size_t decode_lds_bytes(int B, int tbl_ints, int hpw, int slab_bytes) {
 // blocks (the bf16 step's bytes in flight) measured slower than one: the FP8
 // step is bounded by its instruction chain, not by the bytes it waits for.
 constexpr int kDecodeKv8Blocks = 1;
-// V^T bytes per wave: 16 keys (+ pad) x D per block of a step
-constexpr int decode_slab_bytes(int D, bool kv8) { return D * 40 * (kv8 ? kDecodeKv8Blocks : 1); }
+// LDS bytes per decode wave: V^T, 16 keys (+ pad) x D per block of a step,
+// then (fused RoPE step) the cos / sin of 64 angle pairs
+constexpr int decode_slab_bytes(int D, bool kv8, bool rope = false) {
+  return D * 40 * (kv8 ? kDecodeKv8Blocks : 1) + (rope ? 2 * 64 * 4 : 0);
+}
 
 // Prefill LDS bytes per workgroup: two K/V stages, then cu_seqlens_q and
 // seqlens_k when staged.

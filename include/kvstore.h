@@ -368,6 +368,36 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q,
                                     void* workspace, size_t workspace_bytes,
                                     kvs_stream_t stream);
 
+/*
+ * attn_decode_append_paged_rope -- the fused decode step of
+ * attn_decode_append_paged (window > 0: of attn_decode_append_paged_window)
+ * with the "RoPE + KV cache store" step folded in ("Transformer 추론 커널
+ * (3/10)", §2, fused with attention in one launch): q and the new key rows
+ * are rotated as kv_store_rope_paged rotates them, with sequence b's new
+ * token at position seqlens_k[b] - 1; the rotated key row and the unchanged
+ * value row are written to the cache slot, and q is rotated in registers
+ * (the q tensor is not modified).  Result: that of kv_store_rope_paged (q
+ * rotated, positions Lk_b - 1, slots of key Lk_b - 1) followed by
+ * attn_varlen_paged_ex / attn_varlen_paged_window_ex with cu_seqlens_q = 0..B,
+ * up to rounding (the angles are reduced in double and their cos / sin taken
+ * in fp32, so a rotated value may differ from kv_store_rope_paged's in its
+ * last bf16 place).
+ *
+ * bf16 only; rotary_dim a multiple of 64 (neox) or 16 (interleaved), at most
+ * D; otherwise KVS_ERR_UNSUPPORTED.  Other arguments, preconditions and limits
+ * as attn_decode_append_paged.  Allocates nothing.
+ */
+kvs_status attn_decode_append_paged_rope(const kvs_tensor* q,
+                                         const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                         kvs_tensor* k_cache, kvs_tensor* v_cache,
+                                         const kvs_tensor* block_table,
+                                         const kvs_tensor* seqlens_k,
+                                         float scale, int32_t window, const kvs_rope* rope,
+                                         kvs_tensor* out, kvs_tensor* lse,
+                                         const kvs_hints* hints,
+                                         void* workspace, size_t workspace_bytes,
+                                         kvs_stream_t stream);
+
 /* Text of the calling thread's last non-OK status ("" if none).  The pointer is
  * valid until that thread's next library call. */
 const char* kvs_last_error(void);

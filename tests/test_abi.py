@@ -410,3 +410,29 @@ def test_decode_tail_workspace_is_the_decode_parts():
     qd, td = T([N, 32, 128]), T([N, MB], L.KVS_I32, data=FAKE + (B - N) * MB * 4)
     want = lib.attn_varlen_paged_workspace_size(ref(qd), ref(k), ref(td), ctypes.byref(_hint(num_splits=64)))
     assert got == want and got > 0
+
+
+def _call_append_rope(lib, a, rope, window=0):
+    return lib.attn_decode_append_paged_rope(ref(a["q"]), ref(a["kn"]), ref(a["vn"]), ref(a["k"]), ref(a["v"]),
+                                             ref(a["table"]), ref(a["lk"]), ctypes.c_float(0.125), window,
+                                             ctypes.byref(rope) if rope is not None else None, ref(a["out"]),
+                                             ref(a.get("lse")), None, None, 0, None)
+
+
+@pytest.mark.parametrize("dtype,D,kw,expect,msg", [
+    (L.KVS_F32, 64, dict(), L.KVS_ERR_UNSUPPORTED, "bf16 only"),
+    (L.KVS_BF16, 128, dict(rotary_dim=32), L.KVS_ERR_UNSUPPORTED, "multiple of 64"),
+    (L.KVS_BF16, 64, dict(rotary_dim=8, style=1), L.KVS_ERR_UNSUPPORTED, "multiple of 16"),
+    (L.KVS_BF16, 64, dict(style=3), L.KVS_ERR_INVALID, "style"),
+    (L.KVS_BF16, 64, dict(base=-1.0), L.KVS_ERR_INVALID, "base and pos_scale"),
+    (L.KVS_BF16, 64, None, L.KVS_ERR_INVALID, "NULL"),
+])
+def test_fused_rope_validation(lib, dtype, D, kw, expect, msg):
+    a = _append_args(D=D, dtype=dtype)
+    rope = None
+    if kw is not None:
+        rope = L.KvsRope()
+        rope.rotary_dim, rope.style = kw.get("rotary_dim", 0), kw.get("style", 0)
+        rope.base, rope.pos_scale = kw.get("base", 10000.0), 1.0
+    assert _call_append_rope(lib, a, rope) == expect
+    assert msg in lib.kvs_last_error().decode()

@@ -172,3 +172,54 @@ def test_rope_then_attention(dtype, style):
     eo, el = np.max(np.abs(to_f64(out) - ro)), np.max(np.abs(to_f64(lse) - rl))
     print(f"[rope+attention {dtype} {style}] max|dout|={eo:.3e} max|dlse|={el:.3e}", flush=True)
     assert eo <= TOL[dtype] and el <= TOL[dtype]
+
+
+# ------------------------------------------- RoPE inside the fused decode step --
+@pytest.mark.parametrize("D,rd,style", [(64, 64, "neox"), (128, 128, "neox"), (128, 64, "neox"),
+                                        (64, 16, "interleaved"), (128, 128, "interleaved")])
+@pytest.mark.parametrize("heads", [(8, 2), (32, 8)])
+@pytest.mark.parametrize("window,splits", [(0, 0), (0, 7), (33, 0)])
+def test_fused_decode_rope(D, rd, style, heads, window, splits):
+    """attn_decode_append_paged with rope: out / lse against the oracle's
+    attention over the rotated (bf16-rounded) query and new key at position
+    Lk - 1; the new key slots hold the rotated key (within a bf16 ulp of the
+    exact rotation), the new value slots the value bit for bit, every other
+    slot unchanged."""
+    import dataclasses
+
+    from oracle import apply_rope
+    from tests.gpu_side import cache_bits, run_append, to_device_before_append, to_f64
+    from tests.oracle_side import oracle_attention
+    from workloads import make_batch, round_to_bf16
+    Hq, Hkv = heads
+    k_lens = [1, 2, 15, 16, 17, 33, 100, 500, 2000, 64, 65, 31]
+    b = make_batch(1700 + D + rd + Hq + window + splits, [1] * len(k_lens), k_lens, Hq=Hq, Hkv=Hkv, D=D,
+                   dtype="bf16", causal=True, window=window, name=f"fused-rope-{D}-{rd}-{style}")
+    kw = dict(rotary_dim=rd, base=10000.0, style=STYLES[style])
+    pos = (b.k_lens - 1).astype(np.int32)
+    new = b.new_token_rows()
+    rnd = lambda x: round_to_bf16(x.astype(np.float32)).astype(np.float64)
+    k_tok = b.k_tokens.astype(np.float64).copy()
+    k_exact = apply_rope(b.k_tokens[new], pos, **kw)
+    k_tok[new] = rnd(k_exact)
+    rb = dataclasses.replace(b, q=rnd(apply_rope(b.q, pos, **kw)), k_tokens=k_tok)
+    db, kn, vn = to_device_before_append(b)
+    before = cache_bits(db.k_cache).copy()
+    q_before = db.q.clone()
+    out, lse = run_append(db, kn, vn, window=window, num_splits=splits,
+                          rope=dict(rotary_dim=rd, style=style, base=10000.0))
+    assert torch.equal(db.q, q_before), "q must not be modified"
+    ro, rl = oracle_attention(rb)
+    eo, el = np.max(np.abs(to_f64(out) - ro)), np.max(np.abs(to_f64(lse) - rl))
+    print(f"[fused rope {D}/{rd}/{style} {Hq}/{Hkv} w{window} s{splits}] max|dout|={eo:.3e} max|dlse|={el:.3e}",
+          flush=True)
+    assert eo <= 2e-2 and el <= 2e-2
+    # the cache: new K rows rotated, new V rows as given, nothing else touched
+    slots = b.slots[new]
+    kc = to_f64(db.k_cache).reshape(b.num_blocks * 16, Hkv, D)
+    _close(kc[slots], k_exact, "bf16", "new key rows")
+    vbits = cache_bits(db.v_cache).reshape(b.num_blocks * 16, Hkv, D)
+    assert np.array_equal(vbits[slots], _bits(torch.from_numpy(b.v_tokens[new]).to(torch.bfloat16)))
+    after = cache_bits(db.k_cache).reshape(b.num_blocks * 16, -1)
+    other = np.setdiff1d(np.arange(b.num_blocks * 16), slots)
+    assert np.array_equal(after[other], before.reshape(b.num_blocks * 16, -1)[other])
