@@ -410,6 +410,54 @@ def context_sweep(args):
     return res
 
 
+def rope_decode_line(dec, args):
+    """A decode step of a RoPE model on the decode workload: the fused step with
+    RoPE inside (one launch) against kv_store_rope_paged + attn_varlen_paged
+    (two launches), graph replays over 4 replicas."""
+    import torch
+    import attention_kv_store_amd as kvs
+
+    w = Workload(dec, 4)
+    rows = dec.new_token_rows()
+    pos = torch.from_numpy((dec.k_lens - 1).astype("int32")).cuda()
+    res = {}
+
+    def fused(i):
+        db, kn, vn, _, out, lse = w.reps[i % 4]
+        kvs.attn_decode_append_paged(db.q, kn, vn, db.k_cache, db.v_cache, db.block_table, db.seqlens_k, db.scale,
+                                     out=out, lse=lse, workspace=w.ws[i % 4], rope={"style": "neox"})
+
+    def two(i):
+        db, kn, vn, sl, out, lse = w.reps[i % 4]
+        kvs.kv_store_rope_paged(db.q, kn, vn, pos, sl, db.k_cache, db.v_cache)
+        kvs.attn_varlen_paged(db.q, db.k_cache, db.v_cache, db.block_table, db.cu_seqlens_q, db.seqlens_k, db.scale,
+                              True, out=out, lse=lse, workspace=w.ws[i % 4])
+
+    for name, fn in (("fused_one_launch", fused), ("rope_store_then_attention", two)):
+        for i in range(8):
+            fn(i)
+        torch.cuda.synchronize()
+        n = 100
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        nrep = max(2, args.steps // n)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(nrep):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"us_per_step": round(e0.elapsed_time(e1) / (nrep * n) * 1e3, 3), "dispatch": kvs.last_dispatch()}
+        del graph
+    del w
+    torch.cuda.empty_cache()
+    return res
+
+
 def rope_store_line(args):
     """kv_store_rope_paged at the causal prefill workload's shape (16 x 512 new
     rows, 32 / 8 heads, D 128) and the decode workload's (64 rows, 32 / 8 heads,
@@ -758,6 +806,8 @@ def main():
         line["decode_context_sweep"] = context_sweep(args)
         log(f"decode context sweep: {line['decode_context_sweep']}")
         line["rope_store"] = rope_store_line(args)
+        line["rope_decode_step"] = rope_decode_line(dec, args)
+        log(f"rope decode step: {line['rope_decode_step']}")
         log(f"rope + store: {line['rope_store']}")
 
     if not args.no_extras:
