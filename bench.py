@@ -54,7 +54,7 @@ def _src_sha(name: str) -> str:
 
 # kernel symbol (as rocprofv3 names it) and source file of each timed workload
 COUNTED = {
-    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false, false>", "decode.hip"),
+    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false, false, false>", "decode.hip"),
     "causal_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false>", "prefill.hip"),
 }
 
