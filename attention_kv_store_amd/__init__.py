@@ -28,7 +28,8 @@ from typing import Optional
 from . import _lib
 from ._lib import KVS_BF16, KVS_F32, KVS_I32, KvsError, KvsHints, KvsRope, describe, last_dispatch  # noqa: F401
 
-__all__ = ["kv_store_paged", "kv_store_rope_paged", "kv_store_paged_fp8", "attn_varlen_paged_fp8", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
+__all__ = ["kv_store_paged", "kv_store_rope_paged", "kv_store_paged_fp8", "attn_varlen_paged_fp8",
+           "attn_decode_append_paged_fp8", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
 
 
 def _dtype_code(t) -> int:
@@ -233,6 +234,30 @@ def attn_decode_append_paged(q, k_new, v_new, k_cache, v_cache, block_table, seq
     else:
         st = lib.attn_decode_append_paged(*[_ref(x) for x in d], ctypes.c_float(scale), _ref(_desc(out)),
                                           _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes, _stream(q))
+    _lib.check(st)
+    return out, lse
+
+
+def attn_decode_append_paged_fp8(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k,
+                                 scale: float, out=None, lse=None, *, return_lse: bool = True, num_splits: int = 0,
+                                 workspace=None, window: int = 0):
+    """The fused decode step over an FP8 cache: row b of ``k_new`` / ``v_new``
+    (bf16) is quantized as ``kv_store_paged_fp8`` does into key
+    ``seqlens_k[b] - 1`` (codes and scales) and query row b attends over the
+    dequantized keys.  Head dim 64.  Returns ``(out, lse)``."""
+    import torch
+
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    h = _hints(1, 0, num_splits)
+    ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
+    d = [_desc(x) for x in (q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k)]
+    st = lib.attn_decode_append_paged_fp8(*[_ref(x) for x in d], ctypes.c_float(scale), int(window),
+                                          _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
+                                          _stream(q))
     _lib.check(st)
     return out, lse
 

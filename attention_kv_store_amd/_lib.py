@@ -31,6 +31,7 @@ EXPORTS = (
     "attn_varlen_paged_window_ex",
     "attn_decode_append_paged_window",
     "attn_decode_append_paged_rope",
+    "attn_decode_append_paged_fp8",
     "kvs_last_error",
     "kvs_last_dispatch",
     "kvs_release_workspace",
@@ -120,6 +121,9 @@ def load(path: str = LIB_PATH):
                                                   ctypes.POINTER(KvsRope), P, P, ctypes.POINTER(KvsHints), vp,
                                                   ctypes.c_size_t, vp]
     lib.attn_decode_append_paged_rope.restype = st
+    lib.attn_decode_append_paged_fp8.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, P, P,
+                                                 ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
+    lib.attn_decode_append_paged_fp8.restype = st
     lib.kvs_last_error.argtypes = []
     lib.kvs_last_error.restype = ctypes.c_char_p
     lib.kvs_last_dispatch.argtypes = []

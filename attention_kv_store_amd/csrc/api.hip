@@ -527,17 +527,35 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
                          kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
                          const kvs_tensor* seqlens_k, float scale, int window, kvs_tensor* out, kvs_tensor* lse,
                          const kvs_hints* hints, void* workspace, size_t workspace_bytes, kvs_stream_t stream,
-                         const kvs_rope* rope = nullptr) {
+                         const kvs_rope* rope = nullptr, kvs_tensor* k_scale = nullptr,
+                         kvs_tensor* v_scale = nullptr) {
   KVS_TRY(check_hints(hints));
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, nullptr, seqlens_k, scale, 1, out, lse, hints, false,
                     &plan, true, window));
-  KVS_TRY(no_fp8(plan));
+  if (k_scale) {
+    // FP8 cache: the new rows are quantized as kv_store_paged_fp8 does
+    KVS_TRY(check_tensor(k_scale, "k_scale", 1u << KVS_F32, 3));
+    KVS_TRY(check_tensor(v_scale, "v_scale", 1u << KVS_F32, 3));
+    if (!plan.p.kv8) return fail(KVS_ERR_INVALID, "k_cache / v_cache must hold FP8 codes here");
+    const int64_t NB = k_cache->shape[0], Hkv = k_cache->shape[2];
+    for (const kvs_tensor* t : {k_scale, v_scale})
+      if (t->shape[0] != NB || t->shape[1] != Hkv || t->shape[2] != 16)
+        return fail(KVS_ERR_INVALID, "scales must be [NB, Hkv, 16] = [%lld, %lld, 16]", (long long)NB, (long long)Hkv);
+    if (plan.D != 64) return fail(KVS_ERR_UNSUPPORTED, "FP8 fused decode step: head dim 64 only (use kv_store_paged_fp8 + attn_varlen_paged_fp8_ex)");
+    plan.p.k_scale = static_cast<const float*>(k_scale->data);
+    plan.p.v_scale = static_cast<const float*>(v_scale->data);
+    plan.p.k_scale_w = static_cast<float*>(k_scale->data);
+    plan.p.v_scale_w = static_cast<float*>(v_scale->data);
+  } else {
+    KVS_TRY(no_fp8(plan));
+  }
   KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3));
   KVS_TRY(check_tensor(v_new, "v_new", kFloatTypes, 3));
   for (int i = 0; i < 3; ++i)
     if (v_new->shape[i] != k_new->shape[i]) return fail(KVS_ERR_INVALID, "v_new shape != k_new shape");
   if (k_new->dtype != q->dtype || v_new->dtype != q->dtype) return fail(KVS_ERR_INVALID, "k_new / v_new dtype != q dtype");
+  if (rope && plan.p.kv8) return fail(KVS_ERR_UNSUPPORTED, "rope with an FP8 cache in the fused decode step");
   if (k_new->shape[0] != q->shape[0] || k_new->shape[1] != k_cache->shape[2] || k_new->shape[2] != k_cache->shape[3])
     return fail(KVS_ERR_INVALID, "k_new must be [B, Hkv, D] = [%lld, %lld, %lld]", (long long)q->shape[0],
                 (long long)k_cache->shape[2], (long long)k_cache->shape[3]);
@@ -576,9 +594,9 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
     if (need() > kLdsBudget) return fail(KVS_ERR_UNSUPPORTED, "decode batch too large for one workgroup's LDS (B=%d)", p.B);
   }
   KVS_TRY(run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream)));
-  set_dispatch("decode_append_%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s%s",
-               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg,
-               p.dsmall ? "whole" : "window", window_note(p).c_str(), p.rope ? " rope" : "");
+  set_dispatch("decode_append_%s%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s%s",
+               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", p.kv8 ? "_kv_fp8" : "", plan.D, p.nwg, p.Hkv / p.hpw,
+               p.hpw, p.nwg, p.dsmall ? "whole" : "window", window_note(p).c_str(), p.rope ? " rope" : "");
   return KVS_OK;
 }
 
@@ -697,6 +715,19 @@ kvs_status attn_decode_append_paged(const kvs_tensor* q, const kvs_tensor* k_new
   g_err.clear();
   return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, 0, out, lse, hints,
                        workspace, workspace_bytes, stream);
+}
+
+kvs_status attn_decode_append_paged_fp8(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                        kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale,
+                                        kvs_tensor* v_scale, const kvs_tensor* block_table,
+                                        const kvs_tensor* seqlens_k, float scale, int32_t window, kvs_tensor* out,
+                                        kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                        size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
+  if (!k_scale || !v_scale) return fail(KVS_ERR_INVALID, "k_scale / v_scale: descriptor is NULL");
+  return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, window, out, lse, hints,
+                       workspace, workspace_bytes, stream, nullptr, k_scale, v_scale);
 }
 
 kvs_status attn_decode_append_paged_rope(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,

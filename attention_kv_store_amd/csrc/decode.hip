@@ -158,7 +158,8 @@ struct DecodeWave : DecodeRope<ROPE> {
   using KE = typename std::conditional<KV8, uint8_t, E>::type;
   // raw K / V registers of one 8-value chunk: 16 bytes of bf16 or 8 bytes of codes
   using KRaw = typename std::conditional<KV8, u32x2, u32x4>::type;
-  static_assert(!KV8 || (BF16 && !APPEND), "FP8 caches: bf16 queries, no fused append");
+  static_assert(!KV8 || BF16, "FP8 caches: bf16 queries");
+  static_assert(!(KV8 && APPEND) || C::NBS == 1, "FP8 fused step: one block per step");
 
   const AttnParams p;   // by value: a reference would pin the kernel arguments to scratch memory
   const int lane, col, grp, g;
@@ -226,7 +227,15 @@ struct DecodeWave : DecodeRope<ROPE> {
   struct Scales {
     f32x4 ks[C::NBS], vs[C::NBS];   // scales of the lane's 4 keys (4 grp .. 4 grp + 3)
   };
-  struct Buf : std::conditional<KV8, Scales, NoScales>::type {
+  // FP8 fused step: the new K / V rows (bf16, this lane's chunks), loaded with
+  // the step that holds the new key
+  struct ScalesNew : Scales {
+    u32x4 kn[C::KI];
+    u32x4 vn[C::VIL];
+  };
+  using BufBase = typename std::conditional<KV8, typename std::conditional<APPEND, ScalesNew, Scales>::type,
+                                            NoScales>::type;
+  struct Buf : BufBase {
     KRaw k[C::NBS][C::KI];
     KRaw v[C::NBS][2 * C::VIL];
     u32x4 q[C::KI];
@@ -359,6 +368,18 @@ struct DecodeWave : DecodeRope<ROPE> {
     for (int i = 0; i < C::KI; ++i) bf.q[i] = ld16(qp + i * 32 + grp * 8);
     if constexpr (KV8) {
       load_kv8(phys, bf);
+      if constexpr (APPEND) {
+        // the step holding key Lk - 1 also brings in the new rows
+        const int kl = st.Lk - 1;
+        if (st.b >= 0 && (kl >> 4) == st.lblk) {   // wave-uniform
+          const E* kn = new_row(p.k_new, st.b);
+          const E* vn = new_row(p.v_new, st.b);
+#pragma unroll
+          for (int i = 0; i < C::KI; ++i) bf.kn[i] = ld16(kn + i * 32 + grp * 8);
+#pragma unroll
+          for (int it = 0; it < C::VIL; ++it) bf.vn[it] = ld16(vn + ((lane >> 3) + 8 * it) * 8);
+        }
+      }
     } else if constexpr (APPEND) {
       // append: the step holding key kl = Lk - 1 (one step per sequence, a
       // wave-uniform branch) reads that key from the new row; the cache slot
@@ -446,7 +467,86 @@ struct DecodeWave : DecodeRope<ROPE> {
   // first key of sequence st.b that the query row sees (the window's start)
   __device__ __forceinline__ int first_key(const Step& st) const { return WIN ? max(0, st.Lk - p.window) : 0; }
 
+  // FP8 fused step: quantize the new K and V rows exactly as kv_store_paged_fp8
+  // does (absmax of the row over the lanes holding it, s = absmax / 448, codes
+  // of x / s), put codes and scales in place of the unwritten slot's, and write
+  // them to the cache.  K row: lanes col == r (4 lanes, grp 0..3); V row: the 8
+  // lanes with 2 kp (or 2 kp + 1) == r; r = kl - k0.
+  __device__ __forceinline__ void new_rows_fp8(const Step& st, Buf& b) const {
+    if constexpr (KV8 && APPEND) {
+      const int kl = st.Lk - 1, k0 = st.lblk * 16;
+      if (kl < k0 || kl >= k0 + 16) return;   // wave-uniform
+      const int r = kl - k0, kp = lane & 7;
+      auto absmax8 = [](const u32x4& w) {
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16lo_to_f32(w[i])), fabsf(bf16hi_to_f32(w[i]))));
+        return m;
+      };
+      auto codes8 = [](const u32x4& w, float sc) {
+        uint32_t c[2] = {0u, 0u};
+        if (sc > 0.f) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = e4m3_code(bf16lo_to_f32(w[i]) / sc), hi = e4m3_code(bf16hi_to_f32(w[i]) / sc);
+            c[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+          }
+        }
+        return u32x2{c[0], c[1]};
+      };
+      float ak = 0.f;
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i) ak = fmaxf(ak, absmax8(b.kn[i]));
+      ak = fmaxf(ak, __shfl_xor(ak, 16));
+      ak = fmaxf(ak, __shfl_xor(ak, 32));
+      const float sk = ak / 448.f;
+      float av = 0.f;
+#pragma unroll
+      for (int it = 0; it < C::VIL; ++it) av = fmaxf(av, absmax8(b.vn[it]));
+      av = fmaxf(av, __shfl_xor(av, 8));
+      av = fmaxf(av, __shfl_xor(av, 16));
+      av = fmaxf(av, __shfl_xor(av, 32));
+      const float sv = av / 448.f;
+      const float skr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sk), r));
+      const float svr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), r >> 1));
+      const bool store = st.phys >= 0 && st.phys < p.NB;
+      const int64_t so = slot_offset(st.phys, kl);
+      if (col == r) {
+#pragma unroll
+        for (int i = 0; i < C::KI; ++i) {
+          b.k[0][i] = codes8(b.kn[i], sk);
+          if (store) *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.k_cache_w) + so + i * 32 + grp * 8) = b.k[0][i];
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < C::VIL; ++it) {
+        const int dch = (lane >> 3) + 8 * it;
+        const u32x2 vc = codes8(b.vn[it], sv);
+        if (2 * kp == r) b.v[0][2 * it] = vc;
+        if (2 * kp + 1 == r) b.v[0][2 * it + 1] = vc;
+        if (store && (2 * kp == r || 2 * kp + 1 == r))
+          *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.v_cache_w) + so + dch * 8) = vc;
+      }
+      // the lanes holding key r's scales (keys 4 grp .. 4 grp + 3)
+      if (grp == (r >> 2)) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          b.ks[0][q4] = q4 == (r & 3) ? skr : b.ks[0][q4];
+          b.vs[0][q4] = q4 == (r & 3) ? svr : b.vs[0][q4];
+        }
+      }
+      if (store && lane == 0) {
+        const int64_t si = ((int64_t)st.phys * p.Hkv + g) * kPage + (kl & 15);
+        p.k_scale_w[si] = skr;
+        p.v_scale_w[si] = svr;
+      }
+    }
+  }
+
   __device__ __forceinline__ void compute(const Step& st, const Buf& bf) {
+    // FP8 fused step: the new rows' codes go into the step's own buffer (one
+    // of the stream's two, reloaded after this step)
+    if constexpr (KV8 && APPEND) new_rows_fp8(st, const_cast<Buf&>(bf));
     const int k0 = st.lblk * 16;
     const int kend = min(st.Lk, (st.lblk + st.nblk) * 16);
     const int klo = first_key(st);
@@ -843,7 +943,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   using W = DecodeWave<D, BF16, APPEND, WIN, KV8, ROPE>;
   // RoPE: the new rows are written by the waves that attend them (rotated),
   // not during set-up
-  constexpr bool SETUP_APPEND = APPEND && !ROPE;
+  constexpr bool SETUP_APPEND = APPEND && !ROPE && !KV8;
   constexpr int RB = ROPE ? 2 * kRopeLdsPairs * (int)sizeof(float) : 0;   // per-wave cos / sin
   const int win = WIN ? p.window : 0;   // sliding window (0: none)
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1055,12 +1155,12 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       Step cur = gen();
       if (cur.b < 0) return;
       phys_of(cur, ph);
-      if constexpr (ROPE) cur.phys = ph[0];
+      if constexpr (ROPE || (KV8 && APPEND)) cur.phys = ph[0];
       wv.load(cur, ph, bA);
       Step nxt = gen();
       for (;;) {
         phys_of(nxt, ph);
-        if constexpr (ROPE) nxt.phys = ph[0];
+        if constexpr (ROPE || (KV8 && APPEND)) nxt.phys = ph[0];
         wv.load(nxt, ph, bB);
         if (cur.first) {
           wv.reset();
@@ -1072,7 +1172,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
         if (cur.b < 0) break;
         nxt = gen();
         phys_of(nxt, ph);
-        if constexpr (ROPE) nxt.phys = ph[0];
+        if constexpr (ROPE || (KV8 && APPEND)) nxt.phys = ph[0];
         wv.load(nxt, ph, bA);
         if (cur.first) {
           wv.reset();
@@ -1140,7 +1240,11 @@ hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s) {
     if (p.window > 0) return D == 64 ? launch_decode_t<64, true, true, true, false, true>(p, s) : launch_decode_t<128, true, true, true, false, true>(p, s);
     return D == 64 ? launch_decode_t<64, true, true, false, false, true>(p, s) : launch_decode_t<128, true, true, false, false, true>(p, s);
   }
-  if (p.kv8) {   // FP8 caches, bf16 queries, no fused append
+  if (p.kv8) {   // FP8 caches, bf16 queries
+    if (p.append) {   // the fused step: head dim 64 (at 128 the new rows' registers would spill)
+      if (D != 64) return hipErrorInvalidValue;
+      return p.window > 0 ? launch_decode_t<64, true, true, true, true>(p, s) : launch_decode_t<64, true, true, false, true>(p, s);
+    }
     if (p.window > 0) return D == 64 ? launch_decode_t<64, true, false, true, true>(p, s) : launch_decode_t<128, true, false, true, true>(p, s);
     return D == 64 ? launch_decode_t<64, true, false, false, true>(p, s) : launch_decode_t<128, true, false, false, true>(p, s);
   }

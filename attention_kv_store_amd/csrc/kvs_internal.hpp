@@ -69,6 +69,8 @@ struct AttnParams {
   int32_t kv8;
   const float* k_scale;   // [NB, Hkv, 16]
   const float* v_scale;
+  float* k_scale_w;       // FP8 fused decode step: the same scales, written at the new rows
+  float* v_scale_w;
   // fused decode step with RoPE of q and the new key rows (position Lk - 1)
   int32_t rope;
   int32_t rope_rd;        // rotated dims per head

@@ -50,26 +50,6 @@ hipError_t launch_store(const StoreParams& p, DType, hipStream_t s) {
 // [NB, Hkv, 16] scale pool.
 namespace kvs {
 
-// Nearest E4M3 code of a finite y (ties to even), saturating at +-448: the
-// OCP E4M3 format (bias 7, subnormal step 2^-9, largest finite 448).
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), 448.f);
-  uint32_t c;
-  if (a < 0.015625f) {                                  // below 2^-6: multiples of 2^-9
-    c = (uint32_t)__builtin_rintf(a * 512.f);           // exact scaling, ties to even; 8 is 2^-6
-  } else {
-    const uint32_t b = __float_as_uint(a);
-    const uint32_t e = (b >> 23) - 120u;                // E4M3 exponent field: (b >> 23) - 127 + 7
-    const uint32_t mant = b & 0x7FFFFFu;
-    uint32_t m = mant >> 20;                            // 3 kept mantissa bits
-    const uint32_t rest = mant & 0xFFFFFu;
-    m += (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ? 1u : 0u;
-    c = (e << 3) + m;                                   // m == 8 carries into the exponent
-  }
-  return c | sign;
-}
-
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void kv_store_fp8_kernel(StoreFp8Params p) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;

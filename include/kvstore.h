@@ -369,6 +369,33 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q,
                                     kvs_stream_t stream);
 
 /*
+ * attn_decode_append_paged_fp8 -- the fused decode step of
+ * attn_decode_append_paged over an FP8 cache: sequence b's new K/V rows
+ * (bf16, [B, Hkv, D]) are quantized as kv_store_paged_fp8 quantizes them
+ * (codes and scales bit for bit the same) and written to the slot of key
+ * Lk_b - 1, and the query row attends over the dequantized keys, the new one
+ * included.  Result: kv_store_paged_fp8 then attn_varlen_paged_fp8_ex with
+ * cu_seqlens_q = 0..B.  window > 0: the sliding window (0 = none).
+ *
+ *   k_cache, v_cache [NB, 16, Hkv, D] KVS_FP8_E4M3; k_scale, v_scale
+ *   [NB, Hkv, 16] f32 (both written at the new rows); q, k_new, v_new, out bf16
+ * Supported: D = 64 (other head dims: kv_store_paged_fp8 then
+ * attn_varlen_paged_fp8_ex).  Otherwise as attn_decode_append_paged.
+ * Allocates nothing.
+ */
+kvs_status attn_decode_append_paged_fp8(const kvs_tensor* q,
+                                        const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                        kvs_tensor* k_cache, kvs_tensor* v_cache,
+                                        kvs_tensor* k_scale, kvs_tensor* v_scale,
+                                        const kvs_tensor* block_table,
+                                        const kvs_tensor* seqlens_k,
+                                        float scale, int32_t window,
+                                        kvs_tensor* out, kvs_tensor* lse,
+                                        const kvs_hints* hints,
+                                        void* workspace, size_t workspace_bytes,
+                                        kvs_stream_t stream);
+
+/*
  * attn_decode_append_paged_rope -- the fused decode step of
  * attn_decode_append_paged (window > 0: of attn_decode_append_paged_window)
  * with the "RoPE + KV cache store" step folded in ("Transformer 추론 커널
