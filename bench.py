@@ -458,6 +458,68 @@ def rope_decode_line(dec, args):
     return res
 
 
+def fp8_step_line(dec, args):
+    """A decode step over an FP8 cache on the decode workload: the fused step
+    (attn_decode_append_paged_fp8, one launch) against kv_store_paged_fp8 of
+    the 64 new rows + attn_varlen_paged_fp8 (two launches)."""
+    import torch
+    import attention_kv_store_amd as kvs
+
+    rows, new = dec.store_rows(), dec.new_token_rows()
+    reps = []
+    for r in range(4):
+        kc = torch.zeros(dec.pool_shape(), dtype=torch.uint8, device="cuda")
+        vc = torch.zeros_like(kc)
+        ks = torch.zeros(dec.num_blocks, dec.Hkv, 16, dtype=torch.float32, device="cuda")
+        vs = torch.zeros_like(ks)
+        kvs.kv_store_paged_fp8(torch.from_numpy(dec.k_tokens[rows]).to(torch.bfloat16).cuda(),
+                               torch.from_numpy(dec.v_tokens[rows]).to(torch.bfloat16).cuda(),
+                               torch.from_numpy(dec.slots[rows]).cuda(), kc, vc, ks, vs)
+        q = torch.from_numpy(dec.q).to(torch.bfloat16).cuda()
+        kn = torch.from_numpy(dec.k_tokens[new]).to(torch.bfloat16).cuda()
+        vn = torch.from_numpy(dec.v_tokens[new]).to(torch.bfloat16).cuda()
+        sl = torch.from_numpy(dec.slots[new]).cuda()
+        meta = [torch.from_numpy(x).cuda() for x in (dec.block_table, dec.cu_seqlens_q, dec.k_lens)]
+        ws = torch.zeros(max(kvs.workspace_size(q, kc, meta[0]), 1), dtype=torch.uint8, device="cuda")
+        reps.append((q, kn, vn, sl, kc, vc, ks, vs, meta, torch.empty_like(q),
+                     torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device="cuda"), ws))
+
+    def fused(i):
+        q, kn, vn, sl, kc, vc, ks, vs, meta, out, lse, ws = reps[i % 4]
+        kvs.attn_decode_append_paged_fp8(q, kn, vn, kc, vc, ks, vs, meta[0], meta[2], dec.scale, out=out, lse=lse,
+                                         workspace=ws)
+
+    def two(i):
+        q, kn, vn, sl, kc, vc, ks, vs, meta, out, lse, ws = reps[i % 4]
+        kvs.kv_store_paged_fp8(kn, vn, sl, kc, vc, ks, vs)
+        kvs.attn_varlen_paged_fp8(q, kc, vc, ks, vs, *meta, dec.scale, True, out=out, lse=lse, workspace=ws)
+
+    res = {}
+    for name, fn in (("fused_one_launch", fused), ("store_then_attention", two)):
+        for i in range(8):
+            fn(i)
+        torch.cuda.synchronize()
+        n = 100
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        nrep = max(2, args.steps // n)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(nrep):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"us_per_step": round(e0.elapsed_time(e1) / (nrep * n) * 1e3, 3), "dispatch": kvs.last_dispatch()}
+        del graph
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
 def rope_store_line(args):
     """kv_store_rope_paged at the causal prefill workload's shape (16 x 512 new
     rows, 32 / 8 heads, D 128) and the decode workload's (64 rows, 32 / 8 heads,
@@ -802,6 +864,7 @@ def main():
     if not args.no_extras:
         from workloads import causal_prefill_bf16 as _cp
         line["fp8_kv"] = {"decode": fp8_line(dec, args), "prefill": fp8_line(_cp(), args, n=40)}
+        line["fp8_kv"]["decode_step"] = fp8_step_line(dec, args)
         log(f"fp8 cache: {line['fp8_kv']}")
         line["decode_context_sweep"] = context_sweep(args)
         log(f"decode context sweep: {line['decode_context_sweep']}")
