@@ -542,7 +542,6 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
     for (const kvs_tensor* t : {k_scale, v_scale})
       if (t->shape[0] != NB || t->shape[1] != Hkv || t->shape[2] != 16)
         return fail(KVS_ERR_INVALID, "scales must be [NB, Hkv, 16] = [%lld, %lld, 16]", (long long)NB, (long long)Hkv);
-    if (plan.D != 64) return fail(KVS_ERR_UNSUPPORTED, "FP8 fused decode step: head dim 64 only (use kv_store_paged_fp8 + attn_varlen_paged_fp8_ex)");
     plan.p.k_scale = static_cast<const float*>(k_scale->data);
     plan.p.v_scale = static_cast<const float*>(v_scale->data);
     plan.p.k_scale_w = static_cast<float*>(k_scale->data);

@@ -227,11 +227,10 @@ struct DecodeWave : DecodeRope<ROPE> {
   struct Scales {
     f32x4 ks[C::NBS], vs[C::NBS];   // scales of the lane's 4 keys (4 grp .. 4 grp + 3)
   };
-  // FP8 fused step: the new K / V rows (bf16, this lane's chunks), loaded with
-  // the step that holds the new key
+  // FP8 fused step: the new K / V rows (bf16), loaded with the step that holds
+  // the new key; lane l holds elements D/64 l .. D/64 l + D/64 - 1 of each
   struct ScalesNew : Scales {
-    u32x4 kn[C::KI];
-    u32x4 vn[C::VIL];
+    uint32_t kn, vn;
   };
   using BufBase = typename std::conditional<KV8, typename std::conditional<APPEND, ScalesNew, Scales>::type,
                                             NoScales>::type;
@@ -374,10 +373,13 @@ struct DecodeWave : DecodeRope<ROPE> {
         if (st.b >= 0 && (kl >> 4) == st.lblk) {   // wave-uniform
           const E* kn = new_row(p.k_new, st.b);
           const E* vn = new_row(p.v_new, st.b);
-#pragma unroll
-          for (int i = 0; i < C::KI; ++i) bf.kn[i] = ld16(kn + i * 32 + grp * 8);
-#pragma unroll
-          for (int it = 0; it < C::VIL; ++it) bf.vn[it] = ld16(vn + ((lane >> 3) + 8 * it) * 8);
+          if constexpr (D == 64) {
+            bf.kn = kn[lane];
+            bf.vn = vn[lane];
+          } else {
+            bf.kn = *reinterpret_cast<const uint32_t*>(kn + 2 * lane);
+            bf.vn = *reinterpret_cast<const uint32_t*>(vn + 2 * lane);
+          }
         }
       }
     } else if constexpr (APPEND) {
@@ -477,55 +479,68 @@ struct DecodeWave : DecodeRope<ROPE> {
       const int kl = st.Lk - 1, k0 = st.lblk * 16;
       if (kl < k0 || kl >= k0 + 16) return;   // wave-uniform
       const int r = kl - k0, kp = lane & 7;
-      auto absmax8 = [](const u32x4& w) {
-        float m = 0.f;
+      // The row's absmax over the wave, the scale and codes as in
+      // kv_store_paged_fp8 (same fp32 divisions, same code function), each
+      // lane coding its own D/64 elements of each row.
+      constexpr int EPL = D / 64;
+      static_assert(EPL == 1 || EPL == 2, "D is 64 or 128");
+      float xk[EPL], xv[EPL];
+      xk[0] = bf16lo_to_f32(b.kn);
+      xv[0] = bf16lo_to_f32(b.vn);
+      if constexpr (EPL == 2) {
+        xk[1] = bf16hi_to_f32(b.kn);
+        xv[1] = bf16hi_to_f32(b.vn);
+      }
+      float ak = fabsf(xk[0]), av = fabsf(xv[0]);
+      if constexpr (EPL == 2) {
+        ak = fmaxf(ak, fabsf(xk[1]));
+        av = fmaxf(av, fabsf(xv[1]));
+      }
+      const float sk = wave_max(ak) / 448.f;   // the same in every lane
+      const float sv = wave_max(av) / 448.f;
+      uint32_t ck = 0u, cv = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16lo_to_f32(w[i])), fabsf(bf16hi_to_f32(w[i]))));
-        return m;
-      };
-      auto codes8 = [](const u32x4& w, float sc) {
-        uint32_t c[2] = {0u, 0u};
-        if (sc > 0.f) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = e4m3_code(bf16lo_to_f32(w[i]) / sc), hi = e4m3_code(bf16hi_to_f32(w[i]) / sc);
-            c[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
-          }
-        }
-        return u32x2{c[0], c[1]};
-      };
-      float ak = 0.f;
-#pragma unroll
-      for (int i = 0; i < C::KI; ++i) ak = fmaxf(ak, absmax8(b.kn[i]));
-      ak = fmaxf(ak, __shfl_xor(ak, 16));
-      ak = fmaxf(ak, __shfl_xor(ak, 32));
-      const float sk = ak / 448.f;
-      float av = 0.f;
-#pragma unroll
-      for (int it = 0; it < C::VIL; ++it) av = fmaxf(av, absmax8(b.vn[it]));
-      av = fmaxf(av, __shfl_xor(av, 8));
-      av = fmaxf(av, __shfl_xor(av, 16));
-      av = fmaxf(av, __shfl_xor(av, 32));
-      const float sv = av / 448.f;
-      const float skr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sk), r));
-      const float svr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), r >> 1));
-      const bool store = st.phys >= 0 && st.phys < p.NB;
-      const int64_t so = slot_offset(st.phys, kl);
+      for (int e = 0; e < EPL; ++e) {
+        if (sk > 0.f) ck |= e4m3_code(xk[e] / sk) << (8 * e);
+        if (sv > 0.f) cv |= e4m3_code(xv[e] / sv) << (8 * e);
+      }
+      // The codes go through the first 2 D bytes of this wave's slab (which
+      // the step's V^T overwrites afterwards) to the lanes that hold key r:
+      // K chunks i 32 + grp 8 (lanes col == r), V chunks dch (lanes of key
+      // pair kp holding r).  One wave's LDS operations execute in order.
+      uint8_t* cb = reinterpret_cast<uint8_t*>(slab);
+      if constexpr (EPL == 1) {
+        cb[lane] = (uint8_t)ck;
+        cb[D + lane] = (uint8_t)cv;
+      } else {
+        *reinterpret_cast<uint16_t*>(cb + 2 * lane) = (uint16_t)ck;
+        *reinterpret_cast<uint16_t*>(cb + D + 2 * lane) = (uint16_t)cv;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       if (col == r) {
 #pragma unroll
-        for (int i = 0; i < C::KI; ++i) {
-          b.k[0][i] = codes8(b.kn[i], sk);
-          if (store) *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.k_cache_w) + so + i * 32 + grp * 8) = b.k[0][i];
-        }
+        for (int i = 0; i < C::KI; ++i) b.k[0][i] = *reinterpret_cast<const u32x2*>(cb + i * 32 + grp * 8);
       }
 #pragma unroll
       for (int it = 0; it < C::VIL; ++it) {
-        const int dch = (lane >> 3) + 8 * it;
-        const u32x2 vc = codes8(b.vn[it], sv);
+        const u32x2 vc = *reinterpret_cast<const u32x2*>(cb + D + ((lane >> 3) + 8 * it) * 8);
         if (2 * kp == r) b.v[0][2 * it] = vc;
         if (2 * kp + 1 == r) b.v[0][2 * it + 1] = vc;
-        if (store && (2 * kp == r || 2 * kp + 1 == r))
-          *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(p.v_cache_w) + so + dch * 8) = vc;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      const float skr = sk, svr = sv;
+      const bool store = st.phys >= 0 && st.phys < p.NB;
+      const int64_t so = slot_offset(st.phys, kl);
+      if (store) {
+        uint8_t* kd = static_cast<uint8_t*>(p.k_cache_w) + so;
+        uint8_t* vd = static_cast<uint8_t*>(p.v_cache_w) + so;
+        if constexpr (EPL == 1) {
+          kd[lane] = (uint8_t)ck;
+          vd[lane] = (uint8_t)cv;
+        } else {
+          *reinterpret_cast<uint16_t*>(kd + 2 * lane) = (uint16_t)ck;
+          *reinterpret_cast<uint16_t*>(vd + 2 * lane) = (uint16_t)cv;
+        }
       }
       // the lanes holding key r's scales (keys 4 grp .. 4 grp + 3)
       if (grp == (r >> 2)) {
@@ -1241,9 +1256,9 @@ hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s) {
     return D == 64 ? launch_decode_t<64, true, true, false, false, true>(p, s) : launch_decode_t<128, true, true, false, false, true>(p, s);
   }
   if (p.kv8) {   // FP8 caches, bf16 queries
-    if (p.append) {   // the fused step: head dim 64 (at 128 the new rows' registers would spill)
-      if (D != 64) return hipErrorInvalidValue;
-      return p.window > 0 ? launch_decode_t<64, true, true, true, true>(p, s) : launch_decode_t<64, true, true, false, true>(p, s);
+    if (p.append) {   // the fused step
+      if (p.window > 0) return D == 64 ? launch_decode_t<64, true, true, true, true>(p, s) : launch_decode_t<128, true, true, true, true>(p, s);
+      return D == 64 ? launch_decode_t<64, true, true, false, true>(p, s) : launch_decode_t<128, true, true, false, true>(p, s);
     }
     if (p.window > 0) return D == 64 ? launch_decode_t<64, true, false, true, true>(p, s) : launch_decode_t<128, true, false, true, true>(p, s);
     return D == 64 ? launch_decode_t<64, true, false, false, true>(p, s) : launch_decode_t<128, true, false, false, true>(p, s);

@@ -379,9 +379,8 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q,
  *
  *   k_cache, v_cache [NB, 16, Hkv, D] KVS_FP8_E4M3; k_scale, v_scale
  *   [NB, Hkv, 16] f32 (both written at the new rows); q, k_new, v_new, out bf16
- * Supported: D = 64 (other head dims: kv_store_paged_fp8 then
- * attn_varlen_paged_fp8_ex).  Otherwise as attn_decode_append_paged.
- * Allocates nothing.
+ * Otherwise as attn_decode_append_paged (D = 64 or 128).  Allocates
+ * nothing.
  */
 kvs_status attn_decode_append_paged_fp8(const kvs_tensor* q,
                                         const kvs_tensor* k_new, const kvs_tensor* v_new,

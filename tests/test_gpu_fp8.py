@@ -197,9 +197,10 @@ def test_fp8_decode_tail():
     _check_fp8_attention(b, dev, host, decode_tail=4)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("heads", [(8, 2), (32, 8)])
 @pytest.mark.parametrize("window,splits", [(0, 0), (0, 7), (0, 64), (33, 0)])
-def test_fp8_fused_decode_step(heads, window, splits):
+def test_fp8_fused_decode_step(heads, window, splits, D):
     """attn_decode_append_paged_fp8: the pool afterwards (codes and scales) is
     bit for bit the oracle's quantizing store of every row, the new ones
     included; out / lse match the oracle's attention over it."""
@@ -208,8 +209,8 @@ def test_fp8_fused_decode_step(heads, window, splits):
     from workloads import make_batch
     Hq, Hkv = heads
     k_lens = [1, 2, 15, 16, 17, 33, 100, 500, 2000, 64, 65, 31]
-    b = make_batch(1750 + Hq + window + splits, [1] * len(k_lens), k_lens, Hq=Hq, Hkv=Hkv, D=64, dtype="bf16",
-                   window=window, name=f"fp8-fused-{Hq}/{Hkv}-w{window}-s{splits}")
+    b = make_batch(1750 + Hq + window + splits + D, [1] * len(k_lens), k_lens, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
+                   window=window, name=f"fp8-fused-{Hq}/{Hkv}-d{D}-w{window}-s{splits}")
     cached = np.intersect1d(b.store_rows(), b.cached_token_rows())
     new = b.new_token_rows()
     dev = _dev_pool(b.num_blocks, b.Hkv, b.D)
@@ -234,17 +235,5 @@ def test_fp8_fused_decode_step(heads, window, splits):
     ro, rl = attention_oracle(b.q, dequantize_pool(host[0], host[2]), dequantize_pool(host[1], host[3]),
                               b.block_table, b.cu_seqlens_q, b.k_lens, b.scale, True, window=window)
     eo, el = np.max(np.abs(to_f64(out) - ro)), np.max(np.abs(to_f64(lse) - rl))
-    print(f"[fp8 fused {Hq}/{Hkv} w{window} s{splits}] max|dout|={eo:.3e} max|dlse|={el:.3e}", flush=True)
+    print(f"[fp8 fused {Hq}/{Hkv} d{D} w{window} s{splits}] max|dout|={eo:.3e} max|dlse|={el:.3e}", flush=True)
     assert eo <= TOL and el <= TOL
-
-
-def test_fp8_fused_decode_step_head_dim_128_unsupported():
-    import attention_kv_store_amd as kvs
-    from workloads import make_batch
-    b = make_batch(1760, [1, 1], [5, 40], Hq=8, Hkv=2, D=128, dtype="bf16")
-    dev = _dev_pool(b.num_blocks, b.Hkv, b.D)
-    q = torch.from_numpy(b.q).to(torch.bfloat16).cuda()
-    kn = torch.zeros(2, 2, 128, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(kvs.KvsError, match="head dim 64 only"):
-        kvs.attn_decode_append_paged_fp8(q, kn, kn, *dev, torch.from_numpy(b.block_table).cuda(),
-                                         torch.from_numpy(b.k_lens).cuda(), b.scale)
