@@ -21,14 +21,20 @@ define, with no tiling, fusion or reordering beyond that definition:
   / ``dequantize_pool`` -- the FP8 (OCP E4M3) KV cache with one scale per
   token row and KV head (Transformer 추론 커널 (3/10), §7, §19, §24 name FP8 KV,
   quantized layouts and scale layouts; the format is the OCP specification's).
+* ``int8_encode`` / ``int8_decode`` / ``quantize_rows_int8`` /
+  ``kv_store_int8_oracle`` / ``dequantize_pool_int8`` -- the INT8 KV cache
+  with the same scale layout (s = absmax / 127, codes rounded to nearest even
+  and clamped to +-127; §19 and §24 name INT8 KV next to FP8).
 * ``lse_merge`` -- the stable merge of partial results over disjoint key sets
   (Transformer 추론 커널 (3/10), §12 equations for m_new / l_new, and §16).
 
-Pins (tests/test_oracle_pins.py) tie every function to something other than
+Pins (tests/test_oracle_*pins.py) tie every function to something other than
 itself: closed forms, invariants, a multi-precision brute force and CPU torch
-SDPA.  The readings taken where the pages are silent are listed in the design doc.
+SDPA.  Where the pages are silent, each module's docstring states the reading
+it takes.
 """
 from .attention import attention_oracle, gather_sequence, lse_merge, BLOCK_SIZE  # noqa: F401
 from .store import kv_store_oracle  # noqa: F401
 from .rope import INTERLEAVED, NEOX, apply_rope, kv_store_rope_oracle  # noqa: F401
 from .fp8 import dequantize_pool, e4m3_decode, e4m3_encode, kv_store_fp8_oracle, quantize_rows  # noqa: F401
+from .int8 import dequantize_pool_int8, int8_decode, int8_encode, kv_store_int8_oracle, quantize_rows_int8  # noqa: F401
