@@ -8,7 +8,9 @@ Python names mirror the C ABI (include/kvstore.h):
 * ``kv_store_paged_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale,
   v_scale)`` and ``attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale,
   block_table, cu_seqlens_q, seqlens_k, scale, causal, ...)``: the FP8 (E4M3)
-  cache with one scale per token row and KV head
+  cache with one scale per token row and KV head; ``kv_store_paged_int8``,
+  ``attn_varlen_paged_int8`` and ``attn_decode_append_paged_int8``: the same
+  for an INT8 cache (torch.int8 codes)
 * ``attn_varlen_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k,
   scale, causal, out=None, lse=None, ...)`` (``window=W`` selects the
   sliding-window entry point ``attn_varlen_paged_window_ex``)
@@ -29,7 +31,8 @@ from . import _lib
 from ._lib import KVS_BF16, KVS_F32, KVS_I32, KvsError, KvsHints, KvsRope, describe, last_dispatch  # noqa: F401
 
 __all__ = ["kv_store_paged", "kv_store_rope_paged", "kv_store_paged_fp8", "attn_varlen_paged_fp8",
-           "attn_decode_append_paged_fp8", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
+           "attn_decode_append_paged_fp8", "kv_store_paged_int8", "attn_varlen_paged_int8",
+           "attn_decode_append_paged_int8", "attn_varlen_paged", "attn_decode_append_paged", "workspace_size", "last_dispatch", "KvsError", "release_workspace"]
 
 
 def _dtype_code(t) -> int:
@@ -37,7 +40,9 @@ def _dtype_code(t) -> int:
 
     m = {torch.float32: KVS_F32, torch.bfloat16: KVS_BF16, torch.int32: KVS_I32,
          # FP8 caches: E4M3 codes, as torch's float8_e4m3fn or as raw bytes
-         torch.float8_e4m3fn: _lib.KVS_FP8_E4M3, torch.uint8: _lib.KVS_FP8_E4M3}
+         torch.float8_e4m3fn: _lib.KVS_FP8_E4M3, torch.uint8: _lib.KVS_FP8_E4M3,
+         # INT8 caches: signed codes
+         torch.int8: _lib.KVS_INT8}
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
@@ -89,9 +94,20 @@ def kv_store_paged_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_
     _lib.check(lib.kv_store_paged_fp8(*[_ref(x) for x in d], _stream(k_cache)))
 
 
+def kv_store_paged_int8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale) -> None:
+    """Quantize rows of ``k_new`` / ``v_new`` [T, Hkv, D] (f32 / bf16) into the INT8
+    pools [NB, 16, Hkv, D] (torch.int8 codes, scale absmax / 127) at
+    ``slot_mapping``, one fp32 scale per (row, head) into ``k_scale`` /
+    ``v_scale`` [NB, Hkv, 16]."""
+    lib = _lib.load()
+    d = [_desc(x) for x in (k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale)]
+    _lib.check(lib.kv_store_paged_int8(*[_ref(x) for x in d], _stream(k_cache)))
+
+
 def attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k,
                           scale: float, causal: bool = True, out=None, lse=None, *, return_lse: bool = True,
-                          num_splits: int = 0, workspace=None, window: int = 0, decode_tail: int = 0):
+                          num_splits: int = 0, workspace=None, window: int = 0, decode_tail: int = 0,
+                          _entry: str = "attn_varlen_paged_fp8_ex"):
     """Attention over an FP8 cache (values = E4M3(code) * scale of the row and
     head); q / out bf16.  Returns ``(out, lse)``."""
     import torch
@@ -106,11 +122,18 @@ def attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu
     h = _hints(0, 0, num_splits, decode_tail)
     ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
     d = [_desc(x) for x in (q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k)]
-    st = lib.attn_varlen_paged_fp8_ex(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)), int(window),
-                                      _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
-                                      _stream(q))
+    st = getattr(lib, _entry)(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)), int(window),
+                              _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes, _stream(q))
     _lib.check(st)
     return out, lse
+
+
+def attn_varlen_paged_int8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k,
+                           scale: float, causal: bool = True, out=None, lse=None, **kw):
+    """Attention over an INT8 cache (values = code * scale of the row and
+    head); the arguments of ``attn_varlen_paged_fp8``.  Returns ``(out, lse)``."""
+    return attn_varlen_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k,
+                                 scale, causal, out, lse, _entry="attn_varlen_paged_int8_ex", **kw)
 
 
 def _rope(rotary_dim, base, style, pos_scale):
@@ -240,11 +263,11 @@ def attn_decode_append_paged(q, k_new, v_new, k_cache, v_cache, block_table, seq
 
 def attn_decode_append_paged_fp8(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k,
                                  scale: float, out=None, lse=None, *, return_lse: bool = True, num_splits: int = 0,
-                                 workspace=None, window: int = 0):
+                                 workspace=None, window: int = 0, _entry: str = "attn_decode_append_paged_fp8"):
     """The fused decode step over an FP8 cache: row b of ``k_new`` / ``v_new``
     (bf16) is quantized as ``kv_store_paged_fp8`` does into key
     ``seqlens_k[b] - 1`` (codes and scales) and query row b attends over the
-    dequantized keys.  Head dim 64.  Returns ``(out, lse)``."""
+    dequantized keys.  Returns ``(out, lse)``."""
     import torch
 
     lib = _lib.load()
@@ -255,11 +278,19 @@ def attn_decode_append_paged_fp8(q, k_new, v_new, k_cache, v_cache, k_scale, v_s
     h = _hints(1, 0, num_splits)
     ws_ptr, ws_bytes, workspace = _workspace(lib, q, k_cache, block_table, h, workspace)
     d = [_desc(x) for x in (q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k)]
-    st = lib.attn_decode_append_paged_fp8(*[_ref(x) for x in d], ctypes.c_float(scale), int(window),
-                                          _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes,
-                                          _stream(q))
+    st = getattr(lib, _entry)(*[_ref(x) for x in d], ctypes.c_float(scale), int(window),
+                              _ref(_desc(out)), _ref(_desc(lse)), ctypes.byref(h), ws_ptr, ws_bytes, _stream(q))
     _lib.check(st)
     return out, lse
+
+
+def attn_decode_append_paged_int8(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k,
+                                  scale: float, out=None, lse=None, **kw):
+    """The fused decode step over an INT8 cache (the new rows quantized as
+    ``kv_store_paged_int8`` does); the arguments of
+    ``attn_decode_append_paged_fp8``.  Returns ``(out, lse)``."""
+    return attn_decode_append_paged_fp8(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_table,
+                                        seqlens_k, scale, out, lse, _entry="attn_decode_append_paged_int8", **kw)
 
 
 def attn_varlen_paged_plain(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale: float,

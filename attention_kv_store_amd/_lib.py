@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvstore.so")
 
 KVS_OK, KVS_ERR_INVALID, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = range(5)
-KVS_F32, KVS_BF16, KVS_I32, KVS_FP8_E4M3 = 0, 1, 2, 3
+KVS_F32, KVS_BF16, KVS_I32, KVS_FP8_E4M3, KVS_INT8 = 0, 1, 2, 3, 4
 STATUS_NAMES = {0: "KVS_OK", 1: "KVS_ERR_INVALID", 2: "KVS_ERR_UNSUPPORTED", 3: "KVS_ERR_WORKSPACE", 4: "KVS_ERR_HIP"}
 
 # every symbol include/kvstore.h declares
@@ -32,6 +32,9 @@ EXPORTS = (
     "attn_decode_append_paged_window",
     "attn_decode_append_paged_rope",
     "attn_decode_append_paged_fp8",
+    "kv_store_paged_int8",
+    "attn_varlen_paged_int8_ex",
+    "attn_decode_append_paged_int8",
     "kvs_last_error",
     "kvs_last_dispatch",
     "kvs_release_workspace",
@@ -124,6 +127,12 @@ def load(path: str = LIB_PATH):
     lib.attn_decode_append_paged_fp8.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, P, P,
                                                  ctypes.POINTER(KvsHints), vp, ctypes.c_size_t, vp]
     lib.attn_decode_append_paged_fp8.restype = st
+    lib.kv_store_paged_int8.argtypes = lib.kv_store_paged_fp8.argtypes
+    lib.kv_store_paged_int8.restype = st
+    lib.attn_varlen_paged_int8_ex.argtypes = lib.attn_varlen_paged_fp8_ex.argtypes
+    lib.attn_varlen_paged_int8_ex.restype = st
+    lib.attn_decode_append_paged_int8.argtypes = lib.attn_decode_append_paged_fp8.argtypes
+    lib.attn_decode_append_paged_int8.restype = st
     lib.kvs_last_error.argtypes = []
     lib.kvs_last_error.restype = ctypes.c_char_p
     lib.kvs_last_dispatch.argtypes = []

@@ -45,18 +45,19 @@ const char* dtname(int dt) {
     case KVS_BF16: return "bf16";
     case KVS_I32: return "i32";
     case KVS_FP8_E4M3: return "fp8_e4m3";
+    case KVS_INT8: return "int8";
     default: return "?";
   }
 }
 
-int esize(int dt) { return dt == KVS_BF16 ? 2 : (dt == KVS_FP8_E4M3 ? 1 : 4); }
+int esize(int dt) { return dt == KVS_BF16 ? 2 : (dt == KVS_FP8_E4M3 || dt == KVS_INT8 ? 1 : 4); }
 
 // Checks a descriptor: present, dtype in `allowed` (bitmask of 1 << dtype),
 // rank, dense row-major strides, alignment.  Returns KVS_OK or sets g_err.
 kvs_status check_tensor(const kvs_tensor* t, const char* name, unsigned allowed, int ndim,
                         bool allow_empty = false) {
   if (!t) return fail(KVS_ERR_INVALID, "%s: descriptor is NULL", name);
-  if (t->dtype < 0 || t->dtype > 3 || !(allowed & (1u << t->dtype)))
+  if (t->dtype < 0 || t->dtype > KVS_INT8 || !(allowed & (1u << t->dtype)))
     return fail(KVS_ERR_INVALID, "%s: dtype %s not allowed here", name, dtname(t->dtype));
   if (t->ndim != ndim) return fail(KVS_ERR_INVALID, "%s: expected %d dims, got %d", name, ndim, t->ndim);
   int64_t numel = 1;
@@ -89,7 +90,7 @@ kvs_status check_tensor(const kvs_tensor* t, const char* name, unsigned allowed,
   } while (0)
 
 constexpr unsigned kFloatTypes = (1u << KVS_F32) | (1u << KVS_BF16);
-constexpr unsigned kCacheTypes = kFloatTypes | (1u << KVS_FP8_E4M3);   // attention may read FP8 caches
+constexpr unsigned kCacheTypes = kFloatTypes | (1u << KVS_FP8_E4M3) | (1u << KVS_INT8);   // attention may read FP8 / INT8 caches
 constexpr unsigned kIntTypes = (1u << KVS_I32);
 
 // ---- attention plan --------------------------------------------------------
@@ -118,7 +119,7 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
   const int64_t NB = k_cache->shape[0], page = k_cache->shape[1], Hkv = k_cache->shape[2];
   const int64_t B = table->shape[0], MB = table->shape[1];
-  const bool kv8 = k_cache->dtype == KVS_FP8_E4M3;   // FP8 codes: the queries are bf16
+  const bool kv8 = k_cache->dtype == KVS_FP8_E4M3 || k_cache->dtype == KVS_INT8;   // codes: the queries are bf16
   if (kv8 ? q->dtype != KVS_BF16 : k_cache->dtype != q->dtype)
     return fail(KVS_ERR_INVALID, "k_cache dtype %s does not go with q dtype %s", dtname(k_cache->dtype), dtname(q->dtype));
   if (k_cache->shape[3] != D) return fail(KVS_ERR_INVALID, "k_cache head dim %lld != q head dim %lld", (long long)k_cache->shape[3], (long long)D);
@@ -182,7 +183,7 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   p.scale_log2 = scale * 1.4426950408889634f;
   p.causal = causal ? 1 : 0;
   p.window = window;
-  p.kv8 = kv8 ? 1 : 0;
+  p.kv8 = kv8 ? (k_cache->dtype == KVS_INT8 ? 2 : 1) : 0;   // 1: E4M3 codes, 2: INT8 codes
   plan->dt = q->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32;
   plan->D = (int)D;
   plan->decode = (T == B);
@@ -311,7 +312,8 @@ kvs_status get_plain_workspace(size_t need, void** out) {
 }
 
 kvs_status no_fp8(const Plan& plan) {
-  if (plan.p.kv8) return fail(KVS_ERR_INVALID, "FP8 caches need their scales: use attn_varlen_paged_fp8_ex");
+  if (plan.p.kv8)
+    return fail(KVS_ERR_INVALID, "quantized caches need their scales: use the _fp8 / _int8 calls (attn_varlen_paged_fp8_ex, attn_varlen_paged_int8_ex)");
   return KVS_OK;
 }
 
@@ -333,7 +335,7 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
     const hipError_t e = kvs::launch_decode(p, plan.dt, plan.D, stream);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     set_dispatch("decode_%s%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
-                 p.kv8 ? "_kv_fp8" : "", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window",
+                 p.kv8 ? (p.kv8 == 2 ? "_kv_int8" : "_kv_fp8") : "", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window",
                  window_note(p).c_str());
     return KVS_OK;
   }
@@ -343,7 +345,7 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   const hipError_t e = kvs::launch_prefill(p, plan.dt, plan.D, stream);
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   set_dispatch("prefill_%s%s_d%d grid=%d (persistent) waves/wg=%d head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d%s",
-               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", p.kv8 ? "_kv_fp8" : "", plan.D, p.pgrid, p.pnw, p.NHG,
+               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", p.kv8 ? (p.kv8 == 2 ? "_kv_int8" : "_kv_fp8") : "", plan.D, p.pgrid, p.pnw, p.NHG,
                p.HW, 32 * p.TPW, p.meta_lds, window_note(p).c_str());
   return KVS_OK;
 }
@@ -393,12 +395,14 @@ kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new, cons
   return KVS_OK;
 }
 
-kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
-                              kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale, kvs_tensor* v_scale,
-                              kvs_stream_t stream) {
-  g_err.clear();
-  KVS_TRY(check_tensor(k_cache, "k_cache", 1u << KVS_FP8_E4M3, 4));
-  KVS_TRY(check_tensor(v_cache, "v_cache", 1u << KVS_FP8_E4M3, 4));
+// The quantizing store of kv_store_paged_fp8 / kv_store_paged_int8: `code` is
+// the cache dtype (KVS_FP8_E4M3 or KVS_INT8).
+static kvs_status store_q8(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
+                    kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale, kvs_tensor* v_scale,
+                    kvs_stream_t stream, int code) {
+  const char* name = code == KVS_INT8 ? "kv_store_paged_int8" : "kv_store_paged_fp8";
+  KVS_TRY(check_tensor(k_cache, "k_cache", 1u << code, 4));
+  KVS_TRY(check_tensor(v_cache, "v_cache", 1u << code, 4));
   KVS_TRY(check_tensor(k_scale, "k_scale", 1u << KVS_F32, 3));
   KVS_TRY(check_tensor(v_scale, "v_scale", 1u << KVS_F32, 3));
   KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3, true));
@@ -419,7 +423,7 @@ kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new, 
       return fail(KVS_ERR_INVALID, "scales must be [NB, Hkv, 16] = [%lld, %lld, 16]", (long long)NB, (long long)Hkv);
   if (slot_mapping->shape[0] != Tn) return fail(KVS_ERR_INVALID, "slot_mapping has %lld entries for %lld rows", (long long)slot_mapping->shape[0], (long long)Tn);
   if (Tn == 0) {
-    set_dispatch("kv_store_paged_fp8: empty (nothing enqueued)");
+    set_dispatch("%s: empty (nothing enqueued)", name);
     return KVS_OK;
   }
   kvs::StoreFp8Params p{};
@@ -434,10 +438,24 @@ kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new, 
   p.num_slots = NB * 16;
   p.Hkv = (int32_t)Hkv;
   const hipError_t e = kvs::launch_store_fp8(p, k_new->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32, (int)D,
-                                             reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(KVS_ERR_HIP, "kv_store_paged_fp8 launch failed: %s", hipGetErrorString(e));
-  set_dispatch("kv_store_paged_fp8 rows=%lld kv_heads=%lld head_dim=%lld", (long long)Tn, (long long)Hkv, (long long)D);
+                                             code == KVS_INT8, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVS_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(e));
+  set_dispatch("%s rows=%lld kv_heads=%lld head_dim=%lld", name, (long long)Tn, (long long)Hkv, (long long)D);
   return KVS_OK;
+}
+
+kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
+                              kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale, kvs_tensor* v_scale,
+                              kvs_stream_t stream) {
+  g_err.clear();
+  return store_q8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream, KVS_FP8_E4M3);
+}
+
+kvs_status kv_store_paged_int8(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
+                               kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale, kvs_tensor* v_scale,
+                               kvs_stream_t stream) {
+  g_err.clear();
+  return store_q8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream, KVS_INT8);
 }
 
 kvs_status kv_store_rope_paged(kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
@@ -528,7 +546,7 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
                          const kvs_tensor* seqlens_k, float scale, int window, kvs_tensor* out, kvs_tensor* lse,
                          const kvs_hints* hints, void* workspace, size_t workspace_bytes, kvs_stream_t stream,
                          const kvs_rope* rope = nullptr, kvs_tensor* k_scale = nullptr,
-                         kvs_tensor* v_scale = nullptr) {
+                         kvs_tensor* v_scale = nullptr, int q8 = 1) {
   KVS_TRY(check_hints(hints));
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, nullptr, seqlens_k, scale, 1, out, lse, hints, false,
@@ -537,7 +555,8 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
     // FP8 cache: the new rows are quantized as kv_store_paged_fp8 does
     KVS_TRY(check_tensor(k_scale, "k_scale", 1u << KVS_F32, 3));
     KVS_TRY(check_tensor(v_scale, "v_scale", 1u << KVS_F32, 3));
-    if (!plan.p.kv8) return fail(KVS_ERR_INVALID, "k_cache / v_cache must hold FP8 codes here");
+    if (plan.p.kv8 != q8)
+      return fail(KVS_ERR_INVALID, "k_cache / v_cache must hold %s codes here", q8 == 2 ? "INT8" : "FP8 (E4M3)");
     const int64_t NB = k_cache->shape[0], Hkv = k_cache->shape[2];
     for (const kvs_tensor* t : {k_scale, v_scale})
       if (t->shape[0] != NB || t->shape[1] != Hkv || t->shape[2] != 16)
@@ -554,7 +573,7 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
   for (int i = 0; i < 3; ++i)
     if (v_new->shape[i] != k_new->shape[i]) return fail(KVS_ERR_INVALID, "v_new shape != k_new shape");
   if (k_new->dtype != q->dtype || v_new->dtype != q->dtype) return fail(KVS_ERR_INVALID, "k_new / v_new dtype != q dtype");
-  if (rope && plan.p.kv8) return fail(KVS_ERR_UNSUPPORTED, "rope with an FP8 cache in the fused decode step");
+  if (rope && plan.p.kv8) return fail(KVS_ERR_UNSUPPORTED, "rope with a quantized cache in the fused decode step");
   if (k_new->shape[0] != q->shape[0] || k_new->shape[1] != k_cache->shape[2] || k_new->shape[2] != k_cache->shape[3])
     return fail(KVS_ERR_INVALID, "k_new must be [B, Hkv, D] = [%lld, %lld, %lld]", (long long)q->shape[0],
                 (long long)k_cache->shape[2], (long long)k_cache->shape[3]);
@@ -594,7 +613,7 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
   }
   KVS_TRY(run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream)));
   set_dispatch("decode_append_%s%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s%s",
-               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", p.kv8 ? "_kv_fp8" : "", plan.D, p.nwg, p.Hkv / p.hpw,
+               plan.dt == kvs::DType::BF16 ? "bf16" : "f32", p.kv8 ? (p.kv8 == 2 ? "_kv_int8" : "_kv_fp8") : "", plan.D, p.nwg, p.Hkv / p.hpw,
                p.hpw, p.nwg, p.dsmall ? "whole" : "window", window_note(p).c_str(), p.rope ? " rope" : "");
   return KVS_OK;
 }
@@ -729,6 +748,19 @@ kvs_status attn_decode_append_paged_fp8(const kvs_tensor* q, const kvs_tensor* k
                        workspace, workspace_bytes, stream, nullptr, k_scale, v_scale);
 }
 
+kvs_status attn_decode_append_paged_int8(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                         kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale,
+                                         kvs_tensor* v_scale, const kvs_tensor* block_table,
+                                         const kvs_tensor* seqlens_k, float scale, int32_t window, kvs_tensor* out,
+                                         kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                         size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
+  if (!k_scale || !v_scale) return fail(KVS_ERR_INVALID, "k_scale / v_scale: descriptor is NULL");
+  return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, window, out, lse, hints,
+                       workspace, workspace_bytes, stream, nullptr, k_scale, v_scale, 2);
+}
+
 kvs_status attn_decode_append_paged_rope(const kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
                                          kvs_tensor* k_cache, kvs_tensor* v_cache, const kvs_tensor* block_table,
                                          const kvs_tensor* seqlens_k, float scale, int32_t window, const kvs_rope* rope,
@@ -764,16 +796,14 @@ kvs_status attn_varlen_paged_ex(const kvs_tensor* q, const kvs_tensor* k_cache, 
                              reinterpret_cast<hipStream_t>(stream)});
 }
 
-kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
-                                    const kvs_tensor* k_scale, const kvs_tensor* v_scale,
-                                    const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
-                                    const kvs_tensor* seqlens_k, float scale, int causal, int32_t window,
-                                    kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
-                                    size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+static kvs_status varlen_q8(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                            const kvs_tensor* k_scale, const kvs_tensor* v_scale, const kvs_tensor* block_table,
+                            const kvs_tensor* cu_seqlens_q, const kvs_tensor* seqlens_k, float scale, int causal,
+                            int32_t window, kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                            size_t workspace_bytes, kvs_stream_t stream, int code) {
   KVS_TRY(check_hints(hints));
   if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
-  KVS_TRY(check_tensor(k_cache, "k_cache", 1u << KVS_FP8_E4M3, 4));
+  KVS_TRY(check_tensor(k_cache, "k_cache", 1u << code, 4));
   KVS_TRY(check_tensor(k_scale, "k_scale", 1u << KVS_F32, 3));
   KVS_TRY(check_tensor(v_scale, "v_scale", 1u << KVS_F32, 3));
   const int64_t NB = k_cache->shape[0], Hkv = k_cache->shape[2];
@@ -783,6 +813,28 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cac
   return run_hinted(AttnCall{q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k, scale,
                              causal, window, out, lse, hints, workspace, workspace_bytes,
                              reinterpret_cast<hipStream_t>(stream)});
+}
+
+kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                    const kvs_tensor* k_scale, const kvs_tensor* v_scale,
+                                    const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
+                                    const kvs_tensor* seqlens_k, float scale, int causal, int32_t window,
+                                    kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                    size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  return varlen_q8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k, scale, causal, window,
+                   out, lse, hints, workspace, workspace_bytes, stream, KVS_FP8_E4M3);
+}
+
+kvs_status attn_varlen_paged_int8_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                     const kvs_tensor* k_scale, const kvs_tensor* v_scale,
+                                     const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
+                                     const kvs_tensor* seqlens_k, float scale, int causal, int32_t window,
+                                     kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
+                                     size_t workspace_bytes, kvs_stream_t stream) {
+  g_err.clear();
+  return varlen_q8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k, scale, causal, window,
+                   out, lse, hints, workspace, workspace_bytes, stream, KVS_INT8);
 }
 
 kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,

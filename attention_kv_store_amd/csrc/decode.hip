@@ -135,6 +135,23 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(const u32x2& w) {
   return u32x4{e4m3x2_to_bf16x2(w[0], false), e4m3x2_to_bf16x2(w[0], true), e4m3x2_to_bf16x2(w[1], false),
                e4m3x2_to_bf16x2(w[1], true)};
 }
+// 8 INT8 codes -> 8 bf16, exactly (an integer of magnitude <= 128 is a bf16
+// value): each sign-extended byte converted to fp32, then packed
+__device__ __forceinline__ u32x4 i8x8_to_bf16x8(const u32x2& w) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t u = w[h];
+    r[2 * h] = pack_bf16x2((float)(int8_t)(u & 0xFFu), (float)(int8_t)((u >> 8) & 0xFFu));
+    r[2 * h + 1] = pack_bf16x2((float)(int8_t)((u >> 16) & 0xFFu), (float)(int8_t)(u >> 24));
+  }
+  return r;
+}
+template <bool I8>
+__device__ __forceinline__ u32x4 q8x8_to_bf16x8(const u32x2& w) {
+  if constexpr (I8) return i8x8_to_bf16x8(w);
+  else return e4m3x8_to_bf16x8(w);
+}
 
 // RoPE in the fused decode step: per wave, the cos / sin of the current
 // sequence's angles in LDS, and this lane's frequency theta_lane.
@@ -149,10 +166,11 @@ constexpr int kRopeLdsPairs = 64;
 constexpr double kTwoPiHi = 6.283185307179586;       // 2 pi = hi + lo (hi the nearest double)
 constexpr double kTwoPiLo = 2.4492935982947064e-16;
 
-template <int D, bool BF16, bool APPEND, bool WIN, bool KV8, bool ROPE = false>
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8, bool ROPE = false, bool I8 = false>
 struct DecodeWave : DecodeRope<ROPE> {
   using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
   static_assert(!ROPE || (BF16 && APPEND && !KV8), "RoPE: the bf16 fused decode step");
+  static_assert(!I8 || KV8, "INT8 codes are a KV8 cache");
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   // K / V elements: E4M3 codes when KV8 (then q and out are bf16)
   using KE = typename std::conditional<KV8, uint8_t, E>::type;
@@ -496,13 +514,14 @@ struct DecodeWave : DecodeRope<ROPE> {
         ak = fmaxf(ak, fabsf(xk[1]));
         av = fmaxf(av, fabsf(xv[1]));
       }
-      const float sk = wave_max(ak) / 448.f;   // the same in every lane
-      const float sv = wave_max(av) / 448.f;
+      constexpr float QMAX = I8 ? 127.f : 448.f;
+      const float sk = wave_max(ak) / QMAX;   // the same in every lane
+      const float sv = wave_max(av) / QMAX;
       uint32_t ck = 0u, cv = 0u;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        if (sk > 0.f) ck |= e4m3_code(xk[e] / sk) << (8 * e);
-        if (sv > 0.f) cv |= e4m3_code(xv[e] / sv) << (8 * e);
+        if (sk > 0.f) ck |= (I8 ? i8_code(xk[e] / sk) : e4m3_code(xk[e] / sk)) << (8 * e);
+        if (sv > 0.f) cv |= (I8 ? i8_code(xv[e] / sv) : e4m3_code(xv[e] / sv)) << (8 * e);
       }
       // The codes go through the first 2 D bytes of this wave's slab (which
       // the step's V^T overwrites afterwards) to the lanes that hold key r:
@@ -582,8 +601,8 @@ struct DecodeWave : DecodeRope<ROPE> {
         const int dch = (lane >> 3) + 8 * it;
         u32x4 w0, w1;
         if constexpr (KV8) {
-          w0 = v0_ok ? e4m3x8_to_bf16x8(bf.v[j][2 * it]) : zero;
-          w1 = v1_ok ? e4m3x8_to_bf16x8(bf.v[j][2 * it + 1]) : zero;
+          w0 = v0_ok ? q8x8_to_bf16x8<I8>(bf.v[j][2 * it]) : zero;
+          w1 = v1_ok ? q8x8_to_bf16x8<I8>(bf.v[j][2 * it + 1]) : zero;
         } else {
           w0 = v0_ok ? bf.v[j][2 * it] : zero;
           w1 = v1_ok ? bf.v[j][2 * it + 1] : zero;
@@ -639,7 +658,7 @@ struct DecodeWave : DecodeRope<ROPE> {
       } else {
 #pragma unroll
         for (int i = 0; i < C::KI; ++i) {
-          if constexpr (KV8) s[j] = mfma16x16x32_bf16(e4m3x8_to_bf16x8(bf.k[j][i]), q[i], s[j]);
+          if constexpr (KV8) s[j] = mfma16x16x32_bf16(q8x8_to_bf16x8<I8>(bf.k[j][i]), q[i], s[j]);
           else s[j] = mfma16x16x32_bf16(bf.k[j][i], q[i], s[j]);
         }
       }
@@ -952,10 +971,11 @@ struct DecodeWave : DecodeRope<ROPE> {
   }
 };
 
-template <int D, bool BF16, bool APPEND, bool WIN, bool KV8, bool ROPE>
+// I8: the KV8 caches hold INT8 codes, not E4M3.
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8, bool ROPE, bool I8 = false>
 __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
-  using W = DecodeWave<D, BF16, APPEND, WIN, KV8, ROPE>;
+  using W = DecodeWave<D, BF16, APPEND, WIN, KV8, ROPE, I8>;
   // RoPE: the new rows are written by the waves that attend them (rotated),
   // not during set-up
   constexpr bool SETUP_APPEND = APPEND && !ROPE && !KV8;
@@ -1217,8 +1237,10 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   if (nseg > nsplit_seg) stream(nsplit_seg, nseg);
 }
 
-template <int D, bool BF16, bool APPEND, bool WIN, bool KV8 = false, bool ROPE = false>
+template <int D, bool BF16, bool APPEND, bool WIN, bool KV8 = false, bool ROPE = false, bool I8 = false>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
+  static_assert(!I8 || (BF16 && KV8 && !ROPE), "INT8 caches: bf16 queries");
+  const void* kern = reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND, WIN, KV8, ROPE, I8>);
   using C = DCfg<D, KV8 ? kDecodeKv8Blocks : 1>;
   static_assert(C::SLAB + (ROPE ? 2 * kRopeLdsPairs * 4 : 0) == decode_slab_bytes(D, KV8, ROPE),
                 "decode_slab_bytes must match the slab layout");
@@ -1228,8 +1250,7 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
   if (lds > lds_granted.load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, BF16, APPEND, WIN, KV8, ROPE>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
       return e;
@@ -1238,7 +1259,7 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t s) {
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND, WIN, KV8, ROPE>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
+  hipLaunchKernelGGL((decode_kernel<D, BF16, APPEND, WIN, KV8, ROPE, I8>), dim3(p.nwg, p.Hkv / p.hpw), dim3(64 * p.hpw), lds, s, p);
   return hipGetLastError();
 }
 
@@ -1254,6 +1275,14 @@ hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s) {
     if (dt != DType::BF16 || !p.append) return hipErrorInvalidValue;
     if (p.window > 0) return D == 64 ? launch_decode_t<64, true, true, true, false, true>(p, s) : launch_decode_t<128, true, true, true, false, true>(p, s);
     return D == 64 ? launch_decode_t<64, true, true, false, false, true>(p, s) : launch_decode_t<128, true, true, false, false, true>(p, s);
+  }
+  if (p.kv8 == 2) {   // INT8 caches, bf16 queries
+    if (p.append) {   // the fused step
+      if (p.window > 0) return D == 64 ? launch_decode_t<64, true, true, true, true, false, true>(p, s) : launch_decode_t<128, true, true, true, true, false, true>(p, s);
+      return D == 64 ? launch_decode_t<64, true, true, false, true, false, true>(p, s) : launch_decode_t<128, true, true, false, true, false, true>(p, s);
+    }
+    if (p.window > 0) return D == 64 ? launch_decode_t<64, true, false, true, true, false, true>(p, s) : launch_decode_t<128, true, false, true, true, false, true>(p, s);
+    return D == 64 ? launch_decode_t<64, true, false, false, true, false, true>(p, s) : launch_decode_t<128, true, false, false, true, false, true>(p, s);
   }
   if (p.kv8) {   // FP8 caches, bf16 queries
     if (p.append) {   // the fused step

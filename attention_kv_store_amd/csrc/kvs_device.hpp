@@ -176,4 +176,11 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return c | sign;
 }
 
+// INT8 code of y: the nearest integer (ties to even), clamped to +-127, as
+// the byte of its two's complement.
+__device__ __forceinline__ uint32_t i8_code(float y) {
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.f), 127.f);
+  return (uint32_t)(int32_t)r & 0xFFu;
+}
+
 }  // namespace kvs

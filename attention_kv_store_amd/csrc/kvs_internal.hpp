@@ -162,7 +162,8 @@ inline size_t prefill_lds_bytes(int D, bool bf16, int B, int meta_lds) {
 
 hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);
 hipError_t launch_rope_store(const RopeParams& p, DType dt, hipStream_t s);
-hipError_t launch_store_fp8(const StoreFp8Params& p, DType in, int D, hipStream_t s);
+// i8: INT8 codes (scale absmax / 127), else FP8 E4M3 (absmax / 448)
+hipError_t launch_store_fp8(const StoreFp8Params& p, DType in, int D, bool i8, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s);
 

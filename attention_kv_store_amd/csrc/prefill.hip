@@ -105,6 +105,24 @@ __device__ __attribute__((aligned(16))) uint16_t g_zero_row[128];
 // 8 E4M3 codes times a scale, rounded to bf16 (nearest even): one 16-byte
 // chunk of a bf16 row.  The conversion instruction decodes the OCP E4M3
 // format exactly.
+__device__ __forceinline__ u32x4 e4m3x8_scaled_to_bf16(const u32x2& w, float sc);
+// 8 INT8 codes times a scale, rounded to bf16 (nearest even): each code is
+// its sign-extended byte, converted exactly to fp32.
+__device__ __forceinline__ u32x4 i8x8_scaled_to_bf16(const u32x2& w, float sc) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t u = w[h];
+    r[2 * h] = pack_bf16x2((float)(int8_t)(u & 0xFFu) * sc, (float)(int8_t)((u >> 8) & 0xFFu) * sc);
+    r[2 * h + 1] = pack_bf16x2((float)(int8_t)((u >> 16) & 0xFFu) * sc, (float)(int8_t)(u >> 24) * sc);
+  }
+  return r;
+}
+template <bool I8>
+__device__ __forceinline__ u32x4 q8x8_scaled_to_bf16(const u32x2& w, float sc) {
+  if constexpr (I8) return i8x8_scaled_to_bf16(w, sc);
+  else return e4m3x8_scaled_to_bf16(w, sc);
+}
 __device__ __forceinline__ u32x4 e4m3x8_scaled_to_bf16(const u32x2& w, float sc) {
   u32x4 r;
 #pragma unroll
@@ -116,9 +134,11 @@ __device__ __forceinline__ u32x4 e4m3x8_scaled_to_bf16(const u32x2& w, float sc)
   return r;
 }
 
-template <int D, bool BF16, int NW, bool WIN, bool KV8>
+// I8: the KV8 caches hold INT8 codes, not E4M3.
+template <int D, bool BF16, int NW, bool WIN, bool KV8, bool I8 = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(AttnParams p) {
-  static_assert(!KV8 || BF16, "FP8 caches take bf16 queries");
+  static_assert(!KV8 || BF16, "FP8 / INT8 caches take bf16 queries");
+  static_assert(!I8 || KV8, "INT8 codes are a KV8 cache");
   using C = PCfg<D, BF16, NW>;
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -411,8 +431,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int blk = wave * C::KIT + j;
         const int key = kv0 + wave * C::KPW + (j * 64 + lane) / C::CPR;
         const bool live = !edge || (key < s.it.nkeys && (!WIN || key >= s.it.klo));
-        st16(Kd + blk * 1024 + lane * 16, live ? e4m3x8_scaled_to_bf16(k8[j], ks8[j]) : zero);
-        st16(Vd + blk * 1024 + lane * 16, live ? e4m3x8_scaled_to_bf16(v8[j], vs8[j]) : zero);
+        st16(Kd + blk * 1024 + lane * 16, live ? q8x8_scaled_to_bf16<I8>(k8[j], ks8[j]) : zero);
+        st16(Vd + blk * 1024 + lane * 16, live ? q8x8_scaled_to_bf16<I8>(v8[j], vs8[j]) : zero);
       }
     } else if constexpr (!BF16) {
       char* Ks = smem + buf * C::STAGE;
@@ -717,15 +737,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-template <int D, bool BF16, int NW, bool WIN, bool KV8 = false>
+template <int D, bool BF16, int NW, bool WIN, bool KV8 = false, bool I8 = false>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
+  static_assert(!I8 || (BF16 && KV8 && NW == 8), "INT8 caches: bf16 queries, 8-wave workgroups");
+  const void* kern = reinterpret_cast<const void*>(&prefill_kernel<D, BF16, NW, WIN, KV8, I8>);
   const size_t lds = prefill_lds_bytes(D, BF16, p.B, p.meta_lds);
   // dynamic LDS above the default limit must be requested; grow it as needed
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
   if (lds > lds_granted.load(std::memory_order_relaxed)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, BF16, NW, WIN, KV8>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for the caller's next HIP call
       return e;
@@ -734,7 +755,7 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t s) {
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((prefill_kernel<D, BF16, NW, WIN, KV8>), dim3(p.pgrid), dim3(64 * NW), lds, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, BF16, NW, WIN, KV8, I8>), dim3(p.pgrid), dim3(64 * NW), lds, s, p);
   return hipGetLastError();
 }
 
@@ -748,6 +769,11 @@ static hipError_t launch_prefill_w(const AttnParams& p, DType dt, int D, hipStre
 }
 
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s) {
+  if (p.kv8 == 2) {   // INT8 caches: bf16 queries, 8-wave workgroups
+    if (p.pnw != 8) return hipErrorInvalidValue;
+    if (p.window > 0) return D == 64 ? launch_prefill_t<64, true, 8, true, true, true>(p, s) : launch_prefill_t<128, true, 8, true, true, true>(p, s);
+    return D == 64 ? launch_prefill_t<64, true, 8, false, true, true>(p, s) : launch_prefill_t<128, true, 8, false, true, true>(p, s);
+  }
   if (p.kv8) {   // FP8 caches: bf16 queries, 8-wave workgroups
     if (p.pnw != 8) return hipErrorInvalidValue;
     if (p.window > 0) return D == 64 ? launch_prefill_t<64, true, 8, true, true>(p, s) : launch_prefill_t<128, true, 8, true, true>(p, s);

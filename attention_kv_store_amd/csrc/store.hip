@@ -43,14 +43,14 @@ hipError_t launch_store(const StoreParams& p, DType, hipStream_t s) {
 
 }  // namespace kvs
 
-// ---- FP8 (E4M3) store: quantize each (row, KV head) with its own scale ----
+// ---- FP8 (E4M3) / INT8 store: quantize each (row, KV head) with its own scale
 // A 16-lane group takes one token row of one KV head (K or V): its absmax by
-// a 16-lane max, s = absmax / 448 and the codes of x / s, both divisions in
-// fp32 and correctly rounded; the codes go to the row's slot, s to the
-// [NB, Hkv, 16] scale pool.
+// a 16-lane max, s = absmax / 448 (FP8) or absmax / 127 (INT8) and the codes
+// of x / s, both divisions in fp32 and correctly rounded; the codes go to the
+// row's slot, s to the [NB, Hkv, 16] scale pool.
 namespace kvs {
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool I8 = false>
 __global__ __launch_bounds__(256) void kv_store_fp8_kernel(StoreFp8Params p) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int EPL = D / 16;                           // values per lane: 16 lanes per row
@@ -92,13 +92,13 @@ __global__ __launch_bounds__(256) void kv_store_fp8_kernel(StoreFp8Params p) {
   for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
-  const float s = amax / 448.f;                         // correctly rounded fp32 division
+  const float s = amax / (I8 ? 127.f : 448.f);          // correctly rounded fp32 division
   uint32_t packed[EPL / 4];
 #pragma unroll
   for (int q = 0; q < EPL / 4; ++q) {
     uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w |= (s > 0.f ? e4m3_code(x[4 * q + i] / s) : 0u) << (8 * i);
+    for (int i = 0; i < 4; ++i) w |= (s > 0.f ? (I8 ? i8_code(x[4 * q + i] / s) : e4m3_code(x[4 * q + i] / s)) : 0u) << (8 * i);
     packed[q] = w;
   }
   uint8_t* dst = static_cast<uint8_t*>(which ? p.v_cache : p.k_cache) + ((int64_t)slot * p.Hkv + h) * D + sub * EPL;
@@ -113,19 +113,25 @@ __global__ __launch_bounds__(256) void kv_store_fp8_kernel(StoreFp8Params p) {
   }
 }
 
-hipError_t launch_store_fp8(const StoreFp8Params& p, DType in, int D, hipStream_t s) {
+template <bool I8>
+static void launch_store_q8(const StoreFp8Params& p, DType in, int D, dim3 g, hipStream_t s) {
+  if (in == DType::BF16) {
+    if (D == 64) hipLaunchKernelGGL((kv_store_fp8_kernel<true, 64, I8>), g, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((kv_store_fp8_kernel<true, 128, I8>), g, dim3(256), 0, s, p);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((kv_store_fp8_kernel<false, 64, I8>), g, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((kv_store_fp8_kernel<false, 128, I8>), g, dim3(256), 0, s, p);
+  }
+}
+
+hipError_t launch_store_fp8(const StoreFp8Params& p, DType in, int D, bool i8, hipStream_t s) {
   const int64_t threads = p.t_new * p.Hkv * 2 * 16;
   if (threads == 0) return hipSuccess;
   const int64_t grid = (threads + 255) / 256;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid);
-  if (in == DType::BF16) {
-    if (D == 64) hipLaunchKernelGGL((kv_store_fp8_kernel<true, 64>), g, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((kv_store_fp8_kernel<true, 128>), g, dim3(256), 0, s, p);
-  } else {
-    if (D == 64) hipLaunchKernelGGL((kv_store_fp8_kernel<false, 64>), g, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((kv_store_fp8_kernel<false, 128>), g, dim3(256), 0, s, p);
-  }
+  if (i8) launch_store_q8<true>(p, in, D, g, s);
+  else launch_store_q8<false>(p, in, D, g, s);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ typedef enum {
   KVS_ERR_HIP = 4           /* a HIP runtime call or launch failed                       */
 } kvs_status;
 
-typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_I32 = 2, KVS_FP8_E4M3 = 3 } kvs_dtype;   /* FP8: OCP E4M3 codes, 1 byte */
+typedef enum { KVS_F32 = 0, KVS_BF16 = 1, KVS_I32 = 2, KVS_FP8_E4M3 = 3, KVS_INT8 = 4 } kvs_dtype;   /* FP8: OCP E4M3 codes; INT8: signed codes; 1 byte each */
 
 typedef struct {
   void* data;          /* device pointer (16-byte aligned)                 */
@@ -393,6 +393,64 @@ kvs_status attn_decode_append_paged_fp8(const kvs_tensor* q,
                                         const kvs_hints* hints,
                                         void* workspace, size_t workspace_bytes,
                                         kvs_stream_t stream);
+
+/*
+ * INT8 KV cache: the same scale layout and group as the FP8 cache (one fp32
+ * scale s per token row of one KV head, k_scale / v_scale [NB, Hkv, 16]);
+ * codes are signed bytes c in [-127, 127] and the value of a code is c * s.
+ * The pages name INT8 KV next to FP8 ("Transformer 추론 커널 (3/10)", §19,
+ * §24) and fix no encoding; here the symmetric per-row form.
+ *
+ *   k_cache, v_cache [NB, 16, Hkv, D] dtype KVS_INT8 (codes)
+ */
+
+/*
+ * kv_store_paged_int8 -- kv_store_paged_fp8 with INT8 codes: s = absmax / 127
+ * (0 for an all-zero row) and code[d] = the integer nearest to x / s (ties to
+ * even), clamped to +-127, both divisions in fp32, correctly rounded.  Same
+ * arguments, shapes, limits and error behaviour as kv_store_paged_fp8.
+ */
+kvs_status kv_store_paged_int8(const kvs_tensor* k_new, const kvs_tensor* v_new,
+                               const kvs_tensor* slot_mapping,
+                               kvs_tensor* k_cache, kvs_tensor* v_cache,
+                               kvs_tensor* k_scale, kvs_tensor* v_scale,
+                               kvs_stream_t stream);
+
+/*
+ * attn_varlen_paged_int8_ex -- attn_varlen_paged_fp8_ex over an INT8 cache:
+ * K and V are the dequantized values code * scale.  Same arguments, paths,
+ * shapes, limits and workspace rules.  Allocates nothing.
+ */
+kvs_status attn_varlen_paged_int8_ex(const kvs_tensor* q,
+                                     const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                     const kvs_tensor* k_scale, const kvs_tensor* v_scale,
+                                     const kvs_tensor* block_table,
+                                     const kvs_tensor* cu_seqlens_q,
+                                     const kvs_tensor* seqlens_k,
+                                     float scale, int causal, int32_t window,
+                                     kvs_tensor* out, kvs_tensor* lse,
+                                     const kvs_hints* hints,
+                                     void* workspace, size_t workspace_bytes,
+                                     kvs_stream_t stream);
+
+/*
+ * attn_decode_append_paged_int8 -- attn_decode_append_paged_fp8 over an INT8
+ * cache: the new rows are quantized as kv_store_paged_int8 quantizes them
+ * (codes and scales bit for bit the same) and attended with the rest.
+ * Result: kv_store_paged_int8 then attn_varlen_paged_int8_ex with
+ * cu_seqlens_q = 0..B.  Same arguments and limits.  Allocates nothing.
+ */
+kvs_status attn_decode_append_paged_int8(const kvs_tensor* q,
+                                         const kvs_tensor* k_new, const kvs_tensor* v_new,
+                                         kvs_tensor* k_cache, kvs_tensor* v_cache,
+                                         kvs_tensor* k_scale, kvs_tensor* v_scale,
+                                         const kvs_tensor* block_table,
+                                         const kvs_tensor* seqlens_k,
+                                         float scale, int32_t window,
+                                         kvs_tensor* out, kvs_tensor* lse,
+                                         const kvs_hints* hints,
+                                         void* workspace, size_t workspace_bytes,
+                                         kvs_stream_t stream);
 
 /*
  * attn_decode_append_paged_rope -- the fused decode step of

@@ -385,6 +385,67 @@ def test_fp8_store_empty_is_noop(lib):
     assert _call_store_fp8(lib, _store_fp8_args(Tn=0)) == L.KVS_OK
 
 
+# ---- INT8 cache ----------------------------------------------------------------------
+I8 = L.KVS_INT8
+
+
+def _int8_args():
+    a = _fp8_args()
+    a.update(k=T([8, 16, 2, 64], I8), v=T([8, 16, 2, 64], I8))
+    return a
+
+
+def _call_int8(lib, a, causal=1, window=0):
+    return lib.attn_varlen_paged_int8_ex(ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["ks"]), ref(a["vs"]),
+                                         ref(a["table"]), ref(a["cu"]), ref(a["lk"]), ctypes.c_float(0.125), causal,
+                                         window, ref(a["out"]), ref(a.get("lse")), None, None, 0, None)
+
+
+def test_int8_cache_needs_a_scaled_entry(lib):
+    a = _int8_args()
+    assert _call_ex(lib, a) == L.KVS_ERR_INVALID
+    assert "attn_varlen_paged_int8_ex" in lib.kvs_last_error().decode()
+
+
+def test_int8_and_fp8_entries_take_only_their_codes(lib):
+    assert _call_int8(lib, _fp8_args()) == L.KVS_ERR_INVALID      # E4M3 pool at the INT8 entry
+    assert "k_cache" in lib.kvs_last_error().decode()
+    assert _call_fp8(lib, _int8_args()) == L.KVS_ERR_INVALID      # INT8 pool at the FP8 entry
+    assert "k_cache" in lib.kvs_last_error().decode()
+
+
+@pytest.mark.parametrize("mutate,msg", [
+    (lambda a: a.update(ks=T([8, 2, 8], L.KVS_F32)), "scales must be"),
+    (lambda a: a.update(v=T([8, 16, 2, 64], FP8)), "v_cache"),
+    (lambda a: a.update(q=T([2, 4, 64], L.KVS_F32), out=T([2, 4, 64], L.KVS_F32)), "does not go with"),
+])
+def test_int8_attention_validation(lib, mutate, msg):
+    a = _int8_args()
+    mutate(a)
+    assert _call_int8(lib, a) == L.KVS_ERR_INVALID
+    assert msg in lib.kvs_last_error().decode()
+
+
+def _call_store_int8(lib, a):
+    return lib.kv_store_paged_int8(ref(a["kn"]), ref(a["vn"]), ref(a["slots"]), ref(a["k"]), ref(a["v"]),
+                                   ref(a["ks"]), ref(a["vs"]), None)
+
+
+def test_int8_store_validation_and_empty(lib):
+    a = _store_fp8_args()
+    assert _call_store_int8(lib, a) == L.KVS_ERR_INVALID          # E4M3 pools at the INT8 store
+    assert "k_cache" in lib.kvs_last_error().decode()
+    a.update(k=T([4, 16, 2, 64], I8), v=T([4, 16, 2, 64], I8))
+    assert _call_store_fp8(lib, a) == L.KVS_ERR_INVALID           # INT8 pools at the FP8 store
+    a.update(kn=T([4, 2, 96]), vn=T([4, 2, 96]), k=T([4, 16, 2, 96], I8), v=T([4, 16, 2, 96], I8))
+    assert _call_store_int8(lib, a) == L.KVS_ERR_UNSUPPORTED
+    assert "head dim" in lib.kvs_last_error().decode()
+    e = _store_fp8_args(Tn=0)
+    e.update(k=T([4, 16, 2, 64], I8), v=T([4, 16, 2, 64], I8))
+    assert _call_store_int8(lib, e) == L.KVS_OK
+    assert "kv_store_paged_int8: empty" in lib.kvs_last_dispatch().decode()
+
+
 # ---- decode_tail hint ----------------------------------------------------------------
 def _hint(**kw):
     h = L.KvsHints()
