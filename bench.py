@@ -54,8 +54,8 @@ def _src_sha(name: str) -> str:
 
 # kernel symbol (as rocprofv3 names it) and source file of each timed workload
 COUNTED = {
-    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false, false, false>", "decode.hip"),
-    "causal_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false>", "prefill.hip"),
+    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false, false, false, false>", "decode.hip"),
+    "causal_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", "prefill.hip"),
 }
 
 
@@ -292,26 +292,37 @@ def runner_replays(dec, args):
     return res
 
 
-def fp8_line(batch, args, n=100):
-    """A workload over an FP8 (E4M3) cache: every key row quantized by
-    kv_store_paged_fp8 (one scale per row and KV head), then
-    attn_varlen_paged_fp8 timed from graph replays over 4 replicas.  Bytes read
-    per launch: the codes of every visible key row of K and V plus their fp32
-    scales."""
+def _q8_calls(fmt):
+    """(cache dtype, quantizing store, attention, fused decode step) of the FP8
+    (E4M3) or INT8 cache."""
+    import torch
+    import attention_kv_store_amd as kvs
+    if fmt == "int8":
+        return torch.int8, kvs.kv_store_paged_int8, kvs.attn_varlen_paged_int8, kvs.attn_decode_append_paged_int8
+    return torch.uint8, kvs.kv_store_paged_fp8, kvs.attn_varlen_paged_fp8, kvs.attn_decode_append_paged_fp8
+
+
+def fp8_line(batch, args, n=100, fmt="fp8"):
+    """A workload over an FP8 (E4M3) or INT8 cache: every key row quantized by
+    kv_store_paged_fp8 / _int8 (one scale per row and KV head), then
+    attn_varlen_paged_fp8 / _int8 timed from graph replays over 4 replicas.
+    Bytes read per launch: the codes of every visible key row of K and V plus
+    their fp32 scales."""
     import torch
     import attention_kv_store_amd as kvs
     from workloads import attention_flops
 
+    cdt, store, attn, _ = _q8_calls(fmt)
     rows = batch.store_rows()
     reps = []
     for r in range(4):
-        kc = torch.zeros(batch.pool_shape(), dtype=torch.uint8, device="cuda")
+        kc = torch.zeros(batch.pool_shape(), dtype=cdt, device="cuda")
         vc = torch.zeros_like(kc)
         ks = torch.zeros(batch.num_blocks, batch.Hkv, 16, dtype=torch.float32, device="cuda")
         vs = torch.zeros_like(ks)
-        kvs.kv_store_paged_fp8(torch.from_numpy(batch.k_tokens[rows]).to(torch.bfloat16).cuda(),
-                               torch.from_numpy(batch.v_tokens[rows]).to(torch.bfloat16).cuda(),
-                               torch.from_numpy(batch.slots[rows]).cuda(), kc, vc, ks, vs)
+        store(torch.from_numpy(batch.k_tokens[rows]).to(torch.bfloat16).cuda(),
+              torch.from_numpy(batch.v_tokens[rows]).to(torch.bfloat16).cuda(),
+              torch.from_numpy(batch.slots[rows]).cuda(), kc, vc, ks, vs)
         q = torch.from_numpy(batch.q).to(torch.bfloat16).cuda()
         meta = [torch.from_numpy(x).cuda() for x in (batch.block_table, batch.cu_seqlens_q, batch.k_lens)]
         out = torch.empty_like(q)
@@ -321,8 +332,7 @@ def fp8_line(batch, args, n=100):
 
     def call(i):
         q, kc, vc, ks, vs, meta, out, lse, ws = reps[i % 4]
-        kvs.attn_varlen_paged_fp8(q, kc, vc, ks, vs, *meta, batch.scale, batch.causal, out=out, lse=lse,
-                                  workspace=ws)
+        attn(q, kc, vc, ks, vs, *meta, batch.scale, batch.causal, out=out, lse=lse, workspace=ws)
 
     for i in range(8):
         call(i)
@@ -343,7 +353,7 @@ def fp8_line(batch, args, n=100):
     us = e0.elapsed_time(e1) / (nrep * n) * 1e3
     nkeys = int(batch.k_lens.sum())
     read = 2 * nkeys * batch.Hkv * (batch.D + 4)        # codes and scales of K and V
-    res = {"workload": f"{batch.name} with an FP8 (E4M3) cache", "avg_launch_us": round(us, 3),
+    res = {"workload": f"{batch.name} with an {'INT8' if fmt == 'int8' else 'FP8 (E4M3)'} cache", "avg_launch_us": round(us, 3),
            "kv_bytes_per_launch": read, "kv_GBs": round(read / (us * 1e-6) / 1e9, 1),
            "TFLOPs": round(attention_flops(batch) / (us * 1e-6) / 1e12, 1), "dispatch": kvs.last_dispatch()}
     del graph, reps
@@ -458,23 +468,24 @@ def rope_decode_line(dec, args):
     return res
 
 
-def fp8_step_line(dec, args):
-    """A decode step over an FP8 cache on the decode workload: the fused step
-    (attn_decode_append_paged_fp8, one launch) against kv_store_paged_fp8 of
-    the 64 new rows + attn_varlen_paged_fp8 (two launches)."""
+def fp8_step_line(dec, args, fmt="fp8"):
+    """A decode step over an FP8 or INT8 cache on the decode workload: the
+    fused step (attn_decode_append_paged_fp8 / _int8, one launch) against the
+    quantizing store of the 64 new rows + the attention (two launches)."""
     import torch
     import attention_kv_store_amd as kvs
 
+    cdt, store, attn, fused_call = _q8_calls(fmt)
     rows, new = dec.store_rows(), dec.new_token_rows()
     reps = []
     for r in range(4):
-        kc = torch.zeros(dec.pool_shape(), dtype=torch.uint8, device="cuda")
+        kc = torch.zeros(dec.pool_shape(), dtype=cdt, device="cuda")
         vc = torch.zeros_like(kc)
         ks = torch.zeros(dec.num_blocks, dec.Hkv, 16, dtype=torch.float32, device="cuda")
         vs = torch.zeros_like(ks)
-        kvs.kv_store_paged_fp8(torch.from_numpy(dec.k_tokens[rows]).to(torch.bfloat16).cuda(),
-                               torch.from_numpy(dec.v_tokens[rows]).to(torch.bfloat16).cuda(),
-                               torch.from_numpy(dec.slots[rows]).cuda(), kc, vc, ks, vs)
+        store(torch.from_numpy(dec.k_tokens[rows]).to(torch.bfloat16).cuda(),
+              torch.from_numpy(dec.v_tokens[rows]).to(torch.bfloat16).cuda(),
+              torch.from_numpy(dec.slots[rows]).cuda(), kc, vc, ks, vs)
         q = torch.from_numpy(dec.q).to(torch.bfloat16).cuda()
         kn = torch.from_numpy(dec.k_tokens[new]).to(torch.bfloat16).cuda()
         vn = torch.from_numpy(dec.v_tokens[new]).to(torch.bfloat16).cuda()
@@ -486,13 +497,12 @@ def fp8_step_line(dec, args):
 
     def fused(i):
         q, kn, vn, sl, kc, vc, ks, vs, meta, out, lse, ws = reps[i % 4]
-        kvs.attn_decode_append_paged_fp8(q, kn, vn, kc, vc, ks, vs, meta[0], meta[2], dec.scale, out=out, lse=lse,
-                                         workspace=ws)
+        fused_call(q, kn, vn, kc, vc, ks, vs, meta[0], meta[2], dec.scale, out=out, lse=lse, workspace=ws)
 
     def two(i):
         q, kn, vn, sl, kc, vc, ks, vs, meta, out, lse, ws = reps[i % 4]
-        kvs.kv_store_paged_fp8(kn, vn, sl, kc, vc, ks, vs)
-        kvs.attn_varlen_paged_fp8(q, kc, vc, ks, vs, *meta, dec.scale, True, out=out, lse=lse, workspace=ws)
+        store(kn, vn, sl, kc, vc, ks, vs)
+        attn(q, kc, vc, ks, vs, *meta, dec.scale, True, out=out, lse=lse, workspace=ws)
 
     res = {}
     for name, fn in (("fused_one_launch", fused), ("store_then_attention", two)):
@@ -866,6 +876,9 @@ def main():
         line["fp8_kv"] = {"decode": fp8_line(dec, args), "prefill": fp8_line(_cp(), args, n=40)}
         line["fp8_kv"]["decode_step"] = fp8_step_line(dec, args)
         log(f"fp8 cache: {line['fp8_kv']}")
+        line["int8_kv"] = {"decode": fp8_line(dec, args, fmt="int8"), "prefill": fp8_line(_cp(), args, n=40, fmt="int8"),
+                           "decode_step": fp8_step_line(dec, args, fmt="int8")}
+        log(f"int8 cache: {line['int8_kv']}")
         line["decode_context_sweep"] = context_sweep(args)
         log(f"decode context sweep: {line['decode_context_sweep']}")
         line["rope_store"] = rope_store_line(args)
