@@ -13,6 +13,8 @@ from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvstore.so")
+# the same kernels, the calls first checking the device-resident preconditions
+DEBUG_LIB_PATH = os.path.join(_PKG, "libkvstore_debug.so")
 
 KVS_OK, KVS_ERR_INVALID, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = range(5)
 KVS_F32, KVS_BF16, KVS_I32, KVS_FP8_E4M3, KVS_INT8 = 0, 1, 2, 3, 4
@@ -83,11 +85,14 @@ class KvsError(RuntimeError):
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load (once) and return the library.  Raises if it has not been built."""
+def load(path: str = None):
+    """Load (once) and return the library (the debug build when the
+    environment sets KVS_DEBUG=1).  Raises if it has not been built."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = DEBUG_LIB_PATH if os.environ.get("KVS_DEBUG") == "1" else LIB_PATH
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build the HIP library first "

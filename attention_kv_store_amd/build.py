@@ -1,6 +1,10 @@
-"""Build libkvstore.so (all HIP sources, gfx950) in the package directory.
+"""Build libkvstore.so (all HIP sources, gfx950) in the package directory,
+and beside it libkvstore_debug.so: the same kernels with the C ABI built with
+KVS_DEBUG, whose calls first check the device-resident preconditions
+(cu_seqlens_q, seqlens_k, table entries, slots) on the GPU and return
+KVS_ERR_INVALID on a violation (loaded when the environment sets KVS_DEBUG=1).
 
-    python -m attention_kv_store_amd.build            # release build
+    python -m attention_kv_store_amd.build            # both libraries
     python -m attention_kv_store_amd.build --verbose
 
 Every HIP source is compiled with packed-fp32 instructions disabled for the
@@ -19,7 +23,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvstore.so")
+DEBUG_LIB = os.path.join(PKG, "libkvstore_debug.so")
 SOURCES = ["api.hip", "store.hip", "rope.hip", "prefill.hip", "decode.hip", "calib.hip"]
+# the debug library: api.hip again with KVS_DEBUG, plus the check kernel
+DEBUG_SOURCES = [("api.hip", "api_debug.o", ["-DKVS_DEBUG"]), ("validate.hip", "validate.o", [])]
 ARCH = "gfx950"
 
 
@@ -40,9 +47,10 @@ def build(verbose: bool = False, out: str = LIB) -> str:
     ]
     objs = []
     procs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *common, "-c", os.path.join(CSRC, src), "-o", obj]
+    jobs = [(src, src.replace(".hip", ".o"), []) for src in SOURCES] + DEBUG_SOURCES
+    for src, o, extra in jobs:
+        obj = os.path.join(objdir, o)
+        cmd = [hipcc(), *common, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -58,12 +66,15 @@ def build(verbose: bool = False, out: str = LIB) -> str:
             print(log)
     if failed:
         raise RuntimeError("HIP compilation failed")
-    tmp = out + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
+    release = objs[:len(SOURCES)]
+    debug = [o for o in release if not o.endswith(os.sep + "api.o")] + objs[len(SOURCES):]
+    for lib_out, lib_objs in ((out, release), (os.path.join(os.path.dirname(out), os.path.basename(DEBUG_LIB)), debug)):
+        tmp = lib_out + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib_out)
     return out
 
 

@@ -321,8 +321,46 @@ std::string window_note(const kvs::AttnParams& p) {
   return p.window > 0 ? " sliding_window=" + std::to_string(p.window) : std::string();
 }
 
+#ifdef KVS_DEBUG
+// Debug library only: the device-resident preconditions (cu_seqlens_q,
+// seqlens_k, the table entries the call reads, store slots) are checked on
+// the stream before the call's kernels are enqueued; the call waits for the
+// check and a violation returns KVS_ERR_INVALID with nothing else enqueued.
+kvs_status debug_check(const int32_t* cu, const int32_t* lens, const int32_t* table, int64_t B, int64_t T, int MB,
+                       int NB, int window, const int32_t* slots, int64_t n_slots, int64_t num_slots,
+                       hipStream_t s) {
+  const kvs::CheckParams v{cu, lens, table, B, T, MB, NB, window, slots, n_slots, num_slots};
+  int r[4] = {0, 0, 0, 0};
+  const hipError_t e = kvs::run_check(v, s, r);
+  if (e != hipSuccess) return fail(KVS_ERR_HIP, "KVS_DEBUG check did not run: %s", hipGetErrorString(e));
+  switch (r[0]) {
+    case 0: return KVS_OK;
+    case kvs::kCheckCuFirst: return fail(KVS_ERR_INVALID, "KVS_DEBUG: cu_seqlens_q[0] = %d, not 0", r[3]);
+    case kvs::kCheckCuLast:
+      return fail(KVS_ERR_INVALID, "KVS_DEBUG: cu_seqlens_q[B] = %d, not T = %lld", r[3], (long long)T);
+    case kvs::kCheckLq:
+      return fail(KVS_ERR_INVALID, "KVS_DEBUG: sequence %d has %d query rows (needs >= 1, inside [0, T))", r[1], r[3]);
+    case kvs::kCheckLk:
+      return fail(KVS_ERR_INVALID, "KVS_DEBUG: seqlens_k[%d] = %d (needs query rows <= it <= 16 * MB = %d)", r[1],
+                  r[3], 16 * MB);
+    case kvs::kCheckTable:
+      return fail(KVS_ERR_INVALID, "KVS_DEBUG: block_table[%d][%d] = %d, outside [0, NB = %d)", r[1], r[2], r[3], NB);
+    default:
+      return fail(KVS_ERR_INVALID, "KVS_DEBUG: slot_mapping[%d] = %d, outside [0, 16 * NB = %lld)", r[1], r[3],
+                  (long long)num_slots);
+  }
+}
+#define KVS_DEBUG_CHECK(...) KVS_TRY(debug_check(__VA_ARGS__))
+#else
+#define KVS_DEBUG_CHECK(...) \
+  do {                       \
+  } while (0)
+#endif
+
 kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   kvs::AttnParams& p = plan.p;
+  KVS_DEBUG_CHECK(plan.decode ? nullptr : p.cu_q, p.lens_k, p.table, p.B, p.T, p.MB, p.NB, p.window, nullptr, 0, 0,
+                  stream);
   if (plan.decode) {
     if (plan.ws_bytes) {
       if (!ws || ws_bytes < plan.ws_bytes)
@@ -388,6 +426,7 @@ kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new, cons
   p.t_new = Tn;
   p.row_chunks = row_bytes / 16;
   p.num_slots = k_cache->shape[0] * 16;
+  KVS_DEBUG_CHECK(nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, p.slots, Tn, p.num_slots, reinterpret_cast<hipStream_t>(stream));
   const hipError_t e = kvs::launch_store(p, k_new->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32,
                                          reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "kv_store_paged launch failed: %s", hipGetErrorString(e));
@@ -437,6 +476,7 @@ static kvs_status store_q8(const kvs_tensor* k_new, const kvs_tensor* v_new, con
   p.t_new = Tn;
   p.num_slots = NB * 16;
   p.Hkv = (int32_t)Hkv;
+  KVS_DEBUG_CHECK(nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, p.slots, Tn, p.num_slots, reinterpret_cast<hipStream_t>(stream));
   const hipError_t e = kvs::launch_store_fp8(p, k_new->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32, (int)D,
                                              code == KVS_INT8, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(e));
@@ -513,6 +553,7 @@ kvs_status kv_store_rope_paged(kvs_tensor* q, const kvs_tensor* k_new, const kvs
   p.style = rope->style;
   p.inv_scale = 1.0 / rope->pos_scale;
   for (int i = 0; i < rd / 2; ++i) p.inv_freq[i] = std::pow(rope->base, -2.0 * i / (double)rd);
+  KVS_DEBUG_CHECK(nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, p.slots, Tn, p.num_slots, reinterpret_cast<hipStream_t>(stream));
   const hipError_t e = kvs::launch_rope_store(p, k_cache->dtype == KVS_BF16 ? kvs::DType::BF16 : kvs::DType::F32,
                                               reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "kv_store_rope_paged launch failed: %s", hipGetErrorString(e));

@@ -160,6 +160,20 @@ inline size_t prefill_lds_bytes(int D, bool bf16, int B, int meta_lds) {
   return 2 * prefill_stage_bytes(D, bf16) + (meta_lds ? (size_t)(2 * B + 1) * sizeof(int) : 0);
 }
 
+// Device-side precondition check (debug library only): cu_seqlens_q (null:
+// one row per sequence), seqlens_k, the table entries read, store slots.
+struct CheckParams {
+  const int32_t* cu_q;
+  const int32_t* lens_k;
+  const int32_t* table;
+  int64_t B, T;
+  int32_t MB, NB, window;
+  const int32_t* slots;
+  int64_t n_slots, num_slots;
+};
+enum { kCheckCuFirst = 1, kCheckCuLast = 2, kCheckLq = 3, kCheckLk = 4, kCheckTable = 5, kCheckSlot = 6 };
+hipError_t run_check(const CheckParams& v, hipStream_t s, int out[4]);
+
 hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);
 hipError_t launch_rope_store(const RopeParams& p, DType dt, hipStream_t s);
 // i8: INT8 codes (scale absmax / 127), else FP8 E4M3 (absmax / 448)

@@ -31,6 +31,13 @@
  *    checked without a synchronisation; the preconditions stated below for them
  *    are the caller's responsibility, and violating them is undefined behaviour
  *    (out-of-range table entries or slots are out-of-bounds device accesses).
+ *  - Debug library (libkvstore_debug.so: the same kernels, this ABI built with
+ *    KVS_DEBUG): every call first checks those values on the GPU --
+ *    cu_seqlens_q[0] = 0 and cu_seqlens_q[B] = T, 1 <= Lq_b <= Lk_b <= 16 MB,
+ *    each block-table entry the call reads in [0, NB), each store slot below
+ *    16 NB -- waits for the check, and on a violation returns KVS_ERR_INVALID
+ *    naming it with nothing else enqueued.  It synchronises the stream, so it
+ *    cannot be captured into a graph.
  */
 #ifndef KVSTORE_H
 #define KVSTORE_H
