@@ -35,6 +35,26 @@ def test_header_symbols_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_debug_library_exports_the_same_symbols():
+    """libkvstore_debug.so (the ABI built with KVS_DEBUG, same kernels) loads
+    and exports every symbol the header declares, and its host-side checks
+    behave as the release library's (no device call here)."""
+    import os
+    if not os.path.exists(L.DEBUG_LIB_PATH):
+        pytest.skip("debug library not built")
+    dbg = ctypes.CDLL(L.DEBUG_LIB_PATH)
+    for name in L.EXPORTS:
+        assert hasattr(dbg, name), name
+    dbg.kvs_last_error.restype = ctypes.c_char_p
+    dbg.attn_varlen_paged_ex.restype = ctypes.c_int
+    a = _attn_args()
+    a["q"] = T([8, 3, 64])                            # Hq % Hkv != 0: refused on the host
+    st = dbg.attn_varlen_paged_ex(ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["table"]), ref(a["cu"]), ref(a["lk"]),
+                                  ctypes.c_float(0.125), 1, ref(a["out"]), ref(a.get("lse")), None, None,
+                                  ctypes.c_size_t(0), None)
+    assert st == L.KVS_ERR_INVALID, dbg.kvs_last_error()
+
+
 def _attn_args(T_=8, Hq=4, Hkv=2, D=64, NB=8, B=2, MB=2, dtype=L.KVS_BF16):
     return dict(q=T([T_, Hq, D], dtype), k=T([NB, 16, Hkv, D], dtype), v=T([NB, 16, Hkv, D], dtype),
                 table=T([B, MB], L.KVS_I32), cu=T([B + 1], L.KVS_I32), lk=T([B], L.KVS_I32),
