@@ -689,7 +689,7 @@ def main():
         summarize_counters(*args.summarize_counters, args.counter_command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the attention shards by KV head with no exchange; see the design notes).", file=sys.stderr)
         sys.exit(2)
 
