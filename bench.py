@@ -690,7 +690,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the attention shards by KV head with no exchange; see the design notes).", file=sys.stderr)
+              "(the attention would shard by KV head, with no exchange between GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import torch
