@@ -40,7 +40,6 @@ EXPORTS = (
     "kvs_last_error",
     "kvs_last_dispatch",
     "kvs_release_workspace",
-    "kvs_mfma_peak_launch",
 )
 
 
@@ -144,8 +143,6 @@ def load(path: str = None):
     lib.kvs_last_dispatch.restype = ctypes.c_char_p
     lib.kvs_release_workspace.argtypes = []
     lib.kvs_release_workspace.restype = st
-    lib.kvs_mfma_peak_launch.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
-    lib.kvs_mfma_peak_launch.restype = st
     _lib = lib
     return lib
 

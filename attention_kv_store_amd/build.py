@@ -2,7 +2,9 @@
 and beside it libkvstore_debug.so: the same kernels with the C ABI built with
 KVS_DEBUG, whose calls first check the device-resident preconditions
 (cu_seqlens_q, seqlens_k, table entries, slots) on the GPU and return
-KVS_ERR_INVALID on a violation (loaded when the environment sets KVS_DEBUG=1).
+KVS_ERR_INVALID on a violation (loaded when the environment sets KVS_DEBUG=1),
+and libkvstore_calib.so: the benchmark's MFMA calibration kernel
+(include/kvstore_calib.h), kept out of the attention library.
 
     python -m attention_kv_store_amd.build            # both libraries
     python -m attention_kv_store_amd.build --verbose
@@ -24,9 +26,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvstore.so")
 DEBUG_LIB = os.path.join(PKG, "libkvstore_debug.so")
-SOURCES = ["api.hip", "store.hip", "rope.hip", "prefill.hip", "decode.hip", "calib.hip"]
+SOURCES = ["api.hip", "store.hip", "rope.hip", "prefill.hip", "decode.hip"]
 # the debug library: api.hip again with KVS_DEBUG, plus the check kernel
 DEBUG_SOURCES = [("api.hip", "api_debug.o", ["-DKVS_DEBUG"]), ("validate.hip", "validate.o", [])]
+# the benchmark's MFMA calibration kernel, a library of its own
+CALIB_LIB = os.path.join(PKG, "libkvstore_calib.so")
+CALIB_SOURCES = [("calib.hip", "calib.o", [])]
 ARCH = "gfx950"
 
 
@@ -47,7 +52,7 @@ def build(verbose: bool = False, out: str = LIB) -> str:
     ]
     objs = []
     procs = []
-    jobs = [(src, src.replace(".hip", ".o"), []) for src in SOURCES] + DEBUG_SOURCES
+    jobs = [(src, src.replace(".hip", ".o"), []) for src in SOURCES] + DEBUG_SOURCES + CALIB_SOURCES
     for src, o, extra in jobs:
         obj = os.path.join(objdir, o)
         cmd = [hipcc(), *common, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -67,8 +72,11 @@ def build(verbose: bool = False, out: str = LIB) -> str:
     if failed:
         raise RuntimeError("HIP compilation failed")
     release = objs[:len(SOURCES)]
-    debug = [o for o in release if not o.endswith(os.sep + "api.o")] + objs[len(SOURCES):]
-    for lib_out, lib_objs in ((out, release), (os.path.join(os.path.dirname(out), os.path.basename(DEBUG_LIB)), debug)):
+    debug = [o for o in release if not o.endswith(os.sep + "api.o")] + objs[len(SOURCES):len(SOURCES) + len(DEBUG_SOURCES)]
+    calib = objs[len(SOURCES) + len(DEBUG_SOURCES):]
+    out_dir = os.path.dirname(out)
+    for lib_out, lib_objs in ((out, release), (os.path.join(out_dir, os.path.basename(DEBUG_LIB)), debug),
+                              (os.path.join(out_dir, os.path.basename(CALIB_LIB)), calib)):
         tmp = lib_out + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", tmp]
         if verbose:

@@ -60,17 +60,20 @@ kvs_status check_tensor(const kvs_tensor* t, const char* name, unsigned allowed,
   if (t->dtype < 0 || t->dtype > KVS_INT8 || !(allowed & (1u << t->dtype)))
     return fail(KVS_ERR_INVALID, "%s: dtype %s not allowed here", name, dtname(t->dtype));
   if (t->ndim != ndim) return fail(KVS_ERR_INVALID, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  // element counts are formed with overflow checks: a descriptor whose
+  // extents multiply past 2^62 elements describes no real buffer
   int64_t numel = 1;
   for (int i = 0; i < ndim; ++i) {
     if (t->shape[i] < 0) return fail(KVS_ERR_INVALID, "%s: negative extent in dim %d", name, i);
-    numel *= t->shape[i];
+    if (__builtin_mul_overflow(numel, t->shape[i], &numel) || numel > (int64_t(1) << 62))
+      return fail(KVS_ERR_INVALID, "%s: extents too large", name);
   }
   int64_t expect = 1;
   for (int i = ndim - 1; i >= 0; --i) {
     if (t->shape[i] > 1 && t->stride[i] != expect)
       return fail(KVS_ERR_INVALID, "%s: not dense row-major (dim %d stride %lld, expected %lld)", name, i,
                   (long long)t->stride[i], (long long)expect);
-    expect *= t->shape[i];
+    expect *= t->shape[i];   // bounded by numel above
   }
   if (numel == 0) {
     if (!allow_empty) return fail(KVS_ERR_INVALID, "%s: empty tensor", name);
@@ -280,31 +283,34 @@ kvs_status device_cus(int* out) {
 }
 
 // ---- grow-only scratch for the plain call (one buffer per device) ----------
+// Allocated stream-ordered on the call's stream (hipMallocAsync) and zeroed
+// there by the library's own kernel; a smaller buffer it replaces is freed
+// stream-ordered on the same stream, after the work already queued there.
+// Nothing synchronises the device.  Calls on one device that overlap in time
+// share the buffer and are not allowed (documented in the header).
 std::mutex g_ws_mu;
 std::vector<std::pair<void*, size_t>> g_ws;
 
-kvs_status get_plain_workspace(size_t need, void** out) {
+kvs_status get_plain_workspace(size_t need, hipStream_t stream, void** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_ws_mu);
   if ((size_t)dev >= g_ws.size()) g_ws.resize(dev + 1, {nullptr, 0});
   auto& slot = g_ws[dev];
   if (slot.second < need) {
-    if (slot.first) {
-      // the old buffer may still be read by queued kernels
-      if (hipDeviceSynchronize() != hipSuccess) return fail(KVS_ERR_HIP, "hipDeviceSynchronize failed");
-      (void)hipFree(slot.first);
-      slot = {nullptr, 0};
-    }
     void* ptr = nullptr;
-    hipError_t e = hipMalloc(&ptr, need);
-    if (e != hipSuccess) return fail(KVS_ERR_HIP, "hipMalloc(%zu) for decode scratch: %s", need, hipGetErrorString(e));
-    // the decode counters in the scratch must start at zero; kernels leave them zero
-    e = hipMemset(ptr, 0, need);
+    hipError_t e = hipMallocAsync(&ptr, need, stream);
     if (e != hipSuccess) {
-      (void)hipFree(ptr);
-      return fail(KVS_ERR_HIP, "hipMemset of decode scratch: %s", hipGetErrorString(e));
+      (void)hipGetLastError();
+      return fail(KVS_ERR_HIP, "hipMallocAsync(%zu) for decode scratch: %s", need, hipGetErrorString(e));
     }
+    // the decode counters in the scratch must start at zero; kernels leave them zero
+    e = kvs::launch_zero(ptr, need, stream);
+    if (e != hipSuccess) {
+      (void)hipFreeAsync(ptr, stream);
+      return fail(KVS_ERR_HIP, "zeroing the decode scratch: %s", hipGetErrorString(e));
+    }
+    if (slot.first) (void)hipFreeAsync(slot.first, stream);
     slot = {ptr, need};
   }
   *out = slot.first;
@@ -572,7 +578,7 @@ kvs_status attn_varlen_paged(const kvs_tensor* q, const kvs_tensor* k_cache, con
                     false, &plan));
   KVS_TRY(no_fp8(plan));
   void* ws = nullptr;
-  if (plan.ws_bytes) KVS_TRY(get_plain_workspace(plan.ws_bytes, &ws));
+  if (plan.ws_bytes) KVS_TRY(get_plain_workspace(plan.ws_bytes, reinterpret_cast<hipStream_t>(stream), &ws));
   return run_plan(plan, ws, plan.ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -925,9 +931,12 @@ kvs_status kvs_release_workspace(void) {
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_ws_mu);
   if ((size_t)dev < g_ws.size() && g_ws[dev].first) {
+    // the buffer may still be read by work queued on any stream of the device
     if (hipDeviceSynchronize() != hipSuccess) return fail(KVS_ERR_HIP, "hipDeviceSynchronize failed");
-    (void)hipFree(g_ws[dev].first);
+    const hipError_t e = hipFreeAsync(g_ws[dev].first, nullptr);
     g_ws[dev] = {nullptr, 0};
+    if (e != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess)
+      return fail(KVS_ERR_HIP, "freeing the decode scratch failed");
   }
   return KVS_OK;
 }

@@ -1,4 +1,5 @@
-// Device calibration used by the benchmark (not part of the attention path):
+// Device calibration used by the benchmark (libkvstore_calib.so; not part of
+// the attention path):
 // the bf16 MFMA throughput this GPU actually sustains, to set beside the
 // published peak when an attention kernel's MFMA fraction is reported.
 //
@@ -7,7 +8,7 @@
 // its accumulators is stored once so the work cannot be dropped.
 #include <hip/hip_runtime.h>
 
-#include "../../include/kvstore.h"
+#include "../../include/kvstore_calib.h"
 #include "kvs_device.hpp"
 
 namespace kvs {

@@ -175,6 +175,8 @@ enum { kCheckCuFirst = 1, kCheckCuLast = 2, kCheckLq = 3, kCheckLk = 4, kCheckTa
 hipError_t run_check(const CheckParams& v, hipStream_t s, int out[4]);
 
 hipError_t launch_store(const StoreParams& p, DType dt, hipStream_t s);
+// zero `bytes` (a multiple of 16) at p, on stream s
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_rope_store(const RopeParams& p, DType dt, hipStream_t s);
 // i8: INT8 codes (scale absmax / 127), else FP8 E4M3 (absmax / 448)
 hipError_t launch_store_fp8(const StoreFp8Params& p, DType in, int D, bool i8, hipStream_t s);

@@ -41,6 +41,23 @@ hipError_t launch_store(const StoreParams& p, DType, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Zero-fill of a device buffer on a stream (bytes a multiple of 16): the
+// library's own kernel, so that clearing scratch memory is a kernel node when
+// a caller captures the stream into a graph.
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* p, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) st16(p + i, u32x4{0, 0, 0, 0});
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t want = (n16 + 255) / 256;
+  const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, static_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
+
 }  // namespace kvs
 
 // ---- FP8 (E4M3) / INT8 store: quantize each (row, KV head) with its own scale

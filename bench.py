@@ -56,6 +56,8 @@ def _src_sha(name: str) -> str:
 COUNTED = {
     "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false, false, false, false>", "decode.hip"),
     "causal_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", "prefill.hip"),
+    "extend_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", "prefill.hip"),
+    "long_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", "prefill.hip"),
 }
 
 
@@ -131,7 +133,7 @@ class Workload:
 
     def __init__(self, batch, replicas: int, decode_tail: int = 0):
         import torch
-        from tests.gpu_side import to_device
+        from workloads.device import to_device
 
         self.batch = batch
         self.reps = []
@@ -263,7 +265,7 @@ def runner_replays(dec, args):
     import torch
 
     from attention_kv_store_amd.graph_runner import DecodeGraphRunner
-    from tests.gpu_side import to_device
+    from workloads.device import to_device
 
     db = to_device(dec)
     rows = dec.new_token_rows()
@@ -589,8 +591,6 @@ def measure_peaks():
     loop with no memory traffic (kvs_mfma_peak_launch)."""
     import torch
 
-    from attention_kv_store_amd import _lib
-
     def timed(fn, reps):
         fn()
         torch.cuda.synchronize()
@@ -609,7 +609,12 @@ def measure_peaks():
     t_copy = timed(lambda: b.copy_(a), 10)
     copy_gbs = 2 * n / t_copy / 1e9
     del a, b
-    lib = _lib.load()
+    # the calibration kernel lives in its own library (include/kvstore_calib.h)
+    import ctypes
+    calib = ctypes.CDLL(os.path.join(ROOT, "attention_kv_store_amd", "libkvstore_calib.so"))
+    calib.kvs_mfma_peak_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p]
+    calib.kvs_mfma_peak_launch.restype = ctypes.c_int
     src = torch.randn(256, device="cuda").to(torch.bfloat16)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wgs, iters = 8 * cus, 2048
@@ -617,7 +622,9 @@ def measure_peaks():
     stream = torch.cuda.current_stream().cuda_stream
 
     def mfma():
-        _lib.check(lib.kvs_mfma_peak_launch(src.data_ptr(), dst.data_ptr(), wgs, iters, stream))
+        st = calib.kvs_mfma_peak_launch(src.data_ptr(), dst.data_ptr(), wgs, iters, stream)
+        if st != 0:
+            raise RuntimeError(f"kvs_mfma_peak_launch failed with status {st}")
 
     t_mfma = timed(mfma, 5)
     flops = wgs * 4 * 4 * iters * 32768
@@ -643,30 +650,168 @@ def environment():
     return env
 
 
-def cpu_baseline(batch, target_s: float = 10.0):
-    """The oracle, untuned, on the same batch: repeated whole-batch calls until
-    about target_s seconds of host time; K+V bytes / second."""
+def _oracle_pool(batch):
+    """The batch's paged pool as the oracle store builds it (NaN where no row
+    is stored)."""
     import numpy as np
+
+    from oracle import kv_store_oracle
+
+    kc = np.full(batch.pool_shape(), np.nan)
+    vc = np.full(batch.pool_shape(), np.nan)
+    rows = batch.store_rows()
+    return kv_store_oracle(batch.k_tokens[rows].astype(np.float64), batch.v_tokens[rows].astype(np.float64),
+                           batch.slots[rows], kc, vc)
+
+
+def _blas_threads() -> int:
     from threadpoolctl import threadpool_info
 
+    info = threadpool_info()
+    return int(max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1]))
+
+
+def _parity(rows, ref_out, ref_lse, gpu_out, gpu_lse, tol):
+    """max-abs error of the GPU's timed outputs against the oracle on `rows`."""
+    import numpy as np
+
+    eo = float(np.max(np.abs(gpu_out - ref_out[rows])))
+    el = float(np.max(np.abs(gpu_lse - ref_lse[rows])))
+    finite = bool(np.isfinite(gpu_out).all() and np.isfinite(gpu_lse).all())
+    return {"rows": int(len(rows)), "max_abs_out": eo, "max_abs_lse": el, "tol": tol,
+            "ok": bool(finite and eo <= tol and el <= tol)}
+
+
+def cpu_baseline(batch, gpu_out, gpu_lse, target_s: float = 10.0):
+    """The oracle, untuned, on the same batch: repeated whole-batch calls until
+    about target_s seconds of host time; K+V bytes / second.  Its result is
+    also compared with the outputs of the GPU's last timed step."""
+    import numpy as np
+
     from oracle import attention_oracle
-    from tests.oracle_side import oracle_pool
     from workloads import kv_bytes
 
-    kc, vc = oracle_pool(batch)
+    kc, vc = _oracle_pool(batch)
     n, t = 0, 0.0
     while t < target_s:
         t0 = time.perf_counter()
-        attention_oracle(batch.q, kc, vc, batch.block_table, batch.cu_seqlens_q, batch.k_lens,
-                         batch.scale, batch.causal)
+        ro, rl = attention_oracle(batch.q, kc, vc, batch.block_table, batch.cu_seqlens_q, batch.k_lens,
+                                  batch.scale, batch.causal, window=batch.window)
         t += time.perf_counter() - t0
         n += 1
-    info = threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    return {"value": round(kv_bytes(batch) * n / t / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+    cores = _blas_threads()
+    base = {"value": round(kv_bytes(batch) * n / t / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"whole paged_decode_bf16 batch (64 rows, all heads), {n} calls in {t:.1f} s, "
+            "sample": f"whole {batch.name} batch ({batch.T} rows, all heads), {n} calls in {t:.1f} s, "
                       f"numpy float64 with BLAS threads={cores}; {np.__version__}"}
+    rows = np.arange(batch.T)
+    return base, _parity(rows, ro, rl, gpu_out, gpu_lse, 2e-2)
+
+
+def visible_keys(batch, rows):
+    """Keys each query row sees (causal bottom-right, optional window)."""
+    import numpy as np
+
+    seq = np.searchsorted(batch.cu_seqlens_q, rows, side="right") - 1
+    i = rows - batch.cu_seqlens_q[seq]
+    lq, lk = batch.q_lens[seq].astype(np.int64), batch.k_lens[seq].astype(np.int64)
+    if not batch.causal:
+        return lk
+    pos = lk - lq + i
+    vis = np.where(lq > 1, pos + 1, lk)
+    if batch.window:
+        vis = np.minimum(vis, batch.window)
+    return vis
+
+
+def cpu_baseline_prefill(batch, perm, kept, gpu_out, gpu_lse, target_s: float = 8.0):
+    """The oracle, untuned, on a bounded sample of the workload's query rows
+    (a seeded random order of all rows, its first n rows; n grown until one
+    call takes at least target_s / 2 seconds), all heads.
+    Value: the sample's algorithmic FLOPs (4 D per visible key and query head)
+    per second.  The same rows are compared with the GPU's timed outputs
+    (gpu_out / gpu_lse hold the sorted rows `kept`, a superset of the sample)."""
+    import numpy as np
+
+    from oracle import attention_oracle
+
+    kc, vc = _oracle_pool(batch)
+    per_row = 4.0 * batch.D * batch.Hq
+
+    def run(n):
+        rows = np.sort(perm[:n])
+        t0 = time.perf_counter()
+        ro, rl = attention_oracle(batch.q, kc, vc, batch.block_table, batch.cu_seqlens_q, batch.k_lens,
+                                  batch.scale, batch.causal, window=batch.window, rows=rows)
+        return time.perf_counter() - t0, rows, ro, rl
+
+    # grow the sample until one call takes at least half of target_s (the
+    # first calls are dominated by gathering the sequences' K / V)
+    n = min(len(kept), 32)
+    while True:
+        t2, rows, ro, rl = run(n)
+        if t2 >= 0.5 * target_s or n >= len(kept):
+            break
+        n = int(min(len(kept), n * min(8.0, max(2.0, target_s / max(t2, 1e-3)))))
+    fl = per_row * float(visible_keys(batch, rows).sum())
+    cores = _blas_threads()
+    base = {"value": round(fl / t2 / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of the {batch.T} query rows of {batch.name} (seeded random choice), all "
+                      f"{batch.Hq} heads, {fl / 1e9:.1f} GFLOP in {t2:.1f} s, numpy float64 with BLAS "
+                      f"threads={cores}; {np.__version__}"}
+    pos = np.searchsorted(kept, rows)
+    return base, _parity(rows, ro, rl, gpu_out[pos], gpu_lse[pos], 2e-2)
+
+
+# the prefill configurations measured: workload, device replicas rotated so
+# that the working set exceeds the 256 MB Infinity Cache, most timed steps
+PREFILL_CONFIGS = (
+    ("causal_prefill_bf16", 4, 500),
+    ("extend_prefill_bf16", 2, 500),
+    ("long_prefill_bf16", 1, 50),
+)
+PARITY_ROWS = 4096   # GPU output rows kept for the parity check (a seeded random order)
+
+
+def prefill_line(name, replicas, cap, args):
+    """One prefill configuration: each step stores the batch's new K/V rows
+    (kv_store_paged) and runs attn_varlen_paged; the attention launch alone
+    gives roofline.achieved.  Returns the line's entry and the GPU's timed
+    outputs on PARITY_ROWS seeded rows (for the CPU leg's parity check)."""
+    import numpy as np
+    import torch
+
+    import attention_kv_store_amd as kvs
+    from workloads import NAMED, attention_flops, io_bytes
+
+    b = NAMED[name]()
+    w = Workload(b, replicas)
+    steps = min(cap, max(1, args.steps // 4))
+    warm = max(1, min(cap, args.warmup // 4))
+    pms, pattn, _, pstats = time_steps(w, steps, warm, eager=args.eager)
+    disp = kvs.last_dispatch()
+    fl = attention_flops(b)
+    tf = fl / (pattn * 1e-3) / 1e12
+    log(f"{name}: {pms*1e3:.2f} us/step, attention {pattn*1e3:.2f} us -> {tf:.1f} TFLOP/s ({disp})")
+    entry = {
+        "workload": name, "query_rows": b.T, "sequences": b.B, "metric": "attention TFLOP/s",
+        "unit": "TFLOP/s", "ms_per_step": round(pms, 6), "steps": steps, "replicas": replicas,
+        "dispatch": disp, "replay_stats": pstats,
+        "roofline": {
+            "bound": "mfma", "kernel": COUNTED[name][0], "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": _traffic(COUNTED[name][1], name),
+            "flops_per_launch": fl, "avg_launch_us": round(pattn * 1e3, 3), "io_bytes_per_launch": io_bytes(b),
+        },
+    }
+    perm = np.random.default_rng(1234).permutation(b.T)
+    keep = np.sort(perm[:PARITY_ROWS])
+    idx = torch.from_numpy(keep).cuda()
+    _, _, _, _, out, lse = w.reps[0]
+    gout = out.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    glse = lse.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    del w
+    torch.cuda.empty_cache()
+    return entry, (b, perm, keep, gout, glse)
 
 
 def main():
@@ -699,9 +844,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     import attention_kv_store_amd as kvs
-    from workloads import attention_flops, causal_prefill_bf16, io_bytes, kv_bytes, paged_decode_bf16
+    from workloads import attention_flops, io_bytes, kv_bytes, paged_decode_bf16
 
     dec = paged_decode_bf16()
+    prefill_outputs = {}
     log(f"decode batch: B={dec.B} sum(Lk)={int(dec.k_lens.sum())} K+V={kv_bytes(dec)/1e6:.1f} MB")
     w = Workload(dec, args.replicas)
     kvb = kv_bytes(dec)
@@ -721,6 +867,9 @@ def main():
     achieved = kvb / (attn_ms * 1e-3) / 1e9
     log(f"decode, fused: {ms*1e3:.2f} us/step, launch {attn_ms*1e3:.2f} us -> {achieved:.0f} GB/s ({dispatch})")
     traffic = _traffic("decode.hip", "paged_decode_bf16")
+    # the outputs of the last timed step (every replica computes the same)
+    dec_out = w.reps[0][4].float().cpu().numpy().astype("float64")
+    dec_lse = w.reps[0][5].cpu().numpy().astype("float64")
     line = {
         "metric": "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
         "value": round(value, 2),
@@ -784,26 +933,13 @@ def main():
         log(f"graph runner: {line['graph_runner']}")
 
     if not args.no_prefill:
-        pre = causal_prefill_bf16()
-        wp = Workload(pre, args.replicas)
-        psteps = max(1, args.steps // 4)
-        pms, pattn, _, pstats = time_steps(wp, psteps, max(1, args.warmup // 4), eager=args.eager)
-        pdisp = kvs.last_dispatch()
-        fl = attention_flops(pre)
-        tf = fl / (pattn * 1e-3) / 1e12
-        log(f"prefill: {pms*1e3:.2f} us/step, attention {pattn*1e3:.2f} us -> {tf:.1f} TFLOP/s ({pdisp})")
-        line["prefill"] = {
-            "workload": "causal_prefill_bf16",
-            "metric": "attention TFLOP/s", "unit": "TFLOP/s", "bound": "mfma",
-            "kernel": COUNTED["causal_prefill_bf16"][0],
-            "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-            "flops_per_launch": fl, "avg_launch_us": round(pattn * 1e3, 3),
-            "ms_per_step": round(pms, 6), "steps": psteps,
-            "traffic": _traffic("prefill.hip", "causal_prefill_bf16"),
-            "dispatch": pdisp, "replay_stats": pstats,
-        }
-        del wp
-        torch.cuda.empty_cache()
+        # causal prefill (16 x 512), extend over a cached prefix (8 sequences),
+        # one 32768-token prompt
+        line["prefill"] = {}
+        for name, reps, cap in PREFILL_CONFIGS:
+            entry, keep = prefill_line(name, reps, cap, args)
+            line["prefill"][name] = entry
+            prefill_outputs[name] = keep
 
     if not args.no_prefill and not args.no_extras:
         # a mixed serving step in one launch: 2 prompts x 256 new tokens and 30
@@ -890,14 +1026,22 @@ def main():
         peaks = measure_peaks()
         line["measured_peaks"] = peaks
         line["roofline"]["frac_of_measured_copy"] = round(achieved / peaks["copy_GBs"], 4)
-        if "prefill" in line:
-            line["prefill"]["frac_of_measured_mfma"] = round(line["prefill"]["achieved"] / peaks["bf16_mfma_TFLOPs"], 4)
+        for entry in line.get("prefill", {}).values():
+            entry["roofline"]["frac_of_measured_mfma"] = round(entry["roofline"]["achieved"] / peaks["bf16_mfma_TFLOPs"], 4)
         log(f"measured peaks: {peaks}")
     line["env"] = environment()
 
     if not args.no_cpu_baseline:
+        # the oracle on the host cores (rank 0, one GPU), on the same inputs;
+        # the rows it computes also check the GPU's timed outputs
         log("timing the CPU oracle ...")
-        line["cpu_baseline"] = cpu_baseline(dec)
+        line["cpu_baseline"], line["parity"] = cpu_baseline(dec, dec_out, dec_lse)
+        log(f"decode: cpu {line['cpu_baseline']['value']} GB/s, parity {line['parity']}")
+        for name, (b, perm, kept, gout, glse) in prefill_outputs.items():
+            base, par = cpu_baseline_prefill(b, perm, kept, gout, glse)
+            line["prefill"][name]["cpu_baseline"] = base
+            line["prefill"][name]["parity"] = par
+            log(f"{name}: cpu {base['value']} TFLOP/s ({base['sample']}), parity {par}")
     print(json.dumps(line), flush=True)
 
 

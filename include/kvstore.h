@@ -16,8 +16,10 @@
  *  - Every data pointer is a DEVICE pointer on the current HIP device, owned by
  *    the caller, except where a comment says "host".
  *  - Calls are asynchronous on `stream`: they validate on the host, enqueue
- *    kernels, and return.  No call synchronises the device or reads device
- *    memory from the host.
+ *    kernels (and, for the plain attn_varlen_paged, stream-ordered allocations
+ *    on `stream`), and return.  No call reads device memory from the host, and
+ *    none synchronises the device except kvs_release_workspace (a teardown
+ *    call) and the calls of the debug library below.
  *  - The paged pool (k_cache, v_cache) is [num_blocks, 16, Hkv, D]: token row
  *    `r` of physical block `p` holds the K (or V) vectors of all Hkv heads.  A
  *    slot number names one token row: slot = p * 16 + r.  Page size 16 follows
@@ -173,11 +175,17 @@ kvs_status kv_store_rope_paged(kvs_tensor* q, const kvs_tensor* k_new, const kvs
  * Dispatch uses shapes only: T == B (one new row per sequence) takes the decode
  * path; otherwise the prefill/extend path.  The decode path cuts the batch's
  * key blocks into equal ranges (split-KV, "Transformer 추론 커널 (3/10)", §16)
- * and needs scratch memory for the pieces of split sequences: this call keeps
- * one grow-only, zero-initialised device buffer per device for it (allocated
- * on first need; kvs_release_workspace frees it).  Calls on one device that
- * overlap in time (different streams) share that buffer and must not overlap;
- * use attn_varlen_paged_ex with separate workspaces for that.
+ * and needs scratch memory for the pieces of split sequences (§16: partial
+ * results of the pieces, merged afterwards): this call keeps one grow-only
+ * device buffer per device for it.  When a call needs more than the buffer
+ * holds, a new one is allocated stream-ordered on `stream` (hipMallocAsync),
+ * zeroed there by the library's own kernel, and the old one freed
+ * stream-ordered on `stream`; nothing synchronises the device.
+ * kvs_release_workspace frees it.  Calls on one device that overlap in time
+ * (different streams with no ordering between them) share that buffer and are
+ * not allowed; use attn_varlen_paged_ex with separate workspaces for that.  A
+ * call that grows the buffer while its stream is captured into a graph
+ * records the allocation in the graph: capture _ex calls instead.
  */
 kvs_status attn_varlen_paged(const kvs_tensor* q,
                              const kvs_tensor* k_cache, const kvs_tensor* v_cache,
@@ -188,7 +196,11 @@ kvs_status attn_varlen_paged(const kvs_tensor* q,
                              kvs_tensor* out, kvs_tensor* lse,
                              kvs_stream_t stream);
 
-/* Optional host-side hints for attn_varlen_paged_ex; 0 means "unknown / choose". */
+/* Optional host-side hints for attn_varlen_paged_ex; 0 means "unknown / choose".
+ * The kernel-facing bookkeeping of "장부가 커널 인자로 바뀌는 지점과 CUDA graph"
+ * ("장부에서 텐서로") carries host-side max_seqlen_q / max_seqlen_k next to the
+ * device tensors; num_splits is the split-KV degree of "Transformer 추론 커널
+ * (3/10)", §16; decode_tail states the phase order of a mixed batch (§6). */
 typedef struct {
   int32_t max_seqlen_q;  /* upper bound on Lq_b (host value), 0 = unknown; unused now  */
   int32_t max_seqlen_k;  /* upper bound on Lk_b (host value), 0 = unknown; unused now  */
@@ -210,14 +222,18 @@ typedef struct {
 } kvs_hints;
 
 /* Bytes of device scratch attn_varlen_paged_ex needs for these shapes and hints
- * (0 when the chosen path needs none).  Returns (size_t)-1 on invalid shapes. */
+ * (0 when the chosen path needs none): the partial results and merge counters
+ * of a split decode ("Transformer 추론 커널 (3/10)", §16: more pieces mean more
+ * parallelism but a partial buffer and a reduction).  `hints` (may be NULL)
+ * must be the ones the call will get.  Returns (size_t)-1 on invalid shapes. */
 size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k_cache,
                                         const kvs_tensor* block_table,
                                         const kvs_hints* hints);
 
 /*
  * attn_varlen_paged_ex -- attn_varlen_paged with caller-owned scratch and hints.
- * Same computation and argument meaning.  `workspace` is a device buffer of at
+ * Same computation and argument meaning; the scratch holds the split-KV pieces
+ * of "Transformer 추론 커널 (3/10)", §16.  `workspace` is a device buffer of at
  * least attn_varlen_paged_workspace_size(q, k_cache, block_table, hints) bytes,
  * 256-byte aligned (may be NULL when that size is 0).  It must be zero-filled
  * before its first use with this library.  Its first 4 MiB hold the split
@@ -306,7 +322,8 @@ kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q,
 
 /*
  * attn_decode_append_paged_window -- attn_decode_append_paged with the
- * sliding window of attn_varlen_paged_window_ex: sequence b's query row sees
+ * sliding window of attn_varlen_paged_window_ex (the mask variant of
+ * "Transformer 추론 커널 (3/10)", §19 and §24): sequence b's query row sees
  * keys max(0, Lk_b - W) .. Lk_b - 1, the new one included.  Same result as
  * kv_store_paged then attn_varlen_paged_window_ex with cu_seqlens_q = 0..B.
  * W >= 1, else KVS_ERR_INVALID.  Table entries below block
@@ -339,7 +356,8 @@ kvs_status attn_decode_append_paged_window(const kvs_tensor* q,
 
 /*
  * kv_store_paged_fp8 -- quantize new K/V token rows and write them into their
- * slots: for each row t and KV head h, s = absmax_d |x[t, h, d]| / 448 (0 for an
+ * slots (the KV-cache store of "Transformer 추론 커널 (3/10)", §2, into the FP8
+ * layout of §19; the scale layout follows §7): for each row t and KV head h, s = absmax_d |x[t, h, d]| / 448 (0 for an
  * all-zero row) and code[d] = the E4M3 value nearest to x / s (ties to even,
  * saturated at +-448), both divisions in fp32, correctly rounded.
  *
@@ -356,8 +374,8 @@ kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new,
                               kvs_stream_t stream);
 
 /*
- * attn_varlen_paged_fp8_ex -- attn_varlen_paged_ex over an FP8 cache: the
- * same attention with K and V the dequantized values E4M3(code) * scale.
+ * attn_varlen_paged_fp8_ex -- attn_varlen_paged_ex over an FP8 cache (the FP8 KV
+ * dispatch axis of "Transformer 추론 커널 (3/10)", §19): the same attention with K and V the dequantized values E4M3(code) * scale.
  * q, out are bf16.  `window` > 0 selects the sliding window of
  * attn_varlen_paged_window_ex (and needs causal); 0 = none.  Same paths
  * (decode and prefill / extend), shapes, limits and workspace rules as
@@ -377,7 +395,8 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q,
 
 /*
  * attn_decode_append_paged_fp8 -- the fused decode step of
- * attn_decode_append_paged over an FP8 cache: sequence b's new K/V rows
+ * attn_decode_append_paged over an FP8 cache ("Transformer 추론 커널 (3/10)",
+ * §2 store then attention, §19 FP8 KV): sequence b's new K/V rows
  * (bf16, [B, Hkv, D]) are quantized as kv_store_paged_fp8 quantizes them
  * (codes and scales bit for bit the same) and written to the slot of key
  * Lk_b - 1, and the query row attends over the dequantized keys, the new one
@@ -412,7 +431,8 @@ kvs_status attn_decode_append_paged_fp8(const kvs_tensor* q,
  */
 
 /*
- * kv_store_paged_int8 -- kv_store_paged_fp8 with INT8 codes: s = absmax / 127
+ * kv_store_paged_int8 -- kv_store_paged_fp8 with INT8 codes ("Transformer 추론
+ * 커널 (3/10)", §19: INT8 KV next to FP8): s = absmax / 127
  * (0 for an all-zero row) and code[d] = the integer nearest to x / s (ties to
  * even), clamped to +-127, both divisions in fp32, correctly rounded.  Same
  * arguments, shapes, limits and error behaviour as kv_store_paged_fp8.
@@ -424,7 +444,8 @@ kvs_status kv_store_paged_int8(const kvs_tensor* k_new, const kvs_tensor* v_new,
                                kvs_stream_t stream);
 
 /*
- * attn_varlen_paged_int8_ex -- attn_varlen_paged_fp8_ex over an INT8 cache:
+ * attn_varlen_paged_int8_ex -- attn_varlen_paged_fp8_ex over an INT8 cache
+ * ("Transformer 추론 커널 (3/10)", §19):
  * K and V are the dequantized values code * scale.  Same arguments, paths,
  * shapes, limits and workspace rules.  Allocates nothing.
  */
@@ -442,7 +463,7 @@ kvs_status attn_varlen_paged_int8_ex(const kvs_tensor* q,
 
 /*
  * attn_decode_append_paged_int8 -- attn_decode_append_paged_fp8 over an INT8
- * cache: the new rows are quantized as kv_store_paged_int8 quantizes them
+ * cache ("Transformer 추론 커널 (3/10)", §2 and §19): the new rows are quantized as kv_store_paged_int8 quantizes them
  * (codes and scales bit for bit the same) and attended with the rest.
  * Result: kv_store_paged_int8 then attn_varlen_paged_int8_ex with
  * cu_seqlens_q = 0..B.  Same arguments and limits.  Allocates nothing.
@@ -489,29 +510,23 @@ kvs_status attn_decode_append_paged_rope(const kvs_tensor* q,
                                          void* workspace, size_t workspace_bytes,
                                          kvs_stream_t stream);
 
-/* Text of the calling thread's last non-OK status ("" if none).  The pointer is
- * valid until that thread's next library call. */
+/* Text of the calling thread's last non-OK status ("" if none): the reason an
+ * unsupported or invalid call was refused ("Transformer 추론 커널 (3/10)", §20:
+ * a fallback's reason is something to record).  The pointer is valid until
+ * that thread's next library call. */
 const char* kvs_last_error(void);
 
 /* Text naming the kernel variant, grid and split plan of the calling thread's
- * last successful enqueue (so a caller can log which path ran). */
+ * last successful enqueue, so a caller can log which path ran ("Transformer 추론
+ * 커널 (3/10)", §20: the selected kernel's name is a metric to record). */
 const char* kvs_last_dispatch(void);
 
-/* Frees the grow-only scratch buffer that attn_varlen_paged keeps on the current
- * device.  Synchronises the device first (the buffer may be in use). */
+/* Frees the grow-only scratch buffer (the split-KV partials of "Transformer 추론
+ * 커널 (3/10)", §16) that attn_varlen_paged keeps on the current device.  A
+ * teardown call: it synchronises the device first, since work queued on any
+ * stream may still read the buffer.  Returns KVS_ERR_HIP if a HIP call fails. */
 kvs_status kvs_release_workspace(void);
 
-/*
- * kvs_mfma_peak_launch -- device calibration for the benchmark, not part of
- * the attention path: enqueues `workgroups` workgroups of 4 waves, each wave
- * running 4 independent chains of `iters` 32x32x16 bf16 MFMAs (32768 FLOP
- * each) with no memory traffic in the loop; a caller times it with events to
- * get the bf16 MFMA rate this GPU sustains (FLOP = workgroups * 4 * 4 * iters
- * * 32768).  `src`: 512 readable bytes, 16-byte aligned (operand data);
- * `dst`: workgroups * 256 floats written.  KVS_ERR_INVALID on a bad argument
- * (kvs_last_error is not set), KVS_ERR_HIP if the launch fails.
- */
-kvs_status kvs_mfma_peak_launch(const void* src, void* dst, int workgroups, int iters, kvs_stream_t stream);
 
 #ifdef __cplusplus
 }

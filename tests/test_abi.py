@@ -517,3 +517,86 @@ def test_fused_rope_validation(lib, dtype, D, kw, expect, msg):
         rope.base, rope.pos_scale = kw.get("base", 10000.0), 1.0
     assert _call_append_rope(lib, a, rope) == expect
     assert msg in lib.kvs_last_error().decode()
+
+
+# ---------------------------------------------------------------- header ----
+def _declarations(path):
+    """(name, comment block right above it) of every function the header declares."""
+    text = open(path).read()
+    out = []
+    for m in re.finditer(r"^\s*(?:kvs_status|size_t|const char\*)\s+(\w+)\s*\(", text, re.M):
+        head = text[:m.start()]
+        end = head.rfind("*/")
+        start = head.rfind("/*", 0, end)
+        between = head[end + 2:]
+        # the comment must belong to this declaration: only blank lines or an
+        # earlier declaration's closing text may not sit between them
+        assert end >= 0 and ";" not in between, m.group(1)
+        out.append((m.group(1), head[start:end]))
+    return out
+
+
+def test_every_declaration_cites_its_passage():
+    """Each entry point's comment names the passage of the pages that defines
+    the operation (a section sign, or one of the page titles)."""
+    cites = ("§", "tiny-vLLM", "장부가 커널 인자로", "장부에서 텐서로")
+    for hdr in (HDR, os.path.join(os.path.dirname(HDR), "kvstore_calib.h")):
+        for name, comment in _declarations(hdr):
+            assert any(c in comment for c in cites), f"{name} cites no passage"
+
+
+def test_calibration_kernel_lives_outside_the_product_library(lib):
+    """The benchmark's MFMA calibration kernel is exported by its own library,
+    not by libkvstore.so."""
+    assert not hasattr(lib, "kvs_mfma_peak_launch")
+    path = os.path.join(os.path.dirname(L.LIB_PATH), "libkvstore_calib.so")
+    if not os.path.exists(path):
+        pytest.skip("calibration library not built")
+    calib = ctypes.CDLL(path)
+    assert hasattr(calib, "kvs_mfma_peak_launch")
+    calib.kvs_mfma_peak_launch.restype = ctypes.c_int
+    calib.kvs_mfma_peak_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p]
+    # refused on the host (unaligned source), nothing launched
+    assert calib.kvs_mfma_peak_launch(FAKE + 4, FAKE, 1, 1, None) == L.KVS_ERR_INVALID
+
+
+# ------------------------------------------------- host sanitizer build ----
+def test_abi_host_code_under_address_and_ub_sanitizers(tmp_path):
+    """The C-ABI code (validation, planning, workspace handling) built for the
+    host with AddressSanitizer and UndefinedBehaviorSanitizer, linked with
+    host stand-ins for the kernels and the HIP runtime (tests/abi_sanitize),
+    and driven through every entry point with valid and malformed
+    descriptors.  Any memory error, undefined behaviour or unexpected status
+    fails the test."""
+    import shutil
+    import subprocess
+
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    clang = "/opt/rocm/llvm/bin/clang++"
+    if not (os.path.exists(hipcc) and os.path.exists(clang)):
+        pytest.skip("ROCm toolchain not found")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    inc = os.path.join(root, "include")
+    here = os.path.join(root, "tests", "abi_sanitize")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+    host_san = [x for f in san for x in ("-Xarch_host", f)]
+    steps = [
+        [hipcc, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", *host_san,
+         "-Wno-unused-command-line-argument", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         f"-I{inc}", "-c", os.path.join(root, "attention_kv_store_amd", "csrc", "api.hip"),
+         "-o", str(tmp_path / "api.o")],
+        [clang, "-O1", "-g", "-std=c++17", *san, "-D__HIP_PLATFORM_AMD__", f"-I{inc}", "-I/opt/rocm/include",
+         "-c", os.path.join(here, "stubs.cpp"), "-o", str(tmp_path / "stubs.o")],
+        [clang, "-O1", "-g", "-std=c++17", *san, f"-I{inc}", "-c", os.path.join(here, "driver.cpp"),
+         "-o", str(tmp_path / "driver.o")],
+        [clang, *san, str(tmp_path / "api.o"), str(tmp_path / "stubs.o"), str(tmp_path / "driver.o"),
+         "-o", str(tmp_path / "driver")],
+    ]
+    for cmd in steps:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        assert r.returncode == 0, r.stderr[-4000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([str(tmp_path / "driver")], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
+    assert "abi sanitize driver: OK" in r.stdout

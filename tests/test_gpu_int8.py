@@ -187,12 +187,11 @@ def test_int8_prefill_window(W):
 @pytest.mark.parametrize("name", ["causal_prefill_bf16", "mixed_prefill_decode_bf16"])
 def test_int8_named_prefill_workloads(name):
     """The 16 x 512 causal prefill and the mixed 2 x 256 + 30 x 1 batch over an
-    INT8 cache, on sampled rows."""
-    from tests.test_gpu_parity import _sample_rows
+    INT8 cache, every row."""
     from workloads import NAMED
     b = NAMED[name]()
     dev, host = _int8_batch_pools(b)
-    _check_int8_attention(b, dev, host, rows=_sample_rows(b))
+    _check_int8_attention(b, dev, host)
 
 
 @pytest.mark.parametrize("D", [64, 128])

@@ -589,32 +589,36 @@ def test_poison_never_reaches_output():
 
 
 # ------------------------------------------------------ named workloads --
-def _sample_rows(batch, per_seq=4, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = []
-    for s in range(batch.B):
-        r0, r1 = int(batch.cu_seqlens_q[s]), int(batch.cu_seqlens_q[s + 1])
-        rows += [r0, r1 - 1]
-        if r1 - r0 > 2:
-            rows += list(rng.integers(r0, r1, size=min(per_seq, r1 - r0 - 2)))
-    return sorted(set(int(r) for r in rows))
-
-
 @pytest.mark.parametrize("name", ["paged_decode_bf16", "causal_prefill_bf16", "extend_prefill_bf16",
                                   "mixed_prefill_decode_bf16"])
-def test_named_workload_sampled(name):
+def test_named_workload_all_rows(name):
+    """The named workloads at their full sizes, in the launch configuration the
+    benchmark times: every output row and lse of every head against the
+    oracle (so every (sequence, token tile, head group) item of the persistent
+    grid, in its full-size order, is compared)."""
     from workloads import NAMED
     b = NAMED[name]()
     out, lse = _run(b)
-    rows = None if name == "paged_decode_bf16" else _sample_rows(b)
-    _check(b, out, lse, rows=rows)
+    _check(b, out, lse)
 
 
-def test_long_prefill_sampled():
+def long_prefill_check_rows(T, tile=64, edge=2048):
+    """Rows of a T-row prompt compared in full: the first and last row of every
+    `tile`-row token tile, and every row of the first and last `edge`."""
+    rows = set(range(min(edge, T))) | set(range(max(0, T - edge), T))
+    for t0 in range(0, T, tile):
+        rows |= {t0, min(T, t0 + tile) - 1}
+    return sorted(rows)
+
+
+def test_long_prefill_tile_rows():
+    """The 32768-token prompt: the first and last row of each of its 512
+    token tiles (all heads), plus every row of its first and last 2048."""
     from workloads import long_prefill_bf16
     b = long_prefill_bf16()
     out, lse = _run(b)
-    rows = [0, 1, 15, 16, 17, 1000, 4095, 4096, 16383, 20000, 32766, 32767]
+    rows = long_prefill_check_rows(b.T)
+    assert len(rows) == 4992   # 2 x 2048 + 2 rows of each of the 448 tiles in between
     _check(b, out, lse, rows=rows)
 
 
@@ -670,7 +674,7 @@ def test_decode_tail_mixed_named_workload():
     from workloads import mixed_prefill_decode_bf16
     b = mixed_prefill_decode_bf16()
     out, lse = run_attention(to_device(b), decode_tail=30)
-    _check(b, out, lse, rows=_sample_rows(b))
+    _check(b, out, lse)
 
 
 # ------------------------------------------------------------ maximum sizes --

@@ -17,7 +17,7 @@ torch = pytest.importorskip("torch")
 
 pytestmark = pytest.mark.gpu
 
-from tests.test_gpu_parity import _check, _mk, _pool_matches_oracle, _sample_rows  # noqa: E402
+from tests.test_gpu_parity import _check, _mk, _pool_matches_oracle  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -142,8 +142,4 @@ def test_window_named_workload(name):
     from workloads import NAMED
     b = NAMED[name]()
     out, lse = _run(b)
-    rows = None if b.T == b.B else _sample_rows(b)
-    if rows is not None:
-        L = int(b.q_lens[0])
-        rows = sorted(set(rows) | {0, 1, b.window - 1, b.window, b.window + 1, L - 1, L, 2 * L + b.window})
-    _check(b, out, lse, rows=rows)
+    _check(b, out, lse)   # every row
