@@ -303,5 +303,16 @@ def attn_varlen_paged_plain(q, k_cache, v_cache, block_table, cu_seqlens_q, seql
     _lib.check(st)
 
 
+def attn_varlen_paged_noalloc(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale: float,
+                              causal: bool, out, lse=None) -> None:
+    """``attn_varlen_paged_noalloc``: the plain call with the library's static
+    scratch (nothing allocated; shapes needing more scratch are refused)."""
+    lib = _lib.load()
+    d = [_desc(x) for x in (q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k)]
+    st = lib.attn_varlen_paged_noalloc(*[_ref(x) for x in d], ctypes.c_float(scale), int(bool(causal)),
+                                       _ref(_desc(out)), _ref(_desc(lse)), _stream(q))
+    _lib.check(st)
+
+
 def release_workspace() -> None:
     _lib.check(_lib.load().kvs_release_workspace())

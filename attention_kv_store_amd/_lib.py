@@ -27,6 +27,7 @@ EXPORTS = (
     "kv_store_paged_fp8",
     "attn_varlen_paged_fp8_ex",
     "attn_varlen_paged",
+    "attn_varlen_paged_noalloc",
     "attn_varlen_paged_workspace_size",
     "attn_varlen_paged_ex",
     "attn_decode_append_paged",
@@ -110,6 +111,8 @@ def load(path: str = None):
     lib.attn_varlen_paged_fp8_ex.restype = st
     lib.attn_varlen_paged.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, vp]
     lib.attn_varlen_paged.restype = st
+    lib.attn_varlen_paged_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, vp]
+    lib.attn_varlen_paged_noalloc.restype = st
     lib.attn_varlen_paged_workspace_size.argtypes = [P, P, P, ctypes.POINTER(KvsHints)]
     lib.attn_varlen_paged_workspace_size.restype = ctypes.c_size_t
     lib.attn_varlen_paged_ex.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P,

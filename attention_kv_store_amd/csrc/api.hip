@@ -17,26 +17,29 @@
 
 namespace {
 
-thread_local std::string g_err;
-thread_local std::string g_dispatch;
+// The calling thread's last error and dispatch texts: fixed buffers, so no
+// call allocates host memory for them either.
+constexpr size_t kTextBytes = 512;
+thread_local char g_err[kTextBytes];
+thread_local char g_dispatch[kTextBytes];
+
+void clear_error() { g_err[0] = 0; }
 
 kvs_status fail(kvs_status st, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_err, kTextBytes, fmt, ap);
   va_end(ap);
-  g_err = buf;
   return st;
 }
 
 void set_dispatch(const char* fmt, ...) {
-  char buf[512];
+  char buf[kTextBytes];   // the arguments may be g_dispatch itself
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_dispatch = buf;
+  memcpy(g_dispatch, buf, sizeof buf);
 }
 
 const char* dtname(int dt) {
@@ -264,14 +267,15 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
 }
 
 // ---- compute units of the current device (cached per device) ---------------
+constexpr int kMaxDevices = 64;
 std::mutex g_cu_mu;
-std::vector<int> g_cus;
+int g_cus[kMaxDevices];
 
 kvs_status device_cus(int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVS_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
   std::lock_guard<std::mutex> lk(g_cu_mu);
-  if ((size_t)dev >= g_cus.size()) g_cus.resize(dev + 1, 0);
   if (g_cus[dev] == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
@@ -279,6 +283,35 @@ kvs_status device_cus(int* out) {
     g_cus[dev] = n;
   }
   *out = g_cus[dev];
+  return KVS_OK;
+}
+
+// ---- scratch of the no-allocation call (attn_varlen_paged_noalloc) --------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is a stand-in, not a device address): it uses the
+// address hipGetSymbolAddress returns with that device current, kept per
+// device.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scr_mu;
+void* g_scr[kMaxDevices];
+
+kvs_status noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVS_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scr_mu);
+  if (!g_scr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(KVS_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    }
+    g_scr[dev] = ptr;
+  }
+  *out = g_scr[dev];
   return KVS_OK;
 }
 
@@ -323,8 +356,12 @@ kvs_status no_fp8(const Plan& plan) {
   return KVS_OK;
 }
 
-std::string window_note(const kvs::AttnParams& p) {
-  return p.window > 0 ? " sliding_window=" + std::to_string(p.window) : std::string();
+// " sliding_window=W" or "", in a small per-thread buffer
+const char* window_note(const kvs::AttnParams& p) {
+  thread_local char note[32];
+  if (p.window > 0) snprintf(note, sizeof note, " sliding_window=%d", p.window);
+  else note[0] = 0;
+  return note;
 }
 
 #ifdef KVS_DEBUG
@@ -380,7 +417,7 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     set_dispatch("decode_%s%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s", plan.dt == kvs::DType::BF16 ? "bf16" : "f32",
                  p.kv8 ? (p.kv8 == 2 ? "_kv_int8" : "_kv_fp8") : "", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window",
-                 window_note(p).c_str());
+                 window_note(p));
     return KVS_OK;
   }
   int cus = 0;
@@ -390,7 +427,7 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (e != hipSuccess) return fail(KVS_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   set_dispatch("prefill_%s%s_d%d grid=%d (persistent) waves/wg=%d head groups=%d heads/wg=%d tokens/item=%d meta_lds=%d%s",
                plan.dt == kvs::DType::BF16 ? "bf16" : "f32", p.kv8 ? (p.kv8 == 2 ? "_kv_int8" : "_kv_fp8") : "", plan.D, p.pgrid, p.pnw, p.NHG,
-               p.HW, 32 * p.TPW, p.meta_lds, window_note(p).c_str());
+               p.HW, 32 * p.TPW, p.meta_lds, window_note(p));
   return KVS_OK;
 }
 
@@ -400,7 +437,7 @@ extern "C" {
 
 kvs_status kv_store_paged(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
                           kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   KVS_TRY(check_tensor(k_cache, "k_cache", kFloatTypes, 4));
   KVS_TRY(check_tensor(v_cache, "v_cache", kFloatTypes, 4));
   KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3, true));
@@ -493,21 +530,21 @@ static kvs_status store_q8(const kvs_tensor* k_new, const kvs_tensor* v_new, con
 kvs_status kv_store_paged_fp8(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
                               kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale, kvs_tensor* v_scale,
                               kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   return store_q8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream, KVS_FP8_E4M3);
 }
 
 kvs_status kv_store_paged_int8(const kvs_tensor* k_new, const kvs_tensor* v_new, const kvs_tensor* slot_mapping,
                                kvs_tensor* k_cache, kvs_tensor* v_cache, kvs_tensor* k_scale, kvs_tensor* v_scale,
                                kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   return store_q8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream, KVS_INT8);
 }
 
 kvs_status kv_store_rope_paged(kvs_tensor* q, const kvs_tensor* k_new, const kvs_tensor* v_new,
                                const kvs_tensor* positions, const kvs_tensor* slot_mapping, kvs_tensor* k_cache,
                                kvs_tensor* v_cache, const kvs_rope* rope, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   KVS_TRY(check_tensor(k_cache, "k_cache", kFloatTypes, 4));
   KVS_TRY(check_tensor(v_cache, "v_cache", kFloatTypes, 4));
   KVS_TRY(check_tensor(k_new, "k_new", kFloatTypes, 3, true));
@@ -572,7 +609,7 @@ kvs_status attn_varlen_paged(const kvs_tensor* q, const kvs_tensor* k_cache, con
                              const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
                              const kvs_tensor* seqlens_k, float scale, int causal, kvs_tensor* out,
                              kvs_tensor* lse, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   Plan plan;
   KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, nullptr,
                     false, &plan));
@@ -580,6 +617,32 @@ kvs_status attn_varlen_paged(const kvs_tensor* q, const kvs_tensor* k_cache, con
   void* ws = nullptr;
   if (plan.ws_bytes) KVS_TRY(get_plain_workspace(plan.ws_bytes, reinterpret_cast<hipStream_t>(stream), &ws));
   return run_plan(plan, ws, plan.ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+kvs_status attn_varlen_paged_noalloc(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                     const kvs_tensor* block_table, const kvs_tensor* cu_seqlens_q,
+                                     const kvs_tensor* seqlens_k, float scale, int causal, kvs_tensor* out,
+                                     kvs_tensor* lse, kvs_stream_t stream) {
+  clear_error();
+  Plan plan;
+  KVS_TRY(make_plan(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, causal, out, lse, nullptr,
+                    false, &plan));
+  KVS_TRY(no_fp8(plan));
+  void* ws = nullptr;
+  if (plan.ws_bytes) {
+    if (plan.ws_bytes > kNoAllocScratchBytes)
+      return fail(KVS_ERR_WORKSPACE,
+                  "these shapes need %zu bytes of decode scratch; the no-allocation call's static scratch holds %zu "
+                  "(use attn_varlen_paged_ex with a caller workspace)",
+                  plan.ws_bytes, kNoAllocScratchBytes);
+    KVS_TRY(noalloc_scratch(&ws));
+    // the merge counters this call uses (index b * Hkv + g) must start at
+    // zero: clear them on the stream with the library's own kernel
+    const size_t cbytes = align_up((size_t)plan.p.B * plan.p.Hkv * sizeof(int32_t), 16);
+    const hipError_t e = kvs::launch_zero(ws, cbytes, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVS_ERR_HIP, "clearing the static scratch's counters: %s", hipGetErrorString(e));
+  }
+  return run_plan(plan, ws, kNoAllocScratchBytes, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
@@ -661,7 +724,7 @@ kvs_status decode_append(const kvs_tensor* q, const kvs_tensor* k_new, const kvs
   KVS_TRY(run_plan(plan, workspace, workspace_bytes, reinterpret_cast<hipStream_t>(stream)));
   set_dispatch("decode_append_%s%s_d%d grid=(%d,%d) waves/wg=%d ranges=%d table=%s%s%s",
                plan.dt == kvs::DType::BF16 ? "bf16" : "f32", p.kv8 ? (p.kv8 == 2 ? "_kv_int8" : "_kv_fp8") : "", plan.D, p.nwg, p.Hkv / p.hpw,
-               p.hpw, p.nwg, p.dsmall ? "whole" : "window", window_note(p).c_str(), p.rope ? " rope" : "");
+               p.hpw, p.nwg, p.dsmall ? "whole" : "window", window_note(p), p.rope ? " rope" : "");
   return KVS_OK;
 }
 
@@ -762,9 +825,10 @@ kvs_status run_hinted(const AttnCall& c) {
   dec.q = &qd; dec.out = &od; dec.table = &td; dec.cu = &cd; dec.lk = &kd; dec.lse = c.lse ? &ld : nullptr;
   dec.hints = &sub;
   KVS_TRY(run_call(pre));
-  const std::string d1 = g_dispatch;
+  char d1[kTextBytes];
+  memcpy(d1, g_dispatch, kTextBytes);
   KVS_TRY(run_call(dec));
-  set_dispatch("split (decode_tail %lld): %s | %s", (long long)N, d1.c_str(), g_dispatch.c_str());
+  set_dispatch("split (decode_tail %lld): %s | %s", (long long)N, d1, g_dispatch);
   return KVS_OK;
 }
 
@@ -777,7 +841,7 @@ kvs_status attn_decode_append_paged(const kvs_tensor* q, const kvs_tensor* k_new
                                     const kvs_tensor* seqlens_k, float scale, kvs_tensor* out, kvs_tensor* lse,
                                     const kvs_hints* hints, void* workspace, size_t workspace_bytes,
                                     kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, 0, out, lse, hints,
                        workspace, workspace_bytes, stream);
 }
@@ -788,7 +852,7 @@ kvs_status attn_decode_append_paged_fp8(const kvs_tensor* q, const kvs_tensor* k
                                         const kvs_tensor* seqlens_k, float scale, int32_t window, kvs_tensor* out,
                                         kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                         size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
   if (!k_scale || !v_scale) return fail(KVS_ERR_INVALID, "k_scale / v_scale: descriptor is NULL");
   return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, window, out, lse, hints,
@@ -801,7 +865,7 @@ kvs_status attn_decode_append_paged_int8(const kvs_tensor* q, const kvs_tensor* 
                                          const kvs_tensor* seqlens_k, float scale, int32_t window, kvs_tensor* out,
                                          kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                          size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
   if (!k_scale || !v_scale) return fail(KVS_ERR_INVALID, "k_scale / v_scale: descriptor is NULL");
   return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, window, out, lse, hints,
@@ -813,7 +877,7 @@ kvs_status attn_decode_append_paged_rope(const kvs_tensor* q, const kvs_tensor* 
                                          const kvs_tensor* seqlens_k, float scale, int32_t window, const kvs_rope* rope,
                                          kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                          size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   if (window < 0) return fail(KVS_ERR_INVALID, "window must be >= 0 (0: none)");
   if (!rope) return fail(KVS_ERR_INVALID, "rope: parameters are NULL");
   return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, window, out, lse, hints,
@@ -825,7 +889,7 @@ kvs_status attn_decode_append_paged_window(const kvs_tensor* q, const kvs_tensor
                                            const kvs_tensor* seqlens_k, float scale, int32_t window, kvs_tensor* out,
                                            kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                            size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   if (window < 1) return fail(KVS_ERR_INVALID, "window must be >= 1 (got %d)", (int)window);
   return decode_append(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, scale, window, out, lse, hints,
                        workspace, workspace_bytes, stream);
@@ -836,7 +900,7 @@ kvs_status attn_varlen_paged_ex(const kvs_tensor* q, const kvs_tensor* k_cache, 
                                 const kvs_tensor* seqlens_k, float scale, int causal, kvs_tensor* out,
                                 kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                 size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   KVS_TRY(check_hints(hints));
   return run_hinted(AttnCall{q, k_cache, v_cache, nullptr, nullptr, block_table, cu_seqlens_q, seqlens_k, scale,
                              causal, 0, out, lse, hints, workspace, workspace_bytes,
@@ -868,7 +932,7 @@ kvs_status attn_varlen_paged_fp8_ex(const kvs_tensor* q, const kvs_tensor* k_cac
                                     const kvs_tensor* seqlens_k, float scale, int causal, int32_t window,
                                     kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                     size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   return varlen_q8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k, scale, causal, window,
                    out, lse, hints, workspace, workspace_bytes, stream, KVS_FP8_E4M3);
 }
@@ -879,7 +943,7 @@ kvs_status attn_varlen_paged_int8_ex(const kvs_tensor* q, const kvs_tensor* k_ca
                                      const kvs_tensor* seqlens_k, float scale, int causal, int32_t window,
                                      kvs_tensor* out, kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                      size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   return varlen_q8(q, k_cache, v_cache, k_scale, v_scale, block_table, cu_seqlens_q, seqlens_k, scale, causal, window,
                    out, lse, hints, workspace, workspace_bytes, stream, KVS_INT8);
 }
@@ -889,7 +953,7 @@ kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q, const kvs_tensor* k_
                                        const kvs_tensor* seqlens_k, float scale, int32_t window, kvs_tensor* out,
                                        kvs_tensor* lse, const kvs_hints* hints, void* workspace,
                                        size_t workspace_bytes, kvs_stream_t stream) {
-  g_err.clear();
+  clear_error();
   KVS_TRY(check_hints(hints));
   if (window < 1) return fail(KVS_ERR_INVALID, "window must be >= 1 (got %d)", (int)window);
   return run_hinted(AttnCall{q, k_cache, v_cache, nullptr, nullptr, block_table, cu_seqlens_q, seqlens_k, scale, 1,
@@ -899,7 +963,7 @@ kvs_status attn_varlen_paged_window_ex(const kvs_tensor* q, const kvs_tensor* k_
 
 size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k_cache,
                                         const kvs_tensor* block_table, const kvs_hints* hints) {
-  g_err.clear();
+  clear_error();
   if (check_hints(hints) != KVS_OK) return (size_t)-1;
   // with the decode_tail hint only the decode part (the last N sequences,
   // one row each) needs scratch
@@ -921,12 +985,12 @@ size_t attn_varlen_paged_workspace_size(const kvs_tensor* q, const kvs_tensor* k
   return plan.ws_bytes;
 }
 
-const char* kvs_last_error(void) { return g_err.c_str(); }
+const char* kvs_last_error(void) { return g_err; }
 
-const char* kvs_last_dispatch(void) { return g_dispatch.c_str(); }
+const char* kvs_last_dispatch(void) { return g_dispatch; }
 
 kvs_status kvs_release_workspace(void) {
-  g_err.clear();
+  clear_error();
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_ws_mu);

@@ -196,6 +196,29 @@ kvs_status attn_varlen_paged(const kvs_tensor* q,
                              kvs_tensor* out, kvs_tensor* lse,
                              kvs_stream_t stream);
 
+/*
+ * attn_varlen_paged_noalloc -- attn_varlen_paged for callers that cannot
+ * allocate memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, computation, paths and
+ * results as attn_varlen_paged (the same kernels); it allocates nothing, on
+ * the device or the host.  The split decode's scratch is a static device
+ * array of 16 MiB inside the library (one per GPU the library runs on, held
+ * until the process ends); shapes whose split plan needs more return
+ * KVS_ERR_WORKSPACE with nothing enqueued (attn_varlen_paged_workspace_size
+ * with NULL hints gives the need).  Each call first clears the merge counters
+ * it uses with one of the library's kernels on `stream`.  Every call on a GPU
+ * shares that GPU's array, so calls that overlap in time on one GPU (on
+ * different streams with no ordering between them) race and are not allowed.
+ */
+kvs_status attn_varlen_paged_noalloc(const kvs_tensor* q,
+                                     const kvs_tensor* k_cache, const kvs_tensor* v_cache,
+                                     const kvs_tensor* block_table,
+                                     const kvs_tensor* cu_seqlens_q,
+                                     const kvs_tensor* seqlens_k,
+                                     float scale, int causal,
+                                     kvs_tensor* out, kvs_tensor* lse,
+                                     kvs_stream_t stream);
+
 /* Optional host-side hints for attn_varlen_paged_ex; 0 means "unknown / choose".
  * The kernel-facing bookkeeping of "장부가 커널 인자로 바뀌는 지점과 CUDA graph"
  * ("장부에서 텐서로") carries host-side max_seqlen_q / max_seqlen_k next to the

@@ -114,6 +114,16 @@ int main() {
       expect("prefill window", call_ex(p, nullptr, none, 33), KVS_OK);
       Attn d = attn(6, 6, 32, 8, D, dt);
       expect("decode plain", call_plain(d), KVS_OK);
+      expect("decode noalloc", attn_varlen_paged_noalloc(&d.q, &d.k, &d.v, &d.table, &d.cu, &d.lk, 0.125f, 1, &d.out,
+                                                          &d.lse, S),
+             KVS_OK);
+      expect("prefill noalloc", attn_varlen_paged_noalloc(&p.q, &p.k, &p.v, &p.table, &p.cu, &p.lk, 0.125f, 1,
+                                                           &p.out, nullptr, S),
+             KVS_OK);
+      Attn huge = attn(4096, 4096, 32, 8, D, dt);
+      expect("noalloc beyond its scratch", attn_varlen_paged_noalloc(&huge.q, &huge.k, &huge.v, &huge.table, &huge.cu,
+                                                                     &huge.lk, 0.125f, 1, &huge.out, &huge.lse, S),
+             KVS_ERR_WORKSPACE);
       kvs_hints h{0, 0, 64, 0};
       auto ws = workspace(d, &h);
       expect("decode ex", call_ex(d, &h, ws), KVS_OK);

@@ -40,6 +40,16 @@ hipError_t hipFreeAsync(void* p, hipStream_t) {
 }
 hipError_t hipGetLastError(void) { return hipSuccess; }
 const char* hipGetErrorString(hipError_t) { return "host stub"; }
+// a device variable's address: its host shadow stands in for it here
+hipError_t hipGetSymbolAddress(void** p, const void* symbol) {
+  *p = const_cast<void*>(symbol);
+  return hipSuccess;
+}
+// the module registration the compiler emits for a source with device code
+static void* g_module = nullptr;
+void** __hipRegisterFatBinary(const void*) { return &g_module; }
+void __hipRegisterVar(void**, void*, char*, char*, int, size_t, int, int) {}
+void __hipUnregisterFatBinary(void**) {}
 }
 
 namespace kvs {
@@ -49,7 +59,7 @@ hipError_t launch_store(const StoreParams& p, DType, hipStream_t) {
 }
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t) {
   require(p && bytes % 16 == 0, "zero");
-  // the stand-in allocation is host memory: clear it as the kernel would
+  // the stand-in scratch is host memory: clear it as the kernel would
   for (size_t i = 0; i < bytes; ++i) static_cast<unsigned char*>(p)[i] = 0;
   return hipSuccess;
 }
