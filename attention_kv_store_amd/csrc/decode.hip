@@ -190,6 +190,9 @@ struct DecodeWave : DecodeRope<ROPE> {
 
   float m_run, l_run;
   f32x4 o[C::NDB];
+  // the query fragments of the piece being computed (B operand of S^T =
+  // K Q^T): loaded with a piece's first step only, kept across its steps
+  u32x4 qc[C::KI];
 
   __device__ __forceinline__ DecodeWave(const AttnParams& p_, int g_, char* slab_)
       : p(p_), lane(threadIdx.x & 63), col(lane & 15), grp(lane >> 4), g(g_), head_ok(col < p_.G),
@@ -255,7 +258,7 @@ struct DecodeWave : DecodeRope<ROPE> {
   struct Buf : BufBase {
     KRaw k[C::NBS][C::KI];
     KRaw v[C::NBS][2 * C::VIL];
-    u32x4 q[C::KI];
+    u32x4 q[C::KI];   // the query row, loaded only with a piece's first step
   };
   // First element of sequence b's new K (V) row of this wave's KV head.
   __device__ __forceinline__ const E* new_row(const void* base, int b) const {
@@ -379,10 +382,14 @@ struct DecodeWave : DecodeRope<ROPE> {
   // Raw, unconditional loads of one step into `bf` (phys[j] = physical block of
   // the step's j-th block, 0 for blocks past its end).
   __device__ __forceinline__ void load(const Step& st, const int* phys, Buf& bf) {
-    const int hq = st.b < 0 ? 0 : h;
-    const E* qp = static_cast<const E*>(p.q) + ((int64_t)(st.b < 0 ? 0 : st.t) * p.Hq + hq) * D;
+    // the query row comes with the first step of a piece (a wave-uniform
+    // branch); later steps of the piece reuse it
+    if (st.first) {
+      const int hq = st.b < 0 ? 0 : h;
+      const E* qp = static_cast<const E*>(p.q) + ((int64_t)(st.b < 0 ? 0 : st.t) * p.Hq + hq) * D;
 #pragma unroll
-    for (int i = 0; i < C::KI; ++i) bf.q[i] = ld16(qp + i * 32 + grp * 8);
+      for (int i = 0; i < C::KI; ++i) bf.q[i] = ld16(qp + i * 32 + grp * 8);
+    }
     if constexpr (KV8) {
       load_kv8(phys, bf);
       if constexpr (APPEND) {
@@ -623,10 +630,12 @@ struct DecodeWave : DecodeRope<ROPE> {
         }
       }
     }
-    u32x4 q[C::KI];
+    if (st.first) {
 #pragma unroll
-    for (int i = 0; i < C::KI; ++i) q[i] = head_ok ? bf.q[i] : zero;
-    if constexpr (ROPE) rope_rotate(q);
+      for (int i = 0; i < C::KI; ++i) qc[i] = head_ok ? bf.q[i] : zero;
+      if constexpr (ROPE) rope_rotate(qc);
+    }
+    const u32x4 (&q)[C::KI] = qc;
     f32x4 s[C::NBS];
 #pragma unroll
     for (int j = 0; j < C::NBS; ++j) {
@@ -815,7 +824,7 @@ struct DecodeWave : DecodeRope<ROPE> {
   // A sequence's arithmetic is the same whichever workgroup merges it and
   // whatever else that wave merges, so repeated calls give the same bits.
   static constexpr int HB = 4;
-  static constexpr int PC = D == 64 ? 16 : 8;
+  static constexpr int PC = 8;
   struct MUnit {
     int b;     // sequence (< 0: no unit)
     int wf;    // range holding its first block
