@@ -26,7 +26,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvstore.so")
 DEBUG_LIB = os.path.join(PKG, "libkvstore_debug.so")
-SOURCES = ["api.hip", "store.hip", "rope.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["api.hip", "store.hip", "rope.hip", "prefill.hip", "decode.hip", "mixed.hip"]
 # the debug library: api.hip again with KVS_DEBUG, plus the check kernel
 DEBUG_SOURCES = [("api.hip", "api_debug.o", ["-DKVS_DEBUG"]), ("validate.hip", "validate.o", [])]
 # the benchmark's MFMA calibration kernel, a library of its own

@@ -105,12 +105,81 @@ struct Plan {
   kvs::DType dt;
   int D = 0;
   bool decode = false;
-  size_t ws_bytes = 0;   // scratch needed (decode with >1 split)
+  // mixed launch (T != B, bf16): prefill items and one-row decode ranges
+  // share one grid of mixed_grid workgroups
+  bool mixed = false;
+  int mixed_grid = 0;
+  size_t mixed_lds = 0;
+  size_t ws_bytes = 0;   // scratch needed (decode with >1 split, mixed launch)
   size_t ws_po_off = 0;  // byte offset of part_o inside the scratch
   size_t ws_lse_off = 0; // byte offset of part_lse inside the scratch
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- compute units of the current device (cached per device) ---------------
+constexpr int kMaxDevices = 64;
+std::mutex g_cu_mu;
+int g_cus[kMaxDevices];
+
+kvs_status device_cus(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVS_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_cu_mu);
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return fail(KVS_ERR_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed");
+    g_cus[dev] = n;
+  }
+  *out = g_cus[dev];
+  return KVS_OK;
+}
+
+// Decode LDS budget of one workgroup (160 KiB per CU, less the kernels'
+// static LDS).
+constexpr size_t kLdsBudget = 160 * 1024 - 256;
+
+// T != B: whether the batch runs as a mixed launch, and its sizes.  bf16
+// with 8-wave workgroups and KV heads in whole groups of 8 (the decode part's
+// workgroup is the prefill part's 512 threads); otherwise -- and when a limit
+// below is exceeded -- the prefill kernel serves every sequence, one-row ones
+// included.  A batch of one sequence (then with T > 1 rows) has no one-row
+// sequence and runs in the prefill kernel too.  The grid holds one workgroup
+// per CU, and at least 8 more than the decode ranges a range's table window
+// could need.
+kvs_status plan_mixed(Plan* plan, int32_t qdt, bool kv8, int D, int64_t B, int64_t MB) {
+  kvs::AttnParams& p = plan->p;
+  plan->mixed = false;
+  p.mixed = 0;
+  if (qdt != KVS_BF16 || kv8 || p.pnw != 8 || p.Hkv % 8 || p.G > 16 || B < 2 || B > 8192) return KVS_OK;
+  int cus = 0;
+  KVS_TRY(device_cus(&cus));
+  const int64_t nhg = p.Hkv / 8;
+  if (nhg > 64) return KVS_OK;
+  const int64_t need = nhg * ((B * MB + kvs::kDecodeTblWin - 1) / kvs::kDecodeTblWin);
+  const int64_t W = align_up((size_t)std::max<int64_t>(cus, 8 + need), 8);
+  if (W > (1 << 20)) return KVS_OK;
+  if (B * p.Hkv > (int64_t)(kvs::kDecodeCounterBytes / sizeof(int32_t))) return KVS_OK;
+  if ((double)(W + B) * p.Hq * D * sizeof(float) >= 2147483648.0) return KVS_OK;
+  const size_t dec_lds = kvs::decode_lds_bytes((int)B, kvs::decode_tbl_ints((int)B, (int)MB, false) + kvs::decode_mix_ints((int)B),
+                                               8, kvs::decode_slab_bytes(D, false));
+  const size_t pre_lds = kvs::prefill_lds_bytes(D, true, (int)B, p.meta_lds);
+  if (dec_lds > kLdsBudget || pre_lds > kLdsBudget) return KVS_OK;
+  plan->mixed = true;
+  plan->mixed_grid = (int)W;
+  plan->mixed_lds = std::max(dec_lds, pre_lds);
+  p.mixed = 1;
+  p.hpw = 8;
+  p.nwg = (int32_t)W;   // partial slots: at most W ranges + B sequences
+  p.dsmall = 0;
+  const size_t slots = (size_t)W + B;
+  plan->ws_po_off = kvs::kDecodeCounterBytes;
+  plan->ws_lse_off = plan->ws_po_off + align_up(slots * p.Hq * D * sizeof(float), 256);
+  plan->ws_bytes = plan->ws_lse_off + align_up(slots * p.Hq * sizeof(float), 256);
+  return KVS_OK;
+}
 
 // Validates shapes (not device values) and fills the plan.  `v_cache`,
 // `cu`, `lk`, `out`, `lse` may be NULL when only sizing the workspace; `cu`
@@ -218,7 +287,7 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     const int64_t items_bound = (Tb + tile_rows - 1) / tile_rows * B * (int64_t)p.NHG;
     p.items32 = items_bound < ((int64_t)1 << 31) ? 1 : 0;
     kvs::fast_div_magic((uint32_t)p.NHG, &p.nhg_m, &p.nhg_l);
-    return KVS_OK;
+    return plan_mixed(plan, q->dtype, kv8, (int)D, B, MB);
   }
 
   // decode: work plan from shapes and hints only
@@ -237,8 +306,6 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   if (nwg > (1 << 20)) return fail(KVS_ERR_UNSUPPORTED, "num_splits too large");
   p.hpw = hpw;
   p.nwg = (int32_t)nwg;
-  // dynamic LDS a decode workgroup may take (160 KiB per CU, less the kernel's static LDS)
-  constexpr size_t kLdsBudget = 160 * 1024 - 256;
   // partial outputs are addressed with 32-bit byte offsets
   if ((double)(nwg + B) * Hq * D * sizeof(float) >= 2147483648.0)
     return fail(KVS_ERR_UNSUPPORTED, "decode partial buffer would exceed 2 GiB (num_splits %lld)", (long long)nwg);
@@ -263,26 +330,6 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
     plan->ws_lse_off = plan->ws_po_off + align_up(slots * Hq * D * sizeof(float), 256);
     plan->ws_bytes = plan->ws_lse_off + align_up(slots * Hq * sizeof(float), 256);
   }
-  return KVS_OK;
-}
-
-// ---- compute units of the current device (cached per device) ---------------
-constexpr int kMaxDevices = 64;
-std::mutex g_cu_mu;
-int g_cus[kMaxDevices];
-
-kvs_status device_cus(int* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(KVS_ERR_HIP, "hipGetDevice failed");
-  if (dev < 0 || dev >= kMaxDevices) return fail(KVS_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
-  std::lock_guard<std::mutex> lk(g_cu_mu);
-  if (g_cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      return fail(KVS_ERR_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed");
-    g_cus[dev] = n;
-  }
-  *out = g_cus[dev];
   return KVS_OK;
 }
 
@@ -419,6 +466,21 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
                  p.kv8 ? (p.kv8 == 2 ? "_kv_int8" : "_kv_fp8") : "", plan.D, p.nwg, p.Hkv / p.hpw, p.hpw, p.nwg, p.dsmall ? "whole" : "window",
                  window_note(p));
     return KVS_OK;
+  }
+  if (plan.mixed) {
+    if (ws && ws_bytes >= plan.ws_bytes && reinterpret_cast<uintptr_t>(ws) % 256 == 0) {
+      p.counters = static_cast<int32_t*>(ws);
+      p.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.ws_po_off);
+      p.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + plan.ws_lse_off);
+      const hipError_t e = kvs::launch_mixed(p, plan.D, plan.mixed_grid, plan.mixed_lds, stream);
+      if (e != hipSuccess) return fail(KVS_ERR_HIP, "mixed launch failed: %s", hipGetErrorString(e));
+      set_dispatch("mixed_bf16_d%d grid=%d (prefill items of multi-row sequences | decode ranges of one-row sequences, "
+                   "split in-kernel) waves/wg=8 head groups=%d heads/wg=%d tokens/item=%d%s",
+                   plan.D, plan.mixed_grid, p.NHG, p.HW, 32 * p.TPW, window_note(p));
+      return KVS_OK;
+    }
+    // no (or too small a) workspace: every sequence goes through the prefill kernel
+    p.mixed = 0;
   }
   int cus = 0;
   KVS_TRY(device_cus(&cus));
@@ -629,6 +691,8 @@ kvs_status attn_varlen_paged_noalloc(const kvs_tensor* q, const kvs_tensor* k_ca
                     false, &plan));
   KVS_TRY(no_fp8(plan));
   void* ws = nullptr;
+  // a mixed batch whose scratch does not fit runs in the prefill kernel alone
+  if (plan.mixed && plan.ws_bytes > kNoAllocScratchBytes) return run_plan(plan, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
   if (plan.ws_bytes) {
     if (plan.ws_bytes > kNoAllocScratchBytes)
       return fail(KVS_ERR_WORKSPACE,

@@ -95,6 +95,14 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, row_ror<8>(x));
   return max_xor32(max_xor16(x));
 }
+// Sum over all 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += row_ror<1>(x);
+  x += row_ror<2>(x);
+  x += row_ror<4>(x);
+  x += row_ror<8>(x);
+  return sum_xor32(sum_xor16(x));
+}
 // Max / sum over the 16 lanes that share lane % 4.
 __device__ __forceinline__ float max_mod4(float x) {
   x = fmaxf(x, row_ror<4>(x));

@@ -77,6 +77,11 @@ struct AttnParams {
   int32_t rope_style;     // 0: pairs (i, i + rd/2); 1: pairs (2i, 2i + 1)
   double rope_inv_scale;  // 1 / pos_scale
   double rope_l2b;        // log2(base)
+  // mixed launch (T != B): the first workgroups run the prefill items of the
+  // sequences with more than one query row, the others the decode ranges of
+  // the one-row sequences (split and merged as in decode); nwg is then the
+  // capacity of the partial buffer, the decode ranges are formed in-kernel
+  int32_t mixed;
 };
 
 // FP8 store: new rows [T, Hkv, D] (f32 / bf16) quantized into E4M3 code pools
@@ -136,6 +141,9 @@ constexpr int kDecodeTblWin = 2048;          // most blocks in one workgroup's r
 constexpr int kDecodeSmallB = 64;
 constexpr int kDecodeSmallTbl = 16384;
 __host__ __device__ inline int decode_tbl_ints(int B, int MB, bool small) { return small ? ((B * MB + 3) & ~3) : kDecodeTblWin; }
+// the decode part of a mixed launch also keeps, per one-row sequence, its
+// batch index and its query row
+__host__ __device__ inline int decode_mix_ints(int B) { return 2 * ((B + 3) & ~3); }
 inline size_t decode_lds_bytes(int B, int tbl_ints, int hpw, int slab_bytes) {
   const size_t ints = (size_t)((B + 3) & ~3) + (size_t)((B + 1 + 3) & ~3) + (size_t)tbl_ints;
   return ints * sizeof(int) + (size_t)hpw * slab_bytes;
@@ -182,5 +190,7 @@ hipError_t launch_rope_store(const RopeParams& p, DType dt, hipStream_t s);
 hipError_t launch_store_fp8(const StoreFp8Params& p, DType in, int D, bool i8, hipStream_t s);
 hipError_t launch_prefill(const AttnParams& p, DType dt, int D, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s);
+// mixed launch (bf16, 8-wave workgroups): `grid` workgroups, `lds` dynamic LDS bytes
+hipError_t launch_mixed(const AttnParams& p, int D, int grid, size_t lds, hipStream_t s);
 
 }  // namespace kvs

@@ -43,21 +43,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _src_sha(name: str) -> str:
-    """Hash of a kernel's source file together with the shared headers and the
+def _src_sha(names) -> str:
+    """Hash of a kernel's source files together with the shared headers and the
     planner that sets its launch shape."""
     h = hashlib.sha256()
-    for f in (name, "kvs_device.hpp", "kvs_internal.hpp", "api.hip"):
+    for f in (*names, "kvs_device.hpp", "kvs_internal.hpp", "api.hip"):
         h.update(open(os.path.join(ROOT, "attention_kv_store_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
 # kernel symbol (as rocprofv3 names it) and source file of each timed workload
+# (a batch of several sequences with T != B runs as one mixed launch, whose
+# grid here holds only prefill items; a single prompt runs in the prefill kernel)
+MIXED_SRC = ("mixed.hip", "prefill_impl.hpp", "decode_impl.hpp")
 COUNTED = {
-    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false, false, false, false>", "decode.hip"),
-    "causal_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", "prefill.hip"),
-    "extend_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", "prefill.hip"),
-    "long_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", "prefill.hip"),
+    "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false, false, false, false>", ("decode.hip", "decode_impl.hpp")),
+    "causal_prefill_bf16": ("kvs::mixed_kernel<128, false>", MIXED_SRC),
+    "extend_prefill_bf16": ("kvs::mixed_kernel<128, false>", MIXED_SRC),
+    "long_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", ("prefill.hip", "prefill_impl.hpp")),
 }
 
 
@@ -116,7 +119,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> None:
     log(json.dumps(out, indent=1))
 
 
-def _traffic(kernel_src: str, workload: str):
+def _traffic(kernel_src, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None when
     the kernel source changed since they were taken."""
     try:
@@ -866,7 +869,7 @@ def main():
     value = kvb / (ms * 1e-3) / 1e9
     achieved = kvb / (attn_ms * 1e-3) / 1e9
     log(f"decode, fused: {ms*1e3:.2f} us/step, launch {attn_ms*1e3:.2f} us -> {achieved:.0f} GB/s ({dispatch})")
-    traffic = _traffic("decode.hip", "paged_decode_bf16")
+    traffic = _traffic(COUNTED["paged_decode_bf16"][1], "paged_decode_bf16")
     # the outputs of the last timed step (every replica computes the same)
     dec_out = w.reps[0][4].float().cpu().numpy().astype("float64")
     dec_lse = w.reps[0][5].cpu().numpy().astype("float64")
