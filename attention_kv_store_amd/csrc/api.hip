@@ -142,36 +142,37 @@ kvs_status device_cus(int* out) {
 constexpr size_t kLdsBudget = 160 * 1024 - 256;
 
 // T != B: whether the batch runs as a mixed launch, and its sizes.  bf16
-// with 8-wave workgroups and KV heads in whole groups of 8 (the decode part's
-// workgroup is the prefill part's 512 threads); otherwise -- and when a limit
-// below is exceeded -- the prefill kernel serves every sequence, one-row ones
-// included.  A batch of one sequence (then with T > 1 rows) has no one-row
-// sequence and runs in the prefill kernel too.  The grid holds one workgroup
-// per CU, and at least 8 more than the decode ranges a range's table window
-// could need.
+// with KV heads in whole groups of the prefill workgroup's waves (the decode
+// part's workgroup is the prefill part's, one wave per KV head); otherwise --
+// and when a limit below is exceeded -- the prefill kernel serves every
+// sequence, one-row ones included.  A batch of one sequence (then with T > 1
+// rows) has no one-row sequence and runs in the prefill kernel too.  The grid
+// holds the prefill kernel's workgroups per CU, and at least 8 more than the
+// decode ranges a range's table window could need.
 kvs_status plan_mixed(Plan* plan, int32_t qdt, bool kv8, int D, int64_t B, int64_t MB) {
   kvs::AttnParams& p = plan->p;
   plan->mixed = false;
   p.mixed = 0;
-  if (qdt != KVS_BF16 || kv8 || p.pnw != 8 || p.Hkv % 8 || p.G > 16 || B < 2 || B > 8192) return KVS_OK;
+  const int nw = p.pnw;
+  if (qdt != KVS_BF16 || kv8 || (nw != 4 && nw != 8) || p.Hkv % nw || p.G > 16 || B < 2 || B > 8192) return KVS_OK;
   int cus = 0;
   KVS_TRY(device_cus(&cus));
-  const int64_t nhg = p.Hkv / 8;
+  const int64_t nhg = p.Hkv / nw;
   if (nhg > 64) return KVS_OK;
   const int64_t need = nhg * ((B * MB + kvs::kDecodeTblWin - 1) / kvs::kDecodeTblWin);
-  const int64_t W = align_up((size_t)std::max<int64_t>(cus, 8 + need), 8);
+  const int64_t W = align_up((size_t)std::max<int64_t>((int64_t)cus * (nw == 4 ? 2 : 1), 8 + need), 8);
   if (W > (1 << 20)) return KVS_OK;
   if (B * p.Hkv > (int64_t)(kvs::kDecodeCounterBytes / sizeof(int32_t))) return KVS_OK;
   if ((double)(W + B) * p.Hq * D * sizeof(float) >= 2147483648.0) return KVS_OK;
   const size_t dec_lds = kvs::decode_lds_bytes((int)B, kvs::decode_tbl_ints((int)B, (int)MB, false) + kvs::decode_mix_ints((int)B),
-                                               8, kvs::decode_slab_bytes(D, false));
+                                               nw, kvs::decode_slab_bytes(D, false));
   const size_t pre_lds = kvs::prefill_lds_bytes(D, true, (int)B, p.meta_lds);
   if (dec_lds > kLdsBudget || pre_lds > kLdsBudget) return KVS_OK;
   plan->mixed = true;
   plan->mixed_grid = (int)W;
   plan->mixed_lds = std::max(dec_lds, pre_lds);
   p.mixed = 1;
-  p.hpw = 8;
+  p.hpw = nw;
   p.nwg = (int32_t)W;   // partial slots: at most W ranges + B sequences
   p.dsmall = 0;
   const size_t slots = (size_t)W + B;
@@ -265,9 +266,15 @@ kvs_status make_plan(const kvs_tensor* q, const kvs_tensor* k_cache, const kvs_t
   plan->ws_bytes = 0;
 
   if (!plan->decode) {
-    // bf16: one 8-wave workgroup per CU (a K/V tile serves 8 x 32 rows);
-    // fp32: two 4-wave workgroups per CU
-    p.pnw = q->dtype == KVS_BF16 ? 8 : 4;
+    // fp32: two 4-wave workgroups per CU.  bf16: two 4-wave workgroups per
+    // CU, whose separate barriers let one's softmax run under the other's
+    // MFMAs -- unless one KV head's K/V for the widest table row exceeds an
+    // XCD's L2 (4 MiB): the token tiles of a (sequence, head group) pair then
+    // re-read it from HBM, and one 8-wave workgroup per CU (a K/V tile serving
+    // 8 x 32 rows instead of 4 x 32) halves those re-reads.  FP8 / INT8
+    // caches: 8-wave workgroups.
+    const bool wide = 16.0 * (double)MB * (double)D * 2.0 * 2.0 > (double)(4 << 20);
+    p.pnw = q->dtype == KVS_BF16 && (wide || kv8) ? 8 : 4;
     p.HW = p.G % 4 == 0 ? 4 : (p.G % 2 == 0 ? 2 : 1);
     p.TPW = p.pnw / p.HW;
     p.NHG = p.Hq / p.HW;
@@ -475,8 +482,8 @@ kvs_status run_plan(Plan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
       const hipError_t e = kvs::launch_mixed(p, plan.D, plan.mixed_grid, plan.mixed_lds, stream);
       if (e != hipSuccess) return fail(KVS_ERR_HIP, "mixed launch failed: %s", hipGetErrorString(e));
       set_dispatch("mixed_bf16_d%d grid=%d (prefill items of multi-row sequences | decode ranges of one-row sequences, "
-                   "split in-kernel) waves/wg=8 head groups=%d heads/wg=%d tokens/item=%d%s",
-                   plan.D, plan.mixed_grid, p.NHG, p.HW, 32 * p.TPW, window_note(p));
+                   "split in-kernel) waves/wg=%d head groups=%d heads/wg=%d tokens/item=%d%s",
+                   plan.D, plan.mixed_grid, p.pnw, p.NHG, p.HW, 32 * p.TPW, window_note(p));
       return KVS_OK;
     }
     // no (or too small a) workspace: every sequence goes through the prefill kernel

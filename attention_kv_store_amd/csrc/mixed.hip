@@ -24,16 +24,18 @@
 namespace kvs {
 
 // Estimated cost, in decode block-steps of one workgroup: a prefill step (a
-// 64-key tile for 256 query rows of 4 heads) takes about two, and every item
+// 64-key tile for the workgroup's query rows) takes about two, and every item
 // about two more for its set-up and epilogue.
 constexpr float kMixPrefillStep = 2.0f;
 
-template <int D, bool WIN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mixed_kernel(AttnParams p) {
+// NW waves per workgroup (4: two workgroups per CU; 8: one): the prefill
+// part's waves and the decode part's KV heads per workgroup.
+template <int D, bool WIN, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void mixed_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ float s_cpf[8];
-  __shared__ int s_dblk[8];
-  __shared__ int s_ntm[8];
+  __shared__ float s_cpf[NW];
+  __shared__ int s_dblk[NW];
+  __shared__ int s_ntm[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int W = (int)gridDim.x;
   const int nhg = p.Hkv / p.hpw;   // decode head groups (workgroups per range)
@@ -44,12 +46,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // and finds the most token tiles of any sequence (what the prefill part's
   // own set-up would do), so a prefill workgroup starts on its items at once.
   const bool staged = p.meta_lds != 0;
-  int* s_cq = reinterpret_cast<int*>(smem + 2 * PCfg<D, true, 8>::STAGE);   // [B + 1]
+  int* s_cq = reinterpret_cast<int*>(smem + 2 * PCfg<D, true, NW>::STAGE);   // [B + 1]
   int* s_lk = s_cq + p.B + 1;                                              // [B]
   float cpf = 0.f;   // prefill part
   int dblk = 0;      // decode part: key blocks of the one-row sequences
   int ntm = 0;       // most token tiles of a sequence
-  for (int b = tid; b < p.B; b += 512) {
+  for (int b = tid; b < p.B; b += 64 * NW) {
     const int q0 = p.cu_q[b], q1 = p.cu_q[b + 1], lk = p.lens_k[b];
     const int Lq = q1 - q0;
     if (staged) {
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float cp = 0.f;
   int db = 0, nt = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NW; ++i) {
     cp += s_cpf[i];
     db += s_dblk[i];
     nt = max(nt, s_ntm[i]);
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const int w = (int)blockIdx.x;
   if (w < P) {
-    prefill_body<D, true, 8, WIN, false>(p, P, w, nt);
+    prefill_body<D, true, NW, WIN, false>(p, P, w, nt);
   } else {
     const int nd = (W - P) / nhg;   // ranges per head group
     const int v = w - P;
@@ -110,9 +112,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-template <int D, bool WIN>
+template <int D, bool WIN, int NW>
 static hipError_t launch_mixed_t(const AttnParams& p, int grid, size_t lds, hipStream_t s) {
-  const void* kern = reinterpret_cast<const void*>(&mixed_kernel<D, WIN>);
+  const void* kern = reinterpret_cast<const void*>(&mixed_kernel<D, WIN, NW>);
   // dynamic LDS above the default limit must be requested; grow it as needed
   // (per instantiation; atomic so that concurrent first calls are safe)
   static std::atomic<size_t> lds_granted{0};
@@ -126,13 +128,20 @@ static hipError_t launch_mixed_t(const AttnParams& p, int grid, size_t lds, hipS
     while (cur < lds && !lds_granted.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
     }
   }
-  hipLaunchKernelGGL((mixed_kernel<D, WIN>), dim3(grid), dim3(512), lds, s, p);
+  hipLaunchKernelGGL((mixed_kernel<D, WIN, NW>), dim3(grid), dim3(64 * NW), lds, s, p);
   return hipGetLastError();
 }
 
+template <int NW>
+static hipError_t launch_mixed_n(const AttnParams& p, int D, int grid, size_t lds, hipStream_t s) {
+  if (p.window > 0) return D == 64 ? launch_mixed_t<64, true, NW>(p, grid, lds, s) : launch_mixed_t<128, true, NW>(p, grid, lds, s);
+  return D == 64 ? launch_mixed_t<64, false, NW>(p, grid, lds, s) : launch_mixed_t<128, false, NW>(p, grid, lds, s);
+}
+
 hipError_t launch_mixed(const AttnParams& p, int D, int grid, size_t lds, hipStream_t s) {
-  if (p.window > 0) return D == 64 ? launch_mixed_t<64, true>(p, grid, lds, s) : launch_mixed_t<128, true>(p, grid, lds, s);
-  return D == 64 ? launch_mixed_t<64, false>(p, grid, lds, s) : launch_mixed_t<128, false>(p, grid, lds, s);
+  if (p.pnw == 4) return launch_mixed_n<4>(p, D, grid, lds, s);
+  if (p.pnw == 8) return launch_mixed_n<8>(p, D, grid, lds, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvs

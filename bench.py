@@ -58,8 +58,8 @@ def _src_sha(names) -> str:
 MIXED_SRC = ("mixed.hip", "prefill_impl.hpp", "decode_impl.hpp")
 COUNTED = {
     "paged_decode_bf16": ("kvs::decode_kernel<64, true, true, false, false, false, false>", ("decode.hip", "decode_impl.hpp")),
-    "causal_prefill_bf16": ("kvs::mixed_kernel<128, false>", MIXED_SRC),
-    "extend_prefill_bf16": ("kvs::mixed_kernel<128, false>", MIXED_SRC),
+    "causal_prefill_bf16": ("kvs::mixed_kernel<128, false, 4>", MIXED_SRC),
+    "extend_prefill_bf16": ("kvs::mixed_kernel<128, false, 4>", MIXED_SRC),
     "long_prefill_bf16": ("kvs::prefill_kernel<128, true, 8, false, false, false>", ("prefill.hip", "prefill_impl.hpp")),
 }
 

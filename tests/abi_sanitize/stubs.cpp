@@ -85,7 +85,7 @@ hipError_t launch_decode(const AttnParams& p, DType, int D, hipStream_t) {
 }
 hipError_t launch_mixed(const AttnParams& p, int D, int grid, size_t lds, hipStream_t) {
   require(p.mixed == 1 && p.B >= 1 && p.T > p.B && (D == 64 || D == 128) && p.G <= 16, "mixed shape");
-  require(p.pnw == 8 && p.hpw == 8 && p.Hkv % 8 == 0 && p.NHG * p.HW == p.Hq, "mixed map");
+  require((p.pnw == 4 || p.pnw == 8) && p.hpw == p.pnw && p.Hkv % p.pnw == 0 && p.NHG * p.HW == p.Hq, "mixed map");
   require(grid >= 8 && grid % 8 == 0 && grid <= p.nwg && lds > 0 && lds <= 160 * 1024, "mixed grid");
   require(p.counters && p.part_o && p.part_lse && p.cu_q && p.lens_k, "mixed workspace");
   return hipSuccess;

@@ -51,16 +51,27 @@ MK = [700, 40, 1, 2000, 100, 16, 300, 129, 17, 5]
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("heads", [(32, 8), (8, 8), (128, 8), (32, 16)])
-def test_mixed_one_launch_matches_oracle(D, heads):
+@pytest.mark.parametrize("heads", [(32, 8), (8, 8), (128, 8), (32, 16), (16, 4)])
+@pytest.mark.parametrize("wide", [False, True])
+def test_mixed_one_launch_matches_oracle(D, heads, wide):
+    """wide: a block table wide enough that the prefill part takes 8-wave
+    workgroups (one KV head's K/V for a full table row exceeds 4 MiB); else
+    4-wave ones, two per CU.  KV heads must come in whole groups of the
+    workgroup's waves."""
     import attention_kv_store_amd as kvs
     from tests.gpu_side import run_attention, to_device
     Hq, Hkv = heads
+    cols = (4 << 20) // (16 * D * 4) + 1 if wide else 0
     b = _mk(2100 + D + Hq + Hkv, MQ, MK, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", causal=True,
-            name=f"mixed-D{D}-{Hq}x{Hkv}")
+            extra_table_cols=cols, name=f"mixed-D{D}-{Hq}x{Hkv}-{'wide' if wide else 'narrow'}")
     print("case", b.name, flush=True)
     out, lse = run_attention(to_device(b))
-    assert kvs.last_dispatch().startswith("mixed_bf16"), kvs.last_dispatch()
+    disp = kvs.last_dispatch()
+    if wide and Hkv % 8:
+        assert disp.startswith("prefill_bf16"), disp
+    else:
+        assert disp.startswith("mixed_bf16"), disp
+        assert f"waves/wg={8 if wide else 4} " in disp, disp
     _check(b, out, lse)
 
 
@@ -144,11 +155,11 @@ def test_mixed_repeated_calls_bitwise_and_noalloc():
 
 
 def test_mixed_shapes_outside_the_mixed_kernel():
-    """fp32, and KV heads not in whole groups of 8: the prefill kernel serves
+    """fp32, and KV heads not in whole groups of 4: the prefill kernel serves
     the mixed batch (correct, one launch)."""
     import attention_kv_store_amd as kvs
     from tests.gpu_side import run_attention, to_device
-    for dtype, Hq, Hkv in (("fp32", 32, 8), ("bf16", 8, 4)):
+    for dtype, Hq, Hkv in (("fp32", 32, 8), ("bf16", 8, 2)):
         b = _mk(2600 + Hkv, MQ, MK, Hq=Hq, Hkv=Hkv, D=64, dtype=dtype, causal=True, name=f"mixed-{dtype}-{Hkv}")
         print("case", b.name, flush=True)
         out, lse = run_attention(to_device(b))
