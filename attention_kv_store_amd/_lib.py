@@ -15,6 +15,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvstore.so")
 # the same kernels, the calls first checking the device-resident preconditions
 DEBUG_LIB_PATH = os.path.join(_PKG, "libkvstore_debug.so")
+# the attention library with the decode kernel's phase timestamps (profiling)
+PHASES_LIB_PATH = os.path.join(_PKG, "libkvstore_phases.so")
 
 KVS_OK, KVS_ERR_INVALID, KVS_ERR_UNSUPPORTED, KVS_ERR_WORKSPACE, KVS_ERR_HIP = range(5)
 KVS_F32, KVS_BF16, KVS_I32, KVS_FP8_E4M3, KVS_INT8 = 0, 1, 2, 3, 4

@@ -3,8 +3,10 @@ and beside it libkvstore_debug.so: the same kernels with the C ABI built with
 KVS_DEBUG, whose calls first check the device-resident preconditions
 (cu_seqlens_q, seqlens_k, table entries, slots) on the GPU and return
 KVS_ERR_INVALID on a violation (loaded when the environment sets KVS_DEBUG=1),
-and libkvstore_calib.so: the benchmark's MFMA calibration kernel
-(include/kvstore_calib.h), kept out of the attention library.
+libkvstore_calib.so: the benchmark's MFMA calibration kernel
+(include/kvstore_calib.h), kept out of the attention library, and
+libkvstore_phases.so: the attention library with the decode kernel's phase
+timestamps (decode.hip built with KVS_PHASE_TIMES; bench.py --decode-phases).
 
     python -m attention_kv_store_amd.build            # both libraries
     python -m attention_kv_store_amd.build --verbose
@@ -32,6 +34,9 @@ DEBUG_SOURCES = [("api.hip", "api_debug.o", ["-DKVS_DEBUG"]), ("validate.hip", "
 # the benchmark's MFMA calibration kernel, a library of its own
 CALIB_LIB = os.path.join(PKG, "libkvstore_calib.so")
 CALIB_SOURCES = [("calib.hip", "calib.o", [])]
+# the profiling library: decode.hip again with its phase probes
+PHASES_LIB = os.path.join(PKG, "libkvstore_phases.so")
+PHASES_SOURCES = [("decode.hip", "decode_phases.o", ["-DKVS_PHASE_TIMES"])]
 ARCH = "gfx950"
 
 
@@ -52,7 +57,7 @@ def build(verbose: bool = False, out: str = LIB) -> str:
     ]
     objs = []
     procs = []
-    jobs = [(src, src.replace(".hip", ".o"), []) for src in SOURCES] + DEBUG_SOURCES + CALIB_SOURCES
+    jobs = [(src, src.replace(".hip", ".o"), []) for src in SOURCES] + DEBUG_SOURCES + CALIB_SOURCES + PHASES_SOURCES
     for src, o, extra in jobs:
         obj = os.path.join(objdir, o)
         cmd = [hipcc(), *common, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -73,10 +78,13 @@ def build(verbose: bool = False, out: str = LIB) -> str:
         raise RuntimeError("HIP compilation failed")
     release = objs[:len(SOURCES)]
     debug = [o for o in release if not o.endswith(os.sep + "api.o")] + objs[len(SOURCES):len(SOURCES) + len(DEBUG_SOURCES)]
-    calib = objs[len(SOURCES) + len(DEBUG_SOURCES):]
+    n0 = len(SOURCES) + len(DEBUG_SOURCES)
+    calib = objs[n0:n0 + len(CALIB_SOURCES)]
+    phases = [o for o in release if not o.endswith(os.sep + "decode.o")] + objs[n0 + len(CALIB_SOURCES):]
     out_dir = os.path.dirname(out)
     for lib_out, lib_objs in ((out, release), (os.path.join(out_dir, os.path.basename(DEBUG_LIB)), debug),
-                              (os.path.join(out_dir, os.path.basename(CALIB_LIB)), calib)):
+                              (os.path.join(out_dir, os.path.basename(CALIB_LIB)), calib),
+                              (os.path.join(out_dir, os.path.basename(PHASES_LIB)), phases)):
         tmp = lib_out + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", tmp]
         if verbose:

@@ -40,6 +40,18 @@ static hipError_t launch_decode_a(const AttnParams& p, DType dt, int D, hipStrea
   return D == 64 ? launch_decode_t<64, false, APPEND, WIN>(p, s) : launch_decode_t<128, false, APPEND, WIN>(p, s);
 }
 
+#ifdef KVS_PHASE_TIMES
+// the phase timestamps of the last decode launches (KVS_PHASE_TIMES build):
+// copy out the [4096][16] array of 64-bit clock values, or clear it
+extern "C" int kvs_phase_times(void* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_t), sizeof(g_phase_t), 0, hipMemcpyDeviceToHost);
+}
+extern "C" int kvs_phase_clear(void) {
+  static unsigned long long zero[4096][kPhaseSlots];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_phase_t), zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+}
+#endif
+
 hipError_t launch_decode(const AttnParams& p, DType dt, int D, hipStream_t s) {
   if (p.rope) {   // fused decode step with RoPE: bf16 only
     if (dt != DType::BF16 || !p.append) return hipErrorInvalidValue;

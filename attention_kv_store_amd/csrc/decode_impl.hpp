@@ -52,6 +52,31 @@
 
 namespace kvs {
 
+// Phase timestamps (the KVS_PHASE_TIMES build, a profiling library of its
+// own): thread 0 of each workgroup records the device's constant-rate clock
+// (100 MHz) at the decode set-up and publish points into slot [workgroup][k]
+// of a device array, read back by kvs_phase_times.  In the product build the
+// probes are empty.
+#ifdef KVS_PHASE_TIMES
+constexpr int kPhaseSlots = 16;
+static __device__ unsigned long long g_phase_t[4096][kPhaseSlots];
+#define KVS_PHASE(k)                                                                              \
+  do {                                                                                            \
+    if (threadIdx.x == 0 && blockIdx.x < 4096) g_phase_t[blockIdx.x][k] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define KVS_PHASE(k) \
+  do {               \
+  } while (0)
+#endif
+// probe slots: 0 start, 7 lens and table staged (whole table), 1 block prefix,
+// 10 table window, 2 new rows stored, 3 split pieces streamed, 5 partial
+// stores complete, 6 merge counters, 8 the counters' completion bits, 4
+// published and merged, 15 end
+constexpr int kPhaseStart = 0, kPhaseStaged = 7, kPhasePrefix = 1, kPhaseWindow = 10, kPhaseNewRows = 2,
+              kPhaseSplitDone = 3, kPhaseStores = 5, kPhaseCounters = 6, kPhaseFlags = 8, kPhaseMerged = 4,
+              kPhaseEnd = 15;
+
 template <int D, int NBS_ = 1>
 struct DCfg {
   // 16-key blocks per step.  For bf16 / fp32 one block keeps the bytes in
@@ -1012,6 +1037,7 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
   char* slabs = reinterpret_cast<char*>(tbl + decode_tbl_ints(B, p.MB, small));
   __shared__ int wtot[8];
 
+  KVS_PHASE(kPhaseStart);
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = hg * p.hpw + wave;
@@ -1041,6 +1067,7 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
       if (lane == B - 1) sstart[B] = x;
     }
     __syncthreads();
+    KVS_PHASE(kPhaseStaged);
     if constexpr (SETUP_APPEND) wv.append_locate(nr, slens, tbl);
   } else {
     // ---- seqlens_k into LDS ---------------------------------------------------
@@ -1110,10 +1137,12 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
     // window below, and stored once it has arrived
     if constexpr (SETUP_APPEND) nr = wv.append_load(w, nwg, slens);
   }
+  KVS_PHASE(kPhasePrefix);
   const int total = sstart[Bn];
   const int r0 = (int)(((int64_t)w * total) / nwg), r1 = (int)(((int64_t)(w + 1) * total) / nwg);
   if (r0 >= r1) {  // empty range (whole workgroup)
     if constexpr (SETUP_APPEND) wv.append_rows(nr, w, nwg, slens);
+    KVS_PHASE(kPhaseEnd);
     return;
   }
 
@@ -1136,7 +1165,9 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
     }
     __syncthreads();
   }
+  KVS_PHASE(kPhaseWindow);
   if constexpr (SETUP_APPEND) wv.append_rows(nr, w, nwg, slens);
+  KVS_PHASE(kPhaseNewRows);
 
   // Segments of the range, in processing order: the piece of the last sequence
   // Z (its head, unless it starts in this range), the piece of the first
@@ -1212,6 +1243,7 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
   auto publish = [&]() __attribute__((always_inline)) {
     if (split_b0 < 0) return;
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's partial stores are complete
+    KVS_PHASE(kPhaseStores);
     // lane 0 counts the first split sequence, lane 1 the second: one atomic
     // instruction, one round trip
     const int mb = lane == 0 ? split_b0 : split_b1;
@@ -1224,6 +1256,10 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
       if (done) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
     }
     const uint64_t lastm = __ballot(done);
+    KVS_PHASE(kPhaseCounters);
+#ifdef KVS_PHASE_TIMES
+    if (threadIdx.x == 0 && blockIdx.x < 4096) g_phase_t[blockIdx.x][kPhaseFlags] = lastm & 3;
+#endif
     if (lastm & 3) {
       const int ba = (lastm & 1) ? split_b0 : split_b1;
       const int bb = (lastm & 3) == 3 ? split_b1 : ba;   // second sequence, if both are complete
@@ -1287,8 +1323,11 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
   // the pieces that may be split, then publish them, then the whole sequences
   const int nsplit_seg = nseg == 1 ? 1 : 2;
   stream(0, nsplit_seg);
+  KVS_PHASE(kPhaseSplitDone);
   publish();
+  KVS_PHASE(kPhaseMerged);
   if (nseg > nsplit_seg) stream(nsplit_seg, nseg);
+  KVS_PHASE(kPhaseEnd);
 }
 
 template <int D, bool BF16, bool APPEND, bool WIN, bool KV8, bool ROPE, bool I8 = false>

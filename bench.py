@@ -64,55 +64,107 @@ COUNTED = {
 }
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> None:
-    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
-    WRITE_SIZE; KiB per dispatch) into HBM bytes per launch.
+READ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_DRAM_sum")
+WRITE_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum")
 
-    Both counters are scaled by what they read for a plain copy of known size:
-    the kv_store_paged launch that fills a decode replica's pool copies every
-    context row (K+V of all KV heads, 2 * sum(Lk) * Hkv * D * 2 bytes read and
-    written, plus the int32 slots read)."""
+
+def summarize_counters(specs, command: str) -> None:
+    """Turn rocprofv3 --pmc runs of this script into HBM bytes per launch.
+    Each spec is WORKLOAD=READ_CSV,WRITE_CSV: two runs of one command (the
+    workload's kernel among its dispatches), the first counting the L2's read
+    requests to the memory side (READ_COUNTERS: all, 32-byte, 128-byte, and
+    those bound for DRAM), the second its write requests (WRITE_COUNTERS: all,
+    64-byte, bound for DRAM).
+
+    Bytes are the request counts times their sizes (128 B for TCC_BUBBLE, 32 B
+    for the 32-byte ones, 64 B for the rest; writes 64 B or 32 B).  The same
+    sums are taken for a copy of known size -- the kv_store_paged launch that
+    fills a decode replica's pool, 2 * sum(Lk) * Hkv * D * 2 bytes of K+V read
+    and written plus the int32 slots read -- and the ratio of the known to the
+    counted bytes is recorded as a check on those sizes; the per-launch
+    figures are then given both as counted and scaled by that ratio."""
     import csv
-    from collections import defaultdict
 
     from workloads import kv_bytes, paged_decode_bf16
 
-    def load(path, counter):
+    def load(path, names):
         rows = {}
         for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] == counter:
-                rows[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+            if r["Counter_Name"] in names:
+                d = rows.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         return rows
 
-    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    runs = {}
+    for spec in specs:
+        wl, _, files = spec.partition("=")
+        rpath, _, wpath = files.partition(",")
+        if wl not in COUNTED or not rpath or not wpath:
+            raise SystemExit(f"bad spec {spec!r}: WORKLOAD=READ_CSV,WRITE_CSV with WORKLOAD one of {sorted(COUNTED)}")
+        if (rpath, wpath) not in runs:
+            runs[(rpath, wpath)] = (load(rpath, READ_COUNTERS), load(wpath, WRITE_COUNTERS))
+        runs[wl] = runs[(rpath, wpath)]
+
+    def rbytes(c):
+        req, r32, r128 = c["TCC_EA0_RDREQ_sum"], c["TCC_EA0_RDREQ_32B_sum"], c["TCC_BUBBLE_sum"]
+        return 128 * r128 + 32 * r32 + 64 * (req - r128 - r32)
+
+    def wbytes(c):
+        req, w64 = c["TCC_EA0_WRREQ_sum"], c["TCC_EA0_WRREQ_64B_sum"]
+        return 64 * w64 + 32 * (req - w64)
+
     dec = paged_decode_bf16()
     copy_bytes = kv_bytes(dec)                       # K+V rows written (and read)
     slot_bytes = 4 * int(dec.k_lens.sum())
-    cal = [i for i, (k, v) in write.items()
-           if "kv_store_kernel" in k and abs(v * 1024 - copy_bytes) < 0.01 * copy_bytes]
+    # the copy: every run's pool-filling kv_store_paged launches
+    cal = []
+    for key, (rd, wr) in runs.items():
+        if isinstance(key, tuple):
+            cal += [(rd[i], wr[i]) for i, c in wr.items() if "kv_store_kernel" in c["kernel"] and i in rd
+                    and abs(wbytes(c) - copy_bytes) < 0.05 * copy_bytes]
     if not cal:
         raise SystemExit("no full-pool kv_store_paged dispatch found for calibration")
-    f_kib = sum(fetch[i][1] for i in cal) / len(cal)
-    w_kib = sum(write[i][1] for i in cal) / len(cal)
-    read_factor = (copy_bytes + slot_bytes) / (f_kib * 1024)
-    write_factor = copy_bytes / (w_kib * 1024)
+    cr = sum(rbytes(r) for r, _ in cal) / len(cal)
+    cw = sum(wbytes(w) for _, w in cal) / len(cal)
+    read_factor = (copy_bytes + slot_bytes) / cr
+    write_factor = copy_bytes / cw
+
+    def mean(rows, ids, key):
+        return sum(rows[i][key] for i in ids) / len(ids)
+
+    def cal_mean(key):
+        return sum(r[key] for r, _ in cal) / len(cal)
+
     out = {"_calibration": {
         "copy": f"kv_store_paged of all {int(dec.k_lens.sum())} context rows of paged_decode_bf16",
         "copy_read_bytes": copy_bytes + slot_bytes, "copy_write_bytes": copy_bytes,
-        "fetch_kib": round(f_kib, 3), "write_kib": round(w_kib, 3),
-        "read_factor": round(read_factor, 5), "write_factor": round(write_factor, 5),
+        "counted_read_bytes": round(cr), "counted_write_bytes": round(cw),
+        "read_requests": round(cal_mean("TCC_EA0_RDREQ_sum")),
+        "read_requests_32B": round(cal_mean("TCC_EA0_RDREQ_32B_sum")),
+        "read_requests_128B": round(cal_mean("TCC_BUBBLE_sum")),
+        "known_over_counted_read": round(read_factor, 5), "known_over_counted_write": round(write_factor, 5),
         "dispatches": len(cal), "command": command}}
     for wl, (sym, src) in COUNTED.items():
-        fk = [v for k, v in fetch.values() if sym in k]
-        wk = [v for k, v in write.values() if sym in k]
-        if not fk or not wk:
+        if wl not in runs:
             continue
-        fmean, wmean = sum(fk) / len(fk), sum(wk) / len(wk)
-        out[wl] = {"kernel": sym, "kernel_src_sha": _src_sha(src), "dispatches": len(fk),
-                   "fetch_kib": round(fmean, 3), "write_kib": round(wmean, 3),
-                   "read_bytes_per_launch": round(fmean * 1024 * read_factor),
-                   "write_bytes_per_launch": round(wmean * 1024 * write_factor),
-                   "hbm_bytes_per_launch": round(fmean * 1024 * read_factor + wmean * 1024 * write_factor)}
+        rd, wr = runs[wl]
+        ids = [i for i, c in rd.items() if sym in c["kernel"] and i in wr]
+        if not ids:
+            raise SystemExit(f"{wl}: no dispatch of {sym} in its runs")
+        req = mean(rd, ids, "TCC_EA0_RDREQ_sum")
+        r_counted = sum(rbytes(rd[i]) for i in ids) / len(ids)
+        w_counted = sum(wbytes(wr[i]) for i in ids) / len(ids)
+        out[wl] = {"kernel": sym, "kernel_src_sha": _src_sha(src), "dispatches": len(ids),
+                   "read_requests": round(req),
+                   "read_requests_32B": round(mean(rd, ids, "TCC_EA0_RDREQ_32B_sum")),
+                   "read_requests_128B": round(mean(rd, ids, "TCC_BUBBLE_sum")),
+                   "read_requests_to_dram_frac": round(mean(rd, ids, "TCC_EA0_RDREQ_DRAM_sum") / max(req, 1.0), 4),
+                   "write_requests": round(mean(wr, ids, "TCC_EA0_WRREQ_sum")),
+                   "write_requests_64B": round(mean(wr, ids, "TCC_EA0_WRREQ_64B_sum")),
+                   "read_bytes_counted": round(r_counted), "write_bytes_counted": round(w_counted),
+                   "read_bytes_per_launch": round(r_counted * read_factor),
+                   "write_bytes_per_launch": round(w_counted * write_factor),
+                   "hbm_bytes_per_launch": round(r_counted * read_factor + w_counted * write_factor)}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -766,6 +818,77 @@ def cpu_baseline_prefill(batch, perm, kept, gpu_out, gpu_lse, target_s: float = 
     return base, _parity(rows, ro, rl, gpu_out[pos], gpu_lse[pos], 2e-2)
 
 
+PHASE_NAMES = ((0, "start"), (7, "lens and table staged"), (1, "block prefix"), (10, "table window"),
+               (2, "new rows stored"), (3, "split pieces streamed"), (5, "partial stores complete"),
+               (6, "merge counters"), (4, "published and merged"), (15, "end"))
+
+
+def decode_phases(args) -> None:
+    """Per-phase timestamps of the fused decode step at the decode workload:
+    the library built with the decode kernel's phase probes (libkvstore_phases.so)
+    runs GRAPH back-to-back steps from a HIP graph, rotating the replicas; after
+    each replay the probes of its last launch are read (100 MHz device clock,
+    microseconds from the first workgroup's start).  Prints one JSON line."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import attention_kv_store_amd._lib as L
+
+    lib = L.load(L.PHASES_LIB_PATH)
+    lib.kvs_phase_times.argtypes = [ctypes.c_void_p]
+    lib.kvs_phase_times.restype = ctypes.c_int
+    lib.kvs_phase_clear.argtypes = []
+    lib.kvs_phase_clear.restype = ctypes.c_int
+    import attention_kv_store_amd as kvs
+    from workloads import paged_decode_bf16
+
+    dec = paged_decode_bf16()
+    w = Workload(dec, args.replicas)
+    for i in range(8):
+        w.append_attend(i)
+    torch.cuda.synchronize()
+    graph_len = 6
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(graph_len):
+            w.append_attend(i)
+    buf = np.zeros((4096, 16), dtype=np.uint64)
+    reps = []
+    for _ in range(5):
+        if lib.kvs_phase_clear() != 0:
+            raise SystemExit("kvs_phase_clear failed")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        if lib.kvs_phase_times(buf.ctypes.data_as(ctypes.c_void_p)) != 0:
+            raise SystemExit("kvs_phase_times failed")
+        nwg = int(kvs.last_dispatch().split("grid=(")[1].split(",")[0])
+        t = buf[:nwg].astype(np.int64)
+        rel = (t - t[:, 0].min()) / 100.0
+        rel[t == 0] = np.nan
+        ph = {}
+        for k, name in PHASE_NAMES:
+            col = rel[:, k][~np.isnan(rel[:, k])]
+            if col.size:
+                ph[name] = {"n": int(col.size), "min": round(float(col.min()), 2), "p50": round(float(np.median(col)), 2),
+                            "p90": round(float(np.percentile(col, 90)), 2), "max": round(float(col.max()), 2)}
+        end = rel[:, 15]
+        late = np.argsort(np.nan_to_num(end))[-16:]
+        merging = int(np.sum((buf[:nwg, 8] & 3) > 0))
+        reps.append({"launch_us": round(e0.elapsed_time(e1) * 1e3 / graph_len, 2), "workgroups": nwg,
+                     "merging_workgroups": merging, "phases_us": ph,
+                     "latest_16_workgroups_xcd": sorted(int(x) % 8 for x in late)})
+        log(f"decode phases: {reps[-1]['launch_us']} us per launch, end p50 {ph['end']['p50']} max {ph['end']['max']}")
+    print(json.dumps({"decode_phases": {"workload": "paged_decode_bf16", "step": "attn_decode_append_paged",
+                                        "dispatch": kvs.last_dispatch(), "graph_launches": graph_len,
+                                        "replays": reps}}))
+
+
 # the prefill configurations measured: workload, device replicas rotated so
 # that the working set exceeds the 256 MB Infinity Cache, most timed steps
 PREFILL_CONFIGS = (
@@ -829,12 +952,20 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline decode and prefill workloads (no warm, graph-runner, mixed or peak "
                          "figures): the profiler runs use it so each kernel name covers one workload")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="WORKLOAD=READ_CSV,WRITE_CSV",
+                    help="write profiles/traffic_counters.json from rocprofv3 --pmc runs and exit")
+    ap.add_argument("--prefill", default=",".join(n for n, _, _ in PREFILL_CONFIGS),
+                    help="comma-separated prefill configurations to run (the profiler runs take one at a "
+                         "time where two share a kernel)")
     ap.add_argument("--counter-command", default="", help="command line recorded with --summarize-counters")
+    ap.add_argument("--decode-phases", action="store_true",
+                    help="print the decode kernel's per-phase timestamps (libkvstore_phases.so) and exit")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.counter_command)
+        summarize_counters(args.summarize_counters, args.counter_command)
+        return
+    if args.decode_phases:
+        decode_phases(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -939,7 +1070,13 @@ def main():
         # causal prefill (16 x 512), extend over a cached prefix (8 sequences),
         # one 32768-token prompt
         line["prefill"] = {}
+        chosen = [x for x in args.prefill.split(",") if x]
+        unknown = set(chosen) - {n for n, _, _ in PREFILL_CONFIGS}
+        if unknown:
+            raise SystemExit(f"unknown prefill configurations {sorted(unknown)}")
         for name, reps, cap in PREFILL_CONFIGS:
+            if name not in chosen:
+                continue
             entry, keep = prefill_line(name, reps, cap, args)
             line["prefill"][name] = entry
             prefill_outputs[name] = keep
