@@ -96,6 +96,10 @@ struct DCfg {
 };
 
 constexpr int kTblWin = kDecodeTblWin;  // most blocks in one workgroup's range (its table entries sit in LDS)
+// 16-byte table pieces a thread has in flight while staging the whole block
+// table (a small batch's at most kDecodeSmallTbl entries: 8 per thread of an
+// 8-wave workgroup)
+constexpr int kStageLoads = 8;
 // s_waitcnt immediate with vmcnt = 0 and the other counters left alone (gfx9
 // encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -1053,11 +1057,30 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
     // seqlens_k and the whole block table; wave 0 forms the block prefix with
     // one in-register scan (B <= 64)
     if constexpr (SETUP_APPEND) nr = wv.append_fetch(w, nwg);
-    const int nt = B * p.MB;
-    for (int c = tid; c < (nt >> 2); c += nthr) st16(tbl + 4 * c, ld16(p.table + 4 * c));
+    const int L = wave == 0 && lane < B ? p.lens_k[lane] : 0;
+    // the table in 16-byte pieces, kStageLoads per thread issued before any is
+    // written (a write right after its own load would wait for that load,
+    // making the staging one round trip per piece)
+    const int nt = B * p.MB, nch = nt >> 2;
+    auto stage = [&](int c0) __attribute__((always_inline)) {
+      u32x4 v[kStageLoads];
+#pragma unroll
+      for (int k = 0; k < kStageLoads; ++k) {   // unconditional: pieces past the end re-read the last one
+        const int c = c0 + k * nthr + tid;
+        v[k] = ld16(p.table + 4 * min(c, nch - 1));
+      }
+#pragma unroll
+      for (int k = 0; k < kStageLoads; ++k) {
+        const int c = c0 + k * nthr + tid;
+        if (c < nch) st16(tbl + 4 * c, v[k]);
+      }
+    };
+    // the first batch outside any loop, so its loads are issued right behind
+    // the length load (a loop would first wait for the loads before it)
+    if (nch > 0) stage(0);
+    for (int c0 = kStageLoads * nthr; c0 < nch; c0 += kStageLoads * nthr) stage(c0);
     for (int i = (nt & ~3) + tid; i < nt; i += nthr) tbl[i] = p.table[i];
     if (wave == 0) {
-      const int L = lane < B ? p.lens_k[lane] : 0;
       const int nb = seq_blocks(L, win);
       const int x = wave_inclusive_sum(nb);
       if (lane < B) {
