@@ -367,7 +367,7 @@ struct DecodeWave : DecodeRope<ROPE> {
       for (int i = 0; i < C::KI; ++i) {
         const E* ka = kblk + col * tok_stride + i * 32 + grp * 8;
         if constexpr (SUB) ka = key0 + col == kl ? kn + i * 32 + grp * 8 : ka;
-        bf.k[j][i] = ld16(ka);
+        bf.k[j][i] = ld16_nt(ka);
       }
 #pragma unroll
       for (int it = 0; it < C::VIL; ++it) {
@@ -378,8 +378,8 @@ struct DecodeWave : DecodeRope<ROPE> {
           va0 = key0 + 2 * kp == kl ? vn + dch * 8 : va0;
           va1 = key0 + 2 * kp + 1 == kl ? vn + dch * 8 : va1;
         }
-        bf.v[j][2 * it] = ld16(va0);
-        bf.v[j][2 * it + 1] = ld16(va1);
+        bf.v[j][2 * it] = ld16_nt(va0);
+        bf.v[j][2 * it + 1] = ld16_nt(va1);
       }
     }
   }
@@ -394,17 +394,17 @@ struct DecodeWave : DecodeRope<ROPE> {
       const KE* vblk = vbase + (int64_t)phys[j] * kPage * tok_stride;
 #pragma unroll
       for (int i = 0; i < C::KI; ++i)
-        bf.k[j][i] = *reinterpret_cast<const u32x2*>(kblk + col * tok_stride + i * 32 + grp * 8);
+        bf.k[j][i] = ld8_nt(kblk + col * tok_stride + i * 32 + grp * 8);
 #pragma unroll
       for (int it = 0; it < C::VIL; ++it) {
         const int dch = (lane >> 3) + 8 * it;
-        bf.v[j][2 * it] = *reinterpret_cast<const u32x2*>(vblk + (2 * kp) * tok_stride + dch * 8);
-        bf.v[j][2 * it + 1] = *reinterpret_cast<const u32x2*>(vblk + (2 * kp + 1) * tok_stride + dch * 8);
+        bf.v[j][2 * it] = ld8_nt(vblk + (2 * kp) * tok_stride + dch * 8);
+        bf.v[j][2 * it + 1] = ld8_nt(vblk + (2 * kp + 1) * tok_stride + dch * 8);
       }
       // scales [NB, Hkv, 16]: this head's 16 keys of the block are contiguous
       const int64_t so = ((int64_t)phys[j] * p.Hkv + g) * kPage + grp * 4;
-      bf.ks[j] = *reinterpret_cast<const f32x4*>(p.k_scale + so);
-      bf.vs[j] = *reinterpret_cast<const f32x4*>(p.v_scale + so);
+      bf.ks[j] = ldf4_nt(p.k_scale + so);
+      bf.vs[j] = ldf4_nt(p.v_scale + so);
     }
   }
 

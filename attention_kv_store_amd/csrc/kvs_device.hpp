@@ -153,6 +153,19 @@ __device__ __forceinline__ u32x4 ld16_keep(const void* p, bool keep) {
   return keep ? v : u32x4{0, 0, 0, 0};
 }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Non-temporal (streaming) loads, for K / V bytes that a decode launch reads
+// exactly once: they carry the nt cache policy, which tells the caches not to
+// keep the lines; the decode stream runs faster with them than with default
+// loads.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 ld8_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ f32x4 ldf4_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
 
 // Map a linear workgroup id so that each of the 8 XCDs (which receive
 // workgroups round-robin) walks one contiguous range of the logical order;
