@@ -56,8 +56,12 @@ struct PCfg {
   static constexpr int ESZ = BF16 ? 2 : 4;    // element bytes
   // bf16: K and V tiles are row-major without padding, filled by 16-byte
   // global-to-LDS copies; the 16-byte chunks of a row are XOR-swizzled by key
-  // so that the score-operand reads and the transposing V reads hit distinct
-  // banks.  fp32: padded rows written from registers.
+  // so that the lanes of one LDS read hit distinct banks: a score-operand
+  // read (16 bytes per lane, 16 lanes a cycle) takes 16 different chunks of
+  // 16 rows; a transposing V read (8 bytes per lane, 32 lanes a cycle) takes
+  // 4 chunks of each of 4 rows, which the V swizzle moves to 16 different
+  // chunks (rows are 64 banks wide at D = 128, so without it the 4 rows would
+  // share 32 banks).  fp32: padded rows written from registers.
   static constexpr int KROW = BF16 ? D * 2 : D * 4 + 16;   // bytes per K row in LDS
   static constexpr int VROW = BF16 ? D * 2 : D * 4 + 16;   // bytes per V row in LDS
   static constexpr int KTILE = BN * KROW;
@@ -71,7 +75,7 @@ struct PCfg {
   static constexpr int NDB = D / 32;           // 32-wide d blocks of the output
   // bf16 chunk slot of logical chunk c of key row `key`: c ^ swizzle(key)
   __host__ __device__ static constexpr int kswz(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
-  __host__ __device__ static constexpr int vswz(int key) { return D == 128 ? ((key & 3) << 1) : (key & 2); }
+  __host__ __device__ static constexpr int vswz(int key) { return D == 128 ? ((key & 3) << 2) : ((key & 2) << 1); }
 };
 static_assert(PCfg<128, true>::STAGE == 32768 && PCfg<64, true>::STAGE == 16384 &&
                   PCfg<128, false>::STAGE == 2 * 32 * (128 * 4 + 16),
@@ -462,7 +466,9 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
   // bf16 transposing V reads: lane (16-lane group g16, i = lane % 16) reads
   // the 8-byte row of key  base + 4 * (g16 / 2) + i / 4  and d  32 db +
   // 16 (g16 % 2) + 4 (i % 4); the group then holds V^T for 16 d x 4 keys.
-  // The key base is a multiple of 4, so the row's swizzle depends on i / 4.
+  // The key base is a multiple of 4, so the row's swizzle depends on i / 4
+  // (each of the 4 rows a 16-lane group reads lands in its own quarter of the
+  // 64 banks).
   const int tr_i = lane & 15, tr_g = lane >> 4;
   const int tr_row = (4 * (tr_g >> 1) + (tr_i >> 2)) * C::VROW + (tr_i & 1) * 8;
   const int tr_c = 2 * (tr_g & 1) + ((tr_i & 3) >> 1), tr_sw = C::vswz(tr_i >> 2);
