@@ -838,6 +838,33 @@ struct DecodeWave : DecodeRope<ROPE> {
     if (grp == 0) atomic_st(p.part_lse + prow, lse2);
   }
 
+  // A split piece that finishes while the range's other split piece is still
+  // to be streamed is held in registers and stored with that one: a store in
+  // the middle of the stream would hold up the loads after it (they retire
+  // in order with it), for a full write round trip.
+  f32x4 ho[C::NDB];
+  float hlse;
+  uint32_t hslot;
+  __device__ __forceinline__ void hold_partial(int slot) {
+    float inv;
+    hlse = finish(&inv);
+    hslot = (uint32_t)slot;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) ho[db] = f32x4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+  }
+  __device__ __forceinline__ void store_held() {
+    if (!head_ok) return;
+    const uint32_t prow = hslot * (uint32_t)p.Hq + (uint32_t)h;
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(p.part_o, part_bytes());
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const u32x4 v = {__float_as_uint(ho[db][0]), __float_as_uint(ho[db][1]), __float_as_uint(ho[db][2]),
+                       __float_as_uint(ho[db][3])};
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (prow * D + db * 16 + grp * 4) * 4, 0, kDeviceScope);
+    }
+    if (grp == 0) atomic_st(p.part_lse + prow, hlse);
+  }
+
   // ---- merge of split sequences ---------------------------------------------
   // The pieces of sequence b (query row b, blocks [sb0, sb1) on the flattened
   // axis) are the partial slots w + b of the workgroups w whose ranges meet
@@ -1251,7 +1278,10 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
     if (a == s0 && z == s1) {
       wv.store_final(st.t);
     } else {
-      wv.store_partial(w + st.b);
+      // the first split piece is held and stored with the second (see
+      // hold_partial); publish stores it if no second one comes
+      if (split_b0 < 0) wv.hold_partial(w + st.b);
+      else wv.store_partial(w + st.b);
       if (split_b0 < 0) {
         split_b0 = st.b;
         split_n0 = z - a;
@@ -1265,6 +1295,7 @@ __device__ __forceinline__ void decode_body(AttnParams p, const int w, const int
   // head); the wave that completes a count merges that sequence's pieces.
   auto publish = [&]() __attribute__((always_inline)) {
     if (split_b0 < 0) return;
+    wv.store_held();
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's partial stores are complete
     KVS_PHASE(kPhaseStores);
     // lane 0 counts the first split sequence, lane 1 the second: one atomic
