@@ -267,7 +267,7 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
       const int tlast = min(tile * TW + TW, Lq) - 1;
       it.b = b;
       it.hgrp = hgrp;
-      it.kvh = (hgrp * p.HW) / p.G;   // HW divides G: one KV head per item
+      it.kvh = __builtin_amdgcn_readfirstlane((hgrp * p.HW) / p.G);   // HW divides G: one KV head per item
       it.tile = tile;
       it.q0 = q0;
       it.Lq = Lq;
@@ -346,8 +346,9 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
       const int pch = j * 64 + lane;            // chunk of the wave's keys
       const int slot = pch % C::CPR;
       const int key = wave * C::KPW + pch / C::CPR;   // key row in the tile
-      kpo[j] = (uint32_t)((key & 15) * (int)kv_tok_stride + (slot ^ C::kswz(key)) * 8);
-      vpo[j] = (uint32_t)((key & 15) * (int)kv_tok_stride + (slot ^ C::vswz(key)) * 8);
+      // byte offsets for bf16 rows, element (= code byte) offsets for FP8 / INT8
+      kpo[j] = (uint32_t)((key & 15) * (int)kv_tok_stride + (slot ^ C::kswz(key)) * 8) * (KV8 ? 1u : 2u);
+      vpo[j] = (uint32_t)((key & 15) * (int)kv_tok_stride + (slot ^ C::vswz(key)) * 8) * (KV8 ? 1u : 2u);
     }
   }
   // K/V of step s: bf16 -> 16-byte global-to-LDS copies straight into stage
@@ -380,28 +381,41 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
       // this wave's page of the tile (block 0 past the sequence's last page)
       const int pgi = (wave * C::KPW) >> 4;
       const int pk = s.t * C::NPG + pgi < s.it.npages ? __builtin_amdgcn_readlane(pgv, pgi) : 0;
-      const E* kpage = kbase + pk * page_stride;
-      const E* vpage = vbase + pk * page_stride;
+      // the page's base is wave-uniform and each lane adds a fixed 32-bit
+      // byte offset (the scalar-base form of the copy: no per-lane 64-bit
+      // address arithmetic)
+      const char* kpage = reinterpret_cast<const char*>(kbase + pk * page_stride);
+      const char* vpage = reinterpret_cast<const char*>(vbase + pk * page_stride);
       const int kv0 = s.t * C::BN;
       // keys at or past nkeys (only in an item's last tile) and keys before
       // klo (only in its first tiles) copy the zero row
       bool edge = kv0 + wave * C::KPW + C::KPW > s.it.nkeys;   // uniform
       if constexpr (WIN) edge = edge || kv0 + wave * C::KPW < s.it.klo;
-      const E* zero = reinterpret_cast<const E*>(g_zero_row);
+      if (!edge) {
 #pragma unroll
-      for (int j = 0; j < C::KIT; ++j) {
-        const int blk = wave * C::KIT + j;   // 1 KiB block of each tile
-        const E* ks = kpage + kpo[j];
-        const E* vs = vpage + vpo[j];
-        if (edge) {
+        for (int j = 0; j < C::KIT; ++j) {
+          const int blk = wave * C::KIT + j;   // 1 KiB block of each tile
+          // (the empty asm keeps each offset a 32-bit value next to its use, so
+          // the copy takes the scalar-base form)
+          uint32_t ko = kpo[j], vo = vpo[j];
+          asm volatile("" : "+v"(ko), "+v"(vo));
+          copy16_to_lds(kpage + ko, Kd + blk * 1024);
+          copy16_to_lds(vpage + vo, Vd + blk * 1024);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // (keeps this path's copies apart from the edge path's)
+      } else {
+        const char* zero = reinterpret_cast<const char*>(g_zero_row);
+#pragma unroll
+        for (int j = 0; j < C::KIT; ++j) {
+          const int blk = wave * C::KIT + j;
           const int key = wave * C::KPW + (j * 64 + lane) / C::CPR;
           const bool live = kv0 + key < s.it.nkeys && (!WIN || kv0 + key >= s.it.klo);
           const int slot = (j * 64 + lane) % C::CPR;
-          ks = live ? ks : zero + (slot ^ C::kswz(key)) * 8;
-          vs = live ? vs : zero + (slot ^ C::vswz(key)) * 8;
+          const char* ks = live ? kpage + kpo[j] : zero + (slot ^ C::kswz(key)) * 16;
+          const char* vs = live ? vpage + vpo[j] : zero + (slot ^ C::vswz(key)) * 16;
+          copy16_to_lds(ks, Kd + blk * 1024);
+          copy16_to_lds(vs, Vd + blk * 1024);
         }
-        copy16_to_lds(ks, Kd + blk * 1024);
-        copy16_to_lds(vs, Vd + blk * 1024);
       }
     } else {
       int pg[C::NPG];
@@ -703,6 +717,20 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
         }
       }
       l_run += lsum;
+      // bf16: P rounded to bf16 (nearest even), the B operand of the PV MFMAs
+      u32x4 pk[BF16 ? NKB : 1][2];
+      if constexpr (BF16) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            pk[kb][pp] = u32x4{pack_bf16x2(s[kb][8 * pp + 0], s[kb][8 * pp + 1]),
+                               pack_bf16x2(s[kb][8 * pp + 2], s[kb][8 * pp + 3]),
+                               pack_bf16x2(s[kb][8 * pp + 4], s[kb][8 * pp + 5]),
+                               pack_bf16x2(s[kb][8 * pp + 6], s[kb][8 * pp + 7])};
+          }
+        }
+      }
 
       // O^T += V^T . P^T
 #pragma unroll
@@ -710,10 +738,7 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
         if constexpr (BF16) {
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
-            const u32x4 pb = {pack_bf16x2(s[kb][8 * pp + 0], s[kb][8 * pp + 1]),
-                              pack_bf16x2(s[kb][8 * pp + 2], s[kb][8 * pp + 3]),
-                              pack_bf16x2(s[kb][8 * pp + 4], s[kb][8 * pp + 5]),
-                              pack_bf16x2(s[kb][8 * pp + 6], s[kb][8 * pp + 7])};
+            const u32x4 pb = pk[kb][pp];
             // k slot e of this MFMA is key kb*32 + 16 pp + 4 hh + (e % 4) + 8 (e / 4):
             // two transposing reads, keys +0..3 and +8..11 of the lane's group
             const char* vk = Vs + (kb * 32 + 16 * pp) * C::VROW + tr_row;
