@@ -702,6 +702,26 @@ def environment():
                                     text=True, timeout=10).stdout.strip() or None
     except (OSError, subprocess.SubprocessError):
         env["git"] = None
+    # where the repository travels without its history: a hash of the sources
+    # the library is built from
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "attention_kv_store_amd", "csrc"), os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    env["src_sha"] = h.hexdigest()[:16]
+    try:
+        with open("/proc/cpuinfo") as fh:
+            env["host_cpu"] = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        env["host_cpu"] = None
+    # the clocks the system management tool reports (None where it is absent)
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values())) if r.returncode == 0 and r.stdout.strip() else None
+        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()} if isinstance(card, dict) else None
+    except (OSError, subprocess.SubprocessError, ValueError, StopIteration):
+        env["clocks"] = None
     return env
 
 
@@ -726,15 +746,34 @@ def _blas_threads() -> int:
     return int(max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1]))
 
 
-def _parity(rows, ref_out, ref_lse, gpu_out, gpu_lse, tol):
-    """max-abs error of the GPU's timed outputs against the oracle on `rows`."""
+def _parity(rows, ref_out, ref_lse, gpu_out, gpu_lse, tol, batch=None):
+    """Error of the GPU's timed outputs against the oracle on `rows`: max-abs
+    on out and lse (the pass criterion), and for out also the mean-abs error,
+    the relative L2 error, the cosine similarity and, with `batch`, the
+    max-abs error per band of visible keys (the long-context error growth
+    check)."""
     import numpy as np
 
-    eo = float(np.max(np.abs(gpu_out - ref_out[rows])))
+    ref = ref_out[rows]
+    d = gpu_out - ref
+    eo = float(np.max(np.abs(d)))
     el = float(np.max(np.abs(gpu_lse - ref_lse[rows])))
     finite = bool(np.isfinite(gpu_out).all() and np.isfinite(gpu_lse).all())
-    return {"rows": int(len(rows)), "max_abs_out": eo, "max_abs_lse": el, "tol": tol,
-            "ok": bool(finite and eo <= tol and el <= tol)}
+    res = {"rows": int(len(rows)), "max_abs_out": eo, "max_abs_lse": el, "tol": tol,
+           "ok": bool(finite and eo <= tol and el <= tol),
+           "mean_abs_out": float(np.mean(np.abs(d))),
+           "rel_l2_out": float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)),
+           "cosine_out": float(np.sum(gpu_out * ref) / max(np.linalg.norm(gpu_out) * np.linalg.norm(ref), 1e-300))}
+    if batch is not None:
+        vis = visible_keys(batch, np.asarray(rows))
+        per_row = np.max(np.abs(d).reshape(len(rows), -1), axis=1)
+        bands = {}
+        for lo, hi in ((1, 256), (256, 1024), (1024, 4096), (4096, 16384), (16384, 1 << 31)):
+            sel = (vis >= lo) & (vis < hi)
+            if sel.any():
+                bands[f"{lo}-{hi - 1 if hi < (1 << 31) else 'max'}"] = float(per_row[sel].max())
+        res["max_abs_out_by_visible_keys"] = bands
+    return res
 
 
 def cpu_baseline(batch, gpu_out, gpu_lse, target_s: float = 10.0):
@@ -760,7 +799,7 @@ def cpu_baseline(batch, gpu_out, gpu_lse, target_s: float = 10.0):
             "sample": f"whole {batch.name} batch ({batch.T} rows, all heads), {n} calls in {t:.1f} s, "
                       f"numpy float64 with BLAS threads={cores}; {np.__version__}"}
     rows = np.arange(batch.T)
-    return base, _parity(rows, ro, rl, gpu_out, gpu_lse, 2e-2)
+    return base, _parity(rows, ro, rl, gpu_out, gpu_lse, 2e-2, batch)
 
 
 def visible_keys(batch, rows):
@@ -815,7 +854,7 @@ def cpu_baseline_prefill(batch, perm, kept, gpu_out, gpu_lse, target_s: float = 
                       f"{batch.Hq} heads, {fl / 1e9:.1f} GFLOP in {t2:.1f} s, numpy float64 with BLAS "
                       f"threads={cores}; {np.__version__}"}
     pos = np.searchsorted(kept, rows)
-    return base, _parity(rows, ro, rl, gpu_out[pos], gpu_lse[pos], 2e-2)
+    return base, _parity(rows, ro, rl, gpu_out[pos], gpu_lse[pos], 2e-2, batch)
 
 
 PHASE_NAMES = ((0, "start"), (7, "lens and table staged"), (1, "block prefix"), (10, "table window"),
