@@ -164,8 +164,14 @@ inline size_t prefill_stage_bytes(int D, bool bf16) {
   // bf16: 64-key K and V tiles, unpadded rows; fp32: 32-key tiles, rows padded by 16 bytes
   return bf16 ? (size_t)2 * 64 * D * 2 : (size_t)2 * 32 * (D * 4 + 16);
 }
+// Prefill item order by decreasing work: batches of at most kSortB sequences
+// whose workgroups have at most kSortRounds items each; the items of each
+// round (pair and token tile) sit in LDS after the staged metadata.
+constexpr int kSortB = 64;
+constexpr int kSortRounds = 64;
 inline size_t prefill_lds_bytes(int D, bool bf16, int B, int meta_lds) {
-  return 2 * prefill_stage_bytes(D, bf16) + (meta_lds ? (size_t)(2 * B + 1) * sizeof(int) : 0);
+  const size_t meta = (size_t)(2 * B + 1) + (B <= kSortB ? 2 * kSortRounds : 0);
+  return 2 * prefill_stage_bytes(D, bf16) + (meta_lds ? meta * sizeof(int) : 0);
 }
 
 // Device-side precondition check (debug library only): cu_seqlens_q (null:

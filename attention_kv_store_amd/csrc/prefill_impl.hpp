@@ -210,6 +210,87 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
   while ((1u << nt_l) < (uint32_t)NT && nt_l < 31) ++nt_l;
   const uint32_t nt_m = (uint32_t)((((uint64_t)1) << (32 + nt_l)) / (uint32_t)max(NT, 1) - (((uint64_t)1) << 32) + 1);
 
+  // ---- heaviest items first (small batches of unequal sequences) ----------
+  // The order above hands every workgroup the same number of items, which
+  // balances the work when the sequences are alike.  When they differ (an
+  // extend batch: prompts and cached prefixes of many lengths) it does not:
+  // rounds pass over tiles a shorter sequence lacks, and a round takes a few
+  // workgroups to items many times heavier than the rest.  Then this XCD's
+  // items are ranked by decreasing key tiles (ties: sequence, head group,
+  // token tile from the last) and dealt in the same snake order.  Lane b
+  // holds sequence b, and A(c), the number of items of c or more key tiles,
+  // is a wave sum of closed forms, so the item of rank v is found by a
+  // binary search over c and a prefix sum over the sequences of level c.
+  // Each wave finds every NW-th round's item; the list sits in LDS.
+  int* s_pair = s_lk + B;                 // [kSortRounds] pair b * NHG + hgrp of round r, -1: none
+  int* s_tile = s_pair + kSortRounds;     // [kSortRounds] its token tile
+  bool sorted = false;
+  int nrounds_s = 0;
+  if (!WIN && staged && p.items32 && B <= kSortB) {
+    int sLq = 0, sCached = 0, sNT = 0, sMult = 0, sH0 = 0, sLk = 0;
+    if (lane < B) {
+      const int q0 = s_cq[lane], q1 = s_cq[lane + 1];
+      sLk = s_lk[lane];
+      sLq = q1 - q0;
+      sCached = sLk - sLq;
+      sNT = (p.mixed && sLq == 1) ? 0 : (sLq + TW - 1) >> tw_shift;
+      sH0 = ((xcd - (lane * p.NHG) % X) % X + X) % X;   // first head group of sequence `lane` on this XCD
+      sMult = (sNT > 0 && sH0 < p.NHG) ? (p.NHG - 1 - sH0) / X + 1 : 0;
+    }
+    // the same shape for every sequence with items: the order above is as good
+    const float big = 3.0e9f;
+    const float lq_lo = -wave_max(sNT > 0 ? -(float)sLq : -big), lq_hi = wave_max(sNT > 0 ? (float)sLq : -big);
+    const float c_lo = -wave_max(sNT > 0 ? -(float)sCached : -big), c_hi = wave_max(sNT > 0 ? (float)sCached : -big);
+    const int kmax = (int)wave_max(sNT > 0 ? (float)((sLk + C::BN - 1) / C::BN) : 0.f);
+    // first token tile of sequence `lane` whose items see more than (c - 1) * BN keys
+    auto first_tile = [&](int c) __attribute__((always_inline)) {
+      const int keys = C::BN * (c - 1);
+      if (!p.causal) return sLk > keys ? 0 : sNT;
+      const int need = keys - sCached + 1;   // rows the item must reach
+      return need > sLq ? sNT : (need <= 0 ? 0 : ((need + TW - 1) >> tw_shift) - 1);
+    };
+    auto wave_total = [&](int x) __attribute__((always_inline)) {
+      return __builtin_amdgcn_readlane(wave_inclusive_sum(x), 63);
+    };
+    auto items_from_level = [&](int c) __attribute__((always_inline)) { return wave_total(sMult * (sNT - first_tile(c))); };
+    const int nx = items_from_level(1);
+    nrounds_s = (nx + GX - 1) / GX;
+    sorted = (lq_lo != lq_hi || c_lo != c_hi) && nrounds_s <= kSortRounds;
+    if (sorted) {
+      for (int r = wave; r < nrounds_s; r += NW) {
+        const int v = r * GX + ((r & 1) ? GX - 1 - wi : wi);
+        int pair = -1, tile = 0;
+        if (v < nx) {
+          int lo = 1, hi = kmax + 1;   // items_from_level(lo) > v >= items_from_level(hi)
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (items_from_level(mid) > v) lo = mid;
+            else hi = mid;
+          }
+          const int f1 = first_tile(lo + 1), nb = f1 - first_tile(lo);
+          const int cnt = sMult * nb;
+          const int incl = wave_inclusive_sum(cnt);
+          const int o = v - items_from_level(lo + 1);   // rank within level lo
+          const uint64_t hit = __ballot(cnt > 0 && incl - cnt <= o && o < incl);   // one lane, as 0 <= o < incl(63)
+          if (hit != 0) {
+            const int L = (int)__builtin_ctzll(hit);   // the sequence holding it
+            const int j = o - (__builtin_amdgcn_readlane(incl, L) - __builtin_amdgcn_readlane(cnt, L));
+            const int nbL = __builtin_amdgcn_readlane(nb, L);
+            pair = L * p.NHG + __builtin_amdgcn_readlane(sH0, L) + (j / nbL) * X;
+            tile = __builtin_amdgcn_readlane(f1, L) - 1 - j % nbL;
+          }
+        }
+        if (lane == 0) {
+          s_pair[r] = pair;
+          s_tile[r] = tile;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  sorted = __builtin_amdgcn_readfirstlane((int)sorted) != 0;
+  const int64_t nrounds_all = sorted ? nrounds_s : nrounds;
+
   // ---- items --------------------------------------------------------------
   struct Item {
     int r;             // round of this workgroup's item sequence (nrounds: none)
@@ -235,9 +316,16 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
   auto item_from = [&](int r) __attribute__((always_inline)) {
     Item it;
     it.ntiles = 0;
-    for (; r < nrounds; ++r) {
+    for (; r < nrounds_all; ++r) {
       int tile, b, hgrp;
-      if (p.items32) {
+      if (sorted) {
+        const int pair = __builtin_amdgcn_readfirstlane(s_pair[r]);
+        if (pair < 0) continue;
+        tile = __builtin_amdgcn_readfirstlane(s_tile[r]);
+        const uint32_t bq = (__umulhi((uint32_t)pair, p.nhg_m) + (uint32_t)pair) >> p.nhg_l;
+        b = (int)bq;
+        hgrp = pair - (int)bq * p.NHG;
+      } else if (p.items32) {
         // this XCD's item v (< 2^31): local pair v / NT, tile counted down
         const int64_t v64 = (int64_t)r * GX + ((r & 1) ? GX - 1 - wi : wi);
         if (v64 >= NIx) continue;
