@@ -688,20 +688,56 @@ def measure_peaks():
                    f"{wgs} workgroups x 4 waves x 4 chains x {iters} MFMAs, no memory traffic"}
 
 
+def _git_head():
+    """The checked-out commit, read from .git without running git (None where
+    the tree travels without its history)."""
+    try:
+        with open(os.path.join(ROOT, ".git", "HEAD")) as fh:
+            head = fh.read().strip()
+        if head.startswith("ref: "):
+            ref = head[5:]
+            path = os.path.join(ROOT, ".git", ref)
+            if os.path.exists(path):
+                with open(path) as fh:
+                    return fh.read().strip()[:7]
+            with open(os.path.join(ROOT, ".git", "packed-refs")) as fh:
+                return next((l.split()[0][:7] for l in fh if l.rstrip().endswith(" " + ref)), None)
+        return head[:7] or None
+    except (OSError, IndexError):
+        return None
+
+
+def _dpm_clocks():
+    """The current DPM level of each clock domain the GPU's sysfs lists
+    (pp_dpm_sclk, _mclk, _fclk, _socclk: the line marked '*'), or None.  Read
+    from files: no program is started, which a process that has set up the
+    GPU must not do."""
+    out = {}
+    try:
+        cards = sorted(d for d in os.listdir("/sys/class/drm") if d.startswith("card") and d[4:].isdigit())
+    except OSError:
+        return None
+    for card in cards:
+        dev = os.path.join("/sys/class/drm", card, "device")
+        for dom in ("sclk", "mclk", "fclk", "socclk"):
+            try:
+                with open(os.path.join(dev, "pp_dpm_" + dom)) as fh:
+                    cur = next((l.split(":", 1)[1].replace("*", "").strip() for l in fh if "*" in l), None)
+            except (OSError, IndexError):
+                continue
+            if cur:
+                out.setdefault(card, {})[dom] = cur
+    return out or None
+
+
 def environment():
     import platform
-    import subprocess
 
     import torch
 
     env = {"device": torch.cuda.get_device_name(0), "torch": torch.__version__,
            "hip": getattr(torch.version, "hip", None), "host": platform.node(),
-           "host_cpus": len(os.sched_getaffinity(0))}
-    try:
-        env["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
-                                    text=True, timeout=10).stdout.strip() or None
-    except (OSError, subprocess.SubprocessError):
-        env["git"] = None
+           "host_cpus": len(os.sched_getaffinity(0)), "git": _git_head()}
     # where the repository travels without its history: a hash of the sources
     # the library is built from
     h = hashlib.sha256()
@@ -715,13 +751,7 @@ def environment():
             env["host_cpu"] = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
     except OSError:
         env["host_cpu"] = None
-    # the clocks the system management tool reports (None where it is absent)
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        card = next(iter(json.loads(r.stdout).values())) if r.returncode == 0 and r.stdout.strip() else None
-        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()} if isinstance(card, dict) else None
-    except (OSError, subprocess.SubprocessError, ValueError, StopIteration):
-        env["clocks"] = None
+    env["clocks"] = _dpm_clocks()
     return env
 
 

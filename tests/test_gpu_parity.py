@@ -179,6 +179,44 @@ def test_prefill_many_sequences(B):
     _check(b, out, lse)
 
 
+_ORDER_CASES = {
+    # name: (B, rows range, cached range, Hq, Hkv, D, dtype, causal); rows drawn per sequence
+    "b64_causal": (64, (1, 200), (0, 300), 8, 2, 64, "bf16", True),
+    "b65_causal": (65, (1, 200), (0, 300), 8, 2, 64, "bf16", True),
+    "b64_noncausal": (64, (1, 120), (0, 200), 8, 2, 64, "bf16", False),
+    "fp32_one_head_group": (20, (1, 150), (0, 400), 4, 4, 128, "fp32", True),
+    "six_head_groups": (24, (1, 160), (0, 250), 6, 2, 64, "bf16", True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_ORDER_CASES) + ["same_rows_other_prefixes", "one_long_prefix", "with_decode_rows"])
+def test_prefill_heaviest_first_order(case):
+    """Small batches (up to 64 sequences) of unequal sequences take their
+    items heaviest first, ranked in-kernel from the staged lengths; 65
+    sequences, or sequences all of one shape, keep the plain order.  Head
+    groups fewer than the XCDs, one-row sequences of a mixed launch and a
+    long cached prefix (many key-tile levels) included; every row against
+    the oracle."""
+    if case in _ORDER_CASES:
+        B, (qa, qb), (ca, cb), Hq, Hkv, D, dtype, causal = _ORDER_CASES[case]
+        rng = np.random.default_rng(900 + B + Hq)
+        q = [int(x) for x in rng.integers(qa, qb + 1, size=B)]
+        k = [a + int(x) for a, x in zip(q, rng.integers(ca, cb + 1, size=B))]
+    elif case == "same_rows_other_prefixes":
+        q, k = [64] * 12, [64 + 37 * i for i in range(12)]
+        Hq, Hkv, D, dtype, causal = 8, 2, 128, "bf16", True
+    elif case == "one_long_prefix":
+        q, k = [100, 17, 400, 2, 64], [8100, 17, 3400, 72, 64]
+        Hq, Hkv, D, dtype, causal = 8, 2, 64, "bf16", True
+    else:
+        q = [1, 90, 1, 1, 33, 1, 250, 1, 7, 1]
+        k = [300, 90, 17, 1000, 100, 64, 700, 5, 7, 2000]
+        Hq, Hkv, D, dtype, causal = 8, 2, 64, "bf16", True
+    b = _mk(950, q, k, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, causal=causal, name=f"order-{case}")
+    out, lse = _run(b)
+    _check(b, out, lse)
+
+
 # --------------------------------------------------------------- decode ---
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
