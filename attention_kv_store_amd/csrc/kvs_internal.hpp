@@ -167,7 +167,7 @@ inline size_t prefill_stage_bytes(int D, bool bf16) {
 // Prefill item order by decreasing work: batches of at most kSortB sequences
 // whose workgroups have at most kSortRounds items each; the items of each
 // round (pair and token tile) sit in LDS after the staged metadata.
-constexpr int kSortB = 64;
+constexpr int kSortB = 256;
 constexpr int kSortRounds = 64;
 inline size_t prefill_lds_bytes(int D, bool bf16, int B, int meta_lds) {
   const size_t meta = (size_t)(2 * B + 1) + (B <= kSortB ? 2 * kSortRounds : 0);

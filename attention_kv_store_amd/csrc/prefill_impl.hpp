@@ -217,42 +217,65 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
   // rounds pass over tiles a shorter sequence lacks, and a round takes a few
   // workgroups to items many times heavier than the rest.  Then this XCD's
   // items are ranked by decreasing key tiles (ties: sequence, head group,
-  // token tile from the last) and dealt in the same snake order.  Lane b
-  // holds sequence b, and A(c), the number of items of c or more key tiles,
-  // is a wave sum of closed forms, so the item of rank v is found by a
-  // binary search over c and a prefix sum over the sequences of level c.
+  // token tile from the last) and dealt in the same snake order.  Lane l
+  // holds sequences l, l + 64, ..., and A(c), the number of items of c or
+  // more key tiles, is a wave sum of closed forms, so the item of rank v is
+  // found by a binary search over c and a prefix sum over the sequences of
+  // level c.
   // Each wave finds every NW-th round's item; the list sits in LDS.
   int* s_pair = s_lk + B;                 // [kSortRounds] pair b * NHG + hgrp of round r, -1: none
   int* s_tile = s_pair + kSortRounds;     // [kSortRounds] its token tile
   bool sorted = false;
   int nrounds_s = 0;
   if (!WIN && staged && p.items32 && B <= kSortB) {
-    int sLq = 0, sCached = 0, sNT = 0, sMult = 0, sH0 = 0, sLk = 0;
-    if (lane < B) {
-      const int q0 = s_cq[lane], q1 = s_cq[lane + 1];
-      sLk = s_lk[lane];
-      sLq = q1 - q0;
-      sCached = sLk - sLq;
-      sNT = (p.mixed && sLq == 1) ? 0 : (sLq + TW - 1) >> tw_shift;
-      sH0 = ((xcd - (lane * p.NHG) % X) % X + X) % X;   // first head group of sequence `lane` on this XCD
-      sMult = (sNT > 0 && sH0 < p.NHG) ? (p.NHG - 1 - sH0) / X + 1 : 0;
+    constexpr int SQ = kSortB / 64;   // sequences per lane: lane + 64 q
+    const int nq = (B + 63) >> 6;      // blocks of 64 sequences in use
+    int sLq[SQ], sCached[SQ], sNT[SQ], sMult[SQ], sH0[SQ], sLk[SQ];
+    const float big = 3.0e9f;
+    float lq_lo = big, lq_hi = -big, c_lo = big, c_hi = -big, kmaxf = 0.f;
+#pragma unroll
+    for (int q = 0; q < SQ; ++q) {
+      const int b = 64 * q + lane;
+      sLq[q] = sCached[q] = sNT[q] = sMult[q] = sH0[q] = sLk[q] = 0;
+      if (b < B) {
+        sLk[q] = s_lk[b];
+        sLq[q] = s_cq[b + 1] - s_cq[b];
+        sCached[q] = sLk[q] - sLq[q];
+        sNT[q] = (p.mixed && sLq[q] == 1) ? 0 : (sLq[q] + TW - 1) >> tw_shift;
+        sH0[q] = ((xcd - (b * p.NHG) % X) % X + X) % X;   // first head group of sequence b on this XCD
+        sMult[q] = (sNT[q] > 0 && sH0[q] < p.NHG) ? (p.NHG - 1 - sH0[q]) / X + 1 : 0;
+      }
+      if (sNT[q] > 0) {
+        lq_lo = fminf(lq_lo, (float)sLq[q]);
+        lq_hi = fmaxf(lq_hi, (float)sLq[q]);
+        c_lo = fminf(c_lo, (float)sCached[q]);
+        c_hi = fmaxf(c_hi, (float)sCached[q]);
+        kmaxf = fmaxf(kmaxf, (float)((sLk[q] + C::BN - 1) / C::BN));
+      }
     }
     // the same shape for every sequence with items: the order above is as good
-    const float big = 3.0e9f;
-    const float lq_lo = -wave_max(sNT > 0 ? -(float)sLq : -big), lq_hi = wave_max(sNT > 0 ? (float)sLq : -big);
-    const float c_lo = -wave_max(sNT > 0 ? -(float)sCached : -big), c_hi = wave_max(sNT > 0 ? (float)sCached : -big);
-    const int kmax = (int)wave_max(sNT > 0 ? (float)((sLk + C::BN - 1) / C::BN) : 0.f);
-    // first token tile of sequence `lane` whose items see more than (c - 1) * BN keys
-    auto first_tile = [&](int c) __attribute__((always_inline)) {
+    lq_lo = -wave_max(-lq_lo);
+    lq_hi = wave_max(lq_hi);
+    c_lo = -wave_max(-c_lo);
+    c_hi = wave_max(c_hi);
+    const int kmax = (int)wave_max(kmaxf);
+    // first token tile of sequence 64 q + lane whose items see more than (c - 1) * BN keys
+    auto first_tile = [&](int q, int c) __attribute__((always_inline)) {
       const int keys = C::BN * (c - 1);
-      if (!p.causal) return sLk > keys ? 0 : sNT;
-      const int need = keys - sCached + 1;   // rows the item must reach
-      return need > sLq ? sNT : (need <= 0 ? 0 : ((need + TW - 1) >> tw_shift) - 1);
+      if (!p.causal) return sLk[q] > keys ? 0 : sNT[q];
+      const int need = keys - sCached[q] + 1;   // rows the item must reach
+      return need > sLq[q] ? sNT[q] : (need <= 0 ? 0 : ((need + TW - 1) >> tw_shift) - 1);
     };
     auto wave_total = [&](int x) __attribute__((always_inline)) {
       return __builtin_amdgcn_readlane(wave_inclusive_sum(x), 63);
     };
-    auto items_from_level = [&](int c) __attribute__((always_inline)) { return wave_total(sMult * (sNT - first_tile(c))); };
+    auto items_from_level = [&](int c) __attribute__((always_inline)) {
+      int x = 0;
+#pragma unroll
+      for (int q = 0; q < SQ; ++q)
+        if (q < nq) x += sMult[q] * (sNT[q] - first_tile(q, c));
+      return wave_total(x);
+    };
     const int nx = items_from_level(1);
     nrounds_s = (nx + GX - 1) / GX;
     sorted = (lq_lo != lq_hi || c_lo != c_hi) && nrounds_s <= kSortRounds;
@@ -267,17 +290,27 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
             if (items_from_level(mid) > v) lo = mid;
             else hi = mid;
           }
-          const int f1 = first_tile(lo + 1), nb = f1 - first_tile(lo);
-          const int cnt = sMult * nb;
-          const int incl = wave_inclusive_sum(cnt);
-          const int o = v - items_from_level(lo + 1);   // rank within level lo
-          const uint64_t hit = __ballot(cnt > 0 && incl - cnt <= o && o < incl);   // one lane, as 0 <= o < incl(63)
-          if (hit != 0) {
-            const int L = (int)__builtin_ctzll(hit);   // the sequence holding it
-            const int j = o - (__builtin_amdgcn_readlane(incl, L) - __builtin_amdgcn_readlane(cnt, L));
-            const int nbL = __builtin_amdgcn_readlane(nb, L);
-            pair = L * p.NHG + __builtin_amdgcn_readlane(sH0, L) + (j / nbL) * X;
-            tile = __builtin_amdgcn_readlane(f1, L) - 1 - j % nbL;
+          int o = v - items_from_level(lo + 1);   // rank within level lo, counted over the blocks in order
+#pragma unroll
+          for (int q = 0; q < SQ; ++q) {
+            if (q >= nq || pair >= 0) continue;
+            const int f1 = first_tile(q, lo + 1), nb = f1 - first_tile(q, lo);
+            const int cnt = sMult[q] * nb;
+            const int incl = wave_inclusive_sum(cnt);
+            const int tot = __builtin_amdgcn_readlane(incl, 63);
+            if (o >= tot) {
+              o -= tot;
+              continue;
+            }
+            const uint64_t hit = __ballot(cnt > 0 && incl - cnt <= o && o < incl);   // one lane, as 0 <= o < tot
+            if (hit != 0) {
+              const int L = (int)__builtin_ctzll(hit);   // sequence 64 q + L holds it
+              const int j = o - (__builtin_amdgcn_readlane(incl, L) - __builtin_amdgcn_readlane(cnt, L));
+              const int nbL = __builtin_amdgcn_readlane(nb, L);
+              pair = (64 * q + L) * p.NHG + __builtin_amdgcn_readlane(sH0[q], L) + (j / nbL) * X;
+              tile = __builtin_amdgcn_readlane(f1, L) - 1 - j % nbL;
+            }
+            o = -1;   // found (or, impossibly, no lane: none)
           }
         }
         if (lane == 0) {

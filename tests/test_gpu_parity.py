@@ -184,6 +184,9 @@ _ORDER_CASES = {
     "b64_causal": (64, (1, 200), (0, 300), 8, 2, 64, "bf16", True),
     "b65_causal": (65, (1, 200), (0, 300), 8, 2, 64, "bf16", True),
     "b64_noncausal": (64, (1, 120), (0, 200), 8, 2, 64, "bf16", False),
+    "b200_noncausal": (200, (1, 60), (0, 100), 8, 2, 64, "bf16", False),
+    "b256_causal": (256, (1, 80), (0, 150), 8, 2, 64, "bf16", True),
+    "b257_causal": (257, (1, 80), (0, 150), 8, 2, 64, "bf16", True),
     "fp32_one_head_group": (20, (1, 150), (0, 400), 4, 4, 128, "fp32", True),
     "six_head_groups": (24, (1, 160), (0, 250), 6, 2, 64, "bf16", True),
 }
@@ -191,9 +194,10 @@ _ORDER_CASES = {
 
 @pytest.mark.parametrize("case", sorted(_ORDER_CASES) + ["same_rows_other_prefixes", "one_long_prefix", "with_decode_rows"])
 def test_prefill_heaviest_first_order(case):
-    """Small batches (up to 64 sequences) of unequal sequences take their
-    items heaviest first, ranked in-kernel from the staged lengths; 65
-    sequences, or sequences all of one shape, keep the plain order.  Head
+    """Batches of up to 256 unequal sequences take their items heaviest
+    first, ranked in-kernel from the staged lengths (each lane holding
+    sequences l, l + 64, ...); 257 sequences, or sequences all of one shape,
+    keep the plain order.  Head
     groups fewer than the XCDs, one-row sequences of a mixed launch and a
     long cached prefix (many key-tile levels) included; every row against
     the oracle."""
