@@ -210,7 +210,7 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
   while ((1u << nt_l) < (uint32_t)NT && nt_l < 31) ++nt_l;
   const uint32_t nt_m = (uint32_t)((((uint64_t)1) << (32 + nt_l)) / (uint32_t)max(NT, 1) - (((uint64_t)1) << 32) + 1);
 
-  // ---- heaviest items first (small batches of unequal sequences) ----------
+  // ---- heaviest items first (up to 256 sequences of unequal shapes) -------
   // The order above hands every workgroup the same number of items, which
   // balances the work when the sequences are alike.  When they differ (an
   // extend batch: prompts and cached prefixes of many lengths) it does not:
@@ -221,8 +221,7 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
   // holds sequences l, l + 64, ..., and A(c), the number of items of c or
   // more key tiles, is a wave sum of closed forms, so the item of rank v is
   // found by a binary search over c and a prefix sum over the sequences of
-  // level c.
-  // Each wave finds every NW-th round's item; the list sits in LDS.
+  // level c.  Each wave finds every NW-th round's item; the list sits in LDS.
   int* s_pair = s_lk + B;                 // [kSortRounds] pair b * NHG + hgrp of round r, -1: none
   int* s_tile = s_pair + kSortRounds;     // [kSortRounds] its token tile
   bool sorted = false;
