@@ -24,9 +24,11 @@
 namespace kvs {
 
 // Estimated cost, in decode block-steps of one workgroup: a prefill step (a
-// 64-key tile for the workgroup's query rows) takes about two, and every item
-// about two more for its set-up and epilogue.
-constexpr float kMixPrefillStep = 2.0f;
+// 64-key tile for the workgroup's query rows) takes about 1.4, and every item
+// about two steps more for its set-up and epilogue (the weight that ended
+// both parts closest together over mixed batches of 1-8 prompts and 30-63
+// one-row sequences).
+constexpr float kMixPrefillStep = 1.4f;
 
 // NW waves per workgroup (4: two workgroups per CU; 8: one): the prefill
 // part's waves and the decode part's KV heads per workgroup.
