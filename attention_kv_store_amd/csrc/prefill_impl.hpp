@@ -222,11 +222,12 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
   // more key tiles, is a wave sum of closed forms, so the item of rank v is
   // found by a binary search over c and a prefix sum over the sequences of
   // level c.  Each wave finds every NW-th round's item; the list sits in LDS.
+  // (With a window an item's key tiles start at its window's first one.)
   int* s_pair = s_lk + B;                 // [kSortRounds] pair b * NHG + hgrp of round r, -1: none
   int* s_tile = s_pair + kSortRounds;     // [kSortRounds] its token tile
   bool sorted = false;
   int nrounds_s = 0;
-  if (!WIN && staged && p.items32 && B <= kSortB) {
+  if (staged && p.items32 && B <= kSortB) {
     constexpr int SQ = kSortB / 64;   // sequences per lane: lane + 64 q
     const int nq = (B + 63) >> 6;      // blocks of 64 sequences in use
     int sLq[SQ], sCached[SQ], sNT[SQ], sMult[SQ], sH0[SQ], sLk[SQ];
@@ -257,9 +258,15 @@ __device__ __forceinline__ void prefill_body(AttnParams p, const int G, const in
     lq_hi = wave_max(lq_hi);
     c_lo = -wave_max(-c_lo);
     c_hi = wave_max(c_hi);
-    const int kmax = (int)wave_max(kmaxf);
+    // a window: an item spans at most ceil((W + TW - 1) / BN) + 1 key tiles,
+    // so the cost is taken as min(key tiles, that): still non-decreasing over
+    // a sequence's token tiles, and the items at the cap rank as equals
+    const int wcap = WIN ? (int)min(((int64_t)p.window + TW - 1 + C::BN - 1) / C::BN + 1, (int64_t)0x7fffffff)
+                         : 0x7fffffff;
+    const int kmax = min((int)wave_max(kmaxf), wcap);
     // first token tile of sequence 64 q + lane whose items see more than (c - 1) * BN keys
     auto first_tile = [&](int q, int c) __attribute__((always_inline)) {
+      if (c > wcap) return sNT[q];   // past the cap: no item
       const int keys = C::BN * (c - 1);
       if (!p.causal) return sLk[q] > keys ? 0 : sNT[q];
       const int need = keys - sCached[q] + 1;   // rows the item must reach

@@ -192,15 +192,18 @@ _ORDER_CASES = {
 }
 
 
-@pytest.mark.parametrize("case", sorted(_ORDER_CASES) + ["same_rows_other_prefixes", "one_long_prefix", "with_decode_rows"])
+@pytest.mark.parametrize("case", sorted(_ORDER_CASES) + ["same_rows_other_prefixes", "one_long_prefix", "with_decode_rows",
+                                  "window_37", "window_300_fp32", "window_huge"])
 def test_prefill_heaviest_first_order(case):
     """Batches of up to 256 unequal sequences take their items heaviest
     first, ranked in-kernel from the staged lengths (each lane holding
     sequences l, l + 64, ...); 257 sequences, or sequences all of one shape,
     keep the plain order.  Head
     groups fewer than the XCDs, one-row sequences of a mixed launch and a
-    long cached prefix (many key-tile levels) included; every row against
-    the oracle."""
+    long cached prefix (many key-tile levels) included, and windows (the
+    cost capped at the most key tiles a window item spans); every row
+    against the oracle."""
+    window = 0
     if case in _ORDER_CASES:
         B, (qa, qb), (ca, cb), Hq, Hkv, D, dtype, causal = _ORDER_CASES[case]
         rng = np.random.default_rng(900 + B + Hq)
@@ -212,12 +215,18 @@ def test_prefill_heaviest_first_order(case):
     elif case == "one_long_prefix":
         q, k = [100, 17, 400, 2, 64], [8100, 17, 3400, 72, 64]
         Hq, Hkv, D, dtype, causal = 8, 2, 64, "bf16", True
+    elif case.startswith("window"):
+        rng = np.random.default_rng(960)
+        q = [int(x) for x in rng.integers(1, 300, size=30)]
+        k = [a + int(x) for a, x in zip(q, rng.integers(0, 700, size=30))]
+        window = {"window_37": 37, "window_300_fp32": 300, "window_huge": 2**31 - 1}[case]
+        Hq, Hkv, D, dtype, causal = 8, 2, 64, "fp32" if "fp32" in case else "bf16", True
     else:
         q = [1, 90, 1, 1, 33, 1, 250, 1, 7, 1]
         k = [300, 90, 17, 1000, 100, 64, 700, 5, 7, 2000]
         Hq, Hkv, D, dtype, causal = 8, 2, 64, "bf16", True
-    b = _mk(950, q, k, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, causal=causal, name=f"order-{case}")
-    out, lse = _run(b)
+    b = _mk(950, q, k, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, causal=causal, window=window, name=f"order-{case}")
+    out, lse = _run(b, window=window) if window else _run(b)
     _check(b, out, lse)
 
 
