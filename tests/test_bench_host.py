@@ -71,3 +71,28 @@ def test_parity_summary():
     nan = ref.copy()
     nan[0, 0, 0] = np.nan
     assert not bench._parity(rows, ref, lse, nan, lse, 1e-5)["ok"]
+
+
+def test_commit_read_from_git_files(tmp_path, monkeypatch):
+    """_git_head reads the checked-out commit from .git (loose ref, packed ref,
+    detached head) without starting git, and gives None without a .git."""
+    sha = "0123456789abcdef0123456789abcdef01234567"
+    g = tmp_path / ".git"
+    (g / "refs" / "heads").mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (g / "HEAD").write_text("ref: refs/heads/main\n")
+    (g / "refs" / "heads" / "main").write_text(sha + "\n")
+    assert bench._git_head() == sha[:7]
+    (g / "refs" / "heads" / "main").unlink()
+    (g / "packed-refs").write_text("# pack-refs with: peeled\n" + sha + " refs/heads/main\n")
+    assert bench._git_head() == sha[:7]
+    (g / "HEAD").write_text(sha + "\n")
+    assert bench._git_head() == sha[:7]
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path / "none"))
+    assert bench._git_head() is None
+
+
+def test_dpm_clocks_never_raise():
+    """The clock levels come from sysfs files (None where there are none)."""
+    c = bench._dpm_clocks()
+    assert c is None or (isinstance(c, dict) and all(isinstance(v, dict) for v in c.values()))
